@@ -1,0 +1,158 @@
+"""Pins of the oracle's factored second-moment step with update clipping
+(sd-scripts commit 7983d3d 'Fused backward pass', adafactor_step_param;
+konstmish/prodigy PR #25 'no first moment and factored second moment')."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import UNSIGNED, FHParams
+
+
+def ulp32(x):
+    x = np.abs(np.asarray(x, np.float32))
+    return (np.nextafter(x, np.float32(np.inf)) - x).astype(np.float64)
+
+
+def _bf16(x):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _state2d(R, C, w=None, seed=0):
+    n = R * C
+    if w is None:
+        hi, lo = np.zeros(n, np.uint16), np.zeros(n, np.uint16)
+    else:
+        hi, lo = oracle.split(np.ascontiguousarray(w, np.float32))
+    return oracle.TensorState(hi, lo, row=np.zeros(R, np.float32), col=np.zeros(C, np.float32))
+
+
+def _state1d(n, w=None):
+    hi, lo = (np.zeros(n, np.uint16), np.zeros(n, np.uint16)) if w is None else oracle.split(w)
+    _, _, vc, vs = oracle.zero_moments(n)
+    return oracle.TensorState(hi, lo, vc=vc, vs=vs)
+
+
+def test_rank_one_gradient_first_step_is_lr_sign_g():
+    """For g_ij = a_i b_j the factored estimate is exact, U = sign(g)/sqrt(1-b2)
+    has RMS 31.6 > 1, and clipping leaves a step of exactly lr*sign(g)."""
+    rng = np.random.default_rng(1)
+    R, C = 48, 64
+    a = rng.choice([1.0, 1.5, 2.0, 3.0], R) * rng.choice([-1, 1], R) * 2.0 ** -6
+    b = rng.choice([1.0, 1.5, 2.0, 3.0], C) * rng.choice([-1, 1], C) * 2.0 ** -5
+    g = np.outer(a, b).astype(np.float32).reshape(-1)
+    gb = _bf16(g)
+    assert np.array_equal(oracle.bf16_to_f32(gb), g)      # exact in bf16
+    hp = FHParams(lr=3.5e-6)
+    st = _state2d(R, C)
+    oracle.factored_step(st, gb, R, C, hp, 1)
+    w = oracle.join(st.hi, st.lo).astype(np.float64)
+    assert np.max(np.abs(w + hp.lr * np.sign(g)) / hp.lr) < 1e-6
+
+
+def test_one_d_first_step_is_lr_sign_g():
+    rng = np.random.default_rng(2)
+    n = 1000
+    g = _bf16(rng.standard_normal(n) * 1e-3)
+    hp = FHParams(lr=3.5e-6)
+    st = _state1d(n)
+    oracle.factored_step(st, g, 0, 0, hp, 1)
+    w = oracle.join(st.hi, st.lo).astype(np.float64)
+    gf = oracle.bf16_to_f32(g).astype(np.float64)
+    assert np.max(np.abs(w + hp.lr * np.sign(gf)) / hp.lr) < 1e-6
+
+
+@pytest.mark.parametrize("two_d", [True, False])
+def test_zero_gradient_no_nan_and_weights_identical(two_d):
+    """Zero rows/columns were the NaN case of the Prodigy thread; eps1 on g^2
+    before the means keeps every factor finite and U exactly 0."""
+    rng = np.random.default_rng(3)
+    R, C = 32, 40
+    w = (rng.standard_normal(R * C) * 0.02).astype(np.float32)
+    st = _state2d(R, C, w) if two_d else _state1d(R * C, w)
+    hi0, lo0 = st.hi.copy(), st.lo.copy()
+    g = np.zeros(R * C, np.uint16)
+    for t in range(1, 11):
+        oracle.factored_step(st, g, R if two_d else 0, C if two_d else 0, FHParams(), t)
+    assert np.array_equal(st.hi, hi0) and np.array_equal(st.lo, lo0)
+    if two_d:
+        assert np.all(np.isfinite(st.row)) and np.all(np.isfinite(st.col)) and np.all(st.row > 0)
+    else:
+        assert np.all(np.isfinite(st.vs)) and np.all(st.vs > 0)
+
+
+def test_tensor_without_gradient_is_untouched():
+    st = _state2d(8, 16, np.ones(128, np.float32))
+    before = st.copy()
+    oracle.factored_step(st, None, 8, 16, FHParams(), 1)
+    assert np.array_equal(st.hi, before.hi) and np.array_equal(st.row, before.row)
+
+
+def _dbl_factored_2d(w, g, r, c, hp: FHParams):
+    R, C = g.shape
+    q = g * g + hp.eps1
+    r = hp.beta2 * r + (1 - hp.beta2) * q.mean(axis=1)
+    c = hp.beta2 * c + (1 - hp.beta2) * q.mean(axis=0)
+    vhat = np.outer(r, c) / r.mean()                # Adafactor's factored estimate
+    U = g / np.sqrt(vhat)
+    rms = np.sqrt(np.mean(U * U))
+    U = U / max(1.0, rms / hp.clip_threshold)
+    w2 = w - hp.lr * U - hp.lr * hp.weight_decay * w
+    return w2, r, c, rms
+
+
+@pytest.mark.parametrize("preset", [0.0, 1.0])
+@pytest.mark.parametrize("wd", [0.0, 0.01])
+def test_factored_vs_double_brute_force(preset, wd):
+    """[64, 48], 10 lockstep steps, grads N(0,1e-3) with 100x outliers. preset
+    row/col EMAs of 1.0 keep RMS(U) < 1 so the clip is inactive (f = lr)."""
+    rng = np.random.default_rng(4)
+    R, C = 64, 48
+    hp = FHParams(lr=3.5e-6, weight_decay=wd)
+    st = _state2d(R, C, (rng.standard_normal(R * C) * 0.02).astype(np.float32))
+    st.row[:] = preset
+    st.col[:] = preset
+    clipped = []
+    for t in range(1, 11):
+        gf = rng.standard_normal(R * C) * 1e-3
+        gf[rng.random(R * C) < 0.01] *= 100
+        g = _bf16(gf)
+        w = oracle.join(st.hi, st.lo).astype(np.float64)
+        gd = oracle.bf16_to_f32(g).astype(np.float64).reshape(R, C)
+        w2, r, c, rms = _dbl_factored_2d(w.reshape(R, C), gd, st.row.astype(np.float64),
+                                         st.col.astype(np.float64), hp)
+        clipped.append(rms > 1)
+        oracle.factored_step(st, g, R, C, hp, t)
+        assert np.allclose(st.row, r, rtol=1e-6, atol=0) and np.allclose(st.col, c, rtol=1e-6, atol=0)
+        wo = oracle.join(st.hi, st.lo).astype(np.float64)
+        w2 = w2.reshape(-1)
+        du = np.abs(w2 - w)
+        assert np.all(np.abs(wo - w2) <= 2 * ulp32(w2) + 1e-5 * du), t
+    assert all(clipped) if preset == 0.0 else not any(clipped)
+
+
+def test_one_d_vs_double_brute_force():
+    """Unfactored 1-D path with the uint16 codec for v: weights and v codes."""
+    rng = np.random.default_rng(5)
+    n = 700
+    hp = FHParams(lr=3.5e-6)
+    st = _state1d(n, (rng.standard_normal(n) * 0.02).astype(np.float32))
+    for t in range(1, 11):
+        g = _bf16(rng.standard_normal(n) * 1e-3)
+        gd = oracle.bf16_to_f32(g).astype(np.float64)
+        w = oracle.join(st.hi, st.lo).astype(np.float64)
+        nb = oracle.nblocks(n)
+        v0 = (st.vc.astype(np.float64) / 65535) ** 4 * np.repeat(st.vs.astype(np.float64), 256)[:n]
+        v = hp.beta2 * v0 + (1 - hp.beta2) * (gd * gd + hp.eps1)
+        U = gd / np.sqrt(v)
+        rms = np.sqrt(np.mean(U * U))
+        w2 = w - hp.lr * U / max(1.0, rms)
+        oracle.factored_step(st, g, 0, 0, hp, t)
+        wo = oracle.join(st.hi, st.lo).astype(np.float64)
+        assert np.all(np.abs(wo - w2) <= 2 * ulp32(w2) + 1e-5 * np.abs(w2 - w)), t
+        for b in range(nb):
+            vb = v[b * 256:(b + 1) * 256]
+            assert abs(st.vs[b] / vb.max() - 1) < 1e-6
+            k = np.floor(65535 * (vb / vb.max()) ** 0.25 + 0.5)
+            assert np.max(np.abs(st.vc[b * 256:(b + 1) * 256].astype(np.int64) - k)) <= 1
