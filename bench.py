@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused low-precision optimizer step on one MI355X.
+
+One step = one fused NAdam update (one kernel launch) over a whole parameter
+set whose state is resident in HBM: bf16 weight + uint16 residual + bf16
+gradient + uint16 exp_avg / exp_avg_sq codes + per-256 fp32 block scales.
+Inputs are seeded synthetic data of the FLUX shapes (no trained weights or
+datasets are needed). Prints ONE JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flux_dev_12b]
+
+Reported:
+  value      optimizer-updated params/s over the timed steps (wall clock,
+             bracketed by device synchronisation)
+  roofline   the step kernel's average duration from HIP events recorded on
+             its stream around each launch; algorithmic bytes per launch =
+             18 B/param (read hi, lo, grad, m, v; write hi, lo, m, v) + 16 B
+             per 256-block (two scales read and written), against 8 TB/s
+  cpu_baseline  the C oracle, single-threaded, on a bounded sample of the
+             same workload (the leading tensors of the set, one step)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "optimizer-updated params/sec + achieved HBM GB/s (% of MI355X peak), Flux-12B set"
+PEAK_HBM_GBS = 8000.0
+BYTES_PER_PARAM = 18
+BYTES_PER_BLOCK = 16
+KERNEL_SOURCES = ["precision_state_amd/csrc/k_adam.hip", "precision_state_amd/csrc/dev_common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, n_params, n_blocks):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"adam_step_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def build_state(shapes, seed, dev):
+    import torch
+
+    import precision_state_amd as ps
+    import synth
+    states, grads = [], []
+    for tid, s in enumerate(shapes):
+        n = s.numel
+        nb = (n + 255) // 256
+        hi = torch.empty(n, dtype=torch.int16, device=dev)
+        lo = torch.empty(n, dtype=torch.int16, device=dev)
+        g = torch.empty(n, dtype=torch.int16, device=dev)
+        synth.dev_bf16_normal(hi, seed, synth.STREAM_HI, tid, 0, synth.SIGMA_W)
+        synth.dev_u16_uniform(lo, seed, synth.STREAM_LO, tid, 0)
+        synth.dev_bf16_normal(g, seed, synth.STREAM_GRAD, tid, 1, synth.SIGMA_G)
+        st = ps.TensorState(hi, lo, torch.full((n,), -32768, dtype=torch.int16, device=dev),
+                            torch.zeros(nb, dtype=torch.float32, device=dev),
+                            torch.zeros(n, dtype=torch.int16, device=dev),
+                            torch.zeros(nb, dtype=torch.float32, device=dev), rows=s.rows, cols=s.cols)
+        states.append(st)
+        grads.append(g)
+    return states, grads
+
+
+def cpu_baseline(shapes, seed, target_params=40_000_000):
+    """The oracle as it stands, one thread, one NAdam step over the leading
+    tensors of the set (about target_params parameters)."""
+    import oracle
+    import synth
+    sample, total = [], 0
+    for tid, s in enumerate(shapes):
+        if total >= target_params:
+            break
+        sample.append((tid, s))
+        total += s.numel
+    inputs = []
+    for tid, s in sample:
+        n = s.numel
+        st = oracle.TensorState(synth.host_bf16_normal(n, seed, synth.STREAM_HI, tid, 0, synth.SIGMA_W),
+                                synth.host_u16_uniform(n, seed, synth.STREAM_LO, tid, 0), *oracle.zero_moments(n))
+        inputs.append((st, synth.host_bf16_normal(n, seed, synth.STREAM_GRAD, tid, 1, synth.SIGMA_G)))
+    hp = oracle.HParams(algo=oracle.ALGO_NADAM, lr=3.5e-6)
+    t0 = time.perf_counter()
+    for st, g in inputs:
+        oracle.opt_step(st, g, hp, 1)
+    dt = time.perf_counter() - t0
+    cores = 1
+    return {"value": total / dt, "unit": "params/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {len(sample)} tensors of the set ({total} params), one NAdam step, "
+                      f"single thread, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="flux_dev_12b",
+                    choices=["flux_dev_12b", "flux_double_block", "single_1024x3072"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the optimizer step has no cross-GPU "
+              "communication here); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import precision_state_amd as ps
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    shapes = synth.WORKLOADS[args.workload]()
+    n_params = synth.total_params(shapes)
+    n_blocks = sum((s.numel + 255) // 256 for s in shapes)
+    log(f"[bench] {args.workload}: {len(shapes)} tensors, {n_params} params; generating state on {dev}")
+    t0 = time.perf_counter()
+    states, grads = build_state(shapes, args.seed, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] state ready in {time.perf_counter() - t0:.1f} s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
+
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+    recs = ps.make_records(states, grads)
+    stream = torch.cuda.current_stream()
+    step = 0
+    for _ in range(args.warmup):
+        step += 1
+        ps.opt_step_multi(None, None, hp, step, stream=stream, records=recs)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step += 1
+        ev[k][0].record(stream)
+        ps.opt_step_multi(None, None, hp, step, stream=stream, records=recs)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, {kernel_ms:.3f} ms/launch (events)")
+
+    alg_bytes = BYTES_PER_PARAM * n_params + BYTES_PER_BLOCK * n_blocks
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    traffic = read_traffic(args.workload, n_params, n_blocks)
+
+    baseline = None
+    if not args.no_cpu_baseline:
+        del states, grads, recs
+        torch.cuda.empty_cache()
+        log("[bench] timing the oracle on the host (cpu_baseline)")
+        baseline = cpu_baseline(shapes, args.seed)
+        log(f"[bench] oracle: {baseline['value']:.3e} params/s ({baseline['sample']})")
+
+    out = {
+        "metric": METRIC,
+        "value": n_params * args.steps / wall,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "params": n_params, "tensors": len(shapes),
+                   "algo": "nadam", "lr": 3.5e-6, "weight_decay": 0.0,
+                   "state": "bf16 weight + u16 residual + bf16 grad + u16 m/v codes + fp32 per-256 scales",
+                   "hbm_gbs_18B_per_param": BYTES_PER_PARAM * n_params / (kernel_ms * 1e-3) / 1e9,
+                   "kernel_ms": kernel_ms},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
+        "cpu_baseline": baseline,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

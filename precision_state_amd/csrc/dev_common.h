@@ -1,0 +1,144 @@
+// dev_common.h - gfx950 device helpers: residual split/join on packed
+// 16-bit pairs, the uint16 moment codec, and 16-lane DPP reductions.
+//
+// Data layout convention: 16-bit streams are handled as 32-bit words holding
+// two consecutive elements, the even element in the low half.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ps.h"
+
+namespace ps {
+
+// v_perm_b32 byte selectors. perm(s0, s1, sel) picks bytes of the 64-bit
+// value {s0:s1} (s1 = bytes 0..3, s0 = bytes 4..7).
+constexpr uint32_t kSelLoHalves = 0x05040100u;  // {s0.lo16, s1.lo16}
+constexpr uint32_t kSelHiHalves = 0x07060302u;  // {s0.hi16, s1.hi16}
+
+__device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+// ---------------------------------------------------------------------------
+// Residual split / join [KAHAN]: fp32 bits = hi << 16 | lo (TRUNC), or the
+// round-to-nearest-away variant whose join subtracts the carry back out.
+// ---------------------------------------------------------------------------
+
+// Join the even (which = 0) or odd (which = 1) element of a packed pair.
+template <int MODE>
+__device__ __forceinline__ uint32_t join_pair_elem(uint32_t hi2, uint32_t lo2, int which) {
+  uint32_t w = perm(hi2, lo2, which ? kSelHiHalves : kSelLoHalves);
+  if (MODE == PS_SPLIT_NEAREST_AWAY) w -= (w & 0x8000u) << 1;  // hi -= lo >> 15 (mod 2^16)
+  return w;
+}
+
+// Split two fp32 words into packed hi and lo pairs.
+template <int MODE>
+__device__ __forceinline__ void split_pair(uint32_t w_even, uint32_t w_odd, uint32_t& hi2, uint32_t& lo2) {
+  lo2 = perm(w_odd, w_even, kSelLoHalves);
+  if (MODE == PS_SPLIT_NEAREST_AWAY) {
+    w_even += 0x8000u;
+    w_odd += 0x8000u;
+  }
+  hi2 = perm(w_odd, w_even, kSelHiHalves);
+}
+
+// bf16 pair -> two fp32 values.
+__device__ __forceinline__ float bf16_lo(uint32_t g2) { return __uint_as_float(g2 << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t g2) { return __uint_as_float(g2 & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// Moment codec [NADAM second post]: 1/4-power companding, per-block scale.
+// D(h) = ((h*K)^2)^2 with K = fp32(1/Q).
+// ---------------------------------------------------------------------------
+
+constexpr float kK15 = 3.05185094e-05f;  // fp32(1/32767) = 0x38000100
+constexpr float kK16 = 1.52590219e-05f;  // fp32(1/65535) = 0x37800080
+constexpr float kMagic = 8388608.0f;     // 2^23
+
+__device__ __forceinline__ float dmag(float h, float K) {
+  float a = h * K;
+  float t = a * a;
+  return t * t;
+}
+
+// Code value as float, exactly: (2^23 | c) as float is 2^23 + c.
+__device__ __forceinline__ float code_lo_f(uint32_t c2) { return __uint_as_float(perm(0x4B000000u, c2, 0x07060100u)); }
+__device__ __forceinline__ float code_hi_f(uint32_t c2) { return __uint_as_float(perm(0x4B000000u, c2, 0x07060302u)); }
+
+// Signed decode of one code given as (2^23 + c): sign(k) * D(|k|) * s, k = c - 32768.
+__device__ __forceinline__ float dec_signed(float magic_c, float s) {
+  float k = magic_c - (kMagic + 32768.0f);  // exact
+  float t = dmag(k, kK15);                  // (k*K)^2 is sign-free
+  return t * __builtin_copysignf(s, k);
+}
+
+__device__ __forceinline__ float dec_unsigned(float magic_c, float s) {
+  float k = magic_c - kMagic;
+  return dmag(k, kK16) * s;
+}
+
+// Code magnitude of x in [0, 1 + 2^-23] given y ~ x^(1/4) (a few ulp): the
+// nearest code k0 = rint(y*Q) is exact except next to a half-way point, so
+// only the boundary on y's side of k0 is tested, with D evaluated exactly as
+// the definition does. Equal to the definition whenever |y*Q - (x^(1/4))*Q|
+// stays well below 1/2 code.
+template <int Q>
+__device__ __forceinline__ uint32_t code_mag(float x, float y) {
+  constexpr float K = (Q == 32767) ? kK15 : kK16;
+  const float q = (float)Q;
+  float z = __builtin_fmaf(y, q, kMagic);  // 2^23 + rint(y*Q)
+  float kf = z - kMagic;
+  float dl = __builtin_fmaf(y, q, -kf);    // exact sign of y*Q - k0
+  bool up = dl >= 0.0f;
+  float T = dmag(kf + (up ? 0.5f : -0.5f), K);
+  uint32_t k0 = __float_as_uint(z) - 0x4B000000u;
+  return k0 - (up ? 0u : 1u) + (x >= T ? 1u : 0u);
+}
+
+__device__ __forceinline__ float fast_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+
+// Signed code of m given inv = 1/scale (0 for a flushed block).
+__device__ __forceinline__ uint32_t enc_signed(float m, float inv) {
+  float x = __builtin_fabsf(m) * inv;
+  uint32_t k = code_mag<32767>(x, fast_sqrt(fast_sqrt(x)));
+  return m < 0.0f ? 32768u - k : 32768u + k;
+}
+
+// Unsigned code of v >= 0 given inv = 1/scale and y ~ (v*inv)^(1/4).
+__device__ __forceinline__ uint32_t enc_unsigned_y(float v, float inv, float y) {
+  return code_mag<65535>(v * inv, y);
+}
+
+__device__ __forceinline__ uint32_t enc_unsigned(float v, float inv) {
+  float x = __builtin_fabsf(v) * inv;
+  return code_mag<65535>(x, fast_sqrt(fast_sqrt(x)));
+}
+
+// ---------------------------------------------------------------------------
+// 16-lane (one DPP row) butterfly max: every lane of the row gets the max.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_max(float x) {
+  x = __builtin_fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = __builtin_fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = __builtin_fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+  x = __builtin_fmaxf(x, dpp<0x140>(x));  // row_mirror
+  return x;
+}
+
+// Block scale from the block max: blocks below the smallest normal are
+// flushed to 0 so 1/scale never overflows; inv is 0 for them.
+__device__ __forceinline__ void block_scale(float mx, float& s, float& inv) {
+  bool keep = mx >= 0x1p-126f;
+  s = keep ? mx : 0.0f;
+  inv = keep ? 1.0f / mx : 0.0f;
+}
+
+}  // namespace ps

@@ -1,0 +1,290 @@
+// ps_abi.cpp - extern "C" entry points of libps.so: argument validation (all
+// on the host, before any HIP call), the device tensor-table cache, and
+// dispatch to the kernels.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "ps_internal.h"
+
+namespace ps {
+
+namespace {
+thread_local char g_err[512] = "";
+
+bool finite(double x) { return std::isfinite(x); }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+}  // namespace
+
+ps_status fail(ps_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ps_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PS_OK;
+  return fail(PS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------
+
+ps_status check_hparams(const ps_hparams* hp) {
+  if (!hp) return fail(PS_ERR_INVALID_ARG, "hparams is NULL");
+  if (hp->algo != PS_ALGO_ADAM && hp->algo != PS_ALGO_NADAM) return fail(PS_ERR_INVALID_ARG, "unknown algo %d", hp->algo);
+  if (hp->split_mode != PS_SPLIT_TRUNC && hp->split_mode != PS_SPLIT_NEAREST_AWAY)
+    return fail(PS_ERR_INVALID_ARG, "unknown split_mode %d", hp->split_mode);
+  if (!finite(hp->lr) || hp->lr < 0) return fail(PS_ERR_INVALID_ARG, "lr must be finite and >= 0");
+  if (!finite(hp->beta1) || hp->beta1 < 0 || hp->beta1 >= 1) return fail(PS_ERR_INVALID_ARG, "beta1 must be in [0, 1)");
+  if (!finite(hp->beta2) || hp->beta2 < 0 || hp->beta2 >= 1) return fail(PS_ERR_INVALID_ARG, "beta2 must be in [0, 1)");
+  if (!finite(hp->eps) || !(hp->eps > 0)) return fail(PS_ERR_INVALID_ARG, "eps must be finite and > 0");
+  if (!finite(hp->weight_decay) || hp->weight_decay < 0)
+    return fail(PS_ERR_INVALID_ARG, "weight_decay must be finite and >= 0");
+  if (!finite(hp->momentum_decay) || hp->momentum_decay < 0)
+    return fail(PS_ERR_INVALID_ARG, "momentum_decay must be finite and >= 0");
+  return PS_OK;
+}
+
+constexpr int64_t kMaxNumel = int64_t(1) << 40;
+
+ps_status check_array(const void* p, const char* what, int i, uintptr_t align) {
+  if (!p) return fail(PS_ERR_INVALID_ARG, "tensor %d: %s is NULL", i, what);
+  if (!aligned(p, align)) return fail(PS_ERR_ALIGNMENT, "tensor %d: %s is not %d-byte aligned", i, what, (int)align);
+  return PS_OK;
+}
+
+// Validates the records and builds the active list (tensors with numel > 0
+// and a gradient) with the work-item prefix ends.
+ps_status build_active(const ps_tensor* t, int32_t n, std::vector<DevTensor>& recs, std::vector<uint32_t>& ends) {
+  if (n < 0) return fail(PS_ERR_INVALID_ARG, "n_tensors < 0");
+  if (n > 0 && !t) return fail(PS_ERR_INVALID_ARG, "tensors is NULL");
+  uint64_t items = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const ps_tensor& x = t[i];
+    if (x.numel < 0 || x.numel > kMaxNumel) return fail(PS_ERR_SHAPE, "tensor %d: numel %lld out of range", i, (long long)x.numel);
+    if (x.numel == 0 || x.grad == nullptr) continue;
+    ps_status s;
+    if ((s = check_array(x.w_hi, "w_hi", i, 16)) || (s = check_array(x.w_lo, "w_lo", i, 16)) ||
+        (s = check_array(x.grad, "grad", i, 16)) || (s = check_array(x.m_code, "m_code", i, 16)) ||
+        (s = check_array(x.v_code, "v_code", i, 16)) || (s = check_array(x.m_scale, "m_scale", i, 4)) ||
+        (s = check_array(x.v_scale, "v_scale", i, 4)))
+      return s;
+    items += (uint64_t)((x.numel + kItemElems - 1) / kItemElems);
+    if (items > 0xFFFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large (more than 2^32 work items)");
+    recs.push_back(DevTensor{x.w_hi, x.w_lo, x.grad, x.m_code, x.m_scale, x.v_code, x.v_scale, x.numel});
+    ends.push_back((uint32_t)items);
+  }
+  return PS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// device tensor-table cache: one immutable device copy per distinct list
+// ---------------------------------------------------------------------------
+
+struct TableEntry {
+  int device = -1;
+  std::vector<DevTensor> recs;
+  std::vector<uint32_t> ends;
+  void* d_mem = nullptr;  // recs then ends
+  void* h_mem = nullptr;  // pinned source of the upload
+  hipEvent_t ready = nullptr;
+  uint64_t last_use = 0;
+};
+
+std::mutex g_cache_mu;
+std::vector<TableEntry*> g_cache;
+uint64_t g_clock = 0;
+constexpr size_t kCacheMax = 32;
+
+void free_entry(TableEntry* e) {
+  if (e->ready) (void)hipEventDestroy(e->ready);
+  if (e->d_mem) (void)hipFree(e->d_mem);
+  if (e->h_mem) (void)hipHostFree(e->h_mem);
+  delete e;
+}
+
+ps_status get_table(const std::vector<DevTensor>& recs, const std::vector<uint32_t>& ends, hipStream_t s,
+                    TablePtr* out) {
+  int dev = 0;
+  if (ps_status st = hip_check(hipGetDevice(&dev), "hipGetDevice")) return st;
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  const size_t rb = recs.size() * sizeof(DevTensor), eb = ends.size() * sizeof(uint32_t);
+  for (TableEntry* e : g_cache) {
+    if (e->device == dev && e->recs.size() == recs.size() && !memcmp(e->recs.data(), recs.data(), rb) &&
+        !memcmp(e->ends.data(), ends.data(), eb)) {
+      e->last_use = ++g_clock;
+      if (ps_status st = hip_check(hipStreamWaitEvent(s, e->ready, 0), "hipStreamWaitEvent")) return st;
+      *out = TablePtr{(const DevTensor*)e->d_mem, (const uint32_t*)((char*)e->d_mem + rb), (int32_t)recs.size()};
+      return PS_OK;
+    }
+  }
+  if (g_cache.size() >= kCacheMax) {
+    // Evict the least recently used list; wait for all device work first so
+    // that no launch still reads it.
+    size_t victim = 0;
+    for (size_t i = 1; i < g_cache.size(); ++i)
+      if (g_cache[i]->last_use < g_cache[victim]->last_use) victim = i;
+    if (ps_status st = hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize")) return st;
+    free_entry(g_cache[victim]);
+    g_cache.erase(g_cache.begin() + victim);
+  }
+  TableEntry* e = new TableEntry;
+  e->device = dev;
+  e->recs = recs;
+  e->ends = ends;
+  if (hipMalloc(&e->d_mem, rb + eb) != hipSuccess || hipHostMalloc(&e->h_mem, rb + eb, hipHostMallocDefault) != hipSuccess) {
+    free_entry(e);
+    return fail(PS_ERR_NO_MEMORY, "tensor table allocation failed");
+  }
+  memcpy(e->h_mem, recs.data(), rb);
+  memcpy((char*)e->h_mem + rb, ends.data(), eb);
+  ps_status st = hip_check(hipEventCreateWithFlags(&e->ready, hipEventDisableTiming), "hipEventCreate");
+  if (!st) st = hip_check(hipMemcpyAsync(e->d_mem, e->h_mem, rb + eb, hipMemcpyHostToDevice, s), "table upload");
+  if (!st) st = hip_check(hipEventRecord(e->ready, s), "hipEventRecord");
+  if (st) {
+    (void)hipStreamSynchronize(s);
+    free_entry(e);
+    return st;
+  }
+  e->last_use = ++g_clock;
+  g_cache.push_back(e);
+  *out = TablePtr{(const DevTensor*)e->d_mem, (const uint32_t*)((char*)e->d_mem + rb), (int32_t)recs.size()};
+  return PS_OK;
+}
+
+ps_status check_elementwise(int64_t n, std::initializer_list<std::pair<const void*, const char*>> arrays,
+                            std::initializer_list<std::pair<const void*, const char*>> scales) {
+  if (n < 0 || n > kMaxNumel) return fail(PS_ERR_SHAPE, "n = %lld out of range", (long long)n);
+  if (n == 0) return PS_OK;
+  for (auto& a : arrays) {
+    if (!a.first) return fail(PS_ERR_INVALID_ARG, "%s is NULL", a.second);
+    if (!aligned(a.first, 16)) return fail(PS_ERR_ALIGNMENT, "%s is not 16-byte aligned", a.second);
+  }
+  for (auto& a : scales) {
+    if (!a.first) return fail(PS_ERR_INVALID_ARG, "%s is NULL", a.second);
+    if (!aligned(a.first, 4)) return fail(PS_ERR_ALIGNMENT, "%s is not 4-byte aligned", a.second);
+  }
+  return PS_OK;
+}
+
+}  // namespace
+}  // namespace ps
+
+using namespace ps;
+
+extern "C" {
+
+ps_status ps_step_scalars(const ps_hparams* hp, int64_t step, float out[10]) {
+  g_err[0] = 0;
+  if (ps_status s = check_hparams(hp)) return s;
+  if (step < 1) return fail(PS_ERR_INVALID_ARG, "step must be >= 1 (got %lld)", (long long)step);
+  if (!out) return fail(PS_ERR_INVALID_ARG, "out is NULL");
+  StepScalars c;
+  step_scalars(*hp, step, &c);
+  const float v[10] = {c.B1, c.C1, c.B2, c.C2, c.EPS, c.A, c.RS2, c.AG, c.AM, c.CWD};
+  memcpy(out, v, sizeof(v));
+  return PS_OK;
+}
+
+ps_status ps_opt_step_multi(const ps_tensor* tensors, int32_t n_tensors, const ps_hparams* hp, int64_t step,
+                            ps_stream_t stream) {
+  g_err[0] = 0;
+  if (ps_status s = check_hparams(hp)) return s;
+  if (step < 1) return fail(PS_ERR_INVALID_ARG, "step must be >= 1 (got %lld)", (long long)step);
+  std::vector<DevTensor> recs;
+  std::vector<uint32_t> ends;
+  if (ps_status s = build_active(tensors, n_tensors, recs, ends)) return s;
+  if (recs.empty()) return PS_OK;
+  StepScalars c;
+  step_scalars(*hp, step, &c);
+  hipStream_t s = (hipStream_t)stream;
+  const uint32_t total = ends.back();
+  if (recs.size() <= (size_t)kInlineMax) {
+    TableInline tb;
+    memset(&tb, 0, sizeof(tb));
+    for (size_t i = 0; i < recs.size(); ++i) {
+      tb.recs[i] = recs[i];
+      tb.item_end[i] = ends[i];
+    }
+    tb.n = (int32_t)recs.size();
+    return launch_adam_inline(tb, total, *hp, c, s);
+  }
+  TablePtr tp;
+  if (ps_status st = get_table(recs, ends, s, &tp)) return st;
+  return launch_adam_ptr(tp, total, *hp, c, s);
+}
+
+ps_status ps_split(const float* w32, uint16_t* hi, uint16_t* lo, int64_t n, int32_t mode, ps_stream_t stream) {
+  g_err[0] = 0;
+  if (mode != PS_SPLIT_TRUNC && mode != PS_SPLIT_NEAREST_AWAY) return fail(PS_ERR_INVALID_ARG, "unknown split mode %d", mode);
+  if (ps_status s = check_elementwise(n, {{w32, "w32"}, {hi, "hi"}, {lo, "lo"}}, {})) return s;
+  if (n == 0) return PS_OK;
+  return launch_split(w32, hi, lo, n, mode, (hipStream_t)stream);
+}
+
+ps_status ps_join(const uint16_t* hi, const uint16_t* lo, float* w32, int64_t n, int32_t mode, ps_stream_t stream) {
+  g_err[0] = 0;
+  if (mode != PS_SPLIT_TRUNC && mode != PS_SPLIT_NEAREST_AWAY) return fail(PS_ERR_INVALID_ARG, "unknown split mode %d", mode);
+  if (ps_status s = check_elementwise(n, {{w32, "w32"}, {hi, "hi"}, {lo, "lo"}}, {})) return s;
+  if (n == 0) return PS_OK;
+  return launch_join(hi, lo, w32, n, mode, (hipStream_t)stream);
+}
+
+ps_status ps_encode_moments(const float* x, uint16_t* code, float* scale, int64_t n, int32_t kind,
+                            ps_stream_t stream) {
+  g_err[0] = 0;
+  if (kind != PS_MOMENT_SIGNED && kind != PS_MOMENT_UNSIGNED) return fail(PS_ERR_INVALID_ARG, "unknown moment kind %d", kind);
+  if (ps_status s = check_elementwise(n, {{x, "x"}, {code, "code"}}, {{scale, "scale"}})) return s;
+  if (n == 0) return PS_OK;
+  return launch_encode(x, code, scale, n, kind, (hipStream_t)stream);
+}
+
+ps_status ps_decode_moments(const uint16_t* code, const float* scale, float* x, int64_t n, int32_t kind,
+                            ps_stream_t stream) {
+  g_err[0] = 0;
+  if (kind != PS_MOMENT_SIGNED && kind != PS_MOMENT_UNSIGNED) return fail(PS_ERR_INVALID_ARG, "unknown moment kind %d", kind);
+  if (ps_status s = check_elementwise(n, {{x, "x"}, {code, "code"}}, {{scale, "scale"}})) return s;
+  if (n == 0) return PS_OK;
+  return launch_decode(code, scale, x, n, kind, (hipStream_t)stream);
+}
+
+const char* ps_status_string(ps_status s) {
+  switch (s) {
+    case PS_OK: return "ok";
+    case PS_ERR_INVALID_ARG: return "invalid argument";
+    case PS_ERR_ALIGNMENT: return "misaligned pointer";
+    case PS_ERR_SHAPE: return "bad shape";
+    case PS_ERR_UNSUPPORTED: return "unsupported";
+    case PS_ERR_HIP: return "HIP runtime error";
+    case PS_ERR_NO_MEMORY: return "out of memory";
+    case PS_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+const char* ps_last_error(void) { return g_err; }
+
+const char* ps_version(void) { return "precision_state_amd 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+"""Helpers of the GPU parity tests: build the same seeded optimizer state on
+the device (through synth's device fills) and on the host (synth's host fills)
+and compare device results with the oracle's."""
+import math
+
+import numpy as np
+
+import oracle
+import synth
+from synth import SIGMA_G, SIGMA_W, STREAM_GRAD, STREAM_HI, STREAM_LO
+
+DEV = "cuda"
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def ps():
+    import precision_state_amd as _ps
+    return _ps
+
+
+def nblocks(n):
+    return (n + 255) // 256
+
+
+def u16(t):
+    return t.detach().cpu().numpy().view(np.uint16)
+
+
+def f32(t):
+    return t.detach().cpu().numpy()
+
+
+def dev_u16_from(a):
+    T = torch()
+    return T.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).to(DEV)
+
+
+def dev_state(numel, seed=0, tid=0, rows=0, cols=0, factored=False):
+    """Device state: hi ~ bf16(N(0, 0.02)), lo uniform, zero moments."""
+    T = torch()
+    hi = T.empty(numel, dtype=T.int16, device=DEV)
+    lo = T.empty(numel, dtype=T.int16, device=DEV)
+    synth.dev_bf16_normal(hi, seed, STREAM_HI, tid, 0, SIGMA_W)
+    synth.dev_u16_uniform(lo, seed, STREAM_LO, tid, 0)
+    nb = nblocks(numel)
+    st = ps().TensorState(hi, lo, rows=rows, cols=cols)
+    if factored:
+        if rows > 0:
+            st.row_ema = T.zeros(rows, dtype=T.float32, device=DEV)
+            st.col_ema = T.zeros(cols, dtype=T.float32, device=DEV)
+        else:
+            st.v_code = T.zeros(numel, dtype=T.int16, device=DEV)
+            st.v_scale = T.zeros(nb, dtype=T.float32, device=DEV)
+    else:
+        st.m_code = T.full((numel,), -32768, dtype=T.int16, device=DEV)   # 0x8000: zero code
+        st.m_scale = T.zeros(nb, dtype=T.float32, device=DEV)
+        st.v_code = T.zeros(numel, dtype=T.int16, device=DEV)
+        st.v_scale = T.zeros(nb, dtype=T.float32, device=DEV)
+    return st
+
+
+def host_state(numel, seed=0, tid=0, rows=0, factored=False, cols=0):
+    hi = synth.host_bf16_normal(numel, seed, STREAM_HI, tid, 0, SIGMA_W)
+    lo = synth.host_u16_uniform(numel, seed, STREAM_LO, tid, 0)
+    st = oracle.TensorState(hi, lo)
+    if factored:
+        if rows > 0:
+            st.row = np.zeros(rows, np.float32)
+            st.col = np.zeros(cols, np.float32)
+        else:
+            _, _, st.vc, st.vs = oracle.zero_moments(numel)
+    else:
+        st.mc, st.ms, st.vc, st.vs = oracle.zero_moments(numel)
+    return st
+
+
+def dev_grad(numel, seed, tid, step, outlier_p=0.0):
+    T = torch()
+    g = T.empty(numel, dtype=T.int16, device=DEV)
+    synth.dev_bf16_normal(g, seed, STREAM_GRAD, tid, step, SIGMA_G, outlier_p, 100.0)
+    return g
+
+
+def host_grad(numel, seed, tid, step, outlier_p=0.0):
+    return synth.host_bf16_normal(numel, seed, STREAM_GRAD, tid, step, SIGMA_G, outlier_p, 100.0)
+
+
+def to_host(st):
+    """oracle.TensorState copy of a device TensorState."""
+    h = oracle.TensorState(u16(st.w_hi).copy(), u16(st.w_lo).copy())
+    if st.m_code is not None:
+        h.mc, h.ms = u16(st.m_code).copy(), f32(st.m_scale).copy()
+    if st.v_code is not None:
+        h.vc, h.vs = u16(st.v_code).copy(), f32(st.v_scale).copy()
+    if st.row_ema is not None:
+        h.row, h.col = f32(st.row_ema).copy(), f32(st.col_ema).copy()
+    return h
+
+
+def mismatches(dev, host):
+    """Per-field counts of differing elements (bitwise; fp32 compared as bits)."""
+    d = to_host(dev)
+    out = {}
+    for name in ("hi", "lo", "mc", "ms", "vc", "vs", "row", "col"):
+        a, b = getattr(d, name), getattr(host, name)
+        if a is None and b is None:
+            continue
+        out[name] = int(np.count_nonzero(a.view(np.uint32 if a.dtype == np.float32 else np.uint16) !=
+                                         b.view(np.uint32 if b.dtype == np.float32 else np.uint16)))
+    return out
+
+
+def max_code_diff(dev, host):
+    d = to_host(dev)
+    r = {}
+    for name in ("mc", "vc"):
+        a, b = getattr(d, name), getattr(host, name)
+        if a is not None:
+            r[name] = int(np.max(np.abs(a.astype(np.int64) - b.astype(np.int64)), initial=0))
+    return r
+
+
+def sample_blocks(numel, k, rng):
+    """k distinct block indices of a tensor (always including the last)."""
+    nb = nblocks(numel)
+    if nb <= k:
+        return np.arange(nb)
+    idx = rng.choice(nb - 1, size=k - 1, replace=False)
+    return np.sort(np.append(idx, nb - 1))
+
+
+def block_slice(b, numel):
+    return slice(b * 256, min(numel, (b + 1) * 256))

@@ -1,0 +1,95 @@
+"""Host-side checks of libps.so that need no GPU: every symbol of
+include/ps.h is exported, the host-computed step scalars equal the oracle's,
+and invalid arguments are rejected before any device call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def ps():
+    import precision_state_amd as ps
+    return ps
+
+
+def test_library_exports_every_declared_symbol(ps):
+    hdr = open(os.path.join(ROOT, "include", "ps.h")).read()
+    declared = set(re.findall(r"\b(ps_[a-z0-9_]+)\s*\(", hdr))
+    assert len(declared) >= 15
+    missing = [s for s in sorted(declared) if not hasattr(ps.lib(), s)]
+    assert not missing, missing
+    assert set(ps.EXPORTED) == declared
+
+
+@pytest.mark.parametrize("algo", [0, 1])
+@pytest.mark.parametrize("wd", [0.0, 0.01])
+def test_step_scalars_equal_oracle(ps, algo, wd):
+    for lr, b1, b2 in ((3.5e-6, 0.9, 0.999), (1e-3, 0.95, 0.99), (0.1, 0.0, 0.5)):
+        for step in (1, 2, 3, 10, 57, 1000, 123456):
+            hp = ps.HParams(algo=algo, lr=lr, beta1=b1, beta2=b2, weight_decay=wd)
+            got = ps.step_scalars(hp, step)
+            ref = oracle.coeffs(oracle.HParams(algo=algo, lr=lr, beta1=b1, beta2=b2, weight_decay=wd), step)
+            for k, v in ref.items():
+                assert np.float32(got[k]).view(np.uint32) == v.view(np.uint32), (k, step, got[k], v)
+
+
+def _rec(ps, n=1024, **kw):
+    base = dict(w_hi=16, w_lo=32, grad=48, m_code=64, m_scale=80, v_code=96, v_scale=112, row_ema=0, col_ema=0,
+                numel=n, rows=0, cols=0)
+    base.update(kw)
+    return ps.CTensor(**base)
+
+
+def _call(ps, recs, hp=None, step=1):
+    arr = (ps.CTensor * max(1, len(recs)))(*recs)
+    h = (hp or ps.HParams()).c()
+    return ps.lib().ps_opt_step_multi(arr, len(recs), ctypes.byref(h), step, None)
+
+
+def test_invalid_arguments_rejected_on_host(ps):
+    L = ps.lib()
+    assert _call(ps, [_rec(ps)], step=0) == 1
+    assert _call(ps, [_rec(ps)], hp=ps.HParams(algo=7)) == 1
+    assert _call(ps, [_rec(ps)], hp=ps.HParams(split_mode=3)) == 1
+    assert _call(ps, [_rec(ps)], hp=ps.HParams(beta1=1.0)) == 1
+    assert _call(ps, [_rec(ps)], hp=ps.HParams(beta2=-0.1)) == 1
+    assert _call(ps, [_rec(ps)], hp=ps.HParams(eps=0.0)) == 1
+    assert _call(ps, [_rec(ps)], hp=ps.HParams(lr=float("nan"))) == 1
+    assert _call(ps, [_rec(ps)], hp=ps.HParams(weight_decay=-1.0)) == 1
+    assert _call(ps, [_rec(ps, numel=-1)]) == 3
+    assert _call(ps, [_rec(ps, w_lo=0)]) == 1
+    assert "w_lo" in ps.last_error()
+    assert _call(ps, [_rec(ps, m_code=66)]) == 2
+    assert _call(ps, [_rec(ps, v_scale=114)]) == 2
+    h = ps.HParams().c()
+    assert L.ps_opt_step_multi(None, 3, ctypes.byref(h), 1, None) == 1
+    assert L.ps_opt_step_multi(None, 0, None, 1, None) == 1
+    assert L.ps_split(None, None, None, -1, 0, None) == 3
+    assert L.ps_split(16, 32, 48, 10, 5, None) == 1
+    assert L.ps_join(16, 32, 40, 10, 0, None) == 2
+    assert L.ps_encode_moments(16, 32, 0, 10, 0, None) == 1
+    assert L.ps_decode_moments(16, 32, 48, 10, 9, None) == 1
+
+
+def test_empty_and_gradless_lists_are_noops(ps):
+    """Nothing to do means no device call at all, so this runs without a GPU."""
+    assert _call(ps, []) == 0
+    assert _call(ps, [_rec(ps, numel=0, w_hi=0, w_lo=0, grad=0)]) == 0
+    assert _call(ps, [_rec(ps, grad=0, w_hi=0)]) == 0
+    L = ps.lib()
+    assert L.ps_split(None, None, None, 0, 0, None) == 0
+    assert L.ps_encode_moments(None, None, None, 0, 1, None) == 0
+
+
+def test_status_strings(ps):
+    L = ps.lib()
+    for s in range(8):
+        assert L.ps_status_string(s)
+    assert b"gfx950" in L.ps_version()

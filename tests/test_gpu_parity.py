@@ -1,0 +1,290 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, on seeded
+synthetic inputs. Bar: bit-exact residual/join bits and block scales, codes
+within 1, master weights within 4 fp32 ulp after 10 steps; the kernels are
+built to match the oracle bit for bit, so every case here also reports and
+asserts exact equality."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (DEV, block_slice, dev_grad, dev_state, dev_u16_from, f32, host_grad, host_state,
+                      max_code_diff, mismatches, nblocks, sample_blocks, to_host, u16)
+from synth import SIGMA_G, SIGMA_W, STREAM_GRAD, STREAM_HI, STREAM_LO
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import precision_state_amd as ps  # noqa: E402
+
+
+def _ohp(hp: ps.HParams):
+    return oracle.HParams(hp.algo, hp.split_mode, hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
+                          hp.momentum_decay)
+
+
+def _assert_exact(dev, host, what):
+    mm = mismatches(dev, host)
+    print(f"  {what}: mismatches {mm} max code diff {max_code_diff(dev, host)}", flush=True)
+    assert all(v == 0 for v in mm.values()), (what, mm)
+
+
+# ---------------------------------------------------------------------------
+# split / join
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY])
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 255, 1000, 65541, (1 << 22) + 3])
+def test_split_join_match_oracle(mode, n):
+    rng = np.random.default_rng(n)
+    bits = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+    w = torch.from_numpy(bits.view(np.int32)).to(DEV).view(torch.float32)
+    hi = torch.empty(n, dtype=torch.int16, device=DEV)
+    lo = torch.empty(n, dtype=torch.int16, device=DEV)
+    ps.split(w, hi, lo, mode)
+    rhi, rlo = oracle.split(bits.view(np.float32), mode)
+    assert np.array_equal(u16(hi), rhi) and np.array_equal(u16(lo), rlo)
+    back = torch.empty(n, dtype=torch.float32, device=DEV)
+    ps.join(hi, lo, back, mode)
+    assert np.array_equal(f32(back).view(np.uint32), bits)
+    # join of arbitrary (hi, lo) pairs, not only split outputs
+    h2 = rng.integers(0, 65536, n).astype(np.uint16)
+    l2 = rng.integers(0, 65536, n).astype(np.uint16)
+    ps.join(dev_u16_from(h2), dev_u16_from(l2), back, mode)
+    assert np.array_equal(f32(back).view(np.uint32), oracle.join(h2, l2, mode).view(np.uint32))
+
+
+@pytest.mark.parametrize("mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY])
+def test_split_join_roundtrip_all_patterns(mode):
+    """Every 32-bit pattern survives split then join on the device."""
+    chunk = 1 << 28
+    base = torch.arange(chunk, dtype=torch.int64, device=DEV)
+    hi = torch.empty(chunk, dtype=torch.int16, device=DEV)
+    lo = torch.empty(chunk, dtype=torch.int16, device=DEV)
+    back = torch.empty(chunk, dtype=torch.float32, device=DEV)
+    for start in range(0, 1 << 32, chunk):
+        w = (base + start).to(torch.int32)          # wraps to the 32-bit pattern
+        ps.split(w.view(torch.float32), hi, lo, mode)
+        ps.join(hi, lo, back, mode)
+        assert torch.equal(back.view(torch.int32), w), hex(start)
+
+
+# ---------------------------------------------------------------------------
+# moment codec
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", [ps.MOMENT_UNSIGNED, ps.MOMENT_SIGNED])
+def test_codec_exhaustive_all_x_in_unit_interval(kind):
+    """Every fp32 x in [0, 1] (1,065,353,217 patterns) encodes to the oracle's
+    code: each 256-block is [1.0, 255 consecutive patterns], so the scale is 1
+    and x' = x exactly; the device codes must step exactly at the oracle's
+    thresholds D(k - 1/2)."""
+    Q = 65535 if kind == ps.MOMENT_UNSIGNED else 32767
+    nx = 0x3F800000 + 1
+    per = 255
+    nblk = (nx + per - 1) // per
+    x = torch.ones(nblk, 256, dtype=torch.float32, device=DEV)
+    pat = torch.arange(nblk * per, dtype=torch.int64, device=DEV).clamp_(max=nx - 1).to(torch.int32)
+    x[:, 1:] = pat.view(torch.float32).view(nblk, per)
+    del pat
+    code = torch.empty(nblk * 256, dtype=torch.int16, device=DEV)
+    scale = torch.empty(nblk, dtype=torch.float32, device=DEV)
+    ps.encode_moments(x.view(-1), code, scale, kind)
+    assert bool((scale == 1.0).all())
+    del x
+    c = u16(code).reshape(nblk, 256)[:, 1:].reshape(-1)[:nx].astype(np.int32)
+    if kind == ps.MOMENT_SIGNED:
+        assert c.min() >= 32768
+        c -= 32768
+    assert c[0] == 0 and c[-1] == Q
+    assert int(np.max(np.diff(c))) <= 1 and int(np.min(np.diff(c))) >= 0
+    thr = oracle.dec_mag(np.arange(1, Q + 1, dtype=np.float32) - np.float32(0.5),
+                         oracle.SIGNED if kind == ps.MOMENT_SIGNED else oracle.UNSIGNED).view(np.uint32)
+    first = np.searchsorted(c, np.arange(1, Q + 1), side="left")
+    bad = np.flatnonzero(first != thr)
+    assert bad.size == 0, f"{bad.size} thresholds differ; first k={bad[0] + 1}: dev {first[bad[0]]:#x} oracle {thr[bad[0]]:#x}"
+
+
+@pytest.mark.parametrize("kind", [ps.MOMENT_SIGNED, ps.MOMENT_UNSIGNED])
+@pytest.mark.parametrize("n", [0, 1, 255, 256, 257, 1000, 4096, 100003])
+def test_encode_decode_match_oracle(kind, n):
+    rng = np.random.default_rng(1000 + n)
+    x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-12, 2, n)).astype(np.float32)
+    if kind == ps.MOMENT_UNSIGNED:
+        x = np.abs(x)
+    if n > 600:
+        x[256:512] = 0.0                                # a zero block
+        x[512:600] = np.float32(1e-40)                  # subnormal block max
+        x[512:768] = np.where(np.arange(256) < 88, x[512:768], np.float32(-3e-39))
+    okind = oracle.SIGNED if kind == ps.MOMENT_SIGNED else oracle.UNSIGNED
+    rc, rs = oracle.encode(x, okind)
+    xd = torch.from_numpy(x).to(DEV)
+    code = torch.empty(n, dtype=torch.int16, device=DEV)
+    scale = torch.empty(nblocks(n), dtype=torch.float32, device=DEV)
+    ps.encode_moments(xd, code, scale, kind)
+    assert np.array_equal(u16(code), rc)
+    assert np.array_equal(f32(scale).view(np.uint32), rs.view(np.uint32))
+    back = torch.empty(n, dtype=torch.float32, device=DEV)
+    ps.decode_moments(code, scale, back, kind)
+    assert np.array_equal(f32(back).view(np.uint32), oracle.decode(rc, rs, okind).view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", [ps.MOMENT_SIGNED, ps.MOMENT_UNSIGNED])
+def test_decode_all_codes(kind):
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    okind = oracle.SIGNED if kind == ps.MOMENT_SIGNED else oracle.UNSIGNED
+    for s in (0.0, 1.0, 3.7e-5, 2.0 ** -126, 1.7e38):
+        scale = np.full(256, s, np.float32)
+        back = torch.empty(65536, dtype=torch.float32, device=DEV)
+        ps.decode_moments(dev_u16_from(codes), torch.from_numpy(scale).to(DEV), back, kind)
+        assert np.array_equal(f32(back).view(np.uint32), oracle.decode(codes, scale, okind).view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# fused step
+# ---------------------------------------------------------------------------
+
+def test_single_1024x3072_nadam_10_steps_free_running():
+    """One [1024, 3072] tensor, 10 NAdam steps (lr 3.5e-6, betas 0.9/0.999,
+    eps 1e-8, wd 0, seed 0), device and oracle each running on their own."""
+    n = 1024 * 3072
+    dev = dev_state(n, 0, 0)
+    host = host_state(n, 0, 0)
+    _assert_exact(dev, host, "initial state")
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, weight_decay=0.0)
+    for t in range(1, 11):
+        ps.opt_step_multi([dev], [dev_grad(n, 0, 0, t)], hp, t)
+        oracle.opt_step(host, host_grad(n, 0, 0, t), _ohp(hp), t)
+        _assert_exact(dev, host, f"step {t}")
+
+
+@pytest.mark.parametrize("algo", [ps.ALGO_ADAM, ps.ALGO_NADAM])
+@pytest.mark.parametrize("wd", [0.0, 0.01])
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY])
+def test_step_variants(algo, wd, split_mode):
+    n = 100003
+    hp = ps.HParams(algo=algo, weight_decay=wd, split_mode=split_mode, lr=1e-4)
+    dev = dev_state(n, 5, 3)
+    host = host_state(n, 5, 3)
+    for t in range(1, 4):
+        ps.opt_step_multi([dev], [dev_grad(n, 5, 3, t, 0.001)], hp, t)
+        oracle.opt_step(host, host_grad(n, 5, 3, t, 0.001), _ohp(hp), t)
+    _assert_exact(dev, host, f"algo {algo} wd {wd} split {split_mode}")
+
+
+RAGGED = [0, 1, 7, 8, 64, 128, 255, 256, 257, 1000, 1023, 1024, 1025, 3000, 4096, 65539, 131089]
+
+
+@pytest.mark.parametrize("count", [len(RAGGED), 9])
+def test_multi_tensor_ragged_lists(count):
+    """Ragged sizes (tails inside a 16-lane row, partial blocks, partial work
+    items), tensors without a gradient, an empty tensor; 17 tensors take the
+    device-table path, 9 the kernel-argument path."""
+    sizes = RAGGED[:count]
+    hp = ps.HParams(algo=ps.ALGO_NADAM, weight_decay=0.01, lr=1e-4)
+    devs = [dev_state(n, 7, i) for i, n in enumerate(sizes)]
+    hosts = [host_state(n, 7, i) for i, n in enumerate(sizes)]
+    for t in range(1, 4):
+        has_grad = [(i + t) % 4 != 0 for i in range(count)]
+        dg = [dev_grad(n, 7, i, t) if has_grad[i] else None for i, n in enumerate(sizes)]
+        hg = [host_grad(n, 7, i, t) if has_grad[i] else None for i, n in enumerate(sizes)]
+        ps.opt_step_multi(devs, dg, hp, t)
+        oracle.opt_step_multi(hosts, hg, _ohp(hp), t)
+    for i, (d, h) in enumerate(zip(devs, hosts)):
+        _assert_exact(d, h, f"tensor {i} numel {sizes[i]}")
+
+
+def _clone(st):
+    c = ps.TensorState(st.w_hi.clone(), st.w_lo.clone(), st.m_code.clone(), st.m_scale.clone(),
+                       st.v_code.clone(), st.v_scale.clone())
+    return c
+
+
+def _equal(a, b):
+    return all(torch.equal(getattr(a, k), getattr(b, k)) for k in ("w_hi", "w_lo", "m_code", "m_scale",
+                                                                  "v_code", "v_scale"))
+
+
+def test_batched_equals_per_tensor_calls():
+    sizes = RAGGED + [300000, 77]
+    hp = ps.HParams(lr=1e-4)
+    batch = [dev_state(n, 9, i) for i, n in enumerate(sizes)]
+    single = [_clone(s) for s in batch]
+    for t in range(1, 3):
+        grads = [dev_grad(n, 9, i, t) for i, n in enumerate(sizes)]
+        ps.opt_step_multi(batch, grads, hp, t)
+        for s, g in zip(single, grads):
+            ps.opt_step_multi([s], [g], hp, t)
+    assert all(_equal(a, b) for a, b in zip(batch, single))
+
+
+def test_checkpoint_resume_equals_straight_run():
+    """10 straight steps == 5 steps, state copied to host and back, 5 steps."""
+    n = 200000
+    hp = ps.HParams(weight_decay=0.01, lr=1e-4)
+    a = dev_state(n, 11, 0)
+    b = _clone(a)
+    for t in range(1, 11):
+        ps.opt_step_multi([a], [dev_grad(n, 11, 0, t)], hp, t)
+    for t in range(1, 6):
+        ps.opt_step_multi([b], [dev_grad(n, 11, 0, t)], hp, t)
+    saved = {k: getattr(b, k).cpu() for k in ("w_hi", "w_lo", "m_code", "m_scale", "v_code", "v_scale")}
+    b = ps.TensorState(**{k: v.to(DEV) for k, v in saved.items()})
+    for t in range(6, 11):
+        ps.opt_step_multi([b], [dev_grad(n, 11, 0, t)], hp, t)
+    assert _equal(a, b)
+
+
+def _host_block_state(tid, b, numel, seed):
+    sl = block_slice(b, numel)
+    L = sl.stop - sl.start
+    hi = synth.host_bf16_normal(L, seed, STREAM_HI, tid, 0, SIGMA_W, start=sl.start)
+    lo = synth.host_u16_uniform(L, seed, STREAM_LO, tid, 0, start=sl.start)
+    mc, ms, vc, vs = oracle.zero_moments(L)
+    return oracle.TensorState(hi, lo, mc, ms, vc, vs)
+
+
+def check_sampled_blocks(shapes, devs, hp, steps, seed, per_tensor, outlier_p=0.0):
+    """Every 256-block evolves from its own inputs only, so the oracle runs
+    sampled blocks alone, free-running from the synthetic initial state."""
+    rng = np.random.default_rng(seed + 1)
+    total = 0
+    for tid, (shape, d) in enumerate(zip(shapes, devs)):
+        blocks = sample_blocks(shape.numel, per_tensor, rng)
+        dh = to_host(d)
+        for b in blocks:
+            sl = block_slice(b, shape.numel)
+            st = _host_block_state(tid, b, shape.numel, seed)
+            for t in range(1, steps + 1):
+                g = synth.host_bf16_normal(sl.stop - sl.start, seed, STREAM_GRAD, tid, t, SIGMA_G, outlier_p,
+                                           100.0, start=sl.start)
+                oracle.opt_step(st, g, _ohp(hp), t)
+            for name, dv, hv in (("hi", dh.hi[sl], st.hi), ("lo", dh.lo[sl], st.lo), ("mc", dh.mc[sl], st.mc),
+                                 ("vc", dh.vc[sl], st.vc), ("ms", dh.ms[b:b + 1], st.ms),
+                                 ("vs", dh.vs[b:b + 1], st.vs)):
+                assert np.array_equal(dv.view(np.uint32 if dv.dtype == np.float32 else np.uint16),
+                                      hv.view(np.uint32 if hv.dtype == np.float32 else np.uint16)), \
+                    (shape.name, int(b), name)
+        total += len(blocks)
+    return total
+
+
+def test_flux_double_block_3_steps_sampled():
+    """One FLUX double-stream block (24 tensors, 339,831,296 parameters), NAdamW
+    wd 0.01, one multi-tensor launch per step; sampled blocks vs the oracle."""
+    shapes = synth.WORKLOADS["flux_double_block"]()
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, weight_decay=0.01)
+    seed = 0
+    devs = [dev_state(s.numel, seed, i, s.rows, s.cols) for i, s in enumerate(shapes)]
+    recs_dev = None
+    for t in range(1, 4):
+        grads = [dev_grad(s.numel, seed, i, t) for i, s in enumerate(shapes)]
+        recs_dev = ps.make_records(devs, grads)
+        ps.opt_step_multi(None, None, hp, t, records=recs_dev)
+        del grads
+    torch.cuda.synchronize()
+    nblk = check_sampled_blocks(shapes, devs, hp, 3, seed, per_tensor=48)
+    print(f"  {nblk} sampled blocks bit-exact", flush=True)
