@@ -67,26 +67,46 @@ def read_traffic(workload, n_params, n_blocks):
         return None
 
 
-def build_state(shapes, seed, dev):
+def build_state(shapes, seed, dev, layout="slab"):
+    """Optimizer state for every tensor of the set, filled on the device.
+
+    layout "slab": each stream (hi, lo, grad, m codes, v codes, m scales,
+    v scales) is one contiguous allocation and tensors are 256-byte-aligned
+    views into it; "separate": one allocation per tensor and stream."""
     import torch
 
     import precision_state_amd as ps
     import synth
+    align = 128                                    # elements: 256 bytes of a 16-bit stream
+    offs, boffs, n_tot, nb_tot = [], [], 0, 0
+    for s in shapes:
+        offs.append(n_tot)
+        boffs.append(nb_tot)
+        n_tot += (s.numel + align - 1) // align * align
+        nb_tot += ((s.numel + 255) // 256 + 63) // 64 * 64
+    if layout == "slab":
+        slab = {k: torch.empty(n_tot, dtype=torch.int16, device=dev) for k in ("hi", "lo", "g", "mc", "vc")}
+        slab["mc"].fill_(-32768)
+        slab["vc"].zero_()
+        sc = {k: torch.zeros(nb_tot, dtype=torch.float32, device=dev) for k in ("ms", "vs")}
     states, grads = [], []
     for tid, s in enumerate(shapes):
         n = s.numel
         nb = (n + 255) // 256
-        hi = torch.empty(n, dtype=torch.int16, device=dev)
-        lo = torch.empty(n, dtype=torch.int16, device=dev)
-        g = torch.empty(n, dtype=torch.int16, device=dev)
+        if layout == "slab":
+            o, bo = offs[tid], boffs[tid]
+            hi, lo, g = slab["hi"][o:o + n], slab["lo"][o:o + n], slab["g"][o:o + n]
+            mc, vc = slab["mc"][o:o + n], slab["vc"][o:o + n]
+            ms, vs = sc["ms"][bo:bo + nb], sc["vs"][bo:bo + nb]
+        else:
+            hi, lo, g = (torch.empty(n, dtype=torch.int16, device=dev) for _ in range(3))
+            mc = torch.full((n,), -32768, dtype=torch.int16, device=dev)
+            vc = torch.zeros(n, dtype=torch.int16, device=dev)
+            ms, vs = (torch.zeros(nb, dtype=torch.float32, device=dev) for _ in range(2))
         synth.dev_bf16_normal(hi, seed, synth.STREAM_HI, tid, 0, synth.SIGMA_W)
         synth.dev_u16_uniform(lo, seed, synth.STREAM_LO, tid, 0)
         synth.dev_bf16_normal(g, seed, synth.STREAM_GRAD, tid, 1, synth.SIGMA_G)
-        st = ps.TensorState(hi, lo, torch.full((n,), -32768, dtype=torch.int16, device=dev),
-                            torch.zeros(nb, dtype=torch.float32, device=dev),
-                            torch.zeros(n, dtype=torch.int16, device=dev),
-                            torch.zeros(nb, dtype=torch.float32, device=dev), rows=s.rows, cols=s.cols)
-        states.append(st)
+        states.append(ps.TensorState(hi, lo, mc, ms, vc, vs, rows=s.rows, cols=s.cols))
         grads.append(g)
     return states, grads
 
@@ -127,7 +147,12 @@ def main():
     ap.add_argument("--workload", default="flux_dev_12b",
                     choices=["flux_dev_12b", "flux_double_block", "single_1024x3072"])
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--layout", default="slab", choices=["slab", "separate"],
+                    help="state in one contiguous allocation per stream (slab) or one per tensor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
+                    help="after the timed steps, run 3 plain device copies of GIB GiB (counter calibration "
+                         "and the practical copy bandwidth)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -147,7 +172,7 @@ def main():
     n_blocks = sum((s.numel + 255) // 256 for s in shapes)
     log(f"[bench] {args.workload}: {len(shapes)} tensors, {n_params} params; generating state on {dev}")
     t0 = time.perf_counter()
-    states, grads = build_state(shapes, args.seed, dev)
+    states, grads = build_state(shapes, args.seed, dev, args.layout)
     torch.cuda.synchronize()
     log(f"[bench] state ready in {time.perf_counter() - t0:.1f} s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
@@ -176,6 +201,23 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, {kernel_ms:.3f} ms/launch (events)")
 
+    copy_gbs = None
+    if args.calibrate_copy > 0:
+        nbytes = int(args.calibrate_copy * 2**30) // 16 * 16
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        times = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dst.copy_(src)
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        copy_gbs = 2 * nbytes / (min(times) * 1e-3) / 1e9
+        log(f"[bench] plain copy of {nbytes} bytes: best {min(times):.3f} ms = {copy_gbs:.0f} GB/s (read + write)")
+        del src, dst
+
     alg_bytes = BYTES_PER_PARAM * n_params + BYTES_PER_BLOCK * n_blocks
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
     traffic = read_traffic(args.workload, n_params, n_blocks)
@@ -202,10 +244,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "params": n_params, "tensors": len(shapes),
-                   "algo": "nadam", "lr": 3.5e-6, "weight_decay": 0.0,
+                   "algo": "nadam", "lr": 3.5e-6, "weight_decay": 0.0, "layout": args.layout,
                    "state": "bf16 weight + u16 residual + bf16 grad + u16 m/v codes + fp32 per-256 scales",
                    "hbm_gbs_18B_per_param": BYTES_PER_PARAM * n_params / (kernel_ms * 1e-3) / 1e9,
-                   "kernel_ms": kernel_ms},
+                   "kernel_ms": kernel_ms, "copy_gbs": copy_gbs},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "cpu_baseline": baseline,

@@ -100,6 +100,21 @@ __device__ __forceinline__ uint32_t code_mag(float x, float y) {
 
 __device__ __forceinline__ float fast_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
 
+// Correctly rounded sqrt for v == 0 or v >= 2^-96 (finite): the hardware
+// square root is within one ulp, and the exact residuals v - s'*s of its two
+// neighbours (one fma each, normal-range results) decide which of the three
+// candidates is the rounded root. For 0 < v < 2^-96 use __builtin_sqrtf.
+__device__ __forceinline__ float sqrt_rn_fast(float v) {
+  float s = __builtin_amdgcn_sqrtf(v);
+  float sm = __uint_as_float(__float_as_uint(s) - 1u);
+  float sp = __uint_as_float(__float_as_uint(s) + 1u);
+  float rm = __builtin_fmaf(-sm, s, v);
+  float rp = __builtin_fmaf(-sp, s, v);
+  s = rm <= 0.0f ? sm : s;
+  s = rp > 0.0f ? sp : s;
+  return s;
+}
+
 // Signed code of m given inv = 1/scale (0 for a flushed block).
 __device__ __forceinline__ uint32_t enc_signed(float m, float inv) {
   float x = __builtin_fabsf(m) * inv;

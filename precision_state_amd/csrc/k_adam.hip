@@ -6,9 +6,7 @@
 // belongs to one wave; a 256-element block belongs to 16 lanes (one DPP row),
 // and each lane holds 16 elements: two runs of 8 at offsets r*8 and 128 + r*8
 // of its block, so each of the wave's 16-byte loads covers whole 128-byte
-// lines. Waves are persistent and stride over the items; the tensor of an
-// item is found by advancing a cursor over the prefix ends, which only moves
-// forward.
+// lines. Each work item is one 64-lane workgroup.
 //
 // Per element the kernel reads hi, lo, grad, m_code, v_code (10 bytes) and
 // writes hi, lo, m_code, v_code (8 bytes); per block it reads and writes the
@@ -98,6 +96,7 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
   // zero-coded moments, so m = v = 0 and they never raise a maximum.
   float m[16], v[16];
   float mx_m = 0.0f, mx_v = 0.0f;
+  uint32_t tiny = 0xFFFFFFFFu;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int w = j >> 1;
@@ -109,7 +108,11 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
     v[j] = __builtin_fmaf(c.B2, v0, c.C2 * (g * g));
     mx_m = __builtin_fmaxf(mx_m, __builtin_fabsf(m[j]));
     mx_v = __builtin_fmaxf(mx_v, v[j]);
+    tiny = __builtin_elementwise_min(tiny, __float_as_uint(v[j]) - 1u);
   }
+  // 0 < v < 2^-96 anywhere in the wave: the fast square root's residual test
+  // could underflow there, so the whole wave takes the library sequence.
+  const bool slow_sqrt = __builtin_amdgcn_ballot_w64(tiny < 0x0F7FFFFFu) != 0;
 
   // Phase 2: block scales (row-wide max over the 16 lanes).
   float sm, inv_m, sv, inv_v;
@@ -127,7 +130,7 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
       const int j = 2 * w + o;
       float g = o ? bf16_hi(R.g[w]) : bf16_lo(R.g[w]);
       float wf = __uint_as_float(join_pair_elem<SPLIT>(R.h[w], R.l[w], o));
-      float rv = __builtin_sqrtf(v[j]);
+      float rv = slow_sqrt ? __builtin_sqrtf(v[j]) : sqrt_rn_fast(v[j]);
       float d = __builtin_fmaf(rv, c.RS2, c.EPS);
       float u;
       if (ALGO == PS_ALGO_ADAM)
@@ -170,38 +173,29 @@ __device__ __forceinline__ const DevTensor& rec(const TBL& t, int i) { return t.
 template <class TBL>
 __device__ __forceinline__ uint32_t item_end(const TBL& t, int i) { return t.item_end[i]; }
 
+// One work item per 64-lane workgroup. Workgroups are dispatched in index
+// order, so the waves in flight at any moment cover a compact address range;
+// this keeps HBM pages open and measured faster than persistent waves that
+// stride over the items. The tensor of the item is found by a wave-uniform
+// binary search over the prefix ends (scalar loads).
 template <class TBL, int ALGO, bool WD, int SPLIT>
-__global__ __launch_bounds__(256) void k_adam_step(TBL tbl, uint32_t total_items, StepScalars c) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
-  const uint32_t n_waves = gridDim.x * 4u;
-  int t = 0;
-  uint32_t begin = 0;
-  for (uint32_t item = wave; item < total_items; item += n_waves) {
-    while (item >= item_end(tbl, t)) {
-      begin = item_end(tbl, t);
-      ++t;
-    }
-    const DevTensor& T = rec(tbl, t);
-    process_item<ALGO, WD, SPLIT>(T, (int64_t)(item - begin) * kItemElems, lane, c);
+__global__ __launch_bounds__(64) void k_adam_step(TBL tbl, StepScalars c) {
+  const uint32_t item = blockIdx.x;
+  int lo = 0, hi = tbl.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (item_end(tbl, mid) > item)
+      hi = mid;
+    else
+      lo = mid + 1;
   }
+  const uint32_t begin = lo ? item_end(tbl, lo - 1) : 0u;
+  process_item<ALGO, WD, SPLIT>(rec(tbl, lo), (int64_t)(item - begin) * kItemElems, (int)threadIdx.x, c);
 }
 
 template <class TBL, int ALGO, bool WD, int SPLIT>
 ps_status launch_t(const TBL& tbl, uint32_t total_items, const StepScalars& c, hipStream_t s) {
-  auto kern = k_adam_step<TBL, ALGO, WD, SPLIT>;
-  static int occ = 0;
-  if (occ == 0) {
-    int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, 256, 0) != hipSuccess || o < 1) o = 1;
-    occ = o;
-  }
-  uint64_t waves_needed = total_items;
-  uint64_t blocks = (waves_needed + 3) / 4;
-  uint64_t cap = (uint64_t)device_cu_count() * (uint64_t)occ;
-  if (blocks > cap) blocks = cap;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(kern, dim3((uint32_t)blocks), dim3(256), 0, s, tbl, total_items, c);
+  hipLaunchKernelGGL((k_adam_step<TBL, ALGO, WD, SPLIT>), dim3(total_items), dim3(64), 0, s, tbl, c);
   return hip_check(hipGetLastError(), "k_adam_step launch");
 }
 

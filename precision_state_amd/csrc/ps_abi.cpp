@@ -91,7 +91,7 @@ ps_status build_active(const ps_tensor* t, int32_t n, std::vector<DevTensor>& re
         (s = check_array(x.v_scale, "v_scale", i, 4)))
       return s;
     items += (uint64_t)((x.numel + kItemElems - 1) / kItemElems);
-    if (items > 0xFFFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large (more than 2^32 work items)");
+    if (items > 0x7FFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large (more than 2^31 - 1 work items)");
     recs.push_back(DevTensor{x.w_hi, x.w_lo, x.grad, x.m_code, x.m_scale, x.v_code, x.v_scale, x.numel});
     ends.push_back((uint32_t)items);
   }
