@@ -70,44 +70,30 @@ def read_traffic(workload, n_params, n_blocks):
 def build_state(shapes, seed, dev, layout="slab"):
     """Optimizer state for every tensor of the set, filled on the device.
 
-    layout "slab": each stream (hi, lo, grad, m codes, v codes, m scales,
-    v scales) is one contiguous allocation and tensors are 256-byte-aligned
-    views into it; "separate": one allocation per tensor and stream."""
+    layout "slab": one contiguous allocation per state stream
+    (precision_state_amd.StateSlab); "separate": one allocation per tensor and
+    stream."""
     import torch
 
     import precision_state_amd as ps
     import synth
-    align = 128                                    # elements: 256 bytes of a 16-bit stream
-    offs, boffs, n_tot, nb_tot = [], [], 0, 0
-    for s in shapes:
-        offs.append(n_tot)
-        boffs.append(nb_tot)
-        n_tot += (s.numel + align - 1) // align * align
-        nb_tot += ((s.numel + 255) // 256 + 63) // 64 * 64
     if layout == "slab":
-        slab = {k: torch.empty(n_tot, dtype=torch.int16, device=dev) for k in ("hi", "lo", "g", "mc", "vc")}
-        slab["mc"].fill_(-32768)
-        slab["vc"].zero_()
-        sc = {k: torch.zeros(nb_tot, dtype=torch.float32, device=dev) for k in ("ms", "vs")}
-    states, grads = [], []
-    for tid, s in enumerate(shapes):
-        n = s.numel
-        nb = (n + 255) // 256
-        if layout == "slab":
-            o, bo = offs[tid], boffs[tid]
-            hi, lo, g = slab["hi"][o:o + n], slab["lo"][o:o + n], slab["g"][o:o + n]
-            mc, vc = slab["mc"][o:o + n], slab["vc"][o:o + n]
-            ms, vs = sc["ms"][bo:bo + nb], sc["vs"][bo:bo + nb]
-        else:
+        slab = ps.StateSlab([s.numel for s in shapes], dev, shapes2d=[(s.rows, s.cols) for s in shapes])
+        states, grads = slab.states, slab.grads
+    else:
+        states, grads = [], []
+        for s in shapes:
+            n, nb = s.numel, (s.numel + 255) // 256
             hi, lo, g = (torch.empty(n, dtype=torch.int16, device=dev) for _ in range(3))
-            mc = torch.full((n,), -32768, dtype=torch.int16, device=dev)
-            vc = torch.zeros(n, dtype=torch.int16, device=dev)
-            ms, vs = (torch.zeros(nb, dtype=torch.float32, device=dev) for _ in range(2))
-        synth.dev_bf16_normal(hi, seed, synth.STREAM_HI, tid, 0, synth.SIGMA_W)
-        synth.dev_u16_uniform(lo, seed, synth.STREAM_LO, tid, 0)
+            states.append(ps.TensorState(hi, lo, torch.full((n,), -32768, dtype=torch.int16, device=dev),
+                                         torch.zeros(nb, dtype=torch.float32, device=dev),
+                                         torch.zeros(n, dtype=torch.int16, device=dev),
+                                         torch.zeros(nb, dtype=torch.float32, device=dev), rows=s.rows, cols=s.cols))
+            grads.append(g)
+    for tid, (st, g) in enumerate(zip(states, grads)):
+        synth.dev_bf16_normal(st.w_hi, seed, synth.STREAM_HI, tid, 0, synth.SIGMA_W)
+        synth.dev_u16_uniform(st.w_lo, seed, synth.STREAM_LO, tid, 0)
         synth.dev_bf16_normal(g, seed, synth.STREAM_GRAD, tid, 1, synth.SIGMA_G)
-        states.append(ps.TensorState(hi, lo, mc, ms, vc, vs, rows=s.rows, cols=s.cols))
-        grads.append(g)
     return states, grads
 
 
@@ -142,8 +128,8 @@ def cpu_baseline(shapes, seed, target_params=40_000_000):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="flux_dev_12b",
                     choices=["flux_dev_12b", "flux_double_block", "single_1024x3072"])
     ap.add_argument("--seed", type=int, default=0)
@@ -181,11 +167,17 @@ def main():
     recs = ps.make_records(states, grads)
     stream = torch.cuda.current_stream()
     step = 0
+    wev = []
     for _ in range(args.warmup):
         step += 1
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
         ps.opt_step_multi(None, None, hp, step, stream=stream, records=recs)
+        b.record(stream)
+        wev.append((a, b))
     torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done")
+    wt = [a.elapsed_time(b) for a, b in wev]
+    log(f"[bench] warmup {args.warmup} done" + (f": first {wt[0]:.3f} ms, last {wt[-1]:.3f} ms" if wt else ""))
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -197,9 +189,11 @@ def main():
         ev[k][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    per_step = [a.elapsed_time(b) for a, b in ev]
+    kernel_ms = sum(per_step) / args.steps
     ms_per_step = wall * 1e3 / args.steps
-    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, {kernel_ms:.3f} ms/launch (events)")
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, {kernel_ms:.3f} ms/launch (events); "
+        f"per launch min {min(per_step):.3f} max {max(per_step):.3f}")
 
     copy_gbs = None
     if args.calibrate_copy > 0:

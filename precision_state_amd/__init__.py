@@ -170,6 +170,47 @@ class TensorState:
         return self.w_hi.numel()
 
 
+class StateSlab:
+    """Optimizer state of a whole tensor list in one contiguous device
+    allocation per stream (bf16 weights, residuals, gradients, m codes, v codes,
+    m scales, v scales); each tensor gets 256-byte-aligned views. Streaming
+    the step over a few large allocations needs far fewer address translations
+    than one allocation per tensor and stream.
+
+    numels: element count of each tensor. Moments start as the zero codes with
+    zero scales; weights, residuals and gradients are left uninitialised for
+    the caller to fill (or copy into)."""
+
+    ALIGN = 128    # elements of a 16-bit stream = 256 bytes
+
+    def __init__(self, numels, device="cuda", with_grads=True, shapes2d=None):
+        import torch
+        self.numels = list(numels)
+        offs, boffs, n_tot, nb_tot = [], [], 0, 0
+        for n in self.numels:
+            offs.append(n_tot)
+            boffs.append(nb_tot)
+            n_tot += (n + self.ALIGN - 1) // self.ALIGN * self.ALIGN
+            nb_tot += ((n + BLOCK - 1) // BLOCK + 63) // 64 * 64
+        names = ["hi", "lo", "mc", "vc"] + (["g"] if with_grads else [])
+        self.slab = {k: torch.empty(max(1, n_tot), dtype=torch.int16, device=device) for k in names}
+        self.slab["mc"].fill_(-32768)          # 0x8000: the zero code of the signed kind
+        self.slab["vc"].zero_()
+        self.scales = {k: torch.zeros(max(1, nb_tot), dtype=torch.float32, device=device) for k in ("ms", "vs")}
+        self.states, self.grads = [], []
+        for i, n in enumerate(self.numels):
+            o, bo, nb = offs[i], boffs[i], (n + BLOCK - 1) // BLOCK
+            rows, cols = shapes2d[i] if shapes2d else (0, 0)
+            self.states.append(TensorState(self.slab["hi"][o:o + n], self.slab["lo"][o:o + n],
+                                           self.slab["mc"][o:o + n], self.scales["ms"][bo:bo + nb],
+                                           self.slab["vc"][o:o + n], self.scales["vs"][bo:bo + nb],
+                                           rows=rows, cols=cols))
+            self.grads.append(self.slab["g"][o:o + n] if with_grads else None)
+
+    def records(self, grads=None):
+        return make_records(self.states, self.grads if grads is None else grads)
+
+
 def make_records(states: Sequence[TensorState], grads: Sequence[Optional[object]]):
     """ctypes array of ps_tensor records (reusable while the tensors live)."""
     if len(states) != len(grads):

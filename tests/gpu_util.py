@@ -135,3 +135,42 @@ def sample_blocks(numel, k, rng):
 
 def block_slice(b, numel):
     return slice(b * 256, min(numel, (b + 1) * 256))
+
+
+def ohp(hp):
+    """oracle.HParams of a precision_state_amd.HParams."""
+    return oracle.HParams(hp.algo, hp.split_mode, hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
+                          hp.momentum_decay)
+
+
+def _host_block_state(tid, b, numel, seed):
+    sl = block_slice(b, numel)
+    L = sl.stop - sl.start
+    hi = synth.host_bf16_normal(L, seed, STREAM_HI, tid, 0, SIGMA_W, start=sl.start)
+    lo = synth.host_u16_uniform(L, seed, STREAM_LO, tid, 0, start=sl.start)
+    mc, ms, vc, vs = oracle.zero_moments(L)
+    return oracle.TensorState(hi, lo, mc, ms, vc, vs)
+
+
+def check_sampled_blocks(shapes, devs, hp, steps, seed, per_tensor, outlier_p=0.0):
+    """Every 256-block evolves from its own inputs only, so the oracle runs
+    sampled blocks alone, free-running from the synthetic initial state."""
+    rng = np.random.default_rng(seed + 1)
+    total = 0
+    for tid, (shape, d) in enumerate(zip(shapes, devs)):
+        blocks = sample_blocks(shape.numel, per_tensor, rng)
+        for b in blocks:
+            sl = block_slice(b, shape.numel)
+            st = _host_block_state(tid, b, shape.numel, seed)
+            for t in range(1, steps + 1):
+                g = synth.host_bf16_normal(sl.stop - sl.start, seed, STREAM_GRAD, tid, t, SIGMA_G, outlier_p,
+                                           100.0, start=sl.start)
+                oracle.opt_step(st, g, ohp(hp), t)
+            got = {"hi": u16(d.w_hi[sl]), "lo": u16(d.w_lo[sl]), "mc": u16(d.m_code[sl]), "vc": u16(d.v_code[sl]),
+                   "ms": f32(d.m_scale[b:b + 1]).view(np.uint32), "vs": f32(d.v_scale[b:b + 1]).view(np.uint32)}
+            want = {"hi": st.hi, "lo": st.lo, "mc": st.mc, "vc": st.vc, "ms": st.ms.view(np.uint32),
+                    "vs": st.vs.view(np.uint32)}
+            for name in got:
+                assert np.array_equal(got[name], want[name]), (shape.name, int(b), name)
+        total += len(blocks)
+    return total

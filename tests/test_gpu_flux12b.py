@@ -1,0 +1,39 @@
+"""Full-size parity on the FLUX-dev-shaped set (780 tensors, 11,901,408,320
+parameters), in the layout and launch configuration bench.py times: slab
+state, one multi-tensor NAdam launch per step (lr 3.5e-6, betas 0.9/0.999,
+eps 1e-8, wd 0). The oracle checks sampled 256-blocks of every tensor
+(including every partial block), each run free from the synthetic start."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import check_sampled_blocks
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import precision_state_amd as ps  # noqa: E402
+
+
+def test_flux_dev_12b_two_steps_sampled():
+    free, _ = torch.cuda.mem_get_info()
+    if free < 160 * 2**30:
+        pytest.skip(f"needs ~150 GiB of device memory, {free / 2**30:.0f} GiB free")
+    import bench
+    shapes = synth.WORKLOADS["flux_dev_12b"]()
+    seed = 0
+    states, grads = bench.build_state(shapes, seed, "cuda", "slab")
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, weight_decay=0.0)
+    recs = ps.make_records(states, grads)
+    ps.opt_step_multi(None, None, hp, 1, records=recs)
+    for tid, g in enumerate(grads):                 # fresh gradients for step 2
+        synth.dev_bf16_normal(g, seed, synth.STREAM_GRAD, tid, 2, synth.SIGMA_G)
+    ps.opt_step_multi(None, None, hp, 2, records=recs)
+    torch.cuda.synchronize()
+    del grads, recs
+    nblk = check_sampled_blocks(shapes, states, hp, 2, seed, per_tensor=6)
+    print(f"  {nblk} sampled blocks over {len(shapes)} tensors bit-exact", flush=True)
+    assert nblk > 780

@@ -8,9 +8,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import (DEV, block_slice, dev_grad, dev_state, dev_u16_from, f32, host_grad, host_state,
-                      max_code_diff, mismatches, nblocks, sample_blocks, to_host, u16)
-from synth import SIGMA_G, SIGMA_W, STREAM_GRAD, STREAM_HI, STREAM_LO
+from gpu_util import (DEV, check_sampled_blocks, dev_grad, dev_state, dev_u16_from, f32, host_grad,
+                      host_state, max_code_diff, mismatches, nblocks, ohp, to_host, u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,11 +18,6 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import precision_state_amd as ps  # noqa: E402
-
-
-def _ohp(hp: ps.HParams):
-    return oracle.HParams(hp.algo, hp.split_mode, hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
-                          hp.momentum_decay)
 
 
 def _assert_exact(dev, host, what):
@@ -157,7 +151,7 @@ def test_single_1024x3072_nadam_10_steps_free_running():
     hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, weight_decay=0.0)
     for t in range(1, 11):
         ps.opt_step_multi([dev], [dev_grad(n, 0, 0, t)], hp, t)
-        oracle.opt_step(host, host_grad(n, 0, 0, t), _ohp(hp), t)
+        oracle.opt_step(host, host_grad(n, 0, 0, t), ohp(hp), t)
         _assert_exact(dev, host, f"step {t}")
 
 
@@ -171,7 +165,7 @@ def test_step_variants(algo, wd, split_mode):
     host = host_state(n, 5, 3)
     for t in range(1, 4):
         ps.opt_step_multi([dev], [dev_grad(n, 5, 3, t, 0.001)], hp, t)
-        oracle.opt_step(host, host_grad(n, 5, 3, t, 0.001), _ohp(hp), t)
+        oracle.opt_step(host, host_grad(n, 5, 3, t, 0.001), ohp(hp), t)
     _assert_exact(dev, host, f"algo {algo} wd {wd} split {split_mode}")
 
 
@@ -192,7 +186,7 @@ def test_multi_tensor_ragged_lists(count):
         dg = [dev_grad(n, 7, i, t) if has_grad[i] else None for i, n in enumerate(sizes)]
         hg = [host_grad(n, 7, i, t) if has_grad[i] else None for i, n in enumerate(sizes)]
         ps.opt_step_multi(devs, dg, hp, t)
-        oracle.opt_step_multi(hosts, hg, _ohp(hp), t)
+        oracle.opt_step_multi(hosts, hg, ohp(hp), t)
     for i, (d, h) in enumerate(zip(devs, hosts)):
         _assert_exact(d, h, f"tensor {i} numel {sizes[i]}")
 
@@ -236,40 +230,6 @@ def test_checkpoint_resume_equals_straight_run():
     for t in range(6, 11):
         ps.opt_step_multi([b], [dev_grad(n, 11, 0, t)], hp, t)
     assert _equal(a, b)
-
-
-def _host_block_state(tid, b, numel, seed):
-    sl = block_slice(b, numel)
-    L = sl.stop - sl.start
-    hi = synth.host_bf16_normal(L, seed, STREAM_HI, tid, 0, SIGMA_W, start=sl.start)
-    lo = synth.host_u16_uniform(L, seed, STREAM_LO, tid, 0, start=sl.start)
-    mc, ms, vc, vs = oracle.zero_moments(L)
-    return oracle.TensorState(hi, lo, mc, ms, vc, vs)
-
-
-def check_sampled_blocks(shapes, devs, hp, steps, seed, per_tensor, outlier_p=0.0):
-    """Every 256-block evolves from its own inputs only, so the oracle runs
-    sampled blocks alone, free-running from the synthetic initial state."""
-    rng = np.random.default_rng(seed + 1)
-    total = 0
-    for tid, (shape, d) in enumerate(zip(shapes, devs)):
-        blocks = sample_blocks(shape.numel, per_tensor, rng)
-        dh = to_host(d)
-        for b in blocks:
-            sl = block_slice(b, shape.numel)
-            st = _host_block_state(tid, b, shape.numel, seed)
-            for t in range(1, steps + 1):
-                g = synth.host_bf16_normal(sl.stop - sl.start, seed, STREAM_GRAD, tid, t, SIGMA_G, outlier_p,
-                                           100.0, start=sl.start)
-                oracle.opt_step(st, g, _ohp(hp), t)
-            for name, dv, hv in (("hi", dh.hi[sl], st.hi), ("lo", dh.lo[sl], st.lo), ("mc", dh.mc[sl], st.mc),
-                                 ("vc", dh.vc[sl], st.vc), ("ms", dh.ms[b:b + 1], st.ms),
-                                 ("vs", dh.vs[b:b + 1], st.vs)):
-                assert np.array_equal(dv.view(np.uint32 if dv.dtype == np.float32 else np.uint16),
-                                      hv.view(np.uint32 if hv.dtype == np.float32 else np.uint16)), \
-                    (shape.name, int(b), name)
-        total += len(blocks)
-    return total
 
 
 def test_flux_double_block_3_steps_sampled():
