@@ -125,6 +125,70 @@ def cpu_baseline(shapes, seed, target_params=40_000_000):
                       f"single thread, {dt:.1f} s"}
 
 
+def bench_factored(args):
+    """Adafactor-style step (beta1 = 0, factored v, clip 1.0, beta2 0.999,
+    eps1 1e-30, lr 3.5e-6) on the FLUX double-block shapes: 2-D tensors
+    factored, 1-D tensors with the uint16 codec. Grads N(0, 1e-3) with 0.1%
+    outliers at 100x. Algorithmic bytes: 10 B/param (read hi, lo, grad; write
+    hi, lo); the kernels read the gradient three times (14 B/param)."""
+    import torch
+
+    import precision_state_amd as ps
+    import synth
+    dev = "cuda:0"
+    wl = "flux_double_block" if args.workload == "flux_dev_12b" else args.workload
+    shapes = synth.WORKLOADS[wl]()
+    n_params = synth.total_params(shapes)
+    states, grads = [], []
+    for tid, s in enumerate(shapes):
+        n = s.numel
+        hi, lo, g = (torch.empty(n, dtype=torch.int16, device=dev) for _ in range(3))
+        synth.dev_bf16_normal(hi, args.seed, synth.STREAM_HI, tid, 0, synth.SIGMA_W)
+        synth.dev_u16_uniform(lo, args.seed, synth.STREAM_LO, tid, 0)
+        synth.dev_bf16_normal(g, args.seed, synth.STREAM_GRAD, tid, 1, synth.SIGMA_G, 0.001, 100.0)
+        st = ps.TensorState(hi, lo, rows=s.rows, cols=s.cols)
+        if s.is_2d:
+            st.row_ema = torch.zeros(s.rows, dtype=torch.float32, device=dev)
+            st.col_ema = torch.zeros(s.cols, dtype=torch.float32, device=dev)
+        else:
+            st.v_code = torch.zeros(n, dtype=torch.int16, device=dev)
+            st.v_scale = torch.zeros((n + 255) // 256, dtype=torch.float32, device=dev)
+        states.append(st)
+        grads.append(g)
+    recs = ps.make_records(states, grads)
+    ws = torch.empty(ps.factored_workspace_size(None, records=recs), dtype=torch.uint8, device=dev)
+    hp = ps.FactoredHParams(lr=3.5e-6, beta2=0.999, eps1=1e-30, clip_threshold=1.0, weight_decay=0.0)
+    stream = torch.cuda.current_stream()
+    step = 0
+    for _ in range(args.warmup):
+        step += 1
+        ps.factored_step(None, None, hp, step, workspace=ws, stream=stream, records=recs)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(args.steps):
+        step += 1
+        ps.factored_step(None, None, hp, step, workspace=ws, stream=stream, records=recs)
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = a.elapsed_time(b) / args.steps
+    log(f"[bench] factored: {args.steps} steps, {step_ms:.3f} ms/step (events), {wall * 1e3 / args.steps:.3f} wall")
+    gbs10 = 10 * n_params / (step_ms * 1e-3) / 1e9
+    gbs14 = 14 * n_params / (step_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "factored optimizer-updated params/sec (Adafactor-style step, FLUX double-block shapes)",
+        "value": n_params * args.steps / wall, "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl + "_factored", "params": n_params, "tensors": len(shapes), "step_ms": step_ms,
+                   "gbs_10B_per_param": gbs10, "gbs_14B_per_param": gbs14},
+        "roofline": {"bound": "hbm", "achieved": gbs10, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs10 / PEAK_HBM_GBS, "traffic": None},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +199,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--layout", default="slab", choices=["slab", "separate"],
                     help="state in one contiguous allocation per stream (slab) or one per tensor")
+    ap.add_argument("--mode", default="nadam", choices=["nadam", "factored"],
+                    help="nadam: the fused (N)AdamW step (headline); factored: the Adafactor-style step "
+                         "(no first moment, factored second moment, update clipping) on the same shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="after the timed steps, run 3 plain device copies of GIB GiB (counter calibration "
@@ -153,6 +220,8 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.mode == "factored":
+        return bench_factored(args)
     shapes = synth.WORKLOADS[args.workload]()
     n_params = synth.total_params(shapes)
     n_blocks = sum((s.numel + 255) // 256 for s in shapes)

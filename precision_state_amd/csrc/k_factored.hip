@@ -1,0 +1,355 @@
+// k_factored.hip - Adafactor-style step without first moment: factored
+// second moment (row/column EMAs of mean g^2 + eps1), update clipping by the
+// tensor's RMS, decoupled weight decay, residual split [ADAF,
+// adafactor_step_param; PRODIGY, beta1 = 0 / factored / update clipping].
+//
+// 2-D tensors [R, C] are cut into 64 x 256 tiles, one 256-thread workgroup
+// each; thread t handles columns (t % 32) * 8 .. + 8 of rows t / 32 + 8k,
+// k = 0..7, so each half-wave reads one 512-byte row segment per load.
+// Passes over the gradient: tile row/column sums of q = g^2 + eps1 (double);
+// row/column finalize (EMAs, chunk sums of the new row EMA); factors
+// rho_i = 1/sqrt(r_i / rbar), kap_j = 1/sqrt(c_j); tile sums of U^2 (double);
+// clip factor per tensor; apply. 1-D tensors keep v in the uint16 codec and
+// use 1024-element items like the fused (N)AdamW step.
+//
+// All reductions use fixed trees (no atomics), so results are deterministic.
+#include "dev_common.h"
+#include "ps_internal.h"
+
+namespace ps {
+namespace {
+
+constexpr int kT = 256;
+
+// First entry of the wave-uniform prefix-end array greater than x.
+__device__ __forceinline__ int find_end(const uint32_t* __restrict__ end, int n, uint32_t x, uint32_t& begin) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (end[mid] > x)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  begin = lo ? end[lo - 1] : 0u;
+  return lo;
+}
+
+// 8 consecutive 16-bit values of row r starting at column c (bits of missing
+// elements are 0, valid bit j set when column c + j exists).
+__device__ __forceinline__ uint32_t load_row8(const uint16_t* __restrict__ base, const F2D& X, int r, int c,
+                                              uint32_t* w) {
+  w[0] = w[1] = w[2] = w[3] = 0u;
+  if (r >= X.R || c >= X.C) return 0u;
+  const uint16_t* p = base + (size_t)r * (size_t)X.C + (size_t)c;
+  if (X.vec && c + 8 <= X.C) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    return 0xFFu;
+  }
+  uint32_t valid = 0;
+  for (int j = 0; j < 8; ++j)
+    if (c + j < X.C) {
+      w[j >> 1] |= (uint32_t)p[j] << (16 * (j & 1));
+      valid |= 1u << j;
+    }
+  return valid;
+}
+
+__device__ __forceinline__ void store_row8(uint16_t* __restrict__ base, const F2D& X, int r, int c, uint32_t valid,
+                                           const uint32_t* w) {
+  if (r >= X.R || c >= X.C) return;
+  uint16_t* p = base + (size_t)r * (size_t)X.C + (size_t)c;
+  if (valid == 0xFFu && X.vec) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    return;
+  }
+  for (int j = 0; j < 8; ++j)
+    if (valid & (1u << j)) p[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+}
+
+__device__ __forceinline__ float bf16_at(const uint32_t* w, int j) {
+  return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+}
+
+// Sum of a double over the 256 threads of the workgroup, fixed tree.
+__device__ __forceinline__ double block_sum(double x, double* red) {
+  red[threadIdx.x] = x;
+  __syncthreads();
+  for (int o = kT / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  double r = red[0];
+  __syncthreads();
+  return r;
+}
+
+// ---- pass 1: tile row and column sums of q = g^2 + eps1 ---------------------
+__global__ __launch_bounds__(kT) void k_f_stats(FPlan P, FScalars S) {
+  uint32_t begin;
+  const F2D& X = P.t2[find_end(P.tile_end, P.n2, blockIdx.x, begin)];
+  const uint32_t tile = blockIdx.x - begin;
+  const int tr = (int)(tile / (uint32_t)X.ntc), tc = (int)(tile - (uint32_t)tr * X.ntc);
+  const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
+  const int c = tc * kFTileCols + cg * 8;
+  double cacc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) cacc[j] = 0.0;
+  for (int k = 0; k < 8; ++k) {
+    const int r = tr * kFTileRows + rg + 8 * k;
+    uint32_t w[4];
+    const uint32_t valid = load_row8(X.g, X, r, c, w);
+    double rs = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float g = bf16_at(w, j);
+      const float q = (valid >> j & 1u) ? g * g + S.EPS1 : 0.0f;
+      rs += (double)q;
+      cacc[j] += (double)q;
+    }
+    for (int o = 1; o < 32; o <<= 1) rs += __shfl_xor(rs, o, 32);
+    if (cg == 0 && r < X.R) X.rowpart[(size_t)tc * X.R + r] = rs;
+  }
+  __shared__ double lds[8][kFTileCols];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lds[rg][cg * 8 + j] = cacc[j];
+  __syncthreads();
+  const int cc = tc * kFTileCols + (int)threadIdx.x;
+  if (cc < X.C) {
+    double s = 0.0;
+    for (int q = 0; q < 8; ++q) s += lds[q][threadIdx.x];
+    X.colpart[(size_t)tr * X.C + cc] = s;
+  }
+}
+
+// ---- pass 2: row/column EMAs and chunk sums of the new row EMA -------------
+__global__ __launch_bounds__(kT) void k_f_rowcol(FPlan P, FScalars S) {
+  uint32_t begin;
+  const F2D& X = P.t2[find_end(P.rc_end, P.n2, blockIdx.x, begin)];
+  const int w = (int)(blockIdx.x - begin);
+  __shared__ double red[kT];
+  if (w < X.nrw) {
+    const int i = w * kFRowColChunk + (int)threadIdx.x;
+    double rv = 0.0;
+    if (i < X.R) {
+      double s = 0.0;
+      for (int tc = 0; tc < X.ntc; ++tc) s += X.rowpart[(size_t)tc * X.R + i];
+      const float mean = (float)(s / (double)X.C);
+      const float r = __builtin_fmaf(S.B2, X.row[i], S.C2 * mean);
+      X.row[i] = r;
+      rv = (double)r;
+    }
+    const double t = block_sum(rv, red);
+    if (threadIdx.x == 0) X.rpart[w] = t;
+  } else {
+    const int j = (w - X.nrw) * kFRowColChunk + (int)threadIdx.x;
+    if (j < X.C) {
+      double s = 0.0;
+      for (int tr = 0; tr < X.ntr; ++tr) s += X.colpart[(size_t)tr * X.C + j];
+      const float mean = (float)(s / (double)X.R);
+      X.col[j] = __builtin_fmaf(S.B2, X.col[j], S.C2 * mean);
+    }
+  }
+}
+
+// ---- pass 3: factors of V^-1/2 ----------------------------------------------
+__global__ __launch_bounds__(kT) void k_f_factors(FPlan P) {
+  uint32_t begin;
+  const F2D& X = P.t2[find_end(P.rc_end, P.n2, blockIdx.x, begin)];
+  const int w = (int)(blockIdx.x - begin);
+  if (w < X.nrw) {
+    double s = 0.0;
+    for (int q = 0; q < X.nrw; ++q) s += X.rpart[q];
+    const float rbar = (float)(s / (double)X.R);
+    const int i = w * kFRowColChunk + (int)threadIdx.x;
+    if (i < X.R) X.rho[i] = 1.0f / __builtin_sqrtf(X.row[i] / rbar);
+  } else {
+    const int j = (w - X.nrw) * kFRowColChunk + (int)threadIdx.x;
+    if (j < X.C) X.kap[j] = 1.0f / __builtin_sqrtf(X.col[j]);
+  }
+}
+
+// ---- pass 4: tile sums of U^2, U = (g * rho_i) * kap_j ----------------------
+__global__ __launch_bounds__(kT) void k_f_usq(FPlan P) {
+  uint32_t begin;
+  const F2D& X = P.t2[find_end(P.tile_end, P.n2, blockIdx.x, begin)];
+  const uint32_t tile = blockIdx.x - begin;
+  const int tr = (int)(tile / (uint32_t)X.ntc), tc = (int)(tile - (uint32_t)tr * X.ntc);
+  const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
+  const int c = tc * kFTileCols + cg * 8;
+  float kap[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kap[j] = (c + j < X.C) ? X.kap[c + j] : 0.0f;
+  double acc = 0.0;
+  for (int k = 0; k < 8; ++k) {
+    const int r = tr * kFTileRows + rg + 8 * k;
+    uint32_t w[4];
+    const uint32_t valid = load_row8(X.g, X, r, c, w);
+    if (!valid) continue;
+    const float rho = X.rho[r];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float U = (bf16_at(w, j) * rho) * kap[j];
+      acc += (valid >> j & 1u) ? (double)U * (double)U : 0.0;
+    }
+  }
+  __shared__ double red[kT];
+  const double t = block_sum(acc, red);
+  if (threadIdx.x == 0) X.upart[tile] = t;
+}
+
+// ---- 1-D tensors: v update (stored in the workspace) and item sums of U^2 ---
+__global__ __launch_bounds__(64) void k_f1_stats(FPlan P, FScalars S) {
+  uint32_t begin;
+  const F1D& X = P.t1[find_end(P.item_end, P.n1, blockIdx.x, begin)];
+  const int64_t elem0 = (int64_t)(blockIdx.x - begin) * kItemElems;
+  const int lane = threadIdx.x, b = lane >> 4, r = lane & 15;
+  const int64_t blk = (elem0 >> 8) + b;
+  const float vs_old = (blk * kBlock < X.n) ? X.vs[blk] : 0.0f;
+  double acc = 0.0;
+  for (int half = 0; half < 2; ++half) {
+    const int64_t e = elem0 + b * kBlock + half * 128 + r * 8;
+    for (int j = 0; j < 8; ++j) {
+      if (e + j >= X.n) break;
+      const float g = __uint_as_float((uint32_t)X.g[e + j] << 16);
+      const float v0 = dec_unsigned(__uint_as_float(0x4B000000u | X.vc[e + j]), vs_old);
+      const float q = g * g + S.EPS1;
+      const float v = __builtin_fmaf(S.B2, v0, S.C2 * q);
+      X.v[e + j] = v;
+      const float U = g * (1.0f / __builtin_sqrtf(v));
+      acc += (double)U * (double)U;
+    }
+  }
+  for (int o = 1; o < 64; o <<= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) X.upart[blockIdx.x - begin] = acc;
+}
+
+// ---- clip factor per tensor: lr / max(1, RMS(U) / clip) ---------------------
+__global__ __launch_bounds__(kT) void k_f_clip(FPlan P, FScalars S) {
+  const double* parts;
+  int np;
+  double n;
+  float* f;
+  if ((int)blockIdx.x < P.n2) {
+    const F2D& X = P.t2[blockIdx.x];
+    parts = X.upart; np = X.ntr * X.ntc; n = (double)X.R * (double)X.C; f = X.f;
+  } else {
+    const F1D& X = P.t1[blockIdx.x - P.n2];
+    parts = X.upart; np = X.nitems; n = (double)X.n; f = X.f;
+  }
+  double s = 0.0;
+  for (int q = threadIdx.x; q < np; q += kT) s += parts[q];
+  __shared__ double red[kT];
+  const double t = block_sum(s, red);
+  if (threadIdx.x == 0) {
+    const double rms = sqrt(t / n);
+    const double r = rms / S.clip;
+    *f = (float)(S.lr / (r > 1.0 ? r : 1.0));
+  }
+}
+
+// ---- apply to 2-D tensors ----------------------------------------------------
+template <int SPLIT>
+__global__ __launch_bounds__(kT) void k_f_apply(FPlan P, FScalars S) {
+  uint32_t begin;
+  const F2D& X = P.t2[find_end(P.tile_end, P.n2, blockIdx.x, begin)];
+  const uint32_t tile = blockIdx.x - begin;
+  const int tr = (int)(tile / (uint32_t)X.ntc), tc = (int)(tile - (uint32_t)tr * X.ntc);
+  const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
+  const int c = tc * kFTileCols + cg * 8;
+  const float f = *X.f;
+  float kap[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kap[j] = (c + j < X.C) ? X.kap[c + j] : 0.0f;
+  for (int k = 0; k < 8; ++k) {
+    const int r = tr * kFTileRows + rg + 8 * k;
+    uint32_t gw[4], hw[4], lw[4];
+    const uint32_t valid = load_row8(X.g, X, r, c, gw);
+    if (!valid) continue;
+    load_row8(X.hi, X, r, c, hw);
+    load_row8(X.lo, X, r, c, lw);
+    const float rho = X.rho[r];
+    uint32_t oh[4], ol[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t wb[2];
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        const int j = 2 * p + o;
+        const float U = (bf16_at(gw, j) * rho) * kap[j];
+        const float w = __uint_as_float(join_pair_elem<SPLIT>(hw[p], lw[p], o));
+        float x = U * f;
+        if (S.wd) x = __builtin_fmaf(S.CWD, w, x);
+        wb[o] = __float_as_uint(w - x);
+      }
+      split_pair<SPLIT>(wb[0], wb[1], oh[p], ol[p]);
+    }
+    store_row8(X.hi, X, r, c, valid, oh);
+    store_row8(X.lo, X, r, c, valid, ol);
+  }
+}
+
+// ---- apply to 1-D tensors and re-encode v --------------------------------------
+template <int SPLIT>
+__global__ __launch_bounds__(64) void k_f1_apply(FPlan P, FScalars S) {
+  uint32_t begin;
+  const F1D& X = P.t1[find_end(P.item_end, P.n1, blockIdx.x, begin)];
+  const int64_t elem0 = (int64_t)(blockIdx.x - begin) * kItemElems;
+  const int lane = threadIdx.x, b = lane >> 4, r = lane & 15;
+  const int64_t blk = (elem0 >> 8) + b;
+  const float f = *X.f;
+  float v[16];
+  float mx = 0.0f;
+  for (int half = 0; half < 2; ++half) {
+    const int64_t e = elem0 + b * kBlock + half * 128 + r * 8;
+    for (int j = 0; j < 8; ++j) {
+      const int64_t ej = e + j;
+      v[half * 8 + j] = 0.0f;
+      if (ej >= X.n) continue;
+      const float vj = X.v[ej];
+      v[half * 8 + j] = vj;
+      mx = __builtin_fmaxf(mx, vj);
+      const float g = __uint_as_float((uint32_t)X.g[ej] << 16);
+      const float U = g * (1.0f / __builtin_sqrtf(vj));
+      const uint32_t wbits = join_pair_elem<SPLIT>((uint32_t)X.hi[ej], (uint32_t)X.lo[ej], 0);
+      const float w = __uint_as_float(wbits);
+      float x = U * f;
+      if (S.wd) x = __builtin_fmaf(S.CWD, w, x);
+      uint32_t h2, l2;
+      split_pair<SPLIT>(__float_as_uint(w - x), 0u, h2, l2);
+      X.hi[ej] = (uint16_t)h2;
+      X.lo[ej] = (uint16_t)l2;
+    }
+  }
+  float s, inv;
+  block_scale(row16_max(mx), s, inv);
+  for (int half = 0; half < 2; ++half) {
+    const int64_t e = elem0 + b * kBlock + half * 128 + r * 8;
+    for (int j = 0; j < 8; ++j)
+      if (e + j < X.n) X.vc[e + j] = (uint16_t)enc_unsigned(v[half * 8 + j], inv);
+  }
+  if (r == 0 && blk * kBlock < X.n) X.vs[blk] = s;
+}
+
+template <int SPLIT>
+ps_status launch_all(const FPlan& P, const FScalars& S, hipStream_t s) {
+  if (P.n_tiles) hipLaunchKernelGGL(k_f_stats, dim3(P.n_tiles), dim3(kT), 0, s, P, S);
+  if (P.n_items) hipLaunchKernelGGL(k_f1_stats, dim3(P.n_items), dim3(64), 0, s, P, S);
+  if (P.n_rc) hipLaunchKernelGGL(k_f_rowcol, dim3(P.n_rc), dim3(kT), 0, s, P, S);
+  if (P.n_rc) hipLaunchKernelGGL(k_f_factors, dim3(P.n_rc), dim3(kT), 0, s, P);
+  if (P.n_tiles) hipLaunchKernelGGL(k_f_usq, dim3(P.n_tiles), dim3(kT), 0, s, P);
+  hipLaunchKernelGGL(k_f_clip, dim3(P.n2 + P.n1), dim3(kT), 0, s, P, S);
+  if (P.n_tiles) hipLaunchKernelGGL((k_f_apply<SPLIT>), dim3(P.n_tiles), dim3(kT), 0, s, P, S);
+  if (P.n_items) hipLaunchKernelGGL((k_f1_apply<SPLIT>), dim3(P.n_items), dim3(64), 0, s, P, S);
+  return hip_check(hipGetLastError(), "factored step launch");
+}
+
+}  // namespace
+
+ps_status launch_factored(const FPlan& plan, const FScalars& sc, int split_mode, hipStream_t s) {
+  if (split_mode == PS_SPLIT_NEAREST_AWAY) return launch_all<PS_SPLIT_NEAREST_AWAY>(plan, sc, s);
+  return launch_all<PS_SPLIT_TRUNC>(plan, sc, s);
+}
+
+}  // namespace ps

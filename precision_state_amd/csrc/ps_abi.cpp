@@ -44,11 +44,14 @@ int device_cu_count() {
   return cached[dev];
 }
 
-namespace {
-
 // ---------------------------------------------------------------------------
 // validation
 // ---------------------------------------------------------------------------
+
+bool is_finite(double x) { return std::isfinite(x); }
+bool is_aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+namespace {
 
 ps_status check_hparams(const ps_hparams* hp) {
   if (!hp) return fail(PS_ERR_INVALID_ARG, "hparams is NULL");
@@ -99,48 +102,48 @@ ps_status build_active(const ps_tensor* t, int32_t n, std::vector<DevTensor>& re
 }
 
 // ---------------------------------------------------------------------------
-// device tensor-table cache: one immutable device copy per distinct list
+// device blob cache: one immutable device copy per distinct host blob (tensor
+// tables, factored-step plans). A training loop passes the same list every
+// step, so after the first call nothing is uploaded.
 // ---------------------------------------------------------------------------
 
-struct TableEntry {
+struct BlobEntry {
   int device = -1;
-  std::vector<DevTensor> recs;
-  std::vector<uint32_t> ends;
-  void* d_mem = nullptr;  // recs then ends
+  std::vector<unsigned char> key;
+  void* d_mem = nullptr;
   void* h_mem = nullptr;  // pinned source of the upload
   hipEvent_t ready = nullptr;
   uint64_t last_use = 0;
 };
 
 std::mutex g_cache_mu;
-std::vector<TableEntry*> g_cache;
+std::vector<BlobEntry*> g_cache;
 uint64_t g_clock = 0;
-constexpr size_t kCacheMax = 32;
+constexpr size_t kCacheMax = 64;
 
-void free_entry(TableEntry* e) {
+void free_entry(BlobEntry* e) {
   if (e->ready) (void)hipEventDestroy(e->ready);
   if (e->d_mem) (void)hipFree(e->d_mem);
   if (e->h_mem) (void)hipHostFree(e->h_mem);
   delete e;
 }
 
-ps_status get_table(const std::vector<DevTensor>& recs, const std::vector<uint32_t>& ends, hipStream_t s,
-                    TablePtr* out) {
+}  // namespace
+
+ps_status device_blob(const void* data, size_t bytes, hipStream_t s, const void** dptr) {
   int dev = 0;
   if (ps_status st = hip_check(hipGetDevice(&dev), "hipGetDevice")) return st;
   std::lock_guard<std::mutex> lk(g_cache_mu);
-  const size_t rb = recs.size() * sizeof(DevTensor), eb = ends.size() * sizeof(uint32_t);
-  for (TableEntry* e : g_cache) {
-    if (e->device == dev && e->recs.size() == recs.size() && !memcmp(e->recs.data(), recs.data(), rb) &&
-        !memcmp(e->ends.data(), ends.data(), eb)) {
+  for (BlobEntry* e : g_cache) {
+    if (e->device == dev && e->key.size() == bytes && !memcmp(e->key.data(), data, bytes)) {
       e->last_use = ++g_clock;
       if (ps_status st = hip_check(hipStreamWaitEvent(s, e->ready, 0), "hipStreamWaitEvent")) return st;
-      *out = TablePtr{(const DevTensor*)e->d_mem, (const uint32_t*)((char*)e->d_mem + rb), (int32_t)recs.size()};
+      *dptr = e->d_mem;
       return PS_OK;
     }
   }
   if (g_cache.size() >= kCacheMax) {
-    // Evict the least recently used list; wait for all device work first so
+    // Evict the least recently used blob; wait for all device work first so
     // that no launch still reads it.
     size_t victim = 0;
     for (size_t i = 1; i < g_cache.size(); ++i)
@@ -149,18 +152,16 @@ ps_status get_table(const std::vector<DevTensor>& recs, const std::vector<uint32
     free_entry(g_cache[victim]);
     g_cache.erase(g_cache.begin() + victim);
   }
-  TableEntry* e = new TableEntry;
+  BlobEntry* e = new BlobEntry;
   e->device = dev;
-  e->recs = recs;
-  e->ends = ends;
-  if (hipMalloc(&e->d_mem, rb + eb) != hipSuccess || hipHostMalloc(&e->h_mem, rb + eb, hipHostMallocDefault) != hipSuccess) {
+  e->key.assign((const unsigned char*)data, (const unsigned char*)data + bytes);
+  if (hipMalloc(&e->d_mem, bytes) != hipSuccess || hipHostMalloc(&e->h_mem, bytes, hipHostMallocDefault) != hipSuccess) {
     free_entry(e);
-    return fail(PS_ERR_NO_MEMORY, "tensor table allocation failed");
+    return fail(PS_ERR_NO_MEMORY, "device table allocation failed");
   }
-  memcpy(e->h_mem, recs.data(), rb);
-  memcpy((char*)e->h_mem + rb, ends.data(), eb);
+  memcpy(e->h_mem, data, bytes);
   ps_status st = hip_check(hipEventCreateWithFlags(&e->ready, hipEventDisableTiming), "hipEventCreate");
-  if (!st) st = hip_check(hipMemcpyAsync(e->d_mem, e->h_mem, rb + eb, hipMemcpyHostToDevice, s), "table upload");
+  if (!st) st = hip_check(hipMemcpyAsync(e->d_mem, e->h_mem, bytes, hipMemcpyHostToDevice, s), "table upload");
   if (!st) st = hip_check(hipEventRecord(e->ready, s), "hipEventRecord");
   if (st) {
     (void)hipStreamSynchronize(s);
@@ -169,7 +170,21 @@ ps_status get_table(const std::vector<DevTensor>& recs, const std::vector<uint32
   }
   e->last_use = ++g_clock;
   g_cache.push_back(e);
-  *out = TablePtr{(const DevTensor*)e->d_mem, (const uint32_t*)((char*)e->d_mem + rb), (int32_t)recs.size()};
+  *dptr = e->d_mem;
+  return PS_OK;
+}
+
+namespace {
+
+ps_status get_table(const std::vector<DevTensor>& recs, const std::vector<uint32_t>& ends, hipStream_t s,
+                    TablePtr* out) {
+  const size_t rb = recs.size() * sizeof(DevTensor), eb = ends.size() * sizeof(uint32_t);
+  std::vector<unsigned char> blob(rb + eb);
+  memcpy(blob.data(), recs.data(), rb);
+  memcpy(blob.data() + rb, ends.data(), eb);
+  const void* d = nullptr;
+  if (ps_status st = device_blob(blob.data(), blob.size(), s, &d)) return st;
+  *out = TablePtr{(const DevTensor*)d, (const uint32_t*)((const char*)d + rb), (int32_t)recs.size()};
   return PS_OK;
 }
 

@@ -1,0 +1,174 @@
+// ps_factored.cpp - host side of ps_factored_step: validation, workspace
+// layout and the device plan [ADAF, adafactor_step_param; PRODIGY].
+//
+// Workspace (caller-owned device memory), per 2-D tensor [R, C]: row sums per
+// tile column [ntc][R] and column sums per tile row [ntr][C] (double), sums of
+// the new row EMAs per 256-row chunk, rho[R], kap[C], sums of U^2 per tile,
+// the clip factor. Per 1-D tensor: this step's v[n], sums of U^2 per
+// 1024-element item, the clip factor. Every region starts on 256 bytes.
+#include <cstring>
+#include <vector>
+
+#include "ps_internal.h"
+
+namespace ps {
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+ps_status check_fhparams(const ps_factored_hparams* hp) {
+  if (!hp) return fail(PS_ERR_INVALID_ARG, "factored hparams is NULL");
+  if (hp->split_mode != PS_SPLIT_TRUNC && hp->split_mode != PS_SPLIT_NEAREST_AWAY)
+    return fail(PS_ERR_INVALID_ARG, "unknown split_mode %d", hp->split_mode);
+  if (hp->reserved != 0) return fail(PS_ERR_INVALID_ARG, "reserved must be 0");
+  if (!is_finite(hp->lr) || hp->lr < 0) return fail(PS_ERR_INVALID_ARG, "lr must be finite and >= 0");
+  if (!is_finite(hp->beta2) || hp->beta2 < 0 || hp->beta2 >= 1) return fail(PS_ERR_INVALID_ARG, "beta2 must be in [0, 1)");
+  if (!is_finite(hp->eps1) || !(hp->eps1 > 0)) return fail(PS_ERR_INVALID_ARG, "eps1 must be finite and > 0");
+  if (!is_finite(hp->clip_threshold) || !(hp->clip_threshold > 0))
+    return fail(PS_ERR_INVALID_ARG, "clip_threshold must be finite and > 0");
+  if (!is_finite(hp->weight_decay) || hp->weight_decay < 0)
+    return fail(PS_ERR_INVALID_ARG, "weight_decay must be finite and >= 0");
+  return PS_OK;
+}
+
+ps_status check_ptr(const void* p, const char* what, int i, uintptr_t align) {
+  if (!p) return fail(PS_ERR_INVALID_ARG, "tensor %d: %s is NULL", i, what);
+  if (!is_aligned(p, align)) return fail(PS_ERR_ALIGNMENT, "tensor %d: %s is not %d-byte aligned", i, what, (int)align);
+  return PS_OK;
+}
+
+struct Layout {
+  std::vector<F2D> t2;
+  std::vector<F1D> t1;
+  std::vector<uint32_t> tile_end, rc_end, item_end;
+  size_t bytes = 0;
+};
+
+// Validates the list and lays out the workspace starting at `ws` (which may be
+// NULL when only the size is wanted).
+ps_status plan(const ps_tensor* t, int32_t n, char* ws, Layout& L) {
+  if (n < 0) return fail(PS_ERR_INVALID_ARG, "n_tensors < 0");
+  if (n > 0 && !t) return fail(PS_ERR_INVALID_ARG, "tensors is NULL");
+  uint64_t tiles = 0, rc = 0, items = 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { char* p = ws ? ws + off : nullptr; off += up(bytes); return p; };
+  for (int32_t i = 0; i < n; ++i) {
+    const ps_tensor& x = t[i];
+    if (x.numel < 0 || x.numel > (int64_t(1) << 40)) return fail(PS_ERR_SHAPE, "tensor %d: numel out of range", i);
+    if (x.numel == 0 || x.grad == nullptr) continue;
+    ps_status s;
+    if ((s = check_ptr(x.w_hi, "w_hi", i, 16)) || (s = check_ptr(x.w_lo, "w_lo", i, 16)) ||
+        (s = check_ptr(x.grad, "grad", i, 16)))
+      return s;
+    if (x.rows != 0 || x.cols != 0) {
+      if (x.rows < 1 || x.cols < 1 || x.rows > 0x7FFFFFFF || x.cols > 0x7FFFFFFF || x.rows * x.cols != x.numel)
+        return fail(PS_ERR_SHAPE, "tensor %d: rows * cols != numel", i);
+      if ((s = check_ptr(x.row_ema, "row_ema", i, 4)) || (s = check_ptr(x.col_ema, "col_ema", i, 4))) return s;
+      F2D d{};
+      d.hi = x.w_hi; d.lo = x.w_lo; d.g = x.grad; d.row = x.row_ema; d.col = x.col_ema;
+      d.R = (int32_t)x.rows; d.C = (int32_t)x.cols;
+      d.ntr = (d.R + kFTileRows - 1) / kFTileRows;
+      d.ntc = (d.C + kFTileCols - 1) / kFTileCols;
+      d.nrw = (d.R + kFRowColChunk - 1) / kFRowColChunk;
+      d.ncw = (d.C + kFRowColChunk - 1) / kFRowColChunk;
+      d.vec = (d.C % 8) == 0;
+      d.rowpart = (double*)take(sizeof(double) * (size_t)d.ntc * d.R);
+      d.colpart = (double*)take(sizeof(double) * (size_t)d.ntr * d.C);
+      d.rpart = (double*)take(sizeof(double) * (size_t)d.nrw);
+      d.rho = (float*)take(sizeof(float) * (size_t)d.R);
+      d.kap = (float*)take(sizeof(float) * (size_t)d.C);
+      d.upart = (double*)take(sizeof(double) * (size_t)d.ntr * d.ntc);
+      d.f = (float*)take(sizeof(float));
+      tiles += (uint64_t)d.ntr * d.ntc;
+      rc += (uint64_t)d.nrw + d.ncw;
+      if (tiles > 0x7FFFFFFFull || rc > 0x7FFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large");
+      L.t2.push_back(d);
+      L.tile_end.push_back((uint32_t)tiles);
+      L.rc_end.push_back((uint32_t)rc);
+    } else {
+      if ((s = check_ptr(x.v_code, "v_code", i, 16)) || (s = check_ptr(x.v_scale, "v_scale", i, 4))) return s;
+      F1D d{};
+      d.hi = x.w_hi; d.lo = x.w_lo; d.g = x.grad; d.vc = x.v_code; d.vs = x.v_scale; d.n = x.numel;
+      d.nitems = (int32_t)((x.numel + kItemElems - 1) / kItemElems);
+      d.v = (float*)take(sizeof(float) * (size_t)x.numel);
+      d.upart = (double*)take(sizeof(double) * (size_t)d.nitems);
+      d.f = (float*)take(sizeof(float));
+      items += (uint64_t)d.nitems;
+      if (items > 0x7FFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large");
+      L.t1.push_back(d);
+      L.item_end.push_back((uint32_t)items);
+    }
+  }
+  L.bytes = off;
+  return PS_OK;
+}
+
+}  // namespace
+}  // namespace ps
+
+using namespace ps;
+
+extern "C" {
+
+ps_status ps_factored_workspace_size(const ps_tensor* tensors, int32_t n_tensors, size_t* bytes) {
+  if (!bytes) return fail(PS_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  Layout L;
+  if (ps_status s = plan(tensors, n_tensors, nullptr, L)) return s;
+  *bytes = L.bytes;
+  return PS_OK;
+}
+
+ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps_factored_hparams* hp, int64_t step,
+                           void* workspace, size_t workspace_bytes, ps_stream_t stream) {
+  if (ps_status s = check_fhparams(hp)) return s;
+  if (step < 1) return fail(PS_ERR_INVALID_ARG, "step must be >= 1 (got %lld)", (long long)step);
+  Layout L;
+  if (ps_status s = plan(tensors, n_tensors, nullptr, L)) return s;
+  if (L.t2.empty() && L.t1.empty()) return PS_OK;
+  if (!workspace) return fail(PS_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.bytes);
+  if (!is_aligned(workspace, 256)) return fail(PS_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.bytes)
+    return fail(PS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.bytes);
+  Layout W;
+  if (ps_status s = plan(tensors, n_tensors, (char*)workspace, W)) return s;
+
+  // one device blob: F2D[n2] | F1D[n1] | tile_end[n2] | rc_end[n2] | item_end[n1]
+  const size_t b2 = W.t2.size() * sizeof(F2D), b1 = W.t1.size() * sizeof(F1D);
+  const size_t e2 = W.t2.size() * sizeof(uint32_t), e1 = W.t1.size() * sizeof(uint32_t);
+  std::vector<unsigned char> blob(b2 + b1 + 2 * e2 + e1);
+  unsigned char* p = blob.data();
+  if (b2) memcpy(p, W.t2.data(), b2);
+  if (b1) memcpy(p + b2, W.t1.data(), b1);
+  if (e2) memcpy(p + b2 + b1, W.tile_end.data(), e2);
+  if (e2) memcpy(p + b2 + b1 + e2, W.rc_end.data(), e2);
+  if (e1) memcpy(p + b2 + b1 + 2 * e2, W.item_end.data(), e1);
+  hipStream_t s = (hipStream_t)stream;
+  const void* d = nullptr;
+  if (ps_status st = device_blob(blob.data(), blob.size(), s, &d)) return st;
+  const char* dc = (const char*)d;
+  FPlan pl;
+  pl.t2 = (const F2D*)dc;
+  pl.t1 = (const F1D*)(dc + b2);
+  pl.tile_end = (const uint32_t*)(dc + b2 + b1);
+  pl.rc_end = (const uint32_t*)(dc + b2 + b1 + e2);
+  pl.item_end = (const uint32_t*)(dc + b2 + b1 + 2 * e2);
+  pl.n2 = (int32_t)W.t2.size();
+  pl.n1 = (int32_t)W.t1.size();
+  pl.n_tiles = W.tile_end.empty() ? 0 : W.tile_end.back();
+  pl.n_rc = W.rc_end.empty() ? 0 : W.rc_end.back();
+  pl.n_items = W.item_end.empty() ? 0 : W.item_end.back();
+  FScalars sc;
+  sc.B2 = (float)hp->beta2;
+  sc.C2 = (float)(1.0 - hp->beta2);
+  sc.EPS1 = (float)hp->eps1;
+  sc.CWD = (float)(hp->lr * hp->weight_decay);
+  sc.lr = hp->lr;
+  sc.clip = hp->clip_threshold;
+  sc.wd = hp->weight_decay != 0.0;
+  sc.pad = 0;
+  return launch_factored(pl, sc, hp->split_mode, s);
+}
+
+}  // extern "C"

@@ -45,9 +45,72 @@ struct TableInline {
   int32_t n;
 };
 
+// ---- factored step (ps_factored.cpp, k_factored.hip) ----
+constexpr int kFTileRows = 64;     // 2-D tile: 64 rows x 256 columns, one 256-thread workgroup
+constexpr int kFTileCols = 256;
+constexpr int kFRowColChunk = 256; // rows or columns per finalize workgroup
+
+// 2-D tensor [R, C] of a factored step; workspace pointers are per tensor.
+struct F2D {
+  uint16_t* hi;
+  uint16_t* lo;
+  const uint16_t* g;
+  float* row;        // [R] EMA of row means (caller state)
+  float* col;        // [C] EMA of column means (caller state)
+  double* rowpart;   // [ntc][R] row sums per tile column
+  double* colpart;   // [ntr][C] column sums per tile row
+  double* rpart;     // [nrw] sums of the new row EMAs per 256-row chunk
+  float* rho;        // [R] 1/sqrt(r_i / mean r)
+  float* kap;        // [C] 1/sqrt(c_j)
+  double* upart;     // [ntr * ntc] sums of U^2 per tile
+  float* f;          // clip factor lr / max(1, RMS(U)/d)
+  int32_t R, C, ntr, ntc, nrw, ncw;
+  int32_t vec;       // C % 8 == 0: 16-byte row segments
+  int32_t pad;
+};
+
+// 1-D tensor of a factored step (second moment kept in the uint16 codec).
+struct F1D {
+  uint16_t* hi;
+  uint16_t* lo;
+  const uint16_t* g;
+  uint16_t* vc;
+  float* vs;
+  float* v;          // [n] this step's v (workspace)
+  double* upart;     // [nitems] sums of U^2 per 1024-element item
+  float* f;
+  int64_t n;
+  int32_t nitems;
+  int32_t pad;
+};
+
+struct FScalars {
+  float B2, C2, EPS1, CWD;
+  double lr, clip;
+  int32_t wd;
+  int32_t pad;
+};
+
+struct FPlan {      // device tables of one factored call
+  const F2D* t2;
+  const uint32_t* tile_end;    // [n2] prefix ends over 2-D tiles
+  const uint32_t* rc_end;      // [n2] prefix ends over row/column finalize workgroups
+  const F1D* t1;
+  const uint32_t* item_end;    // [n1] prefix ends over 1-D items
+  int32_t n2, n1;
+  uint32_t n_tiles, n_rc, n_items;
+};
+
+ps_status launch_factored(const FPlan& plan, const FScalars& sc, int split_mode, hipStream_t s);
+
 // ---- errors (ps_abi.cpp) ----
 ps_status fail(ps_status s, const char* fmt, ...);
 ps_status hip_check(hipError_t e, const char* what);
+
+// Device copy of a host blob, cached by content (ps_abi.cpp).
+ps_status device_blob(const void* data, size_t bytes, hipStream_t s, const void** dptr);
+bool is_finite(double x);
+bool is_aligned(const void* p, uintptr_t a);
 
 // ---- host scalars (ps_scalars.cpp) ----
 void step_scalars(const ps_hparams& hp, int64_t step, StepScalars* out);

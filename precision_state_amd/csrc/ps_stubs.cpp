@@ -6,15 +6,6 @@ using namespace ps;
 
 extern "C" {
 
-ps_status ps_factored_workspace_size(const ps_tensor*, int32_t, size_t* bytes) {
-  if (bytes) *bytes = 0;
-  return fail(PS_ERR_UNSUPPORTED, "factored step not available in this build");
-}
-
-ps_status ps_factored_step(const ps_tensor*, int32_t, const ps_factored_hparams*, int64_t, void*, size_t, ps_stream_t) {
-  return fail(PS_ERR_UNSUPPORTED, "factored step not available in this build");
-}
-
 ps_status ps_offload_plan_create(const ps_offload_group*, int32_t, ps_offload_plan** plan) {
   if (plan) *plan = nullptr;
   return fail(PS_ERR_UNSUPPORTED, "offload pipeline not available in this build");

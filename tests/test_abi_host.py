@@ -93,3 +93,36 @@ def test_status_strings(ps):
     for s in range(8):
         assert L.ps_status_string(s)
     assert b"gfx950" in L.ps_version()
+
+
+def _frec(ps, n=1024, rows=32, cols=32, **kw):
+    base = dict(w_hi=16, w_lo=32, grad=48, m_code=0, m_scale=0, v_code=96, v_scale=112, row_ema=128, col_ema=144,
+                numel=n, rows=rows, cols=cols)
+    base.update(kw)
+    return ps.CTensor(**base)
+
+
+def test_factored_workspace_size_and_validation(ps):
+    L = ps.lib()
+    size = ctypes.c_size_t(0)
+    arr = (ps.CTensor * 2)(_frec(ps), _frec(ps, n=300, rows=0, cols=0))
+    assert L.ps_factored_workspace_size(arr, 2, ctypes.byref(size)) == 0
+    # 2-D 32x32: rowpart 1x32, colpart 1x32 doubles, rpart 1, rho 32, kap 32 floats, upart 1, f; 1-D 300:
+    # v 300 floats, upart 1, f -- each region rounded up to 256 bytes
+    assert size.value == 256 * (1 + 1 + 1 + 1 + 1 + 1 + 1) + 1280 + 256 + 256
+    bad = (ps.CTensor * 1)(_frec(ps, rows=33))
+    assert L.ps_factored_workspace_size(bad, 1, ctypes.byref(size)) == 3
+    bad = (ps.CTensor * 1)(_frec(ps, row_ema=0))
+    assert L.ps_factored_workspace_size(bad, 1, ctypes.byref(size)) == 1
+    bad = (ps.CTensor * 1)(_frec(ps, n=300, rows=0, cols=0, v_code=98))
+    assert L.ps_factored_workspace_size(bad, 1, ctypes.byref(size)) == 2
+    hp = ps.FactoredHParams().c()
+    assert L.ps_factored_step(arr, 2, ctypes.byref(hp), 1, None, 0, None) == 7
+    assert L.ps_factored_step(arr, 2, ctypes.byref(hp), 1, 4096 + 16, 1 << 20, None) == 2
+    assert L.ps_factored_step(arr, 2, ctypes.byref(hp), 1, 4096, 100, None) == 7
+    assert L.ps_factored_step(arr, 2, ctypes.byref(hp), 0, 4096, 1 << 20, None) == 1
+    for k, v in (("eps1", 0.0), ("clip_threshold", -1.0), ("beta2", 1.0), ("lr", float("inf"))):
+        h = ps.FactoredHParams(**{k: v}).c()
+        assert L.ps_factored_step(arr, 2, ctypes.byref(h), 1, 4096, 1 << 20, None) == 1, k
+    empty = (ps.CTensor * 1)(_frec(ps, grad=0))
+    assert L.ps_factored_step(empty, 1, ctypes.byref(hp), 1, None, 0, None) == 0
