@@ -183,7 +183,10 @@ class StateSlab:
 
     ALIGN = 128    # elements of a 16-bit stream = 256 bytes
 
-    def __init__(self, numels, device="cuda", with_grads=True, shapes2d=None):
+    def __init__(self, numels, device="cuda", with_grads=True, shapes2d=None, host_state=False):
+        """host_state=True puts residuals, codes and scales in pinned host
+        memory (the layout ps_offload_* expects); weights and gradients stay
+        on `device`."""
         import torch
         self.numels = list(numels)
         offs, boffs, n_tot, nb_tot = [], [], 0, 0
@@ -193,10 +196,14 @@ class StateSlab:
             n_tot += (n + self.ALIGN - 1) // self.ALIGN * self.ALIGN
             nb_tot += ((n + BLOCK - 1) // BLOCK + 63) // 64 * 64
         names = ["hi", "lo", "mc", "vc"] + (["g"] if with_grads else [])
-        self.slab = {k: torch.empty(max(1, n_tot), dtype=torch.int16, device=device) for k in names}
+
+        def where(k):
+            return dict(device="cpu", pin_memory=True) if host_state and k in ("lo", "mc", "vc", "ms", "vs") \
+                else dict(device=device)
+        self.slab = {k: torch.empty(max(1, n_tot), dtype=torch.int16, **where(k)) for k in names}
         self.slab["mc"].fill_(-32768)          # 0x8000: the zero code of the signed kind
         self.slab["vc"].zero_()
-        self.scales = {k: torch.zeros(max(1, nb_tot), dtype=torch.float32, device=device) for k in ("ms", "vs")}
+        self.scales = {k: torch.zeros(max(1, nb_tot), dtype=torch.float32, **where(k)) for k in ("ms", "vs")}
         self.states, self.grads = [], []
         for i, n in enumerate(self.numels):
             o, bo, nb = offs[i], boffs[i], (n + BLOCK - 1) // BLOCK
