@@ -189,6 +189,34 @@ def bench_factored(args):
         "cpu_baseline": None}), flush=True)
 
 
+def pcie_ceiling(dev, nbytes=2 << 30):
+    """Pinned host <-> device copy rates: each direction alone and both at once
+    on two streams (hipMemcpyAsync of 2 GiB)."""
+    import torch
+    h = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    d = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+    for _ in range(2):
+        t_h2d = timed(lambda: d[0].copy_(h[0], non_blocking=True))
+        t_d2h = timed(lambda: h[1].copy_(d[1], non_blocking=True))
+
+    def both():
+        with torch.cuda.stream(s1):
+            d[0].copy_(h[0], non_blocking=True)
+        with torch.cuda.stream(s2):
+            h[1].copy_(d[1], non_blocking=True)
+    t_dup = timed(both)
+    return {"h2d": nbytes / t_h2d / 1e9, "d2h": nbytes / t_d2h / 1e9, "dup_h2d": nbytes / t_dup / 1e9,
+            "dup_d2h": nbytes / t_dup / 1e9}
+
+
 def bench_offload(args, n_blocks=57):
     """Host offload: the FLUX double-block tensor set repeated 57 times; each
     block's bf16 weights and gradients in HBM, its residuals, codes and scales
@@ -227,6 +255,9 @@ def bench_offload(args, n_blocks=57):
         groups.append((sts, gs))
     # device views must stay 16-byte aligned: all FLUX double-block sizes are multiples of 8
     torch.cuda.synchronize()
+    pcie = pcie_ceiling(dev)
+    log(f"[bench] pinned-copy ceiling: H2D {pcie['h2d']:.1f} GB/s, D2H {pcie['d2h']:.1f} GB/s, "
+        f"both at once {pcie['dup_h2d']:.1f} + {pcie['dup_d2h']:.1f} GB/s")
     plan = ps.OffloadPlan(groups)
     h2d, d2h = plan.bytes()
     n_params = n_blocks * synth.total_params(shapes)
@@ -253,7 +284,7 @@ def bench_offload(args, n_blocks=57):
         "config": {"workload": f"flux_double_block_x{n_blocks}_offload", "params": n_params,
                    "host_state_sets": H, "pcie_h2d_gbs": h2d / wall / 1e9, "pcie_d2h_gbs": d2h / wall / 1e9,
                    "pcie_total_gbs": (h2d + d2h) / wall / 1e9, "h2d_bytes_per_step": h2d,
-                   "hbm_gbs_kernel_18B": 18 * n_params / wall / 1e9},
+                   "hbm_gbs_kernel_18B": 18 * n_params / wall / 1e9, "pinned_copy_ceiling_gbs": pcie},
         "roofline": {"bound": "pcie", "achieved": (h2d + d2h) / wall / 1e9, "peak": 128.0, "unit": "GB/s",
                      "frac": (h2d + d2h) / wall / 1e9 / 128.0, "traffic": None},
         "cpu_baseline": None}), flush=True)

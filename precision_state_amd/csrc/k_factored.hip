@@ -96,20 +96,45 @@ __global__ __launch_bounds__(kT) void k_f_stats(FPlan P, FScalars S) {
   double cacc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) cacc[j] = 0.0;
+  double rs[8];
   for (int k = 0; k < 8; ++k) {
     const int r = tr * kFTileRows + rg + 8 * k;
     uint32_t w[4];
     const uint32_t valid = load_row8(X.g, X, r, c, w);
-    double rs = 0.0;
+    rs[k] = 0.0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float g = bf16_at(w, j);
       const float q = (valid >> j & 1u) ? g * g + S.EPS1 : 0.0f;
-      rs += (double)q;
+      rs[k] += (double)q;
       cacc[j] += (double)q;
     }
-    for (int o = 1; o < 32; o <<= 1) rs += __shfl_xor(rs, o, 32);
-    if (cg == 0 && r < X.R) X.rowpart[(size_t)tc * X.R + r] = rs;
+  }
+  // Row sums over the 32 column groups of a half-wave by transpose-reduce:
+  // at each exchange a lane keeps half of its rows and receives its partner's
+  // partial of those rows (9 shuffles instead of 8 x 5). Lane bits 4, 3, 2 of
+  // cg select the row k = 4*b4 + 2*b3 + b2 the lane ends with.
+  const int b4 = (cg >> 4) & 1, b3 = (cg >> 3) & 1, b2 = (cg >> 2) & 1;
+  double a[4], bb[2], x;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const double keep = b4 ? rs[4 + q] : rs[q], send = b4 ? rs[q] : rs[4 + q];
+    a[q] = keep + __shfl_xor(send, 16, 32);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const double keep = b3 ? a[2 + q] : a[q], send = b3 ? a[q] : a[2 + q];
+    bb[q] = keep + __shfl_xor(send, 8, 32);
+  }
+  {
+    const double keep = b2 ? bb[1] : bb[0], send = b2 ? bb[0] : bb[1];
+    x = keep + __shfl_xor(send, 4, 32);
+  }
+  x += __shfl_xor(x, 2, 32);
+  x += __shfl_xor(x, 1, 32);
+  {
+    const int r = tr * kFTileRows + rg + 8 * (4 * b4 + 2 * b3 + b2);
+    if ((cg & 3) == 0 && r < X.R) X.rowpart[(size_t)tc * X.R + r] = x;
   }
   __shared__ double lds[8][kFTileCols];
 #pragma unroll
@@ -134,6 +159,7 @@ __global__ __launch_bounds__(kT) void k_f_rowcol(FPlan P, FScalars S) {
     double rv = 0.0;
     if (i < X.R) {
       double s = 0.0;
+#pragma unroll 8
       for (int tc = 0; tc < X.ntc; ++tc) s += X.rowpart[(size_t)tc * X.R + i];
       const float mean = (float)(s / (double)X.C);
       const float r = __builtin_fmaf(S.B2, X.row[i], S.C2 * mean);
@@ -146,6 +172,7 @@ __global__ __launch_bounds__(kT) void k_f_rowcol(FPlan P, FScalars S) {
     const int j = (w - X.nrw) * kFRowColChunk + (int)threadIdx.x;
     if (j < X.C) {
       double s = 0.0;
+#pragma unroll 16
       for (int tr = 0; tr < X.ntr; ++tr) s += X.colpart[(size_t)tr * X.C + j];
       const float mean = (float)(s / (double)X.R);
       X.col[j] = __builtin_fmaf(S.B2, X.col[j], S.C2 * mean);
@@ -173,7 +200,7 @@ __global__ __launch_bounds__(kT) void k_f_factors(FPlan P) {
 // ---- pass 4: tile sums of U^2, U = (g * rho_i) * kap_j ----------------------
 __global__ __launch_bounds__(kT) void k_f_usq(FPlan P) {
   uint32_t begin;
-  const F2D& X = P.t2[find_end(P.tile_end, P.n2, blockIdx.x, begin)];
+  const F2D& X = P.t2[find_end(P.tile_nf_end, P.n2, blockIdx.x, begin)];
   const uint32_t tile = blockIdx.x - begin;
   const int tr = (int)(tile / (uint32_t)X.ntc), tc = (int)(tile - (uint32_t)tr * X.ntc);
   const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
@@ -197,6 +224,123 @@ __global__ __launch_bounds__(kT) void k_f_usq(FPlan P) {
   __shared__ double red[kT];
   const double t = block_sum(acc, red);
   if (threadIdx.x == 0) X.upart[tile] = t;
+}
+
+// ---- flat passes over 2-D tensors with C % 8 == 0 ------------------------------
+// Same mapping as the fused (N)AdamW step: one 1024-element item per 64-lane
+// workgroup, each lane two runs of 8 consecutive elements; a run never
+// crosses a row because C % 8 == 0. Row and column of a run come from one
+// division per workgroup and a wrap test (C >= 1024) or a division per run.
+
+__device__ __forceinline__ void run_rc(uint32_t e, uint32_t off, uint32_t i0, uint32_t j0, uint32_t C, uint32_t& i,
+                                       uint32_t& j) {
+  if (C >= 1024u) {
+    j = j0 + off;
+    i = i0;
+    if (j >= C) {
+      j -= C;
+      ++i;
+    }
+  } else {
+    i = e / C;
+    j = e - i * C;
+  }
+}
+
+struct FlatRun {
+  uint32_t e, i, j;
+  bool ok;
+};
+
+__device__ __forceinline__ void flat_runs(const F2D& X, uint32_t item, FlatRun* run) {
+  const uint32_t n = (uint32_t)X.R * (uint32_t)X.C;
+  const uint32_t C = (uint32_t)X.C;
+  const uint32_t elem0 = item * (uint32_t)kItemElems;
+  const uint32_t i0 = elem0 / C, j0 = elem0 - i0 * C;
+  const uint32_t la = (threadIdx.x >> 4) * (uint32_t)kBlock + (threadIdx.x & 15) * 8u;
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t off = la + 128u * h;
+    run[h].e = elem0 + off;
+    run[h].ok = run[h].e < n;
+    run_rc(run[h].e, off, i0, j0, C, run[h].i, run[h].j);
+  }
+}
+
+__device__ __forceinline__ void load_kap8(const float* __restrict__ kap, uint32_t j, float* k) {
+  const float4 a = *reinterpret_cast<const float4*>(kap + j);
+  const float4 b = *reinterpret_cast<const float4*>(kap + j + 4);
+  k[0] = a.x; k[1] = a.y; k[2] = a.z; k[3] = a.w; k[4] = b.x; k[5] = b.y; k[6] = b.z; k[7] = b.w;
+}
+
+__global__ __launch_bounds__(64) void k_f_usq_flat(FPlan P) {
+  uint32_t begin;
+  const F2D& X = P.t2[find_end(P.item2_end, P.n2, blockIdx.x, begin)];
+  const uint32_t item = blockIdx.x - begin;
+  FlatRun run[2];
+  flat_runs(X, item, run);
+  uint4 gv[2];
+  float kap[2][8], rho[2];
+  for (int h = 0; h < 2; ++h) {
+    if (!run[h].ok) continue;
+    gv[h] = *reinterpret_cast<const uint4*>(X.g + run[h].e);
+    load_kap8(X.kap, run[h].j, kap[h]);
+    rho[h] = X.rho[run[h].i];
+  }
+  double acc = 0.0;
+  for (int h = 0; h < 2; ++h) {
+    if (!run[h].ok) continue;
+    const uint32_t w[4] = {gv[h].x, gv[h].y, gv[h].z, gv[h].w};
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const float U = (bf16_at(w, jj) * rho[h]) * kap[h][jj];
+      acc += (double)U * (double)U;
+    }
+  }
+  for (int o = 1; o < 64; o <<= 1) acc += __shfl_xor(acc, o, 64);
+  if (threadIdx.x == 0) X.upart[item] = acc;
+}
+
+template <int SPLIT>
+__global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
+  uint32_t begin;
+  const F2D& X = P.t2[find_end(P.item2_end, P.n2, blockIdx.x, begin)];
+  const uint32_t item = blockIdx.x - begin;
+  const float f = *X.f;
+  FlatRun run[2];
+  flat_runs(X, item, run);
+  uint4 gv[2], hv[2], lv[2];
+  float kap[2][8], rho[2];
+  for (int h = 0; h < 2; ++h) {
+    if (!run[h].ok) continue;
+    gv[h] = *reinterpret_cast<const uint4*>(X.g + run[h].e);
+    hv[h] = *reinterpret_cast<const uint4*>(X.hi + run[h].e);
+    lv[h] = *reinterpret_cast<const uint4*>(X.lo + run[h].e);
+    load_kap8(X.kap, run[h].j, kap[h]);
+    rho[h] = X.rho[run[h].i];
+  }
+  for (int h = 0; h < 2; ++h) {
+    if (!run[h].ok) continue;
+    const uint32_t gw[4] = {gv[h].x, gv[h].y, gv[h].z, gv[h].w};
+    const uint32_t hw[4] = {hv[h].x, hv[h].y, hv[h].z, hv[h].w};
+    const uint32_t lw[4] = {lv[h].x, lv[h].y, lv[h].z, lv[h].w};
+    uint32_t oh[4], ol[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t wb[2];
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        const int jj = 2 * p + o;
+        const float U = (bf16_at(gw, jj) * rho[h]) * kap[h][jj];
+        const float w = __uint_as_float(join_pair_elem<SPLIT>(hw[p], lw[p], o));
+        float x = U * f;
+        if (S.wd) x = __builtin_fmaf(S.CWD, w, x);
+        wb[o] = __float_as_uint(w - x);
+      }
+      split_pair<SPLIT>(wb[0], wb[1], oh[p], ol[p]);
+    }
+    *reinterpret_cast<uint4*>(X.hi + run[h].e) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+    *reinterpret_cast<uint4*>(X.lo + run[h].e) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+  }
 }
 
 // ---- 1-D tensors: v update (stored in the workspace) and item sums of U^2 ---
@@ -226,24 +370,32 @@ __global__ __launch_bounds__(64) void k_f1_stats(FPlan P, FScalars S) {
 }
 
 // ---- clip factor per tensor: lr / max(1, RMS(U) / clip) ---------------------
-__global__ __launch_bounds__(kT) void k_f_clip(FPlan P, FScalars S) {
+constexpr int kClipT = 1024;
+
+__global__ __launch_bounds__(kClipT) void k_f_clip(FPlan P, FScalars S) {
   const double* parts;
   int np;
   double n;
   float* f;
   if ((int)blockIdx.x < P.n2) {
     const F2D& X = P.t2[blockIdx.x];
-    parts = X.upart; np = X.ntr * X.ntc; n = (double)X.R * (double)X.C; f = X.f;
+    parts = X.upart; np = X.npart; n = (double)X.R * (double)X.C; f = X.f;
   } else {
     const F1D& X = P.t1[blockIdx.x - P.n2];
     parts = X.upart; np = X.nitems; n = (double)X.n; f = X.f;
   }
   double s = 0.0;
-  for (int q = threadIdx.x; q < np; q += kT) s += parts[q];
-  __shared__ double red[kT];
-  const double t = block_sum(s, red);
+#pragma unroll 8
+  for (int q = threadIdx.x; q < np; q += kClipT) s += parts[q];
+  __shared__ double red[kClipT];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = kClipT / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
   if (threadIdx.x == 0) {
-    const double rms = sqrt(t / n);
+    const double rms = sqrt(red[0] / n);
     const double r = rms / S.clip;
     *f = (float)(S.lr / (r > 1.0 ? r : 1.0));
   }
@@ -253,7 +405,7 @@ __global__ __launch_bounds__(kT) void k_f_clip(FPlan P, FScalars S) {
 template <int SPLIT>
 __global__ __launch_bounds__(kT) void k_f_apply(FPlan P, FScalars S) {
   uint32_t begin;
-  const F2D& X = P.t2[find_end(P.tile_end, P.n2, blockIdx.x, begin)];
+  const F2D& X = P.t2[find_end(P.tile_nf_end, P.n2, blockIdx.x, begin)];
   const uint32_t tile = blockIdx.x - begin;
   const int tr = (int)(tile / (uint32_t)X.ntc), tc = (int)(tile - (uint32_t)tr * X.ntc);
   const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
@@ -338,9 +490,11 @@ ps_status launch_all(const FPlan& P, const FScalars& S, hipStream_t s) {
   if (P.n_items) hipLaunchKernelGGL(k_f1_stats, dim3(P.n_items), dim3(64), 0, s, P, S);
   if (P.n_rc) hipLaunchKernelGGL(k_f_rowcol, dim3(P.n_rc), dim3(kT), 0, s, P, S);
   if (P.n_rc) hipLaunchKernelGGL(k_f_factors, dim3(P.n_rc), dim3(kT), 0, s, P);
-  if (P.n_tiles) hipLaunchKernelGGL(k_f_usq, dim3(P.n_tiles), dim3(kT), 0, s, P);
-  hipLaunchKernelGGL(k_f_clip, dim3(P.n2 + P.n1), dim3(kT), 0, s, P, S);
-  if (P.n_tiles) hipLaunchKernelGGL((k_f_apply<SPLIT>), dim3(P.n_tiles), dim3(kT), 0, s, P, S);
+  if (P.n_tiles_nf) hipLaunchKernelGGL(k_f_usq, dim3(P.n_tiles_nf), dim3(kT), 0, s, P);
+  if (P.n_items2) hipLaunchKernelGGL(k_f_usq_flat, dim3(P.n_items2), dim3(64), 0, s, P);
+  hipLaunchKernelGGL(k_f_clip, dim3(P.n2 + P.n1), dim3(kClipT), 0, s, P, S);
+  if (P.n_tiles_nf) hipLaunchKernelGGL((k_f_apply<SPLIT>), dim3(P.n_tiles_nf), dim3(kT), 0, s, P, S);
+  if (P.n_items2) hipLaunchKernelGGL((k_f_apply_flat<SPLIT>), dim3(P.n_items2), dim3(64), 0, s, P, S);
   if (P.n_items) hipLaunchKernelGGL((k_f1_apply<SPLIT>), dim3(P.n_items), dim3(64), 0, s, P, S);
   return hip_check(hipGetLastError(), "factored step launch");
 }

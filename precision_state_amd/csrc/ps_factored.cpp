@@ -41,7 +41,7 @@ ps_status check_ptr(const void* p, const char* what, int i, uintptr_t align) {
 struct Layout {
   std::vector<F2D> t2;
   std::vector<F1D> t1;
-  std::vector<uint32_t> tile_end, rc_end, item_end;
+  std::vector<uint32_t> tile_end, rc_end, tile_nf_end, item2_end, item_end;
   size_t bytes = 0;
 };
 
@@ -50,7 +50,7 @@ struct Layout {
 ps_status plan(const ps_tensor* t, int32_t n, char* ws, Layout& L) {
   if (n < 0) return fail(PS_ERR_INVALID_ARG, "n_tensors < 0");
   if (n > 0 && !t) return fail(PS_ERR_INVALID_ARG, "tensors is NULL");
-  uint64_t tiles = 0, rc = 0, items = 0;
+  uint64_t tiles = 0, rc = 0, items = 0, tiles_nf = 0, items2 = 0;
   size_t off = 0;
   auto take = [&](size_t bytes) { char* p = ws ? ws + off : nullptr; off += up(bytes); return p; };
   for (int32_t i = 0; i < n; ++i) {
@@ -73,19 +73,29 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, Layout& L) {
       d.nrw = (d.R + kFRowColChunk - 1) / kFRowColChunk;
       d.ncw = (d.C + kFRowColChunk - 1) / kFRowColChunk;
       d.vec = (d.C % 8) == 0;
+      d.flat = d.vec && x.numel < (int64_t(1) << 31);
+      d.nitems = d.flat ? (int32_t)((x.numel + kItemElems - 1) / kItemElems) : 0;
+      d.npart = d.flat ? d.nitems : d.ntr * d.ntc;
       d.rowpart = (double*)take(sizeof(double) * (size_t)d.ntc * d.R);
       d.colpart = (double*)take(sizeof(double) * (size_t)d.ntr * d.C);
       d.rpart = (double*)take(sizeof(double) * (size_t)d.nrw);
       d.rho = (float*)take(sizeof(float) * (size_t)d.R);
       d.kap = (float*)take(sizeof(float) * (size_t)d.C);
-      d.upart = (double*)take(sizeof(double) * (size_t)d.ntr * d.ntc);
+      d.upart = (double*)take(sizeof(double) * (size_t)d.npart);
       d.f = (float*)take(sizeof(float));
       tiles += (uint64_t)d.ntr * d.ntc;
       rc += (uint64_t)d.nrw + d.ncw;
-      if (tiles > 0x7FFFFFFFull || rc > 0x7FFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large");
+      if (d.flat)
+        items2 += (uint64_t)d.nitems;
+      else
+        tiles_nf += (uint64_t)d.ntr * d.ntc;
+      if (tiles > 0x7FFFFFFFull || rc > 0x7FFFFFFFull || items2 > 0x7FFFFFFFull)
+        return fail(PS_ERR_SHAPE, "tensor list too large");
       L.t2.push_back(d);
       L.tile_end.push_back((uint32_t)tiles);
       L.rc_end.push_back((uint32_t)rc);
+      L.tile_nf_end.push_back((uint32_t)tiles_nf);
+      L.item2_end.push_back((uint32_t)items2);
     } else {
       if ((s = check_ptr(x.v_code, "v_code", i, 16)) || (s = check_ptr(x.v_scale, "v_scale", i, 4))) return s;
       F1D d{};
@@ -134,16 +144,20 @@ ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps
   Layout W;
   if (ps_status s = plan(tensors, n_tensors, (char*)workspace, W)) return s;
 
-  // one device blob: F2D[n2] | F1D[n1] | tile_end[n2] | rc_end[n2] | item_end[n1]
+  // one device blob: F2D[n2] | F1D[n1] | tile_end | rc_end | tile_nf_end | item2_end [n2] | item_end[n1]
   const size_t b2 = W.t2.size() * sizeof(F2D), b1 = W.t1.size() * sizeof(F1D);
   const size_t e2 = W.t2.size() * sizeof(uint32_t), e1 = W.t1.size() * sizeof(uint32_t);
-  std::vector<unsigned char> blob(b2 + b1 + 2 * e2 + e1);
+  std::vector<unsigned char> blob(b2 + b1 + 4 * e2 + e1);
   unsigned char* p = blob.data();
   if (b2) memcpy(p, W.t2.data(), b2);
   if (b1) memcpy(p + b2, W.t1.data(), b1);
-  if (e2) memcpy(p + b2 + b1, W.tile_end.data(), e2);
-  if (e2) memcpy(p + b2 + b1 + e2, W.rc_end.data(), e2);
-  if (e1) memcpy(p + b2 + b1 + 2 * e2, W.item_end.data(), e1);
+  if (e2) {
+    memcpy(p + b2 + b1, W.tile_end.data(), e2);
+    memcpy(p + b2 + b1 + e2, W.rc_end.data(), e2);
+    memcpy(p + b2 + b1 + 2 * e2, W.tile_nf_end.data(), e2);
+    memcpy(p + b2 + b1 + 3 * e2, W.item2_end.data(), e2);
+  }
+  if (e1) memcpy(p + b2 + b1 + 4 * e2, W.item_end.data(), e1);
   hipStream_t s = (hipStream_t)stream;
   const void* d = nullptr;
   if (ps_status st = device_blob(blob.data(), blob.size(), s, &d)) return st;
@@ -153,12 +167,16 @@ ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps
   pl.t1 = (const F1D*)(dc + b2);
   pl.tile_end = (const uint32_t*)(dc + b2 + b1);
   pl.rc_end = (const uint32_t*)(dc + b2 + b1 + e2);
-  pl.item_end = (const uint32_t*)(dc + b2 + b1 + 2 * e2);
+  pl.tile_nf_end = (const uint32_t*)(dc + b2 + b1 + 2 * e2);
+  pl.item2_end = (const uint32_t*)(dc + b2 + b1 + 3 * e2);
+  pl.item_end = (const uint32_t*)(dc + b2 + b1 + 4 * e2);
   pl.n2 = (int32_t)W.t2.size();
   pl.n1 = (int32_t)W.t1.size();
   pl.n_tiles = W.tile_end.empty() ? 0 : W.tile_end.back();
   pl.n_rc = W.rc_end.empty() ? 0 : W.rc_end.back();
   pl.n_items = W.item_end.empty() ? 0 : W.item_end.back();
+  pl.n_tiles_nf = W.tile_nf_end.empty() ? 0 : W.tile_nf_end.back();
+  pl.n_items2 = W.item2_end.empty() ? 0 : W.item2_end.back();
   FScalars sc;
   sc.B2 = (float)hp->beta2;
   sc.C2 = (float)(1.0 - hp->beta2);

@@ -66,7 +66,9 @@ struct F2D {
   float* f;          // clip factor lr / max(1, RMS(U)/d)
   int32_t R, C, ntr, ntc, nrw, ncw;
   int32_t vec;       // C % 8 == 0: 16-byte row segments
-  int32_t pad;
+  int32_t flat;      // vec and R*C < 2^31: U^2 and apply passes run over 1024-element items
+  int32_t nitems;    // flat: items of 1024 elements
+  int32_t npart;     // entries of upart (nitems if flat, else ntr * ntc)
 };
 
 // 1-D tensor of a factored step (second moment kept in the uint16 codec).
@@ -95,10 +97,12 @@ struct FPlan {      // device tables of one factored call
   const F2D* t2;
   const uint32_t* tile_end;    // [n2] prefix ends over 2-D tiles
   const uint32_t* rc_end;      // [n2] prefix ends over row/column finalize workgroups
+  const uint32_t* tile_nf_end; // [n2] prefix ends over tiles of tensors that are not flat
+  const uint32_t* item2_end;   // [n2] prefix ends over 1024-element items of flat tensors
   const F1D* t1;
   const uint32_t* item_end;    // [n1] prefix ends over 1-D items
   int32_t n2, n1;
-  uint32_t n_tiles, n_rc, n_items;
+  uint32_t n_tiles, n_rc, n_items, n_tiles_nf, n_items2;
 };
 
 ps_status launch_factored(const FPlan& plan, const FScalars& sc, int split_mode, hipStream_t s);
