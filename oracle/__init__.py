@@ -87,6 +87,8 @@ def lib():
             "orc_coeffs_for": ([ctypes.POINTER(_HP), _i64, ctypes.POINTER(_Coeffs)], None),
             "orc_core_step": ([_vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_HP), _i64], None),
             "orc_opt_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_HP), _i64], None),
+            "orc_opt_step_flags": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, ctypes.c_uint32, ctypes.POINTER(_HP),
+                                    _i64], None),
             "orc_factored_2d": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.POINTER(_FHP), _i64], None),
             "orc_factored_1d": ([_vp, _vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_FHP), _i64], None),
         }
@@ -190,6 +192,18 @@ def opt_step(st: TensorState, g, hp: HParams, step: int):
     lib().orc_opt_step(_p(st.hi, np.uint16), _p(st.lo, np.uint16), gp, _p(st.mc, np.uint16),
                        _p(st.ms, np.float32), _p(st.vc, np.uint16), _p(st.vs, np.float32), st.hi.size,
                        ctypes.byref(h), step)
+
+
+FP32_MOMENTS, FP32_PARAM = 1, 2
+
+
+def opt_step_flags(w, lo, g, m, ms, v, vs, flags, hp: HParams, step: int):
+    """In place. w/g: uint16 (bf16 bits) or float32 when FP32_PARAM; m/v: uint16
+    codes with scales ms/vs, or float32 arrays when FP32_MOMENTS."""
+    h = hp.c()
+    ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
+    lib().orc_opt_step_flags(ptr(w), ptr(lo), ptr(g), ptr(m), ptr(ms), ptr(v), ptr(vs), w.size, flags,
+                             ctypes.byref(h), step)
 
 
 def opt_step_multi(states, grads, hp: HParams, step: int):

@@ -277,6 +277,57 @@ void orc_opt_step(uint16_t* hi, uint16_t* lo, const uint16_t* g, uint16_t* mc, f
   }
 }
 
+/* Per-tensor precision policy [NADAM, second post: tensors of <= 4096
+ * elements keep their moments in fp32; third post: the final layer trains in
+ * fp32]. flags bit 0: moments are fp32 arrays m[n], v[n] (no codec, scales
+ * unused); bit 1: the parameter and its gradient are fp32 arrays w[n], g[n]
+ * (no residual). The update is the same element step. */
+enum { ORC_FP32_MOMENTS = 1, ORC_FP32_PARAM = 2 };
+
+void orc_opt_step_flags(void* w, uint16_t* lo, const void* g, void* m, float* ms, void* v, float* vs, int64_t n,
+                        uint32_t flags, const orc_hparams* hp, int64_t step) {
+  if (!g) return;
+  orc_coeffs c;
+  orc_coeffs_for(hp, step, &c);
+  int wd = hp->weight_decay != 0.0;
+  float mbuf[ORC_BLOCK], vbuf[ORC_BLOCK];
+  for (int64_t b = 0; b * ORC_BLOCK < n; ++b) {
+    int64_t base = b * ORC_BLOCK;
+    int L = (int)(n - base < ORC_BLOCK ? n - base : ORC_BLOCK);
+    for (int i = 0; i < L; ++i) {
+      int64_t e = base + i;
+      float wf, gf, m0, v0;
+      if (flags & ORC_FP32_PARAM) {
+        wf = ((float*)w)[e];
+        gf = ((const float*)g)[e];
+      } else {
+        wf = f_of(orc_join1(((uint16_t*)w)[e], lo[e], hp->split_mode));
+        gf = orc_bf16_to_f32(((const uint16_t*)g)[e]);
+      }
+      if (flags & ORC_FP32_MOMENTS) {
+        m0 = ((float*)m)[e];
+        v0 = ((float*)v)[e];
+      } else {
+        m0 = orc_decode1(((uint16_t*)m)[e], ms[b], ORC_SIGNED);
+        v0 = orc_decode1(((uint16_t*)v)[e], vs[b], ORC_UNSIGNED);
+      }
+      float w2 = step_elem(wf, gf, m0, v0, &c, hp->algo, wd, &mbuf[i], &vbuf[i]);
+      if (flags & ORC_FP32_PARAM)
+        ((float*)w)[e] = w2;
+      else
+        orc_split1(u_of(w2), &((uint16_t*)w)[e], &lo[e], hp->split_mode);
+      if (flags & ORC_FP32_MOMENTS) {
+        ((float*)m)[e] = mbuf[i];
+        ((float*)v)[e] = vbuf[i];
+      }
+    }
+    if (!(flags & ORC_FP32_MOMENTS)) {
+      orc_encode_block(mbuf, L, ORC_SIGNED, (uint16_t*)m + base, &ms[b]);
+      orc_encode_block(vbuf, L, ORC_UNSIGNED, (uint16_t*)v + base, &vs[b]);
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Factored second moment with update clipping [ADAF; PRODIGY]              */
 /* ------------------------------------------------------------------------ */

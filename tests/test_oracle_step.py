@@ -211,3 +211,48 @@ def test_quantized_step_vs_double_brute_force(algo, wd, split_mode):
         cv = np.floor(65535 * (v / sv) ** 0.25 + 0.5)
         assert np.max(np.abs(st.mc.astype(np.int64) - cm)) <= 1
         assert np.max(np.abs(st.vc.astype(np.int64) - cv)) <= 1
+
+
+# ---------------------------------------------------------------------------
+# per-tensor precision policy (fp32 moments for small tensors, fp32 final layer)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("algo", [ALGO_ADAM, ALGO_NADAM])
+@pytest.mark.parametrize("wd", [0.0, 0.01])
+def test_policy_flags_reduce_to_pinned_steps(algo, wd):
+    """fp32 moments + fp32 param is exactly the fp32 core step (pinned to
+    torch.optim above); fp32 moments alone is join -> core step -> split;
+    fp32 param with coded moments is the coded step on a TRUNC-split copy of
+    the same fp32 weights (join(split(w)) == w)."""
+    n = 1300
+    hp = HParams(algo=algo, weight_decay=wd, lr=1e-4)
+    rng = np.random.default_rng(21)
+    w32 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g16 = _bf16(rng.standard_normal(n) * 1e-3)
+    g32 = oracle.bf16_to_f32(g16).copy()
+    # both flags == core step
+    w_a, m_a, v_a = w32.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    w_b, m_b, v_b = w32.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in range(1, 4):
+        oracle.core_step(w_a, m_a, v_a, g32, hp, t)
+        oracle.opt_step_flags(w_b, None, g32, m_b, None, v_b, None, oracle.FP32_MOMENTS | oracle.FP32_PARAM, hp, t)
+    assert np.array_equal(w_a.view(np.uint32), w_b.view(np.uint32))
+    assert np.array_equal(m_a.view(np.uint32), m_b.view(np.uint32)) and np.array_equal(v_a, v_b)
+    # fp32 moments with bf16 + residual weights
+    hi, lo = oracle.split(w32)
+    m_c, v_c = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    w_d, m_d, v_d = w32.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in range(1, 4):
+        oracle.opt_step_flags(hi, lo, g16, m_c, None, v_c, None, oracle.FP32_MOMENTS, hp, t)
+        oracle.core_step(w_d, m_d, v_d, g32, hp, t)
+    assert np.array_equal(oracle.join(hi, lo).view(np.uint32), w_d.view(np.uint32))
+    assert np.array_equal(m_c.view(np.uint32), m_d.view(np.uint32))
+    # fp32 param with coded moments == coded step on split weights
+    st = oracle.TensorState(*oracle.split(w32), *oracle.zero_moments(n))
+    w_e = w32.copy()
+    mc, ms, vc, vs = oracle.zero_moments(n)
+    for t in range(1, 4):
+        oracle.opt_step(st, g16, hp, t)
+        oracle.opt_step_flags(w_e, None, g32, mc, ms, vc, vs, oracle.FP32_PARAM, hp, t)
+    assert np.array_equal(oracle.join(st.hi, st.lo).view(np.uint32), w_e.view(np.uint32))
+    assert np.array_equal(st.mc, mc) and np.array_equal(st.vc, vc) and np.array_equal(st.ms, ms)
