@@ -62,6 +62,18 @@ enum { PS_MOMENT_SIGNED = 0, PS_MOMENT_UNSIGNED = 1 };
 /* Elements per moment-scale block. */
 #define PS_BLOCK 256
 
+/* Per-tensor storage flags (ps_tensor.flags) [NADAM, second post: tensors of
+ * at most 4096 elements keep fp32 moments; third post: the final layer trains
+ * in fp32]. The update arithmetic is unchanged; only the storage differs.
+ *   PS_TENSOR_FP32_MOMENTS  m_code and v_code point to float[numel] moments
+ *                           (no codec); m_scale and v_scale are not used
+ *   PS_TENSOR_FP32_PARAM    w_hi points to the float[numel] parameter and grad
+ *                           to a float[numel] gradient (no residual); w_lo is
+ *                           not used
+ * Supported by ps_opt_step_multi only (the factored step and the offload
+ * pipeline reject non-zero flags with PS_ERR_UNSUPPORTED). */
+enum { PS_TENSOR_FP32_MOMENTS = 1u << 0, PS_TENSOR_FP32_PARAM = 1u << 1 };
+
 /* One parameter tensor's state. All arrays are device memory owned by the
  * caller, contiguous, `numel` elements unless noted; 16-bit and fp32 element
  * arrays must be 16-byte aligned, scale arrays 4-byte aligned.
@@ -76,6 +88,7 @@ enum { PS_MOMENT_SIGNED = 0, PS_MOMENT_UNSIGNED = 1 };
  *   rows, cols        factored step only: rows * cols == numel for a 2-D
  *                     tensor (factored), both 0 for a 1-D tensor (v kept in
  *                     v_code / v_scale)
+ * flags       PS_TENSOR_* storage flags (0: the formats above); reserved = 0
  * A tensor with numel == 0 is skipped and its pointers are not read. */
 typedef struct ps_tensor {
   uint16_t* w_hi;
@@ -90,6 +103,8 @@ typedef struct ps_tensor {
   int64_t numel;
   int64_t rows;
   int64_t cols;
+  uint32_t flags;
+  uint32_t reserved;
 } ps_tensor;
 
 /* (N)AdamW hyperparameters [NADAM]. Constraints: algo in {ADAM, NADAM};
@@ -138,7 +153,8 @@ typedef struct ps_factored_hparams {
  * once. `tensors` is a host array of n_tensors records (n_tensors == 0 is a
  * no-op); it is copied during the call. The library keeps a device copy of
  * each distinct tensor list it has seen (for lists longer than 16 records),
- * so repeated calls with the same list upload nothing.
+ * so repeated calls with the same list upload nothing. Tensors with storage
+ * flags go to a second launch with a generic-format kernel.
  * Errors: PS_ERR_INVALID_ARG, PS_ERR_ALIGNMENT, PS_ERR_SHAPE (host checks,
  * before any device work); PS_ERR_HIP; PS_ERR_NO_MEMORY. */
 ps_status ps_opt_step_multi(const ps_tensor* tensors, int32_t n_tensors, const ps_hparams* hp, int64_t step,

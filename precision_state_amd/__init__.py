@@ -26,6 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 ALGO_ADAM, ALGO_NADAM = 0, 1
 SPLIT_TRUNC, SPLIT_NEAREST_AWAY = 0, 1
 MOMENT_SIGNED, MOMENT_UNSIGNED = 0, 1
+TENSOR_FP32_MOMENTS, TENSOR_FP32_PARAM = 1, 2
 BLOCK = 256
 
 STATUS = {0: "PS_OK", 1: "PS_ERR_INVALID_ARG", 2: "PS_ERR_ALIGNMENT", 3: "PS_ERR_SHAPE",
@@ -47,7 +48,8 @@ class CTensor(ctypes.Structure):
     _fields_ = [("w_hi", ctypes.c_void_p), ("w_lo", ctypes.c_void_p), ("grad", ctypes.c_void_p),
                 ("m_code", ctypes.c_void_p), ("m_scale", ctypes.c_void_p), ("v_code", ctypes.c_void_p),
                 ("v_scale", ctypes.c_void_p), ("row_ema", ctypes.c_void_p), ("col_ema", ctypes.c_void_p),
-                ("numel", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+                ("numel", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
 class CHParams(ctypes.Structure):
@@ -164,6 +166,7 @@ class TensorState:
     col_ema: object = None
     rows: int = 0
     cols: int = 0
+    flags: int = 0
 
     @property
     def numel(self):
@@ -225,7 +228,8 @@ def make_records(states: Sequence[TensorState], grads: Sequence[Optional[object]
     arr = (CTensor * max(1, len(states)))()
     for i, (s, g) in enumerate(zip(states, grads)):
         arr[i] = CTensor(_ptr(s.w_hi), _ptr(s.w_lo), _ptr(g), _ptr(s.m_code), _ptr(s.m_scale), _ptr(s.v_code),
-                         _ptr(s.v_scale), _ptr(s.row_ema), _ptr(s.col_ema), s.numel, s.rows, s.cols)
+                         _ptr(s.v_scale), _ptr(s.row_ema), _ptr(s.col_ema), s.numel, s.rows, s.cols,
+                         s.flags, 0)
     return arr, len(states)
 
 

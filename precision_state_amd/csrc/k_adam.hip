@@ -199,6 +199,150 @@ ps_status launch_t(const TBL& tbl, uint32_t total_items, const StepScalars& c, h
   return hip_check(hipGetLastError(), "k_adam_step launch");
 }
 
+// ---------------------------------------------------------------------------
+// Tensors with storage flags: fp32 moments instead of codes and/or an fp32
+// parameter and gradient instead of bf16 + residual. Same lane layout and
+// element arithmetic; the flags are uniform per work item.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void load_f8(const float* p, int64_t e, int64_t n, float* d) {
+  if (e + 8 <= n) {
+    const float4 a = *reinterpret_cast<const float4*>(p + e), b = *reinterpret_cast<const float4*>(p + e + 4);
+    d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w; d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
+    return;
+  }
+  for (int j = 0; j < 8; ++j) d[j] = (e + j < n) ? p[e + j] : 0.0f;
+}
+
+__device__ __forceinline__ void store_f8(float* p, int64_t e, int64_t n, const float* s) {
+  if (e + 8 <= n) {
+    *reinterpret_cast<float4*>(p + e) = make_float4(s[0], s[1], s[2], s[3]);
+    *reinterpret_cast<float4*>(p + e + 4) = make_float4(s[4], s[5], s[6], s[7]);
+    return;
+  }
+  for (int j = 0; j < 8; ++j)
+    if (e + j < n) p[e + j] = s[j];
+}
+
+template <int ALGO, bool WD, int SPLIT>
+__device__ __forceinline__ void process_item_ex(const DevTensorEx& T, int64_t elem0, int lane, const StepScalars& c) {
+  const int b = lane >> 4, r = lane & 15;
+  const int64_t n = T.numel;
+  const int64_t blk = (elem0 >> 8) + b;
+  const bool fpm = (T.flags & PS_TENSOR_FP32_MOMENTS) != 0;   // uniform per item
+  const bool fpp = (T.flags & PS_TENSOR_FP32_PARAM) != 0;
+  const int64_t run[2] = {elem0 + b * kBlock + r * 8, elem0 + b * kBlock + 128 + r * 8};
+  float w[16], g[16], m[16], v[16];
+  uint32_t hw[8], lw[8];
+  float ms_old = 0.0f, vs_old = 0.0f;
+  if (!fpm && blk * kBlock < n) {
+    ms_old = T.ms[blk];
+    vs_old = T.vs[blk];
+  }
+  for (int h = 0; h < 2; ++h) {
+    if (fpp) {
+      load_f8((const float*)T.w, run[h], n, w + 8 * h);
+      load_f8((const float*)T.g, run[h], n, g + 8 * h);
+    } else {
+      uint32_t gw[4];
+      load8_guard((const uint16_t*)T.w, run[h], n, 0u, hw + 4 * h);
+      load8_guard(T.lo, run[h], n, 0u, lw + 4 * h);
+      load8_guard((const uint16_t*)T.g, run[h], n, 0u, gw);
+      for (int j = 0; j < 8; ++j) {
+        w[8 * h + j] = __uint_as_float(join_pair_elem<SPLIT>(hw[4 * h + (j >> 1)], lw[4 * h + (j >> 1)], j & 1));
+        g[8 * h + j] = (j & 1) ? bf16_hi(gw[j >> 1]) : bf16_lo(gw[j >> 1]);
+      }
+    }
+    if (fpm) {
+      load_f8((const float*)T.m, run[h], n, m + 8 * h);
+      load_f8((const float*)T.v, run[h], n, v + 8 * h);
+    } else {
+      uint32_t mw[4], vw[4];
+      load8_guard((const uint16_t*)T.m, run[h], n, 0x80008000u, mw);
+      load8_guard((const uint16_t*)T.v, run[h], n, 0u, vw);
+      for (int j = 0; j < 8; ++j) {
+        m[8 * h + j] = dec_signed((j & 1) ? code_hi_f(mw[j >> 1]) : code_lo_f(mw[j >> 1]), ms_old);
+        v[8 * h + j] = dec_unsigned((j & 1) ? code_hi_f(vw[j >> 1]) : code_lo_f(vw[j >> 1]), vs_old);
+      }
+    }
+  }
+  float mx_m = 0.0f, mx_v = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float m1 = __builtin_fmaf(c.B1, m[k], c.C1 * g[k]);
+    const float v1 = __builtin_fmaf(c.B2, v[k], c.C2 * (g[k] * g[k]));
+    m[k] = m1;
+    v[k] = v1;
+    mx_m = __builtin_fmaxf(mx_m, __builtin_fabsf(m1));
+    mx_v = __builtin_fmaxf(mx_v, v1);
+  }
+  float sm = 0.0f, inv_m = 0.0f, sv = 0.0f, inv_v = 0.0f;
+  if (!fpm) {
+    block_scale(row16_max(mx_m), sm, inv_m);
+    block_scale(row16_max(mx_v), sv, inv_v);
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float d = __builtin_fmaf(__builtin_sqrtf(v[k]), c.RS2, c.EPS);
+    float u;
+    if (ALGO == PS_ALGO_ADAM)
+      u = c.A * (m[k] / d);
+    else
+      u = __builtin_fmaf(c.AG, g[k], c.AM * m[k]) / d;
+    if (WD) u = __builtin_fmaf(c.CWD, w[k], u);
+    w[k] = w[k] - u;
+  }
+  for (int h = 0; h < 2; ++h) {
+    if (fpp) {
+      store_f8((float*)T.w, run[h], n, w + 8 * h);
+    } else {
+      uint32_t oh[4], ol[4];
+      for (int q = 0; q < 4; ++q)
+        split_pair<SPLIT>(__float_as_uint(w[8 * h + 2 * q]), __float_as_uint(w[8 * h + 2 * q + 1]), oh[q], ol[q]);
+      store8_guard((uint16_t*)T.w, run[h], n, oh);
+      store8_guard(T.lo, run[h], n, ol);
+    }
+    if (fpm) {
+      store_f8((float*)T.m, run[h], n, m + 8 * h);
+      store_f8((float*)T.v, run[h], n, v + 8 * h);
+    } else {
+      uint32_t om[4], ov[4];
+      for (int q = 0; q < 4; ++q) {
+        const int k = 8 * h + 2 * q;
+        om[q] = enc_signed(m[k], inv_m) | (enc_signed(m[k + 1], inv_m) << 16);
+        ov[q] = enc_unsigned(v[k], inv_v) | (enc_unsigned(v[k + 1], inv_v) << 16);
+      }
+      store8_guard((uint16_t*)T.m, run[h], n, om);
+      store8_guard((uint16_t*)T.v, run[h], n, ov);
+    }
+  }
+  if (!fpm && r == 0 && blk * kBlock < n) {
+    T.ms[blk] = sm;
+    T.vs[blk] = sv;
+  }
+}
+
+template <int ALGO, bool WD, int SPLIT>
+__global__ __launch_bounds__(64) void k_adam_step_ex(TableExPtr tbl, StepScalars c) {
+  const uint32_t item = blockIdx.x;
+  int lo = 0, hi = tbl.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (tbl.item_end[mid] > item)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  const uint32_t begin = lo ? tbl.item_end[lo - 1] : 0u;
+  process_item_ex<ALGO, WD, SPLIT>(tbl.recs[lo], (int64_t)(item - begin) * kItemElems, (int)threadIdx.x, c);
+}
+
+template <int ALGO, bool WD, int SPLIT>
+ps_status launch_ex_t(const TableExPtr& tbl, uint32_t total_items, const StepScalars& c, hipStream_t s) {
+  hipLaunchKernelGGL((k_adam_step_ex<ALGO, WD, SPLIT>), dim3(total_items), dim3(64), 0, s, tbl, c);
+  return hip_check(hipGetLastError(), "k_adam_step_ex launch");
+}
+
 template <class TBL>
 ps_status dispatch(const TBL& tbl, uint32_t total_items, const ps_hparams& hp, const StepScalars& c,
                    hipStream_t s) {
@@ -228,6 +372,24 @@ ps_status launch_adam_ptr(const TablePtr& tbl, uint32_t total_items, const ps_hp
 ps_status launch_adam_inline(const TableInline& tbl, uint32_t total_items, const ps_hparams& hp,
                              const StepScalars& c, hipStream_t s) {
   return dispatch(tbl, total_items, hp, c, s);
+}
+
+ps_status launch_adam_ex(const TableExPtr& tbl, uint32_t total_items, const ps_hparams& hp, const StepScalars& c,
+                         hipStream_t s) {
+  const bool wd = hp.weight_decay != 0.0;
+  const bool na = hp.split_mode == PS_SPLIT_NEAREST_AWAY;
+#define PS_CASE(A, W, S) \
+  if (hp.algo == A && wd == W && na == (S == PS_SPLIT_NEAREST_AWAY)) return launch_ex_t<A, W, S>(tbl, total_items, c, s);
+  PS_CASE(PS_ALGO_NADAM, false, PS_SPLIT_TRUNC)
+  PS_CASE(PS_ALGO_NADAM, true, PS_SPLIT_TRUNC)
+  PS_CASE(PS_ALGO_ADAM, false, PS_SPLIT_TRUNC)
+  PS_CASE(PS_ALGO_ADAM, true, PS_SPLIT_TRUNC)
+  PS_CASE(PS_ALGO_NADAM, false, PS_SPLIT_NEAREST_AWAY)
+  PS_CASE(PS_ALGO_NADAM, true, PS_SPLIT_NEAREST_AWAY)
+  PS_CASE(PS_ALGO_ADAM, false, PS_SPLIT_NEAREST_AWAY)
+  PS_CASE(PS_ALGO_ADAM, true, PS_SPLIT_NEAREST_AWAY)
+#undef PS_CASE
+  return fail(PS_ERR_UNSUPPORTED, "no kernel for algo %d split_mode %d", hp.algo, hp.split_mode);
 }
 
 }  // namespace ps

@@ -77,26 +77,40 @@ ps_status check_array(const void* p, const char* what, int i, uintptr_t align) {
   return PS_OK;
 }
 
-// Validates the records and builds the active list (tensors with numel > 0
-// and a gradient) with the work-item prefix ends.
-ps_status build_active(const ps_tensor* t, int32_t n, std::vector<DevTensor>& recs, std::vector<uint32_t>& ends) {
+// Validates the records and builds the active lists (tensors with numel > 0
+// and a gradient) with their work-item prefix ends: default formats in recs,
+// tensors with storage flags in xrecs.
+ps_status build_active(const ps_tensor* t, int32_t n, std::vector<DevTensor>& recs, std::vector<uint32_t>& ends,
+                       std::vector<DevTensorEx>& xrecs, std::vector<uint32_t>& xends) {
   if (n < 0) return fail(PS_ERR_INVALID_ARG, "n_tensors < 0");
   if (n > 0 && !t) return fail(PS_ERR_INVALID_ARG, "tensors is NULL");
-  uint64_t items = 0;
+  uint64_t items = 0, xitems = 0;
+  const uint32_t known = PS_TENSOR_FP32_MOMENTS | PS_TENSOR_FP32_PARAM;
   for (int32_t i = 0; i < n; ++i) {
     const ps_tensor& x = t[i];
     if (x.numel < 0 || x.numel > kMaxNumel) return fail(PS_ERR_SHAPE, "tensor %d: numel %lld out of range", i, (long long)x.numel);
+    if ((x.flags & ~known) || x.reserved) return fail(PS_ERR_INVALID_ARG, "tensor %d: unknown flags", i);
     if (x.numel == 0 || x.grad == nullptr) continue;
+    const bool fpm = x.flags & PS_TENSOR_FP32_MOMENTS, fpp = x.flags & PS_TENSOR_FP32_PARAM;
     ps_status s;
-    if ((s = check_array(x.w_hi, "w_hi", i, 16)) || (s = check_array(x.w_lo, "w_lo", i, 16)) ||
-        (s = check_array(x.grad, "grad", i, 16)) || (s = check_array(x.m_code, "m_code", i, 16)) ||
-        (s = check_array(x.v_code, "v_code", i, 16)) || (s = check_array(x.m_scale, "m_scale", i, 4)) ||
-        (s = check_array(x.v_scale, "v_scale", i, 4)))
+    if ((s = check_array(x.w_hi, "w_hi", i, 16)) || (s = check_array(x.grad, "grad", i, 16)) ||
+        (s = check_array(x.m_code, "m_code", i, 16)) || (s = check_array(x.v_code, "v_code", i, 16)))
       return s;
-    items += (uint64_t)((x.numel + kItemElems - 1) / kItemElems);
-    if (items > 0x7FFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large (more than 2^31 - 1 work items)");
-    recs.push_back(DevTensor{x.w_hi, x.w_lo, x.grad, x.m_code, x.m_scale, x.v_code, x.v_scale, x.numel});
-    ends.push_back((uint32_t)items);
+    if (!fpp && (s = check_array(x.w_lo, "w_lo", i, 16))) return s;
+    if (!fpm && ((s = check_array(x.m_scale, "m_scale", i, 4)) || (s = check_array(x.v_scale, "v_scale", i, 4))))
+      return s;
+    const uint64_t nit = (uint64_t)((x.numel + kItemElems - 1) / kItemElems);
+    if (x.flags) {
+      xitems += nit;
+      if (xitems > 0x7FFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large (more than 2^31 - 1 work items)");
+      xrecs.push_back(DevTensorEx{x.w_hi, x.w_lo, x.grad, x.m_code, x.m_scale, x.v_code, x.v_scale, x.numel, x.flags, 0});
+      xends.push_back((uint32_t)xitems);
+    } else {
+      items += nit;
+      if (items > 0x7FFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large (more than 2^31 - 1 work items)");
+      recs.push_back(DevTensor{x.w_hi, x.w_lo, x.grad, x.m_code, x.m_scale, x.v_code, x.v_scale, x.numel});
+      ends.push_back((uint32_t)items);
+    }
   }
   return PS_OK;
 }
@@ -229,11 +243,24 @@ ps_status ps_opt_step_multi(const ps_tensor* tensors, int32_t n_tensors, const p
   if (step < 1) return fail(PS_ERR_INVALID_ARG, "step must be >= 1 (got %lld)", (long long)step);
   std::vector<DevTensor> recs;
   std::vector<uint32_t> ends;
-  if (ps_status s = build_active(tensors, n_tensors, recs, ends)) return s;
-  if (recs.empty()) return PS_OK;
+  std::vector<DevTensorEx> xrecs;
+  std::vector<uint32_t> xends;
+  if (ps_status s = build_active(tensors, n_tensors, recs, ends, xrecs, xends)) return s;
+  if (recs.empty() && xrecs.empty()) return PS_OK;
   StepScalars c;
   step_scalars(*hp, step, &c);
   hipStream_t s = (hipStream_t)stream;
+  if (!xrecs.empty()) {
+    const size_t rb = xrecs.size() * sizeof(DevTensorEx), eb = xends.size() * sizeof(uint32_t);
+    std::vector<unsigned char> blob(rb + eb);
+    memcpy(blob.data(), xrecs.data(), rb);
+    memcpy(blob.data() + rb, xends.data(), eb);
+    const void* d = nullptr;
+    if (ps_status st = device_blob(blob.data(), blob.size(), s, &d)) return st;
+    TableExPtr tx{(const DevTensorEx*)d, (const uint32_t*)((const char*)d + rb), (int32_t)xrecs.size()};
+    if (ps_status st = launch_adam_ex(tx, xends.back(), *hp, c, s)) return st;
+  }
+  if (recs.empty()) return PS_OK;
   const uint32_t total = ends.back();
   if (recs.size() <= (size_t)kInlineMax) {
     TableInline tb;

@@ -56,6 +56,7 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, Layout& L) {
   for (int32_t i = 0; i < n; ++i) {
     const ps_tensor& x = t[i];
     if (x.numel < 0 || x.numel > (int64_t(1) << 40)) return fail(PS_ERR_SHAPE, "tensor %d: numel out of range", i);
+    if (x.flags || x.reserved) return fail(PS_ERR_UNSUPPORTED, "tensor %d: storage flags are not supported here", i);
     if (x.numel == 0 || x.grad == nullptr) continue;
     ps_status s;
     if ((s = check_ptr(x.w_hi, "w_hi", i, 16)) || (s = check_ptr(x.w_lo, "w_lo", i, 16)) ||

@@ -26,6 +26,26 @@ struct DevTensor {
   int64_t numel;
 };
 
+// Device record of a tensor with storage flags (generic-format kernel).
+struct DevTensorEx {
+  void* w;          // bf16 bits, or float when PS_TENSOR_FP32_PARAM
+  uint16_t* lo;
+  const void* g;    // bf16 bits, or float when PS_TENSOR_FP32_PARAM
+  void* m;          // codes, or float when PS_TENSOR_FP32_MOMENTS
+  float* ms;
+  void* v;
+  float* vs;
+  int64_t numel;
+  uint32_t flags;
+  uint32_t pad;
+};
+
+struct TableExPtr {
+  const DevTensorEx* recs;
+  const uint32_t* item_end;
+  int32_t n;
+};
+
 // fp32 scalars of one update (see ps_step_scalars).
 struct StepScalars {
   float B1, C1, B2, C2, EPS, A, RS2, AG, AM, CWD;
@@ -127,6 +147,8 @@ ps_status launch_adam_ptr(const TablePtr& tbl, uint32_t total_items, const ps_hp
                           hipStream_t s);
 ps_status launch_adam_inline(const TableInline& tbl, uint32_t total_items, const ps_hparams& hp,
                              const StepScalars& c, hipStream_t s);
+ps_status launch_adam_ex(const TableExPtr& tbl, uint32_t total_items, const ps_hparams& hp, const StepScalars& c,
+                         hipStream_t s);
 ps_status launch_split(const float* w, uint16_t* hi, uint16_t* lo, int64_t n, int mode, hipStream_t s);
 ps_status launch_join(const uint16_t* hi, const uint16_t* lo, float* w, int64_t n, int mode, hipStream_t s);
 ps_status launch_encode(const float* x, uint16_t* code, float* scale, int64_t n, int kind, hipStream_t s);

@@ -121,6 +121,10 @@ ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_group
         destroy(p);
         return fail(PS_ERR_SHAPE, "group %d tensor %d: numel out of range", g, i);
       }
+      if (x.flags || x.reserved) {
+        destroy(p);
+        return fail(PS_ERR_UNSUPPORTED, "group %d tensor %d: storage flags are not supported here", g, i);
+      }
       if (x.numel == 0 || !x.grad) continue;
       ps_status st;
       if ((st = check_dev(x.w_hi, "w_hi", g, i)) || (st = check_dev(x.grad, "grad", g, i)) ||

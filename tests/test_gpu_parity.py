@@ -248,3 +248,75 @@ def test_flux_double_block_3_steps_sampled():
     torch.cuda.synchronize()
     nblk = check_sampled_blocks(shapes, devs, hp, 3, seed, per_tensor=48)
     print(f"  {nblk} sampled blocks bit-exact", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# per-tensor storage flags (fp32 moments for small tensors, fp32 final layer)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY])
+def test_storage_flags_match_oracle(split_mode):
+    """A list mixing the default format with fp32 moments (tensors of <= 4096
+    elements on the pages) and fp32 parameters (the final layer), ragged
+    sizes, both the kernel-argument and the device-table paths, 3 NAdamW
+    steps; bit-exact against the oracle."""
+    sizes = [64, 128, 3072, 4096, 1000, 300001, 257, 18432, 3000, 5, 6144 * 8, 2048, 100, 4096, 77, 65536, 999]
+    flag_of = [ps.TENSOR_FP32_MOMENTS if n <= 4096 else 0 for n in sizes]
+    flag_of[5] = ps.TENSOR_FP32_PARAM
+    flag_of[10] = ps.TENSOR_FP32_PARAM | ps.TENSOR_FP32_MOMENTS
+    hp = ps.HParams(algo=ps.ALGO_NADAM, weight_decay=0.01, lr=1e-4, split_mode=split_mode)
+    for count in (len(sizes), 9):
+        devs, hosts = [], []
+        for i, (n, fl) in enumerate(zip(sizes[:count], flag_of[:count])):
+            hi = synth.host_bf16_normal(n, 13, synth.STREAM_HI, i, 0, synth.SIGMA_W)
+            lo = synth.host_u16_uniform(n, 13, synth.STREAM_LO, i, 0)
+            h = {"flags": fl}
+            if fl & ps.TENSOR_FP32_PARAM:
+                h["w"] = oracle.join(hi, lo, split_mode)
+                h["lo"] = None
+            else:
+                h["w"], h["lo"] = hi.copy(), lo.copy()
+            if fl & ps.TENSOR_FP32_MOMENTS:
+                h["m"], h["v"], h["ms"], h["vs"] = np.zeros(n, np.float32), np.zeros(n, np.float32), None, None
+            else:
+                h["m"], h["ms"], h["v"], h["vs"] = oracle.zero_moments(n)
+            hosts.append(h)
+            to_dev = lambda a: None if a is None else torch.from_numpy(  # noqa: E731
+                a.view(np.int16) if a.dtype == np.uint16 else a.copy()).to(DEV)
+            st = ps.TensorState(to_dev(h["w"].copy()), to_dev(h["lo"]), to_dev(h["m"].copy()), to_dev(h["ms"]),
+                                to_dev(h["v"].copy()), to_dev(h["vs"]), flags=fl)
+            if st.w_lo is None:
+                st.w_lo = torch.empty(0, dtype=torch.int16, device=DEV)   # unused for fp32 parameters
+            if st.m_scale is None:
+                st.m_scale = st.v_scale = torch.empty(0, dtype=torch.float32, device=DEV)
+            devs.append(st)
+        for t in range(1, 4):
+            grads_d, grads_h = [], []
+            for i, (n, fl) in enumerate(zip(sizes[:count], flag_of[:count])):
+                g16 = synth.host_bf16_normal(n, 13, synth.STREAM_GRAD, i, t, synth.SIGMA_G)
+                if fl & ps.TENSOR_FP32_PARAM:
+                    g32 = oracle.bf16_to_f32(g16).copy()
+                    grads_h.append(g32)
+                    grads_d.append(torch.from_numpy(g32).to(DEV))
+                else:
+                    grads_h.append(g16)
+                    grads_d.append(torch.from_numpy(g16.view(np.int16)).to(DEV))
+            ps.opt_step_multi(devs, grads_d, hp, t)
+            for h, g in zip(hosts, grads_h):
+                oracle.opt_step_flags(h["w"], h["lo"], g, h["m"], h["ms"], h["v"], h["vs"], h["flags"], ohp(hp), t)
+        torch.cuda.synchronize()
+        for i, (d, h) in enumerate(zip(devs, hosts)):
+            fl = h["flags"]
+            got_w = d.w_hi.cpu().numpy()
+            assert np.array_equal(got_w.view(np.uint32 if fl & ps.TENSOR_FP32_PARAM else np.uint16),
+                                  h["w"].view(np.uint32 if fl & ps.TENSOR_FP32_PARAM else np.uint16)), (count, i, "w")
+            if not fl & ps.TENSOR_FP32_PARAM:
+                assert np.array_equal(u16(d.w_lo), h["lo"]), (count, i, "lo")
+            for k in ("m", "v"):
+                got = getattr(d, k + "_code").cpu().numpy()
+                want = h[k]
+                assert np.array_equal(got.view(np.uint32 if want.dtype == np.float32 else np.uint16),
+                                      want.view(np.uint32 if want.dtype == np.float32 else np.uint16)), (count, i, k)
+            if not fl & ps.TENSOR_FP32_MOMENTS:
+                assert np.array_equal(f32(d.m_scale).view(np.uint32), h["ms"].view(np.uint32)), (count, i, "ms")
+                assert np.array_equal(f32(d.v_scale).view(np.uint32), h["vs"].view(np.uint32)), (count, i, "vs")
