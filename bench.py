@@ -36,6 +36,23 @@ BYTES_PER_BLOCK = 16
 KERNEL_SOURCES = ["precision_state_amd/csrc/k_adam.hip", "precision_state_amd/csrc/dev_common.h"]
 
 
+def step_bytes(numel, flags=0):
+    """Algorithmic HBM bytes of one step of one tensor: the weight words read
+    and written (bf16 + residual, or fp32), the gradient read, the two moments
+    read and written (uint16 codes + per-256 scales, fp32, or f24)."""
+    import precision_state_amd as ps
+    nblk = -(-numel // 256)
+    w = 8 * numel
+    g = (4 if flags & ps.TENSOR_FP32_PARAM else 2) * numel
+    if flags & ps.TENSOR_FP32_MOMENTS:
+        mv = 16 * numel
+    elif flags & getattr(ps, "TENSOR_F24_MOMENTS", 0):
+        mv = 12 * numel
+    else:
+        mv = 8 * numel + BYTES_PER_BLOCK * nblk
+    return w + g + mv
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -306,6 +323,9 @@ def main():
     ap.add_argument("--mode", default="nadam", choices=["nadam", "factored", "offload"],
                     help="nadam: the fused (N)AdamW step (headline); factored: the Adafactor-style step "
                          "(no first moment, factored second moment, update clipping) on the same shapes")
+    ap.add_argument("--policy", action="store_true",
+                    help="nadam mode: fp32 moments for tensors of <= 4096 elements and an fp32 final layer "
+                         "(PS_TENSOR_FP32_MOMENTS / PS_TENSOR_FP32_PARAM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="after the timed steps, run 3 plain device copies of GIB GiB (counter calibration "
@@ -339,6 +359,23 @@ def main():
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
 
     hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+    n_small = n_final = 0
+    if args.policy:
+        for i, (s, st) in enumerate(zip(shapes, states)):
+            if s.name.startswith("final_layer."):
+                w32 = torch.empty(s.numel, dtype=torch.float32, device=dev)
+                ps.join(st.w_hi, st.w_lo, w32)
+                st.w_hi, st.w_lo = w32, torch.empty(0, dtype=torch.int16, device=dev)
+                grads[i] = grads[i].view(torch.bfloat16).float()
+                st.flags |= ps.TENSOR_FP32_PARAM
+                n_final += 1
+            if s.numel <= 4096:
+                st.m_code = torch.zeros(s.numel, dtype=torch.float32, device=dev)
+                st.v_code = torch.zeros(s.numel, dtype=torch.float32, device=dev)
+                st.flags |= ps.TENSOR_FP32_MOMENTS
+                n_small += 1
+        torch.cuda.synchronize()
+        log(f"[bench] policy: {n_small} tensors with fp32 moments, {n_final} fp32 final-layer tensors")
     recs = ps.make_records(states, grads)
     stream = torch.cuda.current_stream()
     step = 0
@@ -387,9 +424,9 @@ def main():
         log(f"[bench] plain copy of {nbytes} bytes: best {min(times):.3f} ms = {copy_gbs:.0f} GB/s (read + write)")
         del src, dst
 
-    alg_bytes = BYTES_PER_PARAM * n_params + BYTES_PER_BLOCK * n_blocks
+    alg_bytes = sum(step_bytes(s.numel, st.flags) for s, st in zip(shapes, states))
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
-    traffic = read_traffic(args.workload, n_params, n_blocks)
+    traffic = None if args.policy else read_traffic(args.workload, n_params, n_blocks)
 
     baseline = None
     if not args.no_cpu_baseline:
@@ -414,6 +451,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "params": n_params, "tensors": len(shapes),
                    "algo": "nadam", "lr": 3.5e-6, "weight_decay": 0.0, "layout": args.layout,
+                   "policy": {"fp32_moment_tensors": n_small, "fp32_param_tensors": n_final} if args.policy else None,
                    "state": "bf16 weight + u16 residual + bf16 grad + u16 m/v codes + fp32 per-256 scales",
                    "hbm_gbs_18B_per_param": BYTES_PER_PARAM * n_params / (kernel_ms * 1e-3) / 1e9,
                    "kernel_ms": kernel_ms, "copy_gbs": copy_gbs},
