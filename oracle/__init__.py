@@ -89,6 +89,8 @@ def lib():
             "orc_opt_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_HP), _i64], None),
             "orc_opt_step_flags": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, ctypes.c_uint32, ctypes.POINTER(_HP),
                                     _i64], None),
+            "orc_f24_encode": ([_vp, _i64, _vp], None),
+            "orc_f24_decode": ([_vp, _i64, _vp], None),
             "orc_factored_2d": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.POINTER(_FHP), _i64], None),
             "orc_factored_1d": ([_vp, _vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_FHP), _i64], None),
         }
@@ -194,15 +196,31 @@ def opt_step(st: TensorState, g, hp: HParams, step: int):
                        ctypes.byref(h), step)
 
 
-FP32_MOMENTS, FP32_PARAM = 1, 2
+FP32_MOMENTS, FP32_PARAM, F24_MOMENTS = 1, 2, 4
+
+
+def f24_encode(x):
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(3 * x.size, np.uint8)
+    lib().orc_f24_encode(x.ctypes.data, x.size, out.ctypes.data)
+    return out
+
+
+def f24_decode(b):
+    b = np.ascontiguousarray(b, np.uint8)
+    out = np.empty(b.size // 3, np.float32)
+    lib().orc_f24_decode(b.ctypes.data, out.size, out.ctypes.data)
+    return out
 
 
 def opt_step_flags(w, lo, g, m, ms, v, vs, flags, hp: HParams, step: int):
     """In place. w/g: uint16 (bf16 bits) or float32 when FP32_PARAM; m/v: uint16
-    codes with scales ms/vs, or float32 arrays when FP32_MOMENTS."""
+    codes with scales ms/vs, float32 arrays when FP32_MOMENTS, or uint8 f24
+    arrays (3 bytes per value) when F24_MOMENTS."""
     h = hp.c()
     ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
-    lib().orc_opt_step_flags(ptr(w), ptr(lo), ptr(g), ptr(m), ptr(ms), ptr(v), ptr(vs), w.size, flags,
+    n = w.size
+    lib().orc_opt_step_flags(ptr(w), ptr(lo), ptr(g), ptr(m), ptr(ms), ptr(v), ptr(vs), n, flags,
                              ctypes.byref(h), step)
 
 

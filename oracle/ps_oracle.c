@@ -281,8 +281,33 @@ void orc_opt_step(uint16_t* hi, uint16_t* lo, const uint16_t* g, uint16_t* mc, f
  * elements keep their moments in fp32; third post: the final layer trains in
  * fp32]. flags bit 0: moments are fp32 arrays m[n], v[n] (no codec, scales
  * unused); bit 1: the parameter and its gradient are fp32 arrays w[n], g[n]
- * (no residual). The update is the same element step. */
-enum { ORC_FP32_MOMENTS = 1, ORC_FP32_PARAM = 2 };
+ * (no residual); bit 2: moments are f24 arrays (3 bytes per value, scales
+ * unused). The update is the same element step. */
+enum { ORC_FP32_MOMENTS = 1, ORC_FP32_PARAM = 2, ORC_F24_MOMENTS = 4 };
+
+/* f24 storage [NADAM, third post]: the upper three bytes of the fp32 word,
+ * i.e. 8 more mantissa bits than bf16. Rounding to 24 bits is to nearest,
+ * ties to even (the pages do not say). Stored little-endian, 3 bytes per
+ * value. */
+void orc_f24_encode1(float x, uint8_t* out) {
+  uint32_t b = u_of(x);
+  uint32_t r = (b + 0x7Fu + ((b >> 8) & 1u)) >> 8;
+  out[0] = (uint8_t)r;
+  out[1] = (uint8_t)(r >> 8);
+  out[2] = (uint8_t)(r >> 16);
+}
+
+float orc_f24_decode1(const uint8_t* in) {
+  return f_of(((uint32_t)in[0] << 8) | ((uint32_t)in[1] << 16) | ((uint32_t)in[2] << 24));
+}
+
+void orc_f24_encode(const float* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) orc_f24_encode1(x[i], out + 3 * i);
+}
+
+void orc_f24_decode(const uint8_t* in, int64_t n, float* x) {
+  for (int64_t i = 0; i < n; ++i) x[i] = orc_f24_decode1(in + 3 * i);
+}
 
 void orc_opt_step_flags(void* w, uint16_t* lo, const void* g, void* m, float* ms, void* v, float* vs, int64_t n,
                         uint32_t flags, const orc_hparams* hp, int64_t step) {
@@ -307,6 +332,9 @@ void orc_opt_step_flags(void* w, uint16_t* lo, const void* g, void* m, float* ms
       if (flags & ORC_FP32_MOMENTS) {
         m0 = ((float*)m)[e];
         v0 = ((float*)v)[e];
+      } else if (flags & ORC_F24_MOMENTS) {
+        m0 = orc_f24_decode1((uint8_t*)m + 3 * e);
+        v0 = orc_f24_decode1((uint8_t*)v + 3 * e);
       } else {
         m0 = orc_decode1(((uint16_t*)m)[e], ms[b], ORC_SIGNED);
         v0 = orc_decode1(((uint16_t*)v)[e], vs[b], ORC_UNSIGNED);
@@ -319,9 +347,12 @@ void orc_opt_step_flags(void* w, uint16_t* lo, const void* g, void* m, float* ms
       if (flags & ORC_FP32_MOMENTS) {
         ((float*)m)[e] = mbuf[i];
         ((float*)v)[e] = vbuf[i];
+      } else if (flags & ORC_F24_MOMENTS) {
+        orc_f24_encode1(mbuf[i], (uint8_t*)m + 3 * e);
+        orc_f24_encode1(vbuf[i], (uint8_t*)v + 3 * e);
       }
     }
-    if (!(flags & ORC_FP32_MOMENTS)) {
+    if (!(flags & (ORC_FP32_MOMENTS | ORC_F24_MOMENTS))) {
       orc_encode_block(mbuf, L, ORC_SIGNED, (uint16_t*)m + base, &ms[b]);
       orc_encode_block(vbuf, L, ORC_UNSIGNED, (uint16_t*)v + base, &vs[b]);
     }

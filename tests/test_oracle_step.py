@@ -256,3 +256,23 @@ def test_policy_flags_reduce_to_pinned_steps(algo, wd):
         oracle.opt_step_flags(w_e, None, g32, mc, ms, vc, vs, oracle.FP32_PARAM, hp, t)
     assert np.array_equal(oracle.join(st.hi, st.lo).view(np.uint32), w_e.view(np.uint32))
     assert np.array_equal(st.mc, mc) and np.array_equal(st.vc, vc) and np.array_equal(st.ms, ms)
+
+
+def test_f24_moment_step_equals_core_step_on_f24_rounded_moments():
+    """With F24 moments each step equals the fp32 core step whose moments are
+    rounded to f24 after every update (the storage is the only difference)."""
+    n = 999
+    hp = HParams(lr=1e-4)
+    rng = np.random.default_rng(33)
+    w32 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    hi, lo = oracle.split(w32)
+    m24, v24 = oracle.f24_encode(np.zeros(n, np.float32)), oracle.f24_encode(np.zeros(n, np.float32))
+    w_r, m_r, v_r = w32.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in range(1, 6):
+        g16 = _bf16(rng.standard_normal(n) * 1e-3)
+        oracle.opt_step_flags(hi, lo, g16, m24, None, v24, None, oracle.F24_MOMENTS, hp, t)
+        oracle.core_step(w_r, m_r, v_r, oracle.bf16_to_f32(g16).copy(), hp, t)
+        m_r = oracle.f24_decode(oracle.f24_encode(m_r))
+        v_r = oracle.f24_decode(oracle.f24_encode(v_r))
+    assert np.array_equal(oracle.join(hi, lo).view(np.uint32), w_r.view(np.uint32))
+    assert np.array_equal(oracle.f24_decode(m24).view(np.uint32), m_r.view(np.uint32))
