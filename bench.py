@@ -31,7 +31,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "optimizer-updated params/sec + achieved HBM GB/s (% of MI355X peak), Flux-12B set"
 PEAK_HBM_GBS = 8000.0
-BYTES_PER_PARAM = 18
 BYTES_PER_BLOCK = 16
 KERNEL_SOURCES = ["precision_state_amd/csrc/k_adam.hip", "precision_state_amd/csrc/dev_common.h"]
 
@@ -65,10 +64,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload, n_params, n_blocks):
+def read_traffic(workload, moments="codec"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"adam_step_{workload}_counters.txt")
+    tag = "" if moments == "codec" else f"_{moments}"
+    path = os.path.join(ROOT, "profiles", f"adam_step_{workload}{tag}_counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -84,20 +84,23 @@ def read_traffic(workload, n_params, n_blocks):
         return None
 
 
-def build_state(shapes, seed, dev, layout="slab"):
+def build_state(shapes, seed, dev, layout="slab", moments="codec"):
     """Optimizer state for every tensor of the set, filled on the device.
 
     layout "slab": one contiguous allocation per state stream
     (precision_state_amd.StateSlab); "separate": one allocation per tensor and
-    stream."""
+    stream. moments "f24" (slab only): f24 moment arrays instead of codes."""
     import torch
 
     import precision_state_amd as ps
     import synth
     if layout == "slab":
-        slab = ps.StateSlab([s.numel for s in shapes], dev, shapes2d=[(s.rows, s.cols) for s in shapes])
+        slab = ps.StateSlab([s.numel for s in shapes], dev, shapes2d=[(s.rows, s.cols) for s in shapes],
+                            moments=moments)
         states, grads = slab.states, slab.grads
     else:
+        if moments != "codec":
+            raise ValueError("f24 moments need the slab layout")
         states, grads = [], []
         for s in shapes:
             n, nb = s.numel, (s.numel + 255) // 256
@@ -326,6 +329,9 @@ def main():
     ap.add_argument("--policy", action="store_true",
                     help="nadam mode: fp32 moments for tensors of <= 4096 elements and an fp32 final layer "
                          "(PS_TENSOR_FP32_MOMENTS / PS_TENSOR_FP32_PARAM)")
+    ap.add_argument("--moments", default="codec", choices=["codec", "f24"],
+                    help="nadam mode: moment storage, uint16 codes + per-256 scales (codec) or the upper three "
+                         "bytes of fp32 (f24, PS_TENSOR_F24_MOMENTS)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="after the timed steps, run 3 plain device copies of GIB GiB (counter calibration "
@@ -350,10 +356,9 @@ def main():
         return bench_offload(args)
     shapes = synth.WORKLOADS[args.workload]()
     n_params = synth.total_params(shapes)
-    n_blocks = sum((s.numel + 255) // 256 for s in shapes)
     log(f"[bench] {args.workload}: {len(shapes)} tensors, {n_params} params; generating state on {dev}")
     t0 = time.perf_counter()
-    states, grads = build_state(shapes, args.seed, dev, args.layout)
+    states, grads = build_state(shapes, args.seed, dev, args.layout, args.moments)
     torch.cuda.synchronize()
     log(f"[bench] state ready in {time.perf_counter() - t0:.1f} s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
@@ -372,7 +377,7 @@ def main():
             if s.numel <= 4096:
                 st.m_code = torch.zeros(s.numel, dtype=torch.float32, device=dev)
                 st.v_code = torch.zeros(s.numel, dtype=torch.float32, device=dev)
-                st.flags |= ps.TENSOR_FP32_MOMENTS
+                st.flags = (st.flags & ~ps.TENSOR_F24_MOMENTS) | ps.TENSOR_FP32_MOMENTS
                 n_small += 1
         torch.cuda.synchronize()
         log(f"[bench] policy: {n_small} tensors with fp32 moments, {n_final} fp32 final-layer tensors")
@@ -426,7 +431,7 @@ def main():
 
     alg_bytes = sum(step_bytes(s.numel, st.flags) for s, st in zip(shapes, states))
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
-    traffic = None if args.policy else read_traffic(args.workload, n_params, n_blocks)
+    traffic = None if args.policy else read_traffic(args.workload, args.moments)
 
     baseline = None
     if not args.no_cpu_baseline:
@@ -452,8 +457,10 @@ def main():
         "config": {"workload": args.workload, "params": n_params, "tensors": len(shapes),
                    "algo": "nadam", "lr": 3.5e-6, "weight_decay": 0.0, "layout": args.layout,
                    "policy": {"fp32_moment_tensors": n_small, "fp32_param_tensors": n_final} if args.policy else None,
-                   "state": "bf16 weight + u16 residual + bf16 grad + u16 m/v codes + fp32 per-256 scales",
-                   "hbm_gbs_18B_per_param": BYTES_PER_PARAM * n_params / (kernel_ms * 1e-3) / 1e9,
+                   "moments": args.moments,
+                   "state": "bf16 weight + u16 residual + bf16 grad + " +
+                            ("u16 m/v codes + fp32 per-256 scales" if args.moments == "codec" else
+                             "f24 m/v (upper 3 bytes of fp32)"),
                    "kernel_ms": kernel_ms, "copy_gbs": copy_gbs},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},

@@ -70,9 +70,16 @@ enum { PS_MOMENT_SIGNED = 0, PS_MOMENT_UNSIGNED = 1 };
  *   PS_TENSOR_FP32_PARAM    w_hi points to the float[numel] parameter and grad
  *                           to a float[numel] gradient (no residual); w_lo is
  *                           not used
+ *   PS_TENSOR_F24_MOMENTS   [NADAM, third post: moments in the upper three
+ *                           bytes of fp32] m_code and v_code point to
+ *                           uint8[3 * numel]: value i is bytes 3i..3i+2, the
+ *                           fp32 word's bits 8..31 little-endian (low byte
+ *                           implied zero), rounded to nearest, ties to even;
+ *                           m_scale and v_scale are not used. Excludes
+ *                           PS_TENSOR_FP32_MOMENTS.
  * Supported by ps_opt_step_multi only (the factored step and the offload
  * pipeline reject non-zero flags with PS_ERR_UNSUPPORTED). */
-enum { PS_TENSOR_FP32_MOMENTS = 1u << 0, PS_TENSOR_FP32_PARAM = 1u << 1 };
+enum { PS_TENSOR_FP32_MOMENTS = 1u << 0, PS_TENSOR_FP32_PARAM = 1u << 1, PS_TENSOR_F24_MOMENTS = 1u << 2 };
 
 /* One parameter tensor's state. All arrays are device memory owned by the
  * caller, contiguous, `numel` elements unless noted; 16-bit and fp32 element

@@ -26,7 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 ALGO_ADAM, ALGO_NADAM = 0, 1
 SPLIT_TRUNC, SPLIT_NEAREST_AWAY = 0, 1
 MOMENT_SIGNED, MOMENT_UNSIGNED = 0, 1
-TENSOR_FP32_MOMENTS, TENSOR_FP32_PARAM = 1, 2
+TENSOR_FP32_MOMENTS, TENSOR_FP32_PARAM, TENSOR_F24_MOMENTS = 1, 2, 4
 BLOCK = 256
 
 STATUS = {0: "PS_OK", 1: "PS_ERR_INVALID_ARG", 2: "PS_ERR_ALIGNMENT", 3: "PS_ERR_SHAPE",
@@ -186,10 +186,11 @@ class StateSlab:
 
     ALIGN = 128    # elements of a 16-bit stream = 256 bytes
 
-    def __init__(self, numels, device="cuda", with_grads=True, shapes2d=None, host_state=False):
+    def __init__(self, numels, device="cuda", with_grads=True, shapes2d=None, host_state=False, moments="codec"):
         """host_state=True puts residuals, codes and scales in pinned host
         memory (the layout ps_offload_* expects); weights and gradients stay
-        on `device`."""
+        on `device`. moments="f24" stores both moments as f24 arrays (3 bytes
+        per value, zero-initialised, no scales; TENSOR_F24_MOMENTS)."""
         import torch
         self.numels = list(numels)
         offs, boffs, n_tot, nb_tot = [], [], 0, 0
@@ -198,23 +199,37 @@ class StateSlab:
             boffs.append(nb_tot)
             n_tot += (n + self.ALIGN - 1) // self.ALIGN * self.ALIGN
             nb_tot += ((n + BLOCK - 1) // BLOCK + 63) // 64 * 64
-        names = ["hi", "lo", "mc", "vc"] + (["g"] if with_grads else [])
+        if moments not in ("codec", "f24"):
+            raise ValueError("moments must be 'codec' or 'f24'")
+        f24 = moments == "f24"
+        names = ["hi", "lo"] + ([] if f24 else ["mc", "vc"]) + (["g"] if with_grads else [])
 
         def where(k):
             return dict(device="cpu", pin_memory=True) if host_state and k in ("lo", "mc", "vc", "ms", "vs") \
                 else dict(device=device)
         self.slab = {k: torch.empty(max(1, n_tot), dtype=torch.int16, **where(k)) for k in names}
-        self.slab["mc"].fill_(-32768)          # 0x8000: the zero code of the signed kind
-        self.slab["vc"].zero_()
-        self.scales = {k: torch.zeros(max(1, nb_tot), dtype=torch.float32, **where(k)) for k in ("ms", "vs")}
+        if f24:
+            for k in ("mc", "vc"):
+                self.slab[k] = torch.zeros(max(1, 3 * n_tot), dtype=torch.uint8, **where(k))
+            self.scales = {}
+        else:
+            self.slab["mc"].fill_(-32768)          # 0x8000: the zero code of the signed kind
+            self.slab["vc"].zero_()
+            self.scales = {k: torch.zeros(max(1, nb_tot), dtype=torch.float32, **where(k)) for k in ("ms", "vs")}
         self.states, self.grads = [], []
         for i, n in enumerate(self.numels):
             o, bo, nb = offs[i], boffs[i], (n + BLOCK - 1) // BLOCK
             rows, cols = shapes2d[i] if shapes2d else (0, 0)
-            self.states.append(TensorState(self.slab["hi"][o:o + n], self.slab["lo"][o:o + n],
-                                           self.slab["mc"][o:o + n], self.scales["ms"][bo:bo + nb],
-                                           self.slab["vc"][o:o + n], self.scales["vs"][bo:bo + nb],
-                                           rows=rows, cols=cols))
+            if f24:
+                self.states.append(TensorState(self.slab["hi"][o:o + n], self.slab["lo"][o:o + n],
+                                               self.slab["mc"][3 * o:3 * (o + n)], None,
+                                               self.slab["vc"][3 * o:3 * (o + n)], None,
+                                               rows=rows, cols=cols, flags=TENSOR_F24_MOMENTS))
+            else:
+                self.states.append(TensorState(self.slab["hi"][o:o + n], self.slab["lo"][o:o + n],
+                                               self.slab["mc"][o:o + n], self.scales["ms"][bo:bo + nb],
+                                               self.slab["vc"][o:o + n], self.scales["vs"][bo:bo + nb],
+                                               rows=rows, cols=cols))
             self.grads.append(self.slab["g"][o:o + n] if with_grads else None)
 
     def records(self, grads=None):

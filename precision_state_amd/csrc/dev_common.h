@@ -12,6 +12,11 @@
 
 namespace ps {
 
+// Global (HBM) address space: accesses through it compile to global_* rather
+// than flat_* instructions (no LDS aperture check, uniform-base addressing).
+#define GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // v_perm_b32 byte selectors. perm(s0, s1, sel) picks bytes of the 64-bit
 // value {s0:s1} (s1 = bytes 0..3, s0 = bytes 4..7).
 constexpr uint32_t kSelLoHalves = 0x05040100u;  // {s0.lo16, s1.lo16}
@@ -154,6 +159,33 @@ __device__ __forceinline__ void block_scale(float mx, float& s, float& inv) {
   bool keep = mx >= 0x1p-126f;
   s = keep ? mx : 0.0f;
   inv = keep ? 1.0f / mx : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// f24 moment storage [NADAM third post]: the upper three bytes of the fp32
+// word, rounded to nearest (ties to even), packed little-endian at 3 bytes
+// per value. Eight values occupy six 32-bit words.
+// ---------------------------------------------------------------------------
+
+// fp32 word rounded to its upper 24 bits (low byte zero).
+__device__ __forceinline__ uint32_t f24_round(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7Fu + ((u >> 8) & 1u)) & 0xFFFFFF00u;
+}
+
+// Four values from three packed words (bytes 0..11).
+__device__ __forceinline__ void f24_unpack4(uint32_t a, uint32_t b, uint32_t c, float* x) {
+  x[0] = __uint_as_float(a << 8);                        // bytes 0..2
+  x[1] = __uint_as_float(perm(b, a, 0x0504030Cu));       // bytes 3..5
+  x[2] = __uint_as_float(perm(c, b, 0x0403020Cu));       // bytes 6..8
+  x[3] = __uint_as_float(c & 0xFFFFFF00u);               // bytes 9..11
+}
+
+// Three packed words from four rounded words t[0..3] (low bytes zero).
+__device__ __forceinline__ void f24_pack4(const uint32_t* t, uint32_t& a, uint32_t& b, uint32_t& c) {
+  a = perm(t[1], t[0], 0x05030201u);
+  b = perm(t[2], t[1], 0x06050302u);
+  c = perm(t[3], t[2], 0x07060503u);
 }
 
 }  // namespace ps

@@ -22,12 +22,12 @@ struct Regs {       // one lane's 16 elements, 16-bit streams as packed pairs
 };
 
 __device__ __forceinline__ void load8(const uint16_t* p, uint32_t* dst) {
-  uint4 v = *reinterpret_cast<const uint4*>(p);
+  const u32x4 v = *(const GLOBAL u32x4*)p;
   dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
 }
 
 __device__ __forceinline__ void store8(uint16_t* p, const uint32_t* src) {
-  *reinterpret_cast<uint4*>(p) = make_uint4(src[0], src[1], src[2], src[3]);
+  *(GLOBAL u32x4*)p = u32x4{src[0], src[1], src[2], src[3]};
 }
 
 // Guarded variants for the last work item of a tensor: element e + j exists
@@ -37,9 +37,10 @@ __device__ __forceinline__ void load8_guard(const uint16_t* p, int64_t e, int64_
     load8(p + e, dst);
     return;
   }
+  const GLOBAL uint16_t* q = (const GLOBAL uint16_t*)p;
   for (int j = 0; j < 4; ++j) {
-    uint32_t lo = (e + 2 * j < n) ? p[e + 2 * j] : (fill & 0xFFFFu);
-    uint32_t hi = (e + 2 * j + 1 < n) ? p[e + 2 * j + 1] : (fill >> 16);
+    uint32_t lo = (e + 2 * j < n) ? q[e + 2 * j] : (fill & 0xFFFFu);
+    uint32_t hi = (e + 2 * j + 1 < n) ? q[e + 2 * j + 1] : (fill >> 16);
     dst[j] = lo | (hi << 16);
   }
 }
@@ -49,8 +50,41 @@ __device__ __forceinline__ void store8_guard(uint16_t* p, int64_t e, int64_t n, 
     store8(p + e, src);
     return;
   }
+  GLOBAL uint16_t* q = (GLOBAL uint16_t*)p;
   for (int j = 0; j < 8; ++j)
-    if (e + j < n) p[e + j] = (uint16_t)(src[j >> 1] >> (16 * (j & 1)));
+    if (e + j < n) q[e + j] = (uint16_t)(src[j >> 1] >> (16 * (j & 1)));
+}
+
+// Phase 3 of a work item: update, residual split and moment encode of one
+// lane's 16 elements. SLOW selects the library square root for the whole wave.
+template <int ALGO, bool WD, int SPLIT, bool SLOW>
+__device__ __forceinline__ void update_encode(const Regs& R, const float* m, const float* v, const StepScalars& c,
+                                              float inv_m, float inv_v, float sq_inv_v, uint32_t* oh, uint32_t* ol,
+                                              uint32_t* omc, uint32_t* ovc) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t wb[2], cm[2], cv[2];
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      const int j = 2 * w + o;
+      float g = o ? bf16_hi(R.g[w]) : bf16_lo(R.g[w]);
+      float wf = __uint_as_float(join_pair_elem<SPLIT>(R.h[w], R.l[w], o));
+      float rv = SLOW ? __builtin_sqrtf(v[j]) : sqrt_rn_fast(v[j]);
+      float d = __builtin_fmaf(rv, c.RS2, c.EPS);
+      float u;
+      if (ALGO == PS_ALGO_ADAM)
+        u = c.A * (m[j] / d);
+      else
+        u = __builtin_fmaf(c.AG, g, c.AM * m[j]) / d;
+      if (WD) u = __builtin_fmaf(c.CWD, wf, u);
+      wb[o] = __float_as_uint(wf - u);
+      cm[o] = enc_signed(m[j], inv_m);
+      cv[o] = enc_unsigned_y(v[j], inv_v, fast_sqrt(rv * sq_inv_v));
+    }
+    split_pair<SPLIT>(wb[0], wb[1], oh[w], ol[w]);
+    omc[w] = cm[0] | (cm[1] << 16);
+    ovc[w] = cv[0] | (cv[1] << 16);
+  }
 }
 
 template <int ALGO, bool WD, int SPLIT>
@@ -78,8 +112,8 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
     load8(pg + la, R.g); load8(pg + lb, R.g + 4);
     load8(pm + la, R.mc); load8(pm + lb, R.mc + 4);
     load8(pv + la, R.vc); load8(pv + lb, R.vc + 4);
-    ms_old = T.ms[blk];
-    vs_old = T.vs[blk];
+    ms_old = ((const GLOBAL float*)T.ms)[blk];
+    vs_old = ((const GLOBAL float*)T.vs)[blk];
   } else {
     load8_guard(T.hi, ea, n, 0u, R.h); load8_guard(T.hi, eb, n, 0u, R.h + 4);
     load8_guard(T.lo, ea, n, 0u, R.l); load8_guard(T.lo, eb, n, 0u, R.l + 4);
@@ -87,8 +121,8 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
     load8_guard(T.mc, ea, n, 0x80008000u, R.mc); load8_guard(T.mc, eb, n, 0x80008000u, R.mc + 4);
     load8_guard(T.vc, ea, n, 0u, R.vc); load8_guard(T.vc, eb, n, 0u, R.vc + 4);
     if (blk * kBlock < n) {
-      ms_old = T.ms[blk];
-      vs_old = T.vs[blk];
+      ms_old = ((const GLOBAL float*)T.ms)[blk];
+      vs_old = ((const GLOBAL float*)T.vs)[blk];
     }
   }
 
@@ -120,32 +154,13 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
   block_scale(row16_max(mx_v), sv, inv_v);
   const float sq_inv_v = fast_sqrt(inv_v);
 
-  // Phase 3: update, split, encode.
+  // Phase 3: update, split, encode. The wave-uniform choice of square root
+  // is taken once so the common path carries no per-element branch.
   uint32_t oh[8], ol[8], omc[8], ovc[8];
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t wb[2], cm[2], cv[2];
-#pragma unroll
-    for (int o = 0; o < 2; ++o) {
-      const int j = 2 * w + o;
-      float g = o ? bf16_hi(R.g[w]) : bf16_lo(R.g[w]);
-      float wf = __uint_as_float(join_pair_elem<SPLIT>(R.h[w], R.l[w], o));
-      float rv = slow_sqrt ? __builtin_sqrtf(v[j]) : sqrt_rn_fast(v[j]);
-      float d = __builtin_fmaf(rv, c.RS2, c.EPS);
-      float u;
-      if (ALGO == PS_ALGO_ADAM)
-        u = c.A * (m[j] / d);
-      else
-        u = __builtin_fmaf(c.AG, g, c.AM * m[j]) / d;
-      if (WD) u = __builtin_fmaf(c.CWD, wf, u);
-      wb[o] = __float_as_uint(wf - u);
-      cm[o] = enc_signed(m[j], inv_m);
-      cv[o] = enc_unsigned_y(v[j], inv_v, fast_sqrt(rv * sq_inv_v));
-    }
-    split_pair<SPLIT>(wb[0], wb[1], oh[w], ol[w]);
-    omc[w] = cm[0] | (cm[1] << 16);
-    ovc[w] = cv[0] | (cv[1] << 16);
-  }
+  if (slow_sqrt)
+    update_encode<ALGO, WD, SPLIT, true>(R, m, v, c, inv_m, inv_v, sq_inv_v, oh, ol, omc, ovc);
+  else
+    update_encode<ALGO, WD, SPLIT, false>(R, m, v, c, inv_m, inv_v, sq_inv_v, oh, ol, omc, ovc);
 
   if (full) {
     uint16_t* ph = T.hi + elem0;
@@ -163,8 +178,8 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
     store8_guard(T.vc, ea, n, ovc); store8_guard(T.vc, eb, n, ovc + 4);
   }
   if (r == 0 && blk * kBlock < n) {
-    T.ms[blk] = sm;
-    T.vs[blk] = sv;
+    ((GLOBAL float*)T.ms)[blk] = sm;
+    ((GLOBAL float*)T.vs)[blk] = sv;
   }
 }
 
@@ -200,28 +215,75 @@ ps_status launch_t(const TBL& tbl, uint32_t total_items, const StepScalars& c, h
 }
 
 // ---------------------------------------------------------------------------
-// Tensors with storage flags: fp32 moments instead of codes and/or an fp32
+// Tensors with storage flags: fp32 or f24 moments instead of codes and/or an fp32
 // parameter and gradient instead of bf16 + residual. Same lane layout and
 // element arithmetic; the flags are uniform per work item.
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ void load_f8(const float* p, int64_t e, int64_t n, float* d) {
+  const GLOBAL float* q = (const GLOBAL float*)p;
   if (e + 8 <= n) {
-    const float4 a = *reinterpret_cast<const float4*>(p + e), b = *reinterpret_cast<const float4*>(p + e + 4);
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 a = *(const GLOBAL f32x4*)(q + e), b = *(const GLOBAL f32x4*)(q + e + 4);
     d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w; d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
     return;
   }
-  for (int j = 0; j < 8; ++j) d[j] = (e + j < n) ? p[e + j] : 0.0f;
+  for (int j = 0; j < 8; ++j) d[j] = (e + j < n) ? q[e + j] : 0.0f;
 }
 
 __device__ __forceinline__ void store_f8(float* p, int64_t e, int64_t n, const float* s) {
+  GLOBAL float* q = (GLOBAL float*)p;
   if (e + 8 <= n) {
-    *reinterpret_cast<float4*>(p + e) = make_float4(s[0], s[1], s[2], s[3]);
-    *reinterpret_cast<float4*>(p + e + 4) = make_float4(s[4], s[5], s[6], s[7]);
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    *(GLOBAL f32x4*)(q + e) = f32x4{s[0], s[1], s[2], s[3]};
+    *(GLOBAL f32x4*)(q + e + 4) = f32x4{s[4], s[5], s[6], s[7]};
     return;
   }
   for (int j = 0; j < 8; ++j)
-    if (e + j < n) p[e + j] = s[j];
+    if (e + j < n) q[e + j] = s[j];
+}
+
+// Eight f24 values of elements e..e+7 (24 bytes at byte offset 3e, which is
+// 8-byte aligned since e is a multiple of 8).
+__device__ __forceinline__ void load_f24x8(const uint8_t* p, int64_t e, int64_t n, float* d) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const GLOBAL uint8_t* b8 = (const GLOBAL uint8_t*)p;
+  if (e + 8 <= n) {
+    const GLOBAL u32x2* q = (const GLOBAL u32x2*)(b8 + 3 * e);
+    const u32x2 a = q[0], b = q[1], c = q[2];
+    f24_unpack4(a.x, a.y, b.x, d);
+    f24_unpack4(b.y, c.x, c.y, d + 4);
+    return;
+  }
+  for (int j = 0; j < 8; ++j) {
+    const int64_t o = 3 * (e + j);
+    d[j] = (e + j < n) ? __uint_as_float(((uint32_t)b8[o] << 8) | ((uint32_t)b8[o + 1] << 16) | ((uint32_t)b8[o + 2] << 24))
+                       : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void store_f24x8(uint8_t* p, int64_t e, int64_t n, const float* s) {
+  uint32_t t[8];
+  for (int j = 0; j < 8; ++j) t[j] = f24_round(s[j]);
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  GLOBAL uint8_t* b8 = (GLOBAL uint8_t*)p;
+  if (e + 8 <= n) {
+    uint32_t w[6];
+    f24_pack4(t, w[0], w[1], w[2]);
+    f24_pack4(t + 4, w[3], w[4], w[5]);
+    GLOBAL u32x2* q = (GLOBAL u32x2*)(b8 + 3 * e);
+    q[0] = u32x2{w[0], w[1]};
+    q[1] = u32x2{w[2], w[3]};
+    q[2] = u32x2{w[4], w[5]};
+    return;
+  }
+  for (int j = 0; j < 8; ++j)
+    if (e + j < n) {
+      const int64_t o = 3 * (e + j);
+      b8[o] = (uint8_t)(t[j] >> 8);
+      b8[o + 1] = (uint8_t)(t[j] >> 16);
+      b8[o + 2] = (uint8_t)(t[j] >> 24);
+    }
 }
 
 template <int ALGO, bool WD, int SPLIT>
@@ -231,13 +293,15 @@ __device__ __forceinline__ void process_item_ex(const DevTensorEx& T, int64_t el
   const int64_t blk = (elem0 >> 8) + b;
   const bool fpm = (T.flags & PS_TENSOR_FP32_MOMENTS) != 0;   // uniform per item
   const bool fpp = (T.flags & PS_TENSOR_FP32_PARAM) != 0;
+  const bool f24 = (T.flags & PS_TENSOR_F24_MOMENTS) != 0;
+  const bool codec = !fpm && !f24;
   const int64_t run[2] = {elem0 + b * kBlock + r * 8, elem0 + b * kBlock + 128 + r * 8};
   float w[16], g[16], m[16], v[16];
   uint32_t hw[8], lw[8];
   float ms_old = 0.0f, vs_old = 0.0f;
-  if (!fpm && blk * kBlock < n) {
-    ms_old = T.ms[blk];
-    vs_old = T.vs[blk];
+  if (codec && blk * kBlock < n) {
+    ms_old = ((const GLOBAL float*)T.ms)[blk];
+    vs_old = ((const GLOBAL float*)T.vs)[blk];
   }
   for (int h = 0; h < 2; ++h) {
     if (fpp) {
@@ -256,6 +320,9 @@ __device__ __forceinline__ void process_item_ex(const DevTensorEx& T, int64_t el
     if (fpm) {
       load_f8((const float*)T.m, run[h], n, m + 8 * h);
       load_f8((const float*)T.v, run[h], n, v + 8 * h);
+    } else if (f24) {
+      load_f24x8((const uint8_t*)T.m, run[h], n, m + 8 * h);
+      load_f24x8((const uint8_t*)T.v, run[h], n, v + 8 * h);
     } else {
       uint32_t mw[4], vw[4];
       load8_guard((const uint16_t*)T.m, run[h], n, 0x80008000u, mw);
@@ -277,7 +344,7 @@ __device__ __forceinline__ void process_item_ex(const DevTensorEx& T, int64_t el
     mx_v = __builtin_fmaxf(mx_v, v1);
   }
   float sm = 0.0f, inv_m = 0.0f, sv = 0.0f, inv_v = 0.0f;
-  if (!fpm) {
+  if (codec) {
     block_scale(row16_max(mx_m), sm, inv_m);
     block_scale(row16_max(mx_v), sv, inv_v);
   }
@@ -305,6 +372,9 @@ __device__ __forceinline__ void process_item_ex(const DevTensorEx& T, int64_t el
     if (fpm) {
       store_f8((float*)T.m, run[h], n, m + 8 * h);
       store_f8((float*)T.v, run[h], n, v + 8 * h);
+    } else if (f24) {
+      store_f24x8((uint8_t*)T.m, run[h], n, m + 8 * h);
+      store_f24x8((uint8_t*)T.v, run[h], n, v + 8 * h);
     } else {
       uint32_t om[4], ov[4];
       for (int q = 0; q < 4; ++q) {
@@ -316,9 +386,9 @@ __device__ __forceinline__ void process_item_ex(const DevTensorEx& T, int64_t el
       store8_guard((uint16_t*)T.v, run[h], n, ov);
     }
   }
-  if (!fpm && r == 0 && blk * kBlock < n) {
-    T.ms[blk] = sm;
-    T.vs[blk] = sv;
+  if (codec && r == 0 && blk * kBlock < n) {
+    ((GLOBAL float*)T.ms)[blk] = sm;
+    ((GLOBAL float*)T.vs)[blk] = sv;
   }
 }
 

@@ -85,19 +85,22 @@ ps_status build_active(const ps_tensor* t, int32_t n, std::vector<DevTensor>& re
   if (n < 0) return fail(PS_ERR_INVALID_ARG, "n_tensors < 0");
   if (n > 0 && !t) return fail(PS_ERR_INVALID_ARG, "tensors is NULL");
   uint64_t items = 0, xitems = 0;
-  const uint32_t known = PS_TENSOR_FP32_MOMENTS | PS_TENSOR_FP32_PARAM;
+  const uint32_t known = PS_TENSOR_FP32_MOMENTS | PS_TENSOR_FP32_PARAM | PS_TENSOR_F24_MOMENTS;
   for (int32_t i = 0; i < n; ++i) {
     const ps_tensor& x = t[i];
     if (x.numel < 0 || x.numel > kMaxNumel) return fail(PS_ERR_SHAPE, "tensor %d: numel %lld out of range", i, (long long)x.numel);
     if ((x.flags & ~known) || x.reserved) return fail(PS_ERR_INVALID_ARG, "tensor %d: unknown flags", i);
+    if ((x.flags & PS_TENSOR_FP32_MOMENTS) && (x.flags & PS_TENSOR_F24_MOMENTS))
+      return fail(PS_ERR_INVALID_ARG, "tensor %d: FP32_MOMENTS and F24_MOMENTS are exclusive", i);
     if (x.numel == 0 || x.grad == nullptr) continue;
-    const bool fpm = x.flags & PS_TENSOR_FP32_MOMENTS, fpp = x.flags & PS_TENSOR_FP32_PARAM;
+    const bool no_scales = x.flags & (PS_TENSOR_FP32_MOMENTS | PS_TENSOR_F24_MOMENTS);
+    const bool fpp = x.flags & PS_TENSOR_FP32_PARAM;
     ps_status s;
     if ((s = check_array(x.w_hi, "w_hi", i, 16)) || (s = check_array(x.grad, "grad", i, 16)) ||
         (s = check_array(x.m_code, "m_code", i, 16)) || (s = check_array(x.v_code, "v_code", i, 16)))
       return s;
     if (!fpp && (s = check_array(x.w_lo, "w_lo", i, 16))) return s;
-    if (!fpm && ((s = check_array(x.m_scale, "m_scale", i, 4)) || (s = check_array(x.v_scale, "v_scale", i, 4))))
+    if (!no_scales && ((s = check_array(x.m_scale, "m_scale", i, 4)) || (s = check_array(x.v_scale, "v_scale", i, 4))))
       return s;
     const uint64_t nit = (uint64_t)((x.numel + kItemElems - 1) / kItemElems);
     if (x.flags) {

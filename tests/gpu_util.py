@@ -152,13 +152,36 @@ def _host_block_state(tid, b, numel, seed):
     return oracle.TensorState(hi, lo, mc, ms, vc, vs)
 
 
+def _check_f24_block(tid, b, numel, d, hp, steps, seed, outlier_p):
+    sl = block_slice(b, numel)
+    L = sl.stop - sl.start
+    hi = synth.host_bf16_normal(L, seed, STREAM_HI, tid, 0, SIGMA_W, start=sl.start)
+    lo = synth.host_u16_uniform(L, seed, STREAM_LO, tid, 0, start=sl.start)
+    m, v = np.zeros(3 * L, np.uint8), np.zeros(3 * L, np.uint8)
+    for t in range(1, steps + 1):
+        g = synth.host_bf16_normal(L, seed, STREAM_GRAD, tid, t, SIGMA_G, outlier_p, 100.0, start=sl.start)
+        oracle.opt_step_flags(hi, lo, g, m, None, v, None, oracle.F24_MOMENTS, ohp(hp), t)
+    b3 = slice(3 * sl.start, 3 * sl.stop)
+    got = {"hi": u16(d.w_hi[sl]), "lo": u16(d.w_lo[sl]), "m": d.m_code[b3].cpu().numpy(),
+           "v": d.v_code[b3].cpu().numpy()}
+    want = {"hi": hi, "lo": lo, "m": m, "v": v}
+    for name in got:
+        assert np.array_equal(got[name], want[name]), (tid, int(b), name)
+
+
 def check_sampled_blocks(shapes, devs, hp, steps, seed, per_tensor, outlier_p=0.0):
     """Every 256-block evolves from its own inputs only, so the oracle runs
-    sampled blocks alone, free-running from the synthetic initial state."""
+    sampled blocks alone, free-running from the synthetic initial state.
+    Tensors with f24 moments are checked through the oracle's flagged step."""
     rng = np.random.default_rng(seed + 1)
     total = 0
     for tid, (shape, d) in enumerate(zip(shapes, devs)):
         blocks = sample_blocks(shape.numel, per_tensor, rng)
+        if d.flags & oracle.F24_MOMENTS:
+            for b in blocks:
+                _check_f24_block(tid, b, shape.numel, d, hp, steps, seed, outlier_p)
+            total += len(blocks)
+            continue
         for b in blocks:
             sl = block_slice(b, shape.numel)
             st = _host_block_state(tid, b, shape.numel, seed)

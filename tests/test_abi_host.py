@@ -68,6 +68,10 @@ def test_invalid_arguments_rejected_on_host(ps):
     assert "w_lo" in ps.last_error()
     assert _call(ps, [_rec(ps, m_code=66)]) == 2
     assert _call(ps, [_rec(ps, v_scale=114)]) == 2
+    assert _call(ps, [_rec(ps, flags=8)]) == 1
+    assert _call(ps, [_rec(ps, flags=ps.TENSOR_FP32_MOMENTS | ps.TENSOR_F24_MOMENTS)]) == 1
+    assert "exclusive" in ps.last_error()
+    assert _call(ps, [_rec(ps, flags=ps.TENSOR_F24_MOMENTS, m_code=8)]) == 2
     h = ps.HParams().c()
     assert L.ps_opt_step_multi(None, 3, ctypes.byref(h), 1, None) == 1
     assert L.ps_opt_step_multi(None, 0, None, 1, None) == 1

@@ -254,16 +254,27 @@ def test_flux_double_block_3_steps_sampled():
 # per-tensor storage flags (fp32 moments for small tensors, fp32 final layer)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY])
-def test_storage_flags_match_oracle(split_mode):
-    """A list mixing the default format with fp32 moments (tensors of <= 4096
-    elements on the pages) and fp32 parameters (the final layer), ragged
-    sizes, both the kernel-argument and the device-table paths, 3 NAdamW
-    steps; bit-exact against the oracle."""
-    sizes = [64, 128, 3072, 4096, 1000, 300001, 257, 18432, 3000, 5, 6144 * 8, 2048, 100, 4096, 77, 65536, 999]
-    flag_of = [ps.TENSOR_FP32_MOMENTS if n <= 4096 else 0 for n in sizes]
-    flag_of[5] = ps.TENSOR_FP32_PARAM
+def _flag_mix(sizes, large):
+    """fp32 moments for tensors of <= 4096 elements; `large` (0: the codec, or
+    f24) for the rest; fp32 parameters on two of them."""
+    flag_of = [ps.TENSOR_FP32_MOMENTS if n <= 4096 else large for n in sizes]
+    flag_of[5] = ps.TENSOR_FP32_PARAM | large
     flag_of[10] = ps.TENSOR_FP32_PARAM | ps.TENSOR_FP32_MOMENTS
+    if large:
+        flag_of[9] = flag_of[16] = large          # ragged f24 tensors of 5 and 999 elements
+    return flag_of
+
+
+@pytest.mark.parametrize("split_mode,large", [(ps.SPLIT_TRUNC, 0), (ps.SPLIT_NEAREST_AWAY, 0),
+                                              (ps.SPLIT_TRUNC, ps.TENSOR_F24_MOMENTS),
+                                              (ps.SPLIT_NEAREST_AWAY, ps.TENSOR_F24_MOMENTS)])
+def test_storage_flags_match_oracle(split_mode, large):
+    """A list mixing the default format with fp32 moments (tensors of <= 4096
+    elements on the pages), f24 moments and fp32 parameters (the final
+    layer), ragged sizes, both the kernel-argument and the device-table
+    paths, 3 NAdamW steps; bit-exact against the oracle."""
+    sizes = [64, 128, 3072, 4096, 1000, 300001, 257, 18432, 3000, 5, 6144 * 8, 2048, 100, 4096, 77, 65536, 999]
+    flag_of = _flag_mix(sizes, large)
     hp = ps.HParams(algo=ps.ALGO_NADAM, weight_decay=0.01, lr=1e-4, split_mode=split_mode)
     for count in (len(sizes), 9):
         devs, hosts = [], []
@@ -278,6 +289,8 @@ def test_storage_flags_match_oracle(split_mode):
                 h["w"], h["lo"] = hi.copy(), lo.copy()
             if fl & ps.TENSOR_FP32_MOMENTS:
                 h["m"], h["v"], h["ms"], h["vs"] = np.zeros(n, np.float32), np.zeros(n, np.float32), None, None
+            elif fl & ps.TENSOR_F24_MOMENTS:
+                h["m"], h["v"], h["ms"], h["vs"] = np.zeros(3 * n, np.uint8), np.zeros(3 * n, np.uint8), None, None
             else:
                 h["m"], h["ms"], h["v"], h["vs"] = oracle.zero_moments(n)
             hosts.append(h)
@@ -315,8 +328,9 @@ def test_storage_flags_match_oracle(split_mode):
             for k in ("m", "v"):
                 got = getattr(d, k + "_code").cpu().numpy()
                 want = h[k]
-                assert np.array_equal(got.view(np.uint32 if want.dtype == np.float32 else np.uint16),
-                                      want.view(np.uint32 if want.dtype == np.float32 else np.uint16)), (count, i, k)
-            if not fl & ps.TENSOR_FP32_MOMENTS:
+                as_bits = {np.dtype(np.float32): np.uint32, np.dtype(np.uint16): np.uint16,
+                           np.dtype(np.uint8): np.uint8}[want.dtype]
+                assert np.array_equal(got.view(as_bits), want.view(as_bits)), (count, i, k)
+            if not fl & (ps.TENSOR_FP32_MOMENTS | ps.TENSOR_F24_MOMENTS):
                 assert np.array_equal(f32(d.m_scale).view(np.uint32), h["ms"].view(np.uint32)), (count, i, "ms")
                 assert np.array_equal(f32(d.v_scale).view(np.uint32), h["vs"].view(np.uint32)), (count, i, "vs")
