@@ -153,6 +153,15 @@ __device__ __forceinline__ float row16_max(float x) {
   return x;
 }
 
+// Max over the 32 lanes of a row pair (rows 0-1 and rows 2-3 of the wave):
+// the row butterfly, then one exchange of the two rows (v_permlane16_swap
+// hands each row the other row's values).
+__device__ __forceinline__ float row32_max(float x) {
+  x = row16_max(x);
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
 // Block scale from the block max: blocks below the smallest normal are
 // flushed to 0 so 1/scale never overflows; inv is 0 for them.
 __device__ __forceinline__ void block_scale(float mx, float& s, float& inv) {

@@ -1,12 +1,20 @@
 // k_adam.hip - fused multi-tensor (N)AdamW step on residual-split bf16
 // weights with uint16-coded moments [NADAM; KAHAN].
 //
-// Mapping (gfx950, wave64): the tensor list is cut into work items of 1024
-// elements (4 moment blocks) that never cross a tensor boundary. A work item
-// belongs to one wave; a 256-element block belongs to 16 lanes (one DPP row),
-// and each lane holds 16 elements: two runs of 8 at offsets r*8 and 128 + r*8
-// of its block, so each of the wave's 16-byte loads covers whole 128-byte
-// lines. Each work item is one 64-lane workgroup.
+// Mapping (gfx950, wave64): the tensor list is cut into work items of 512
+// elements (2 moment blocks) that never cross a tensor boundary; one work
+// item is one 64-lane workgroup. A 256-element block belongs to 32 lanes (a
+// pair of DPP rows) and each lane holds one run of 8 consecutive elements at
+// offset r*8 of its block, so the block's 32 lanes read and write 512
+// contiguous bytes of every 16-bit stream with 16-byte accesses. The block
+// maximum is a butterfly within each row plus one row-pair exchange.
+//
+// Order of memory traffic within a wave: gradient and moment codes first
+// (they decide the block scales), the weight words only once the scales are
+// known, just before the update needs them. Spreading each wave's traffic
+// this way, with 8 elements per lane (77 VGPRs, 6 waves per SIMD), measured
+// markedly faster than loading every stream up front with 16 elements per
+// lane.
 //
 // Per element the kernel reads hi, lo, grad, m_code, v_code (10 bytes) and
 // writes hi, lo, m_code, v_code (8 bytes); per block it reads and writes the
@@ -16,10 +24,6 @@
 
 namespace ps {
 namespace {
-
-struct Regs {       // one lane's 16 elements, 16-bit streams as packed pairs
-  uint32_t h[8], l[8], g[8], mc[8], vc[8];
-};
 
 __device__ __forceinline__ void load8(const uint16_t* p, uint32_t* dst) {
   const u32x4 v = *(const GLOBAL u32x4*)p;
@@ -55,22 +59,32 @@ __device__ __forceinline__ void store8_guard(uint16_t* p, int64_t e, int64_t n, 
     if (e + j < n) q[e + j] = (uint16_t)(src[j >> 1] >> (16 * (j & 1)));
 }
 
-// Phase 3 of a work item: update, residual split and moment encode of one
-// lane's 16 elements. SLOW selects the library square root for the whole wave.
+// Update, residual split and moment encode of one lane's 8 elements, then the
+// stores. The weight words are loaded here, after the block scales are
+// known. SLOW selects the library square root for the whole wave.
 template <int ALGO, bool WD, int SPLIT, bool SLOW>
-__device__ __forceinline__ void update_encode(const Regs& R, const float* m, const float* v, const StepScalars& c,
-                                              float inv_m, float inv_v, float sq_inv_v, uint32_t* oh, uint32_t* ol,
-                                              uint32_t* omc, uint32_t* ovc) {
+__device__ __forceinline__ void update_store(const DevTensor& T, int64_t e, int64_t n, bool full, const uint32_t* gw,
+                                             const float* m, const float* v, const StepScalars& c, float inv_m,
+                                             float inv_v, float sq_inv_v) {
+  uint32_t hw[4], lw[4];
+  if (full) {
+    load8(T.hi + e, hw);
+    load8(T.lo + e, lw);
+  } else {
+    load8_guard(T.hi, e, n, 0u, hw);
+    load8_guard(T.lo, e, n, 0u, lw);
+  }
+  uint32_t oh[4], ol[4], omc[4], ovc[4];
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
+  for (int w = 0; w < 4; ++w) {
     uint32_t wb[2], cm[2], cv[2];
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
       const int j = 2 * w + o;
-      float g = o ? bf16_hi(R.g[w]) : bf16_lo(R.g[w]);
-      float wf = __uint_as_float(join_pair_elem<SPLIT>(R.h[w], R.l[w], o));
-      float rv = SLOW ? __builtin_sqrtf(v[j]) : sqrt_rn_fast(v[j]);
-      float d = __builtin_fmaf(rv, c.RS2, c.EPS);
+      const float g = o ? bf16_hi(gw[w]) : bf16_lo(gw[w]);
+      const float wf = __uint_as_float(join_pair_elem<SPLIT>(hw[w], lw[w], o));
+      const float rv = SLOW ? __builtin_sqrtf(v[j]) : sqrt_rn_fast(v[j]);
+      const float d = __builtin_fmaf(rv, c.RS2, c.EPS);
       float u;
       if (ALGO == PS_ALGO_ADAM)
         u = c.A * (m[j] / d);
@@ -85,59 +99,58 @@ __device__ __forceinline__ void update_encode(const Regs& R, const float* m, con
     omc[w] = cm[0] | (cm[1] << 16);
     ovc[w] = cv[0] | (cv[1] << 16);
   }
+  if (full) {
+    store8(T.hi + e, oh);
+    store8(T.lo + e, ol);
+    store8(T.mc + e, omc);
+    store8(T.vc + e, ovc);
+  } else {
+    store8_guard(T.hi, e, n, oh);
+    store8_guard(T.lo, e, n, ol);
+    store8_guard(T.mc, e, n, omc);
+    store8_guard(T.vc, e, n, ovc);
+  }
 }
 
 template <int ALGO, bool WD, int SPLIT>
 __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, int lane, const StepScalars& c) {
-  const int b = lane >> 4;                 // block of the item, 0..3
-  const int r = lane & 15;                 // lane within the block's DPP row
+  const int b = lane >> 5;                 // block of the item, 0..1
+  const int r = lane & 31;                 // lane within the block's row pair
   const int64_t n = T.numel;
   const int64_t blk = (elem0 >> 8) + b;    // block index within the tensor
-  const int64_t ea = elem0 + b * kBlock + r * 8;
-  const int64_t eb = ea + 128;
-  const bool full = elem0 + kItemElems <= n;  // uniform per wave
+  const int64_t e = elem0 + b * kBlock + r * 8;
+  const bool full = elem0 + kStepItemElems <= n;  // uniform per wave
 
-  Regs R;
+  uint32_t gw[4], mw[4], vw[4];
   float ms_old = 0.0f, vs_old = 0.0f;
-  // Full items: uniform base pointers plus 32-bit lane offsets.
-  const uint32_t la = (uint32_t)(b * kBlock + r * 8), lb = la + 128;
   if (full) {
-    const uint16_t* ph = T.hi + elem0;
-    const uint16_t* pl = T.lo + elem0;
-    const uint16_t* pg = T.g + elem0;
-    const uint16_t* pm = T.mc + elem0;
-    const uint16_t* pv = T.vc + elem0;
-    load8(ph + la, R.h); load8(ph + lb, R.h + 4);
-    load8(pl + la, R.l); load8(pl + lb, R.l + 4);
-    load8(pg + la, R.g); load8(pg + lb, R.g + 4);
-    load8(pm + la, R.mc); load8(pm + lb, R.mc + 4);
-    load8(pv + la, R.vc); load8(pv + lb, R.vc + 4);
+    load8(T.g + e, gw);
+    load8(T.mc + e, mw);
+    load8(T.vc + e, vw);
     ms_old = ((const GLOBAL float*)T.ms)[blk];
     vs_old = ((const GLOBAL float*)T.vs)[blk];
   } else {
-    load8_guard(T.hi, ea, n, 0u, R.h); load8_guard(T.hi, eb, n, 0u, R.h + 4);
-    load8_guard(T.lo, ea, n, 0u, R.l); load8_guard(T.lo, eb, n, 0u, R.l + 4);
-    load8_guard(T.g, ea, n, 0u, R.g); load8_guard(T.g, eb, n, 0u, R.g + 4);
-    load8_guard(T.mc, ea, n, 0x80008000u, R.mc); load8_guard(T.mc, eb, n, 0x80008000u, R.mc + 4);
-    load8_guard(T.vc, ea, n, 0u, R.vc); load8_guard(T.vc, eb, n, 0u, R.vc + 4);
+    load8_guard(T.g, e, n, 0u, gw);
+    load8_guard(T.mc, e, n, 0x80008000u, mw);
+    load8_guard(T.vc, e, n, 0u, vw);
     if (blk * kBlock < n) {
       ms_old = ((const GLOBAL float*)T.ms)[blk];
       vs_old = ((const GLOBAL float*)T.vs)[blk];
     }
   }
 
-  // Phase 1: decode, EMA, block maxima. Missing tail elements have g = 0 and
+  // Decode, EMA, block maxima. Missing tail elements have g = 0 and
   // zero-coded moments, so m = v = 0 and they never raise a maximum.
-  float m[16], v[16];
+  float m[8], v[8];
   float mx_m = 0.0f, mx_v = 0.0f;
   uint32_t tiny = 0xFFFFFFFFu;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < 8; ++j) {
     const int w = j >> 1;
     const bool odd = j & 1;
-    float g = odd ? bf16_hi(R.g[w]) : bf16_lo(R.g[w]);
-    float m0 = dec_signed(odd ? code_hi_f(R.mc[w]) : code_lo_f(R.mc[w]), ms_old);
-    float v0 = dec_unsigned(odd ? code_hi_f(R.vc[w]) : code_lo_f(R.vc[w]), vs_old);
+    const float g = odd ? bf16_hi(gw[w]) : bf16_lo(gw[w]);
+    const float m0 = dec_signed(odd ? code_hi_f(mw[w]) : code_lo_f(mw[w]), ms_old);
+    const float v0 = dec_unsigned(odd ? code_hi_f(vw[w]) : code_lo_f(vw[w]), vs_old);
     m[j] = __builtin_fmaf(c.B1, m0, c.C1 * g);
     v[j] = __builtin_fmaf(c.B2, v0, c.C2 * (g * g));
     mx_m = __builtin_fmaxf(mx_m, __builtin_fabsf(m[j]));
@@ -148,35 +161,16 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
   // could underflow there, so the whole wave takes the library sequence.
   const bool slow_sqrt = __builtin_amdgcn_ballot_w64(tiny < 0x0F7FFFFFu) != 0;
 
-  // Phase 2: block scales (row-wide max over the 16 lanes).
+  // Block scales (32-lane maximum).
   float sm, inv_m, sv, inv_v;
-  block_scale(row16_max(mx_m), sm, inv_m);
-  block_scale(row16_max(mx_v), sv, inv_v);
+  block_scale(row32_max(mx_m), sm, inv_m);
+  block_scale(row32_max(mx_v), sv, inv_v);
   const float sq_inv_v = fast_sqrt(inv_v);
 
-  // Phase 3: update, split, encode. The wave-uniform choice of square root
-  // is taken once so the common path carries no per-element branch.
-  uint32_t oh[8], ol[8], omc[8], ovc[8];
   if (slow_sqrt)
-    update_encode<ALGO, WD, SPLIT, true>(R, m, v, c, inv_m, inv_v, sq_inv_v, oh, ol, omc, ovc);
+    update_store<ALGO, WD, SPLIT, true>(T, e, n, full, gw, m, v, c, inv_m, inv_v, sq_inv_v);
   else
-    update_encode<ALGO, WD, SPLIT, false>(R, m, v, c, inv_m, inv_v, sq_inv_v, oh, ol, omc, ovc);
-
-  if (full) {
-    uint16_t* ph = T.hi + elem0;
-    uint16_t* pl = T.lo + elem0;
-    uint16_t* pm = T.mc + elem0;
-    uint16_t* pv = T.vc + elem0;
-    store8(ph + la, oh); store8(ph + lb, oh + 4);
-    store8(pl + la, ol); store8(pl + lb, ol + 4);
-    store8(pm + la, omc); store8(pm + lb, omc + 4);
-    store8(pv + la, ovc); store8(pv + lb, ovc + 4);
-  } else {
-    store8_guard(T.hi, ea, n, oh); store8_guard(T.hi, eb, n, oh + 4);
-    store8_guard(T.lo, ea, n, ol); store8_guard(T.lo, eb, n, ol + 4);
-    store8_guard(T.mc, ea, n, omc); store8_guard(T.mc, eb, n, omc + 4);
-    store8_guard(T.vc, ea, n, ovc); store8_guard(T.vc, eb, n, ovc + 4);
-  }
+    update_store<ALGO, WD, SPLIT, false>(T, e, n, full, gw, m, v, c, inv_m, inv_v, sq_inv_v);
   if (r == 0 && blk * kBlock < n) {
     ((GLOBAL float*)T.ms)[blk] = sm;
     ((GLOBAL float*)T.vs)[blk] = sv;
@@ -205,7 +199,7 @@ __global__ __launch_bounds__(64) void k_adam_step(TBL tbl, StepScalars c) {
       lo = mid + 1;
   }
   const uint32_t begin = lo ? item_end(tbl, lo - 1) : 0u;
-  process_item<ALGO, WD, SPLIT>(rec(tbl, lo), (int64_t)(item - begin) * kItemElems, (int)threadIdx.x, c);
+  process_item<ALGO, WD, SPLIT>(rec(tbl, lo), (int64_t)(item - begin) * kStepItemElems, (int)threadIdx.x, c);
 }
 
 template <class TBL, int ALGO, bool WD, int SPLIT>
@@ -215,8 +209,8 @@ ps_status launch_t(const TBL& tbl, uint32_t total_items, const StepScalars& c, h
 }
 
 // ---------------------------------------------------------------------------
-// Tensors with storage flags: fp32 or f24 moments instead of codes and/or an fp32
-// parameter and gradient instead of bf16 + residual. Same lane layout and
+// Tensors with storage flags: fp32 or f24 moments instead of codes and/or an
+// fp32 parameter and gradient instead of bf16 + residual. Same lane layout and
 // element arithmetic; the flags are uniform per work item.
 // ---------------------------------------------------------------------------
 
@@ -288,54 +282,51 @@ __device__ __forceinline__ void store_f24x8(uint8_t* p, int64_t e, int64_t n, co
 
 template <int ALGO, bool WD, int SPLIT>
 __device__ __forceinline__ void process_item_ex(const DevTensorEx& T, int64_t elem0, int lane, const StepScalars& c) {
-  const int b = lane >> 4, r = lane & 15;
+  const int b = lane >> 5, r = lane & 31;
   const int64_t n = T.numel;
   const int64_t blk = (elem0 >> 8) + b;
+  const int64_t e = elem0 + b * kBlock + r * 8;
   const bool fpm = (T.flags & PS_TENSOR_FP32_MOMENTS) != 0;   // uniform per item
   const bool fpp = (T.flags & PS_TENSOR_FP32_PARAM) != 0;
   const bool f24 = (T.flags & PS_TENSOR_F24_MOMENTS) != 0;
   const bool codec = !fpm && !f24;
-  const int64_t run[2] = {elem0 + b * kBlock + r * 8, elem0 + b * kBlock + 128 + r * 8};
-  float w[16], g[16], m[16], v[16];
-  uint32_t hw[8], lw[8];
+  float w[8], g[8], m[8], v[8];
   float ms_old = 0.0f, vs_old = 0.0f;
   if (codec && blk * kBlock < n) {
     ms_old = ((const GLOBAL float*)T.ms)[blk];
     vs_old = ((const GLOBAL float*)T.vs)[blk];
   }
-  for (int h = 0; h < 2; ++h) {
-    if (fpp) {
-      load_f8((const float*)T.w, run[h], n, w + 8 * h);
-      load_f8((const float*)T.g, run[h], n, g + 8 * h);
-    } else {
-      uint32_t gw[4];
-      load8_guard((const uint16_t*)T.w, run[h], n, 0u, hw + 4 * h);
-      load8_guard(T.lo, run[h], n, 0u, lw + 4 * h);
-      load8_guard((const uint16_t*)T.g, run[h], n, 0u, gw);
-      for (int j = 0; j < 8; ++j) {
-        w[8 * h + j] = __uint_as_float(join_pair_elem<SPLIT>(hw[4 * h + (j >> 1)], lw[4 * h + (j >> 1)], j & 1));
-        g[8 * h + j] = (j & 1) ? bf16_hi(gw[j >> 1]) : bf16_lo(gw[j >> 1]);
-      }
+  if (fpp) {
+    load_f8((const float*)T.w, e, n, w);
+    load_f8((const float*)T.g, e, n, g);
+  } else {
+    uint32_t hw[4], lw[4], gw[4];
+    load8_guard((const uint16_t*)T.w, e, n, 0u, hw);
+    load8_guard(T.lo, e, n, 0u, lw);
+    load8_guard((const uint16_t*)T.g, e, n, 0u, gw);
+    for (int j = 0; j < 8; ++j) {
+      w[j] = __uint_as_float(join_pair_elem<SPLIT>(hw[j >> 1], lw[j >> 1], j & 1));
+      g[j] = (j & 1) ? bf16_hi(gw[j >> 1]) : bf16_lo(gw[j >> 1]);
     }
-    if (fpm) {
-      load_f8((const float*)T.m, run[h], n, m + 8 * h);
-      load_f8((const float*)T.v, run[h], n, v + 8 * h);
-    } else if (f24) {
-      load_f24x8((const uint8_t*)T.m, run[h], n, m + 8 * h);
-      load_f24x8((const uint8_t*)T.v, run[h], n, v + 8 * h);
-    } else {
-      uint32_t mw[4], vw[4];
-      load8_guard((const uint16_t*)T.m, run[h], n, 0x80008000u, mw);
-      load8_guard((const uint16_t*)T.v, run[h], n, 0u, vw);
-      for (int j = 0; j < 8; ++j) {
-        m[8 * h + j] = dec_signed((j & 1) ? code_hi_f(mw[j >> 1]) : code_lo_f(mw[j >> 1]), ms_old);
-        v[8 * h + j] = dec_unsigned((j & 1) ? code_hi_f(vw[j >> 1]) : code_lo_f(vw[j >> 1]), vs_old);
-      }
+  }
+  if (fpm) {
+    load_f8((const float*)T.m, e, n, m);
+    load_f8((const float*)T.v, e, n, v);
+  } else if (f24) {
+    load_f24x8((const uint8_t*)T.m, e, n, m);
+    load_f24x8((const uint8_t*)T.v, e, n, v);
+  } else {
+    uint32_t mw[4], vw[4];
+    load8_guard((const uint16_t*)T.m, e, n, 0x80008000u, mw);
+    load8_guard((const uint16_t*)T.v, e, n, 0u, vw);
+    for (int j = 0; j < 8; ++j) {
+      m[j] = dec_signed((j & 1) ? code_hi_f(mw[j >> 1]) : code_lo_f(mw[j >> 1]), ms_old);
+      v[j] = dec_unsigned((j & 1) ? code_hi_f(vw[j >> 1]) : code_lo_f(vw[j >> 1]), vs_old);
     }
   }
   float mx_m = 0.0f, mx_v = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
+  for (int k = 0; k < 8; ++k) {
     const float m1 = __builtin_fmaf(c.B1, m[k], c.C1 * g[k]);
     const float v1 = __builtin_fmaf(c.B2, v[k], c.C2 * (g[k] * g[k]));
     m[k] = m1;
@@ -345,11 +336,11 @@ __device__ __forceinline__ void process_item_ex(const DevTensorEx& T, int64_t el
   }
   float sm = 0.0f, inv_m = 0.0f, sv = 0.0f, inv_v = 0.0f;
   if (codec) {
-    block_scale(row16_max(mx_m), sm, inv_m);
-    block_scale(row16_max(mx_v), sv, inv_v);
+    block_scale(row32_max(mx_m), sm, inv_m);
+    block_scale(row32_max(mx_v), sv, inv_v);
   }
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
+  for (int k = 0; k < 8; ++k) {
     const float d = __builtin_fmaf(__builtin_sqrtf(v[k]), c.RS2, c.EPS);
     float u;
     if (ALGO == PS_ALGO_ADAM)
@@ -359,32 +350,29 @@ __device__ __forceinline__ void process_item_ex(const DevTensorEx& T, int64_t el
     if (WD) u = __builtin_fmaf(c.CWD, w[k], u);
     w[k] = w[k] - u;
   }
-  for (int h = 0; h < 2; ++h) {
-    if (fpp) {
-      store_f8((float*)T.w, run[h], n, w + 8 * h);
-    } else {
-      uint32_t oh[4], ol[4];
-      for (int q = 0; q < 4; ++q)
-        split_pair<SPLIT>(__float_as_uint(w[8 * h + 2 * q]), __float_as_uint(w[8 * h + 2 * q + 1]), oh[q], ol[q]);
-      store8_guard((uint16_t*)T.w, run[h], n, oh);
-      store8_guard(T.lo, run[h], n, ol);
+  if (fpp) {
+    store_f8((float*)T.w, e, n, w);
+  } else {
+    uint32_t oh[4], ol[4];
+    for (int q = 0; q < 4; ++q)
+      split_pair<SPLIT>(__float_as_uint(w[2 * q]), __float_as_uint(w[2 * q + 1]), oh[q], ol[q]);
+    store8_guard((uint16_t*)T.w, e, n, oh);
+    store8_guard(T.lo, e, n, ol);
+  }
+  if (fpm) {
+    store_f8((float*)T.m, e, n, m);
+    store_f8((float*)T.v, e, n, v);
+  } else if (f24) {
+    store_f24x8((uint8_t*)T.m, e, n, m);
+    store_f24x8((uint8_t*)T.v, e, n, v);
+  } else {
+    uint32_t om[4], ov[4];
+    for (int q = 0; q < 4; ++q) {
+      om[q] = enc_signed(m[2 * q], inv_m) | (enc_signed(m[2 * q + 1], inv_m) << 16);
+      ov[q] = enc_unsigned(v[2 * q], inv_v) | (enc_unsigned(v[2 * q + 1], inv_v) << 16);
     }
-    if (fpm) {
-      store_f8((float*)T.m, run[h], n, m + 8 * h);
-      store_f8((float*)T.v, run[h], n, v + 8 * h);
-    } else if (f24) {
-      store_f24x8((uint8_t*)T.m, run[h], n, m + 8 * h);
-      store_f24x8((uint8_t*)T.v, run[h], n, v + 8 * h);
-    } else {
-      uint32_t om[4], ov[4];
-      for (int q = 0; q < 4; ++q) {
-        const int k = 8 * h + 2 * q;
-        om[q] = enc_signed(m[k], inv_m) | (enc_signed(m[k + 1], inv_m) << 16);
-        ov[q] = enc_unsigned(v[k], inv_v) | (enc_unsigned(v[k + 1], inv_v) << 16);
-      }
-      store8_guard((uint16_t*)T.m, run[h], n, om);
-      store8_guard((uint16_t*)T.v, run[h], n, ov);
-    }
+    store8_guard((uint16_t*)T.m, e, n, om);
+    store8_guard((uint16_t*)T.v, e, n, ov);
   }
   if (codec && r == 0 && blk * kBlock < n) {
     ((GLOBAL float*)T.ms)[blk] = sm;
@@ -404,7 +392,7 @@ __global__ __launch_bounds__(64) void k_adam_step_ex(TableExPtr tbl, StepScalars
       lo = mid + 1;
   }
   const uint32_t begin = lo ? tbl.item_end[lo - 1] : 0u;
-  process_item_ex<ALGO, WD, SPLIT>(tbl.recs[lo], (int64_t)(item - begin) * kItemElems, (int)threadIdx.x, c);
+  process_item_ex<ALGO, WD, SPLIT>(tbl.recs[lo], (int64_t)(item - begin) * kStepItemElems, (int)threadIdx.x, c);
 }
 
 template <int ALGO, bool WD, int SPLIT>

@@ -102,7 +102,7 @@ ps_status build_active(const ps_tensor* t, int32_t n, std::vector<DevTensor>& re
     if (!fpp && (s = check_array(x.w_lo, "w_lo", i, 16))) return s;
     if (!no_scales && ((s = check_array(x.m_scale, "m_scale", i, 4)) || (s = check_array(x.v_scale, "v_scale", i, 4))))
       return s;
-    const uint64_t nit = (uint64_t)((x.numel + kItemElems - 1) / kItemElems);
+    const uint64_t nit = (uint64_t)((x.numel + kStepItemElems - 1) / kStepItemElems);
     if (x.flags) {
       xitems += nit;
       if (xitems > 0x7FFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large (more than 2^31 - 1 work items)");

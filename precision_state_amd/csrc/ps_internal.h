@@ -10,8 +10,10 @@
 namespace ps {
 
 constexpr int kBlock = PS_BLOCK;   // elements per moment-scale block
-constexpr int kItemBlocks = 4;     // blocks per wave work item (16 lanes per block)
+constexpr int kItemBlocks = 4;     // blocks per 1024-element work item (elementwise and factored kernels)
 constexpr int kItemElems = kBlock * kItemBlocks;
+constexpr int kStepItemBlocks = 2; // blocks per (N)AdamW step work item: one wave, 32 lanes per block
+constexpr int kStepItemElems = kBlock * kStepItemBlocks;
 constexpr int kInlineMax = 16;     // tensor lists up to this size travel in kernel arguments
 
 // Device record of one tensor in a multi-tensor launch (64 bytes).
@@ -52,7 +54,7 @@ struct StepScalars {
 };
 
 // Work decomposition of a tensor list: tensor t owns the work items
-// [item_end[t-1], item_end[t]); one work item is kItemElems elements.
+// [item_end[t-1], item_end[t]); one work item is kStepItemElems elements.
 struct TablePtr {
   const DevTensor* recs;
   const uint32_t* item_end;

@@ -152,7 +152,7 @@ ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_group
       q.vs = base_vs + osc;
       o16 += up256(b16);
       osc += up256(bsc);
-      items += (uint64_t)((x.numel + kItemElems - 1) / kItemElems);
+      items += (uint64_t)((x.numel + kStepItemElems - 1) / kStepItemElems);
       if (items > 0x7FFFFFFFull) {
         destroy(p);
         return fail(PS_ERR_SHAPE, "group %d too large", g);
