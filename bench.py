@@ -315,7 +315,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default 30, offload mode 1): the GPU needs about a second of "
+                         "this load to reach steady clocks")
     ap.add_argument("--workload", default="flux_dev_12b",
                     choices=["flux_dev_12b", "flux_double_block", "single_1024x3072"])
     ap.add_argument("--seed", type=int, default=0)
@@ -337,6 +339,8 @@ def main():
                     help="after the timed steps, run 3 plain device copies of GIB GiB (counter calibration "
                          "and the practical copy bandwidth)")
     args = ap.parse_args()
+    if args.warmup is None:
+        args.warmup = 1 if args.mode == "offload" else 30
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the optimizer step has no cross-GPU "
