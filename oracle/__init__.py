@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libps_oracle.so")
 
 ALGO_ADAM, ALGO_NADAM = 0, 1
-SPLIT_TRUNC, SPLIT_NEAREST_AWAY = 0, 1
+SPLIT_TRUNC, SPLIT_NEAREST_AWAY, SPLIT_STOCHASTIC = 0, 1, 2
 SIGNED, UNSIGNED = 0, 1
 BLOCK = 256
 
@@ -24,7 +24,8 @@ _vp, _i64, _int, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_
 class _HP(ctypes.Structure):
     _fields_ = [("algo", ctypes.c_int32), ("split_mode", ctypes.c_int32), ("lr", ctypes.c_double),
                 ("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
-                ("weight_decay", ctypes.c_double), ("momentum_decay", ctypes.c_double)]
+                ("weight_decay", ctypes.c_double), ("momentum_decay", ctypes.c_double),
+                ("seed", ctypes.c_uint64), ("tensor", ctypes.c_int64)]
 
 
 class _FHP(ctypes.Structure):
@@ -47,10 +48,12 @@ class HParams:
     eps: float = 1e-8
     weight_decay: float = 0.0
     momentum_decay: float = 4e-3
+    seed: int = 0      # stochastic rounding only
+    tensor: int = 0    # stochastic rounding only: the tensor's index in the step's list
 
     def c(self):
         return _HP(self.algo, self.split_mode, self.lr, self.beta1, self.beta2, self.eps, self.weight_decay,
-                   self.momentum_decay)
+                   self.momentum_decay, self.seed, self.tensor)
 
 
 @dataclass
@@ -90,6 +93,11 @@ def lib():
             "orc_opt_step_flags": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, ctypes.c_uint32, ctypes.POINTER(_HP),
                                     _i64], None),
             "orc_f24_encode": ([_vp, _i64, _vp], None),
+            "orc_splitmix64_mix": ([ctypes.c_uint64], ctypes.c_uint64),
+            "orc_splitmix64_at": ([ctypes.c_uint64, ctypes.c_uint64], ctypes.c_uint64),
+            "orc_sr_rand16": ([ctypes.c_uint64, _i64, _i64, _i64], ctypes.c_uint16),
+            "orc_sr_bf16": ([ctypes.c_float, ctypes.c_uint16], ctypes.c_uint16),
+            "orc_sr_rand16_array": ([ctypes.c_uint64, _i64, _i64, _i64, _i64, _vp], None),
             "orc_f24_decode": ([_vp, _i64, _vp], None),
             "orc_factored_2d": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.POINTER(_FHP), _i64], None),
             "orc_factored_1d": ([_vp, _vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_FHP), _i64], None),
@@ -197,6 +205,23 @@ def opt_step(st: TensorState, g, hp: HParams, step: int):
 
 
 FP32_MOMENTS, FP32_PARAM, F24_MOMENTS = 1, 2, 4
+
+
+def splitmix64_at(state, k):
+    """Output k (0-based) of the SplitMix64 stream starting at `state`."""
+    return lib().orc_splitmix64_at(state, k)
+
+
+def sr_rand16(seed, step, tensor, e0, n):
+    """The stochastic-rounding random 16-bit values of elements e0 .. e0+n-1."""
+    out = np.empty(n, np.uint16)
+    lib().orc_sr_rand16_array(seed, step, tensor, e0, n, out.ctypes.data)
+    return out
+
+
+def sr_bf16(x, r):
+    """Stochastic rounding of the fp32 value x to bf16 bits with the random 16 bits r."""
+    return lib().orc_sr_bf16(float(np.float32(x)), int(r))
 
 
 def f24_encode(x):

@@ -48,13 +48,15 @@
 #define ORC_BLOCK 256
 
 enum { ORC_ALGO_ADAM = 0, ORC_ALGO_NADAM = 1 };
-enum { ORC_SPLIT_TRUNC = 0, ORC_SPLIT_NEAREST_AWAY = 1 };
+enum { ORC_SPLIT_TRUNC = 0, ORC_SPLIT_NEAREST_AWAY = 1, ORC_SPLIT_STOCHASTIC = 2 };
 enum { ORC_SIGNED = 0, ORC_UNSIGNED = 1 };
 
 typedef struct {
   int32_t algo;
   int32_t split_mode;
   double lr, beta1, beta2, eps, weight_decay, momentum_decay;
+  uint64_t seed;    /* stochastic rounding: the run's seed */
+  int64_t tensor;   /* stochastic rounding: the tensor's key (its index in the step's list) */
 } orc_hparams;
 
 typedef struct {
@@ -101,6 +103,60 @@ void orc_join(const uint16_t* hi, const uint16_t* lo, float* w, int64_t n, int m
 
 void orc_split(const float* w, uint16_t* hi, uint16_t* lo, int64_t n, int mode) {
   for (int64_t i = 0; i < n; ++i) orc_split1(u_of(w[i]), &hi[i], &lo[i], mode);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stochastic rounding to bf16 without a residual [KAHAN, PR #2159 body: the */
+/* default the residual replaces; NADAM opening post: "stochastic updates"] */
+/* ------------------------------------------------------------------------ */
+
+/* SplitMix64 (Steele, Lea, Flood, "Fast splittable pseudorandom number
+ * generators", OOPSLA 2014): the state advances by the golden-ratio
+ * increment and each output is the state passed through this finaliser. */
+#define ORC_GOLDEN 0x9E3779B97F4A7C15ull
+uint64_t orc_splitmix64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+/* Output number k (0-based) of the SplitMix64 stream whose state starts at s. */
+uint64_t orc_splitmix64_at(uint64_t s, uint64_t k) { return orc_splitmix64_mix(s + (k + 1) * ORC_GOLDEN); }
+
+/* The random 16 bits of element e of tensor `tensor` at update `step` (step
+ * taken modulo 2^32, tensor modulo 2^32): the stream starts at
+ * mix(seed ^ mix(step << 32 | tensor)); output e/4 covers elements 4(e/4) ..
+ * 4(e/4)+3, element e taking bits 16(e%4) .. 16(e%4)+15. */
+uint16_t orc_sr_rand16(uint64_t seed, int64_t step, int64_t tensor, int64_t e) {
+  uint64_t key = ((uint64_t)(uint32_t)step << 32) | (uint32_t)tensor;
+  uint64_t s = orc_splitmix64_mix(seed ^ orc_splitmix64_mix(key));
+  uint64_t word = orc_splitmix64_at(s, (uint64_t)e >> 2);
+  return (uint16_t)(word >> (16 * (e & 3)));
+}
+
+/* Round x to one of its two neighbouring bf16 values: away from zero with
+ * probability equal to the discarded low 16 bits / 2^16, the fractional
+ * distance to the next bf16 in magnitude. With r uniform on [0, 2^16) this is
+ * the upper half of bits(x) + r (a carry out of the low half is the round
+ * away, across binades too). */
+uint16_t orc_sr_bf16(float x, uint16_t r) { return (uint16_t)((u_of(x) + r) >> 16); }
+
+/* Master weight and split in a given mode. STOCHASTIC has no residual: the
+ * weight is the bf16 value itself and lo is neither read nor written. */
+static float join_at(const uint16_t* hi, const uint16_t* lo, int64_t e, int mode) {
+  if (mode == ORC_SPLIT_STOCHASTIC) return f_of((uint32_t)hi[e] << 16);
+  return f_of(orc_join1(hi[e], lo[e], mode));
+}
+
+static void split_at(float w, uint16_t* hi, uint16_t* lo, int64_t e, const orc_hparams* hp, int64_t step) {
+  if (hp->split_mode == ORC_SPLIT_STOCHASTIC)
+    hi[e] = orc_sr_bf16(w, orc_sr_rand16(hp->seed, step, hp->tensor, e));
+  else
+    orc_split1(u_of(w), &hi[e], &lo[e], hp->split_mode);
+}
+
+void orc_sr_rand16_array(uint64_t seed, int64_t step, int64_t tensor, int64_t e0, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_sr_rand16(seed, step, tensor, e0 + i);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -265,12 +321,12 @@ void orc_opt_step(uint16_t* hi, uint16_t* lo, const uint16_t* g, uint16_t* mc, f
     int L = (int)(n - base < ORC_BLOCK ? n - base : ORC_BLOCK);
     for (int i = 0; i < L; ++i) {
       int64_t e = base + i;
-      float w = f_of(orc_join1(hi[e], lo[e], hp->split_mode));
+      float w = join_at(hi, lo, e, hp->split_mode);
       float gf = orc_bf16_to_f32(g[e]);
       float m0 = orc_decode1(mc[e], ms[b], ORC_SIGNED);
       float v0 = orc_decode1(vc[e], vs[b], ORC_UNSIGNED);
       float w2 = step_elem(w, gf, m0, v0, &c, hp->algo, wd, &mbuf[i], &vbuf[i]);
-      orc_split1(u_of(w2), &hi[e], &lo[e], hp->split_mode);
+      split_at(w2, hi, lo, e, hp, step);
     }
     orc_encode_block(mbuf, L, ORC_SIGNED, mc + base, &ms[b]);
     orc_encode_block(vbuf, L, ORC_UNSIGNED, vc + base, &vs[b]);
@@ -326,7 +382,7 @@ void orc_opt_step_flags(void* w, uint16_t* lo, const void* g, void* m, float* ms
         wf = ((float*)w)[e];
         gf = ((const float*)g)[e];
       } else {
-        wf = f_of(orc_join1(((uint16_t*)w)[e], lo[e], hp->split_mode));
+        wf = join_at((uint16_t*)w, lo, e, hp->split_mode);
         gf = orc_bf16_to_f32(((const uint16_t*)g)[e]);
       }
       if (flags & ORC_FP32_MOMENTS) {
@@ -343,7 +399,7 @@ void orc_opt_step_flags(void* w, uint16_t* lo, const void* g, void* m, float* ms
       if (flags & ORC_FP32_PARAM)
         ((float*)w)[e] = w2;
       else
-        orc_split1(u_of(w2), &((uint16_t*)w)[e], &lo[e], hp->split_mode);
+        split_at(w2, (uint16_t*)w, lo, e, hp, step);
       if (flags & ORC_FP32_MOMENTS) {
         ((float*)m)[e] = mbuf[i];
         ((float*)v)[e] = vbuf[i];
