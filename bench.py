@@ -35,13 +35,14 @@ BYTES_PER_BLOCK = 16
 KERNEL_SOURCES = ["precision_state_amd/csrc/k_adam.hip", "precision_state_amd/csrc/dev_common.h"]
 
 
-def step_bytes(numel, flags=0):
+def step_bytes(numel, flags=0, residual=True):
     """Algorithmic HBM bytes of one step of one tensor: the weight words read
-    and written (bf16 + residual, or fp32), the gradient read, the two moments
-    read and written (uint16 codes + per-256 scales, fp32, or f24)."""
+    and written (bf16 + residual, bf16 alone under stochastic rounding, or
+    fp32), the gradient read, the two moments read and written (uint16 codes +
+    per-256 scales, fp32, or f24)."""
     import precision_state_amd as ps
     nblk = -(-numel // 256)
-    w = 8 * numel
+    w = (8 if residual or flags & ps.TENSOR_FP32_PARAM else 4) * numel
     g = (4 if flags & ps.TENSOR_FP32_PARAM else 2) * numel
     if flags & ps.TENSOR_FP32_MOMENTS:
         mv = 16 * numel
@@ -334,6 +335,9 @@ def main():
     ap.add_argument("--moments", default="codec", choices=["codec", "f24"],
                     help="nadam mode: moment storage, uint16 codes + per-256 scales (codec) or the upper three "
                          "bytes of fp32 (f24, PS_TENSOR_F24_MOMENTS)")
+    ap.add_argument("--split", default="trunc", choices=["trunc", "nearest_away", "stochastic"],
+                    help="nadam mode: residual split mode; stochastic = stochastic rounding to bf16 with no "
+                         "residual (PS_SPLIT_STOCHASTIC, 14 B/param)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="after the timed steps, run 3 plain device copies of GIB GiB (counter calibration "
@@ -367,7 +371,10 @@ def main():
     log(f"[bench] state ready in {time.perf_counter() - t0:.1f} s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
 
-    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+    split = {"trunc": ps.SPLIT_TRUNC, "nearest_away": ps.SPLIT_NEAREST_AWAY,
+             "stochastic": ps.SPLIT_STOCHASTIC}[args.split]
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                    split_mode=split, seed=args.seed)
     n_small = n_final = 0
     if args.policy:
         for i, (s, st) in enumerate(zip(shapes, states)):
@@ -433,9 +440,9 @@ def main():
         log(f"[bench] plain copy of {nbytes} bytes: best {min(times):.3f} ms = {copy_gbs:.0f} GB/s (read + write)")
         del src, dst
 
-    alg_bytes = sum(step_bytes(s.numel, st.flags) for s, st in zip(shapes, states))
+    alg_bytes = sum(step_bytes(s.numel, st.flags, split != ps.SPLIT_STOCHASTIC) for s, st in zip(shapes, states))
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
-    traffic = None if args.policy else read_traffic(args.workload, args.moments)
+    traffic = None if args.policy or args.split != "trunc" else read_traffic(args.workload, args.moments)
 
     baseline = None
     if not args.no_cpu_baseline:
@@ -461,8 +468,9 @@ def main():
         "config": {"workload": args.workload, "params": n_params, "tensors": len(shapes),
                    "algo": "nadam", "lr": 3.5e-6, "weight_decay": 0.0, "layout": args.layout,
                    "policy": {"fp32_moment_tensors": n_small, "fp32_param_tensors": n_final} if args.policy else None,
-                   "moments": args.moments,
-                   "state": "bf16 weight + u16 residual + bf16 grad + " +
+                   "moments": args.moments, "split": args.split,
+                   "state": ("bf16 weight (stochastic rounding, no residual)" if args.split == "stochastic"
+                             else "bf16 weight + u16 residual") + " + bf16 grad + " +
                             ("u16 m/v codes + fp32 per-256 scales" if args.moments == "codec" else
                              "f24 m/v (upper 3 bytes of fp32)"),
                    "kernel_ms": kernel_ms, "copy_gbs": copy_gbs},

@@ -56,7 +56,7 @@ enum {
 };
 
 enum { PS_ALGO_ADAM = 0, PS_ALGO_NADAM = 1 };
-enum { PS_SPLIT_TRUNC = 0, PS_SPLIT_NEAREST_AWAY = 1 };
+enum { PS_SPLIT_TRUNC = 0, PS_SPLIT_NEAREST_AWAY = 1, PS_SPLIT_STOCHASTIC = 2 };
 enum { PS_MOMENT_SIGNED = 0, PS_MOMENT_UNSIGNED = 1 };
 
 /* Elements per moment-scale block. */
@@ -115,9 +115,25 @@ typedef struct ps_tensor {
 } ps_tensor;
 
 /* (N)AdamW hyperparameters [NADAM]. Constraints: algo in {ADAM, NADAM};
- * split_mode in {TRUNC, NEAREST_AWAY}; lr >= 0; 0 <= beta1 < 1; 0 <= beta2 < 1;
- * eps > 0; weight_decay >= 0; momentum_decay >= 0 (NAdam's psi, 0.004 by
- * default); all finite. */
+ * split_mode in {TRUNC, NEAREST_AWAY, STOCHASTIC}; lr >= 0; 0 <= beta1 < 1;
+ * 0 <= beta2 < 1; eps > 0; weight_decay >= 0; momentum_decay >= 0 (NAdam's
+ * psi, 0.004 by default); all finite.
+ *
+ * split_mode STOCHASTIC [KAHAN, PR #2159 body: the stochastic rounding the
+ * residual replaces; NADAM opening post]: no residual. w_lo is neither read
+ * nor written (may be NULL); the master weight is the bf16 value itself, and
+ * the updated fp32 weight w' is rounded to one of its two neighbouring bf16
+ * values, away from zero with probability (low 16 bits of w') / 2^16:
+ *   hi = (bits(w') + r) >> 16
+ * with r the element's random 16 bits. They come from a SplitMix64 stream
+ * (Steele, Lea, Flood, OOPSLA 2014; mix(z) = its output finaliser, G =
+ * 0x9E3779B97F4A7C15): for the tensor at index i of the list and update
+ * `step`, the stream starts at s = mix(seed ^ mix((step mod 2^32) << 32 | i));
+ * element e takes bits 16*(e % 4) .. 16*(e % 4) + 15 of mix(s + (e/4 + 1) * G).
+ * The same (seed, step, list position) always gives the same bits.
+ * Supported by ps_opt_step_multi only; ps_split, ps_join and the offload
+ * pipeline return PS_ERR_UNSUPPORTED for it. `seed` is not read in the other
+ * modes. */
 typedef struct ps_hparams {
   int32_t algo;
   int32_t split_mode;
@@ -127,6 +143,7 @@ typedef struct ps_hparams {
   double eps;
   double weight_decay;
   double momentum_decay;
+  uint64_t seed;
 } ps_hparams;
 
 /* Factored-second-moment hyperparameters [ADAF; PRODIGY]: no first moment,

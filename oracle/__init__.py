@@ -5,6 +5,7 @@ cpu_baseline leg may import this module. All arrays are host numpy arrays;
 every function mirrors one C entry point of ps_oracle.c.
 """
 import ctypes
+import dataclasses
 import os
 from dataclasses import dataclass
 
@@ -25,7 +26,7 @@ class _HP(ctypes.Structure):
     _fields_ = [("algo", ctypes.c_int32), ("split_mode", ctypes.c_int32), ("lr", ctypes.c_double),
                 ("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
                 ("weight_decay", ctypes.c_double), ("momentum_decay", ctypes.c_double),
-                ("seed", ctypes.c_uint64), ("tensor", ctypes.c_int64)]
+                ("seed", ctypes.c_uint64), ("tensor", ctypes.c_int64), ("elem0", ctypes.c_int64)]
 
 
 class _FHP(ctypes.Structure):
@@ -50,10 +51,11 @@ class HParams:
     momentum_decay: float = 4e-3
     seed: int = 0      # stochastic rounding only
     tensor: int = 0    # stochastic rounding only: the tensor's index in the step's list
+    elem0: int = 0     # stochastic rounding only: tensor index of the arrays' first element
 
     def c(self):
         return _HP(self.algo, self.split_mode, self.lr, self.beta1, self.beta2, self.eps, self.weight_decay,
-                   self.momentum_decay, self.seed, self.tensor)
+                   self.momentum_decay, self.seed, self.tensor, self.elem0)
 
 
 @dataclass
@@ -250,8 +252,9 @@ def opt_step_flags(w, lo, g, m, ms, v, vs, flags, hp: HParams, step: int):
 
 
 def opt_step_multi(states, grads, hp: HParams, step: int):
-    for st, g in zip(states, grads):
-        opt_step(st, g, hp, step)
+    """The list step: tensor i is keyed by its index for stochastic rounding."""
+    for i, (st, g) in enumerate(zip(states, grads)):
+        opt_step(st, g, dataclasses.replace(hp, tensor=i), step)
 
 
 def factored_step(st: TensorState, g, rows: int, cols: int, hp: FHParams, step: int):

@@ -57,6 +57,7 @@ typedef struct {
   double lr, beta1, beta2, eps, weight_decay, momentum_decay;
   uint64_t seed;    /* stochastic rounding: the run's seed */
   int64_t tensor;   /* stochastic rounding: the tensor's key (its index in the step's list) */
+  int64_t elem0;    /* stochastic rounding: index within the tensor of the arrays' element 0 */
 } orc_hparams;
 
 typedef struct {
@@ -150,7 +151,7 @@ static float join_at(const uint16_t* hi, const uint16_t* lo, int64_t e, int mode
 
 static void split_at(float w, uint16_t* hi, uint16_t* lo, int64_t e, const orc_hparams* hp, int64_t step) {
   if (hp->split_mode == ORC_SPLIT_STOCHASTIC)
-    hi[e] = orc_sr_bf16(w, orc_sr_rand16(hp->seed, step, hp->tensor, e));
+    hi[e] = orc_sr_bf16(w, orc_sr_rand16(hp->seed, step, hp->tensor, hp->elem0 + e));
   else
     orc_split1(u_of(w), &hi[e], &lo[e], hp->split_mode);
 }

@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 ALGO_ADAM, ALGO_NADAM = 0, 1
-SPLIT_TRUNC, SPLIT_NEAREST_AWAY = 0, 1
+SPLIT_TRUNC, SPLIT_NEAREST_AWAY, SPLIT_STOCHASTIC = 0, 1, 2
 MOMENT_SIGNED, MOMENT_UNSIGNED = 0, 1
 TENSOR_FP32_MOMENTS, TENSOR_FP32_PARAM, TENSOR_F24_MOMENTS = 1, 2, 4
 BLOCK = 256
@@ -55,7 +55,7 @@ class CTensor(ctypes.Structure):
 class CHParams(ctypes.Structure):
     _fields_ = [("algo", ctypes.c_int32), ("split_mode", ctypes.c_int32), ("lr", ctypes.c_double),
                 ("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
-                ("weight_decay", ctypes.c_double), ("momentum_decay", ctypes.c_double)]
+                ("weight_decay", ctypes.c_double), ("momentum_decay", ctypes.c_double), ("seed", ctypes.c_uint64)]
 
 
 class CFHParams(ctypes.Structure):
@@ -133,10 +133,11 @@ class HParams:
     eps: float = 1e-8
     weight_decay: float = 0.0
     momentum_decay: float = 4e-3
+    seed: int = 0          # SPLIT_STOCHASTIC: the random stream's seed (see ps_hparams in include/ps.h)
 
     def c(self):
         return CHParams(self.algo, self.split_mode, self.lr, self.beta1, self.beta2, self.eps,
-                        self.weight_decay, self.momentum_decay)
+                        self.weight_decay, self.momentum_decay, self.seed)
 
 
 @dataclass

@@ -50,6 +50,39 @@ __device__ __forceinline__ void split_pair(uint32_t w_even, uint32_t w_odd, uint
   hi2 = perm(w_odd, w_even, kSelHiHalves);
 }
 
+// ---------------------------------------------------------------------------
+// Stochastic rounding without a residual (split mode STOCHASTIC): random 16
+// bits per element from a SplitMix64 stream (Steele, Lea, Flood, OOPSLA
+// 2014) keyed on (seed, update number, tensor index).
+// ---------------------------------------------------------------------------
+constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;
+
+__device__ __forceinline__ uint64_t splitmix64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Start of the stream of tensor `tid` at update `step`.
+__device__ __forceinline__ uint64_t sr_stream(uint64_t seed, uint32_t step, uint32_t tid) {
+  return splitmix64_mix(seed ^ splitmix64_mix(((uint64_t)step << 32) | tid));
+}
+
+// Random bits of elements e .. e+7 (e a multiple of 8): outputs e/4 and
+// e/4 + 1 of the stream, element e + j taking bits 16*(j % 4) of output
+// e/4 + j/4.
+__device__ __forceinline__ void sr_bits8(uint64_t s, int64_t e, uint64_t* w2) {
+  const uint64_t x = s + ((uint64_t)(e >> 2) + 1) * kGolden;
+  w2[0] = splitmix64_mix(x);
+  w2[1] = splitmix64_mix(x + kGolden);
+}
+
+// bf16 pair of two fp32 words rounded stochastically with the random 16-bit
+// values r0 and r1: the upper halves of bits + r.
+__device__ __forceinline__ uint32_t sr_pair(uint32_t w_even, uint32_t w_odd, uint32_t r0, uint32_t r1) {
+  return perm(w_odd + r1, w_even + r0, kSelHiHalves);
+}
+
 // bf16 pair -> two fp32 values.
 __device__ __forceinline__ float bf16_lo(uint32_t g2) { return __uint_as_float(g2 << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t g2) { return __uint_as_float(g2 & 0xFFFF0000u); }

@@ -66,14 +66,17 @@ template <int ALGO, bool WD, int SPLIT, bool SLOW>
 __device__ __forceinline__ void update_store(const DevTensor& T, int64_t e, int64_t n, bool full, const uint32_t* gw,
                                              const float* m, const float* v, const StepScalars& c, float inv_m,
                                              float inv_v, float sq_inv_v) {
-  uint32_t hw[4], lw[4];
+  constexpr bool SR = SPLIT == PS_SPLIT_STOCHASTIC;
+  uint32_t hw[4], lw[4] = {0u, 0u, 0u, 0u};
   if (full) {
     load8(T.hi + e, hw);
-    load8(T.lo + e, lw);
+    if (!SR) load8(T.lo + e, lw);
   } else {
     load8_guard(T.hi, e, n, 0u, hw);
-    load8_guard(T.lo, e, n, 0u, lw);
+    if (!SR) load8_guard(T.lo, e, n, 0u, lw);
   }
+  uint64_t rnd[2] = {0u, 0u};
+  if (SR) sr_bits8(sr_stream(c.sr_seed, c.sr_step, T.tid), e, rnd);
   uint32_t oh[4], ol[4], omc[4], ovc[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -82,7 +85,8 @@ __device__ __forceinline__ void update_store(const DevTensor& T, int64_t e, int6
     for (int o = 0; o < 2; ++o) {
       const int j = 2 * w + o;
       const float g = o ? bf16_hi(gw[w]) : bf16_lo(gw[w]);
-      const float wf = __uint_as_float(join_pair_elem<SPLIT>(hw[w], lw[w], o));
+      const float wf = SR ? (o ? bf16_hi(hw[w]) : bf16_lo(hw[w]))
+                          : __uint_as_float(join_pair_elem<SPLIT>(hw[w], lw[w], o));
       const float rv = SLOW ? __builtin_sqrtf(v[j]) : sqrt_rn_fast(v[j]);
       const float d = __builtin_fmaf(rv, c.RS2, c.EPS);
       float u;
@@ -95,18 +99,23 @@ __device__ __forceinline__ void update_store(const DevTensor& T, int64_t e, int6
       cm[o] = enc_signed(m[j], inv_m);
       cv[o] = enc_unsigned_y(v[j], inv_v, fast_sqrt(rv * sq_inv_v));
     }
-    split_pair<SPLIT>(wb[0], wb[1], oh[w], ol[w]);
+    if (SR) {
+      const uint64_t q = rnd[w >> 1] >> (32 * (w & 1));
+      oh[w] = sr_pair(wb[0], wb[1], (uint32_t)q & 0xFFFFu, (uint32_t)(q >> 16) & 0xFFFFu);
+    } else {
+      split_pair<SPLIT>(wb[0], wb[1], oh[w], ol[w]);
+    }
     omc[w] = cm[0] | (cm[1] << 16);
     ovc[w] = cv[0] | (cv[1] << 16);
   }
   if (full) {
     store8(T.hi + e, oh);
-    store8(T.lo + e, ol);
+    if (!SR) store8(T.lo + e, ol);
     store8(T.mc + e, omc);
     store8(T.vc + e, ovc);
   } else {
     store8_guard(T.hi, e, n, oh);
-    store8_guard(T.lo, e, n, ol);
+    if (!SR) store8_guard(T.lo, e, n, ol);
     store8_guard(T.mc, e, n, omc);
     store8_guard(T.vc, e, n, ovc);
   }
@@ -300,12 +309,13 @@ __device__ __forceinline__ void process_item_ex(const DevTensorEx& T, int64_t el
     load_f8((const float*)T.w, e, n, w);
     load_f8((const float*)T.g, e, n, g);
   } else {
-    uint32_t hw[4], lw[4], gw[4];
+    uint32_t hw[4], lw[4] = {0u, 0u, 0u, 0u}, gw[4];
     load8_guard((const uint16_t*)T.w, e, n, 0u, hw);
-    load8_guard(T.lo, e, n, 0u, lw);
+    if (SPLIT != PS_SPLIT_STOCHASTIC) load8_guard(T.lo, e, n, 0u, lw);
     load8_guard((const uint16_t*)T.g, e, n, 0u, gw);
     for (int j = 0; j < 8; ++j) {
-      w[j] = __uint_as_float(join_pair_elem<SPLIT>(hw[j >> 1], lw[j >> 1], j & 1));
+      w[j] = SPLIT == PS_SPLIT_STOCHASTIC ? ((j & 1) ? bf16_hi(hw[j >> 1]) : bf16_lo(hw[j >> 1]))
+                                         : __uint_as_float(join_pair_elem<SPLIT>(hw[j >> 1], lw[j >> 1], j & 1));
       g[j] = (j & 1) ? bf16_hi(gw[j >> 1]) : bf16_lo(gw[j >> 1]);
     }
   }
@@ -352,6 +362,16 @@ __device__ __forceinline__ void process_item_ex(const DevTensorEx& T, int64_t el
   }
   if (fpp) {
     store_f8((float*)T.w, e, n, w);
+  } else if (SPLIT == PS_SPLIT_STOCHASTIC) {
+    uint64_t rnd[2];
+    sr_bits8(sr_stream(c.sr_seed, c.sr_step, T.tid), e, rnd);
+    uint32_t oh[4];
+    for (int q = 0; q < 4; ++q) {
+      const uint64_t b = rnd[q >> 1] >> (32 * (q & 1));
+      oh[q] = sr_pair(__float_as_uint(w[2 * q]), __float_as_uint(w[2 * q + 1]), (uint32_t)b & 0xFFFFu,
+                      (uint32_t)(b >> 16) & 0xFFFFu);
+    }
+    store8_guard((uint16_t*)T.w, e, n, oh);
   } else {
     uint32_t oh[4], ol[4];
     for (int q = 0; q < 4; ++q)
@@ -405,17 +425,15 @@ template <class TBL>
 ps_status dispatch(const TBL& tbl, uint32_t total_items, const ps_hparams& hp, const StepScalars& c,
                    hipStream_t s) {
   const bool wd = hp.weight_decay != 0.0;
-  const bool na = hp.split_mode == PS_SPLIT_NEAREST_AWAY;
 #define PS_CASE(A, W, S) \
-  if (hp.algo == A && wd == W && na == (S == PS_SPLIT_NEAREST_AWAY)) return launch_t<TBL, A, W, S>(tbl, total_items, c, s);
-  PS_CASE(PS_ALGO_NADAM, false, PS_SPLIT_TRUNC)
-  PS_CASE(PS_ALGO_NADAM, true, PS_SPLIT_TRUNC)
-  PS_CASE(PS_ALGO_ADAM, false, PS_SPLIT_TRUNC)
-  PS_CASE(PS_ALGO_ADAM, true, PS_SPLIT_TRUNC)
-  PS_CASE(PS_ALGO_NADAM, false, PS_SPLIT_NEAREST_AWAY)
-  PS_CASE(PS_ALGO_NADAM, true, PS_SPLIT_NEAREST_AWAY)
-  PS_CASE(PS_ALGO_ADAM, false, PS_SPLIT_NEAREST_AWAY)
-  PS_CASE(PS_ALGO_ADAM, true, PS_SPLIT_NEAREST_AWAY)
+  if (hp.algo == A && wd == W && hp.split_mode == S) return launch_t<TBL, A, W, S>(tbl, total_items, c, s);
+#define PS_CASES(S) \
+  PS_CASE(PS_ALGO_NADAM, false, S) PS_CASE(PS_ALGO_NADAM, true, S) PS_CASE(PS_ALGO_ADAM, false, S) \
+  PS_CASE(PS_ALGO_ADAM, true, S)
+  PS_CASES(PS_SPLIT_TRUNC)
+  PS_CASES(PS_SPLIT_NEAREST_AWAY)
+  PS_CASES(PS_SPLIT_STOCHASTIC)
+#undef PS_CASES
 #undef PS_CASE
   return fail(PS_ERR_UNSUPPORTED, "no kernel for algo %d split_mode %d", hp.algo, hp.split_mode);
 }
@@ -435,17 +453,15 @@ ps_status launch_adam_inline(const TableInline& tbl, uint32_t total_items, const
 ps_status launch_adam_ex(const TableExPtr& tbl, uint32_t total_items, const ps_hparams& hp, const StepScalars& c,
                          hipStream_t s) {
   const bool wd = hp.weight_decay != 0.0;
-  const bool na = hp.split_mode == PS_SPLIT_NEAREST_AWAY;
 #define PS_CASE(A, W, S) \
-  if (hp.algo == A && wd == W && na == (S == PS_SPLIT_NEAREST_AWAY)) return launch_ex_t<A, W, S>(tbl, total_items, c, s);
-  PS_CASE(PS_ALGO_NADAM, false, PS_SPLIT_TRUNC)
-  PS_CASE(PS_ALGO_NADAM, true, PS_SPLIT_TRUNC)
-  PS_CASE(PS_ALGO_ADAM, false, PS_SPLIT_TRUNC)
-  PS_CASE(PS_ALGO_ADAM, true, PS_SPLIT_TRUNC)
-  PS_CASE(PS_ALGO_NADAM, false, PS_SPLIT_NEAREST_AWAY)
-  PS_CASE(PS_ALGO_NADAM, true, PS_SPLIT_NEAREST_AWAY)
-  PS_CASE(PS_ALGO_ADAM, false, PS_SPLIT_NEAREST_AWAY)
-  PS_CASE(PS_ALGO_ADAM, true, PS_SPLIT_NEAREST_AWAY)
+  if (hp.algo == A && wd == W && hp.split_mode == S) return launch_ex_t<A, W, S>(tbl, total_items, c, s);
+#define PS_CASES(S) \
+  PS_CASE(PS_ALGO_NADAM, false, S) PS_CASE(PS_ALGO_NADAM, true, S) PS_CASE(PS_ALGO_ADAM, false, S) \
+  PS_CASE(PS_ALGO_ADAM, true, S)
+  PS_CASES(PS_SPLIT_TRUNC)
+  PS_CASES(PS_SPLIT_NEAREST_AWAY)
+  PS_CASES(PS_SPLIT_STOCHASTIC)
+#undef PS_CASES
 #undef PS_CASE
   return fail(PS_ERR_UNSUPPORTED, "no kernel for algo %d split_mode %d", hp.algo, hp.split_mode);
 }

@@ -56,7 +56,8 @@ namespace {
 ps_status check_hparams(const ps_hparams* hp) {
   if (!hp) return fail(PS_ERR_INVALID_ARG, "hparams is NULL");
   if (hp->algo != PS_ALGO_ADAM && hp->algo != PS_ALGO_NADAM) return fail(PS_ERR_INVALID_ARG, "unknown algo %d", hp->algo);
-  if (hp->split_mode != PS_SPLIT_TRUNC && hp->split_mode != PS_SPLIT_NEAREST_AWAY)
+  if (hp->split_mode != PS_SPLIT_TRUNC && hp->split_mode != PS_SPLIT_NEAREST_AWAY &&
+      hp->split_mode != PS_SPLIT_STOCHASTIC)
     return fail(PS_ERR_INVALID_ARG, "unknown split_mode %d", hp->split_mode);
   if (!finite(hp->lr) || hp->lr < 0) return fail(PS_ERR_INVALID_ARG, "lr must be finite and >= 0");
   if (!finite(hp->beta1) || hp->beta1 < 0 || hp->beta1 >= 1) return fail(PS_ERR_INVALID_ARG, "beta1 must be in [0, 1)");
@@ -80,8 +81,8 @@ ps_status check_array(const void* p, const char* what, int i, uintptr_t align) {
 // Validates the records and builds the active lists (tensors with numel > 0
 // and a gradient) with their work-item prefix ends: default formats in recs,
 // tensors with storage flags in xrecs.
-ps_status build_active(const ps_tensor* t, int32_t n, std::vector<DevTensor>& recs, std::vector<uint32_t>& ends,
-                       std::vector<DevTensorEx>& xrecs, std::vector<uint32_t>& xends) {
+ps_status build_active(const ps_tensor* t, int32_t n, bool residual, std::vector<DevTensor>& recs,
+                       std::vector<uint32_t>& ends, std::vector<DevTensorEx>& xrecs, std::vector<uint32_t>& xends) {
   if (n < 0) return fail(PS_ERR_INVALID_ARG, "n_tensors < 0");
   if (n > 0 && !t) return fail(PS_ERR_INVALID_ARG, "tensors is NULL");
   uint64_t items = 0, xitems = 0;
@@ -99,19 +100,20 @@ ps_status build_active(const ps_tensor* t, int32_t n, std::vector<DevTensor>& re
     if ((s = check_array(x.w_hi, "w_hi", i, 16)) || (s = check_array(x.grad, "grad", i, 16)) ||
         (s = check_array(x.m_code, "m_code", i, 16)) || (s = check_array(x.v_code, "v_code", i, 16)))
       return s;
-    if (!fpp && (s = check_array(x.w_lo, "w_lo", i, 16))) return s;
+    if (!fpp && residual && (s = check_array(x.w_lo, "w_lo", i, 16))) return s;
     if (!no_scales && ((s = check_array(x.m_scale, "m_scale", i, 4)) || (s = check_array(x.v_scale, "v_scale", i, 4))))
       return s;
     const uint64_t nit = (uint64_t)((x.numel + kStepItemElems - 1) / kStepItemElems);
     if (x.flags) {
       xitems += nit;
       if (xitems > 0x7FFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large (more than 2^31 - 1 work items)");
-      xrecs.push_back(DevTensorEx{x.w_hi, x.w_lo, x.grad, x.m_code, x.m_scale, x.v_code, x.v_scale, x.numel, x.flags, 0});
+      xrecs.push_back(DevTensorEx{x.w_hi, x.w_lo, x.grad, x.m_code, x.m_scale, x.v_code, x.v_scale, x.numel, x.flags,
+                                  (uint32_t)i});
       xends.push_back((uint32_t)xitems);
     } else {
       items += nit;
       if (items > 0x7FFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large (more than 2^31 - 1 work items)");
-      recs.push_back(DevTensor{x.w_hi, x.w_lo, x.grad, x.m_code, x.m_scale, x.v_code, x.v_scale, x.numel});
+      recs.push_back(DevTensor{x.w_hi, x.w_lo, x.grad, x.m_code, x.m_scale, x.v_code, x.v_scale, x.numel, (uint32_t)i, 0});
       ends.push_back((uint32_t)items);
     }
   }
@@ -248,7 +250,8 @@ ps_status ps_opt_step_multi(const ps_tensor* tensors, int32_t n_tensors, const p
   std::vector<uint32_t> ends;
   std::vector<DevTensorEx> xrecs;
   std::vector<uint32_t> xends;
-  if (ps_status s = build_active(tensors, n_tensors, recs, ends, xrecs, xends)) return s;
+  if (ps_status s = build_active(tensors, n_tensors, hp->split_mode != PS_SPLIT_STOCHASTIC, recs, ends, xrecs, xends))
+    return s;
   if (recs.empty() && xrecs.empty()) return PS_OK;
   StepScalars c;
   step_scalars(*hp, step, &c);
@@ -282,6 +285,7 @@ ps_status ps_opt_step_multi(const ps_tensor* tensors, int32_t n_tensors, const p
 
 ps_status ps_split(const float* w32, uint16_t* hi, uint16_t* lo, int64_t n, int32_t mode, ps_stream_t stream) {
   g_err[0] = 0;
+  if (mode == PS_SPLIT_STOCHASTIC) return fail(PS_ERR_UNSUPPORTED, "ps_split: stochastic rounding needs a step and seed");
   if (mode != PS_SPLIT_TRUNC && mode != PS_SPLIT_NEAREST_AWAY) return fail(PS_ERR_INVALID_ARG, "unknown split mode %d", mode);
   if (ps_status s = check_elementwise(n, {{w32, "w32"}, {hi, "hi"}, {lo, "lo"}}, {})) return s;
   if (n == 0) return PS_OK;
@@ -290,6 +294,7 @@ ps_status ps_split(const float* w32, uint16_t* hi, uint16_t* lo, int64_t n, int3
 
 ps_status ps_join(const uint16_t* hi, const uint16_t* lo, float* w32, int64_t n, int32_t mode, ps_stream_t stream) {
   g_err[0] = 0;
+  if (mode == PS_SPLIT_STOCHASTIC) return fail(PS_ERR_UNSUPPORTED, "ps_join: stochastic rounding keeps no residual");
   if (mode != PS_SPLIT_TRUNC && mode != PS_SPLIT_NEAREST_AWAY) return fail(PS_ERR_INVALID_ARG, "unknown split mode %d", mode);
   if (ps_status s = check_elementwise(n, {{w32, "w32"}, {hi, "hi"}, {lo, "lo"}}, {})) return s;
   if (n == 0) return PS_OK;

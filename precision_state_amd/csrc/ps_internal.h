@@ -26,6 +26,8 @@ struct DevTensor {
   uint16_t* vc;
   float* vs;
   int64_t numel;
+  uint32_t tid;      // index in the caller's list (stochastic rounding stream key)
+  uint32_t pad;
 };
 
 // Device record of a tensor with storage flags (generic-format kernel).
@@ -39,7 +41,7 @@ struct DevTensorEx {
   float* vs;
   int64_t numel;
   uint32_t flags;
-  uint32_t pad;
+  uint32_t tid;     // index in the caller's list (stochastic rounding stream key)
 };
 
 struct TableExPtr {
@@ -51,6 +53,9 @@ struct TableExPtr {
 // fp32 scalars of one update (see ps_step_scalars).
 struct StepScalars {
   float B1, C1, B2, C2, EPS, A, RS2, AG, AM, CWD;
+  uint32_t sr_step;   // stochastic rounding: the update number mod 2^32
+  uint32_t pad;
+  uint64_t sr_seed;   // stochastic rounding: the run's seed
 };
 
 // Work decomposition of a tensor list: tensor t owns the work items

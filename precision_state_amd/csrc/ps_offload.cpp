@@ -234,6 +234,8 @@ ps_status ps_offload_run(ps_offload_plan* p, const ps_hparams* hp, int64_t step,
   if (!p) return fail(PS_ERR_INVALID_ARG, "plan is NULL");
   if (!hp) return fail(PS_ERR_INVALID_ARG, "hparams is NULL");
   const ps_hparams h = *hp;
+  if (h.split_mode == PS_SPLIT_STOCHASTIC)
+    return fail(PS_ERR_UNSUPPORTED, "the offload pipeline keeps residuals; stochastic rounding is not supported");
   float scratch_out[10];
   // the resident path's validation of the hyperparameters and the step
   if (ps_status s = ps_step_scalars(&h, step, scratch_out)) return s;

@@ -35,6 +35,9 @@ void step_scalars(const ps_hparams& hp, int64_t t, StepScalars* o) {
   o->AG = (float)(lr * (1.0 - mu_t) / (1.0 - prod));
   o->AM = (float)(lr * mu_next / (1.0 - prod * mu_next));
   o->CWD = (float)(lr * hp.weight_decay);
+  o->sr_step = (uint32_t)t;
+  o->pad = 0;
+  o->sr_seed = hp.split_mode == PS_SPLIT_STOCHASTIC ? hp.seed : 0;
 }
 
 }  // namespace ps

@@ -137,10 +137,12 @@ def block_slice(b, numel):
     return slice(b * 256, min(numel, (b + 1) * 256))
 
 
-def ohp(hp):
-    """oracle.HParams of a precision_state_amd.HParams."""
+def ohp(hp, tensor=0, elem0=0):
+    """oracle.HParams of a precision_state_amd.HParams; tensor = the tensor's
+    index in the device call's list and elem0 = the index within the tensor of
+    the host arrays' first element (both only matter for stochastic rounding)."""
     return oracle.HParams(hp.algo, hp.split_mode, hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
-                          hp.momentum_decay)
+                          hp.momentum_decay, hp.seed, tensor, elem0)
 
 
 def _host_block_state(tid, b, numel, seed):
@@ -160,7 +162,7 @@ def _check_f24_block(tid, b, numel, d, hp, steps, seed, outlier_p):
     m, v = np.zeros(3 * L, np.uint8), np.zeros(3 * L, np.uint8)
     for t in range(1, steps + 1):
         g = synth.host_bf16_normal(L, seed, STREAM_GRAD, tid, t, SIGMA_G, outlier_p, 100.0, start=sl.start)
-        oracle.opt_step_flags(hi, lo, g, m, None, v, None, oracle.F24_MOMENTS, ohp(hp), t)
+        oracle.opt_step_flags(hi, lo, g, m, None, v, None, oracle.F24_MOMENTS, ohp(hp, tid, sl.start), t)
     b3 = slice(3 * sl.start, 3 * sl.stop)
     got = {"hi": u16(d.w_hi[sl]), "lo": u16(d.w_lo[sl]), "m": d.m_code[b3].cpu().numpy(),
            "v": d.v_code[b3].cpu().numpy()}
@@ -188,7 +190,7 @@ def check_sampled_blocks(shapes, devs, hp, steps, seed, per_tensor, outlier_p=0.
             for t in range(1, steps + 1):
                 g = synth.host_bf16_normal(sl.stop - sl.start, seed, STREAM_GRAD, tid, t, SIGMA_G, outlier_p,
                                            100.0, start=sl.start)
-                oracle.opt_step(st, g, ohp(hp), t)
+                oracle.opt_step(st, g, ohp(hp, tid, sl.start), t)
             got = {"hi": u16(d.w_hi[sl]), "lo": u16(d.w_lo[sl]), "mc": u16(d.m_code[sl]), "vc": u16(d.v_code[sl]),
                    "ms": f32(d.m_scale[b:b + 1]).view(np.uint32), "vs": f32(d.v_scale[b:b + 1]).view(np.uint32)}
             want = {"hi": st.hi, "lo": st.lo, "mc": st.mc, "vc": st.vc, "ms": st.ms.view(np.uint32),

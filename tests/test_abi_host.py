@@ -69,6 +69,15 @@ def test_invalid_arguments_rejected_on_host(ps):
     assert _call(ps, [_rec(ps, m_code=66)]) == 2
     assert _call(ps, [_rec(ps, v_scale=114)]) == 2
     assert _call(ps, [_rec(ps, flags=8)]) == 1
+    assert _call(ps, [_rec(ps)], hp=ps.HParams(split_mode=3)) == 1
+    # stochastic rounding keeps no residual: a NULL w_lo passes validation (the
+    # next check, m_scale's alignment, is the one that fails here)
+    assert _call(ps, [_rec(ps, w_lo=0, m_scale=81)], hp=ps.HParams(split_mode=ps.SPLIT_STOCHASTIC)) == 2
+    assert "m_scale" in ps.last_error()
+    assert _call(ps, [_rec(ps, w_lo=0, m_scale=81)], hp=ps.HParams(split_mode=ps.SPLIT_TRUNC)) == 1
+    assert "w_lo" in ps.last_error()
+    assert L.ps_split(16, 32, 48, 10, ps.SPLIT_STOCHASTIC, None) == 4
+    assert L.ps_join(16, 32, 48, 10, ps.SPLIT_STOCHASTIC, None) == 4
     assert _call(ps, [_rec(ps, flags=ps.TENSOR_FP32_MOMENTS | ps.TENSOR_F24_MOMENTS)]) == 1
     assert "exclusive" in ps.last_error()
     assert _call(ps, [_rec(ps, flags=ps.TENSOR_F24_MOMENTS, m_code=8)]) == 2

@@ -172,13 +172,15 @@ def test_step_variants(algo, wd, split_mode):
 RAGGED = [0, 1, 7, 8, 64, 128, 255, 256, 257, 1000, 1023, 1024, 1025, 3000, 4096, 65539, 131089]
 
 
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_STOCHASTIC])
 @pytest.mark.parametrize("count", [len(RAGGED), 9])
-def test_multi_tensor_ragged_lists(count):
+def test_multi_tensor_ragged_lists(count, split_mode):
     """Ragged sizes (tails inside a 16-lane row, partial blocks, partial work
     items), tensors without a gradient, an empty tensor; 17 tensors take the
-    device-table path, 9 the kernel-argument path."""
+    device-table path, 9 the kernel-argument path. Stochastic rounding: the
+    residual arrays stay untouched on both sides."""
     sizes = RAGGED[:count]
-    hp = ps.HParams(algo=ps.ALGO_NADAM, weight_decay=0.01, lr=1e-4)
+    hp = ps.HParams(algo=ps.ALGO_NADAM, weight_decay=0.01, lr=1e-4, split_mode=split_mode, seed=2024)
     devs = [dev_state(n, 7, i) for i, n in enumerate(sizes)]
     hosts = [host_state(n, 7, i) for i, n in enumerate(sizes)]
     for t in range(1, 4):
@@ -232,11 +234,14 @@ def test_checkpoint_resume_equals_straight_run():
     assert _equal(a, b)
 
 
-def test_flux_double_block_3_steps_sampled():
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_STOCHASTIC])
+def test_flux_double_block_3_steps_sampled(split_mode):
     """One FLUX double-stream block (24 tensors, 339,831,296 parameters), NAdamW
-    wd 0.01, one multi-tensor launch per step; sampled blocks vs the oracle."""
+    wd 0.01, one multi-tensor launch per step; sampled blocks vs the oracle
+    (stochastic rounding: the oracle draws each sampled block's random bits at
+    the block's own element offsets)."""
     shapes = synth.WORKLOADS["flux_double_block"]()
-    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, weight_decay=0.01)
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, weight_decay=0.01, split_mode=split_mode, seed=31337)
     seed = 0
     devs = [dev_state(s.numel, seed, i, s.rows, s.cols) for i, s in enumerate(shapes)]
     recs_dev = None
@@ -267,7 +272,8 @@ def _flag_mix(sizes, large):
 
 @pytest.mark.parametrize("split_mode,large", [(ps.SPLIT_TRUNC, 0), (ps.SPLIT_NEAREST_AWAY, 0),
                                               (ps.SPLIT_TRUNC, ps.TENSOR_F24_MOMENTS),
-                                              (ps.SPLIT_NEAREST_AWAY, ps.TENSOR_F24_MOMENTS)])
+                                              (ps.SPLIT_NEAREST_AWAY, ps.TENSOR_F24_MOMENTS),
+                                              (ps.SPLIT_STOCHASTIC, ps.TENSOR_F24_MOMENTS)])
 def test_storage_flags_match_oracle(split_mode, large):
     """A list mixing the default format with fp32 moments (tensors of <= 4096
     elements on the pages), f24 moments and fp32 parameters (the final
@@ -275,7 +281,7 @@ def test_storage_flags_match_oracle(split_mode, large):
     paths, 3 NAdamW steps; bit-exact against the oracle."""
     sizes = [64, 128, 3072, 4096, 1000, 300001, 257, 18432, 3000, 5, 6144 * 8, 2048, 100, 4096, 77, 65536, 999]
     flag_of = _flag_mix(sizes, large)
-    hp = ps.HParams(algo=ps.ALGO_NADAM, weight_decay=0.01, lr=1e-4, split_mode=split_mode)
+    hp = ps.HParams(algo=ps.ALGO_NADAM, weight_decay=0.01, lr=1e-4, split_mode=split_mode, seed=77)
     for count in (len(sizes), 9):
         devs, hosts = [], []
         for i, (n, fl) in enumerate(zip(sizes[:count], flag_of[:count])):
@@ -283,7 +289,7 @@ def test_storage_flags_match_oracle(split_mode, large):
             lo = synth.host_u16_uniform(n, 13, synth.STREAM_LO, i, 0)
             h = {"flags": fl}
             if fl & ps.TENSOR_FP32_PARAM:
-                h["w"] = oracle.join(hi, lo, split_mode)
+                h["w"] = oracle.join(hi, lo, ps.SPLIT_TRUNC if split_mode == ps.SPLIT_STOCHASTIC else split_mode)
                 h["lo"] = None
             else:
                 h["w"], h["lo"] = hi.copy(), lo.copy()
@@ -300,6 +306,8 @@ def test_storage_flags_match_oracle(split_mode, large):
                                 to_dev(h["v"].copy()), to_dev(h["vs"]), flags=fl)
             if st.w_lo is None:
                 st.w_lo = torch.empty(0, dtype=torch.int16, device=DEV)   # unused for fp32 parameters
+            if split_mode == ps.SPLIT_STOCHASTIC and i % 2 == 0:
+                st.w_lo = None                                            # no residual array at all
             if st.m_scale is None:
                 st.m_scale = st.v_scale = torch.empty(0, dtype=torch.float32, device=DEV)
             devs.append(st)
@@ -315,15 +323,15 @@ def test_storage_flags_match_oracle(split_mode, large):
                     grads_h.append(g16)
                     grads_d.append(torch.from_numpy(g16.view(np.int16)).to(DEV))
             ps.opt_step_multi(devs, grads_d, hp, t)
-            for h, g in zip(hosts, grads_h):
-                oracle.opt_step_flags(h["w"], h["lo"], g, h["m"], h["ms"], h["v"], h["vs"], h["flags"], ohp(hp), t)
+            for i, (h, g) in enumerate(zip(hosts, grads_h)):
+                oracle.opt_step_flags(h["w"], h["lo"], g, h["m"], h["ms"], h["v"], h["vs"], h["flags"], ohp(hp, i), t)
         torch.cuda.synchronize()
         for i, (d, h) in enumerate(zip(devs, hosts)):
             fl = h["flags"]
             got_w = d.w_hi.cpu().numpy()
             assert np.array_equal(got_w.view(np.uint32 if fl & ps.TENSOR_FP32_PARAM else np.uint16),
                                   h["w"].view(np.uint32 if fl & ps.TENSOR_FP32_PARAM else np.uint16)), (count, i, "w")
-            if not fl & ps.TENSOR_FP32_PARAM:
+            if not fl & ps.TENSOR_FP32_PARAM and d.w_lo is not None:
                 assert np.array_equal(u16(d.w_lo), h["lo"]), (count, i, "lo")
             for k in ("m", "v"):
                 got = getattr(d, k + "_code").cpu().numpy()
