@@ -32,7 +32,7 @@ class _HP(ctypes.Structure):
 class _FHP(ctypes.Structure):
     _fields_ = [("split_mode", ctypes.c_int32), ("reserved", ctypes.c_int32), ("lr", ctypes.c_double),
                 ("beta2", ctypes.c_double), ("eps1", ctypes.c_double), ("clip_threshold", ctypes.c_double),
-                ("weight_decay", ctypes.c_double)]
+                ("weight_decay", ctypes.c_double), ("decay_rate", ctypes.c_double), ("beta1", ctypes.c_double)]
 
 
 class _Coeffs(ctypes.Structure):
@@ -66,9 +66,12 @@ class FHParams:
     eps1: float = 1e-30
     clip_threshold: float = 1.0
     weight_decay: float = 0.0
+    decay_rate: float = 0.0   # < 0: beta2 at update t is 1 - t^decay_rate (Adafactor's schedule)
+    beta1: float = 0.0        # > 0: first moment of the clipped update, in mc/ms (signed codec)
 
     def c(self):
-        return _FHP(self.split_mode, 0, self.lr, self.beta2, self.eps1, self.clip_threshold, self.weight_decay)
+        return _FHP(self.split_mode, 0, self.lr, self.beta2, self.eps1, self.clip_threshold, self.weight_decay,
+                    self.decay_rate, self.beta1)
 
 
 _lib = None
@@ -101,8 +104,8 @@ def lib():
             "orc_sr_bf16": ([ctypes.c_float, ctypes.c_uint16], ctypes.c_uint16),
             "orc_sr_rand16_array": ([ctypes.c_uint64, _i64, _i64, _i64, _i64, _vp], None),
             "orc_f24_decode": ([_vp, _i64, _vp], None),
-            "orc_factored_2d": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.POINTER(_FHP), _i64], None),
-            "orc_factored_1d": ([_vp, _vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_FHP), _i64], None),
+            "orc_factored_2d": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.POINTER(_FHP), _i64], None),
+            "orc_factored_1d": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_FHP), _i64], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -261,12 +264,16 @@ def factored_step(st: TensorState, g, rows: int, cols: int, hp: FHParams, step: 
     """rows == 0: 1-D tensor (codec second moment); else 2-D [rows, cols]."""
     h = hp.c()
     gp = None if g is None else _p(g, np.uint16)
+    if hp.beta1 != 0.0:
+        mcp, msp = _p(st.mc, np.uint16), _p(st.ms, np.float32)
+    else:
+        mcp = msp = None
     if rows > 0:
         lib().orc_factored_2d(_p(st.hi, np.uint16), _p(st.lo, np.uint16), gp, _p(st.row, np.float32),
-                              _p(st.col, np.float32), rows, cols, ctypes.byref(h), step)
+                              _p(st.col, np.float32), mcp, msp, rows, cols, ctypes.byref(h), step)
     else:
         lib().orc_factored_1d(_p(st.hi, np.uint16), _p(st.lo, np.uint16), gp, _p(st.vc, np.uint16),
-                              _p(st.vs, np.float32), st.hi.size, ctypes.byref(h), step)
+                              _p(st.vs, np.float32), mcp, msp, st.hi.size, ctypes.byref(h), step)
 
 
 def bf16_to_f32(b):

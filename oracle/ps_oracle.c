@@ -64,6 +64,8 @@ typedef struct {
   int32_t split_mode;
   int32_t reserved;
   double lr, beta2, eps1, clip_threshold, weight_decay;
+  double decay_rate; /* 0: constant beta2; < 0: beta2 at update t is 1 - t^decay_rate [ADAF] */
+  double beta1;      /* 0: no first moment; > 0: EMA of the clipped update, kept in the signed codec [ADAF] */
 } orc_fhparams;
 
 /* Step-dependent fp32 scalars, each computed in double and rounded once. */
@@ -420,6 +422,25 @@ void orc_opt_step_flags(void* w, uint16_t* lo, const void* g, void* m, float* ms
 /* Factored second moment with update clipping [ADAF; PRODIGY]              */
 /* ------------------------------------------------------------------------ */
 
+/* beta2 of update t: the constant, or Adafactor's schedule 1 - t^decay_rate;
+ * each of B2 and C2 = 1 - beta2 rounded once from double. */
+static void f_beta2(const orc_fhparams* hp, int64_t t, float* B2, float* C2) {
+  double b2 = hp->decay_rate != 0.0 ? 1.0 - pow((double)t, hp->decay_rate) : hp->beta2;
+  *B2 = (float)b2;
+  *C2 = (float)(1.0 - b2);
+}
+
+/* The optional first moment [ADAF]: an EMA of the clipped, lr-scaled update x
+ * (before weight decay) replaces x. The block's values go to mbuf for the
+ * signed-codec encode. */
+static float f_first_moment(float x, const uint16_t* mc, const float* ms, int64_t e, float B1, float C1,
+                            float* mbuf) {
+  float m0 = orc_decode1(mc[e], ms[e / ORC_BLOCK], ORC_SIGNED);
+  float m = fmaf(B1, m0, C1 * x);
+  mbuf[e % ORC_BLOCK] = m;
+  return m;
+}
+
 /* Update clipping factor: lr / max(1, RMS(U) / d) with RMS over the tensor. */
 static float clip_factor(double sum_sq, int64_t n, const orc_fhparams* hp) {
   double rms = sqrt(sum_sq / (double)n);
@@ -429,11 +450,13 @@ static float clip_factor(double sum_sq, int64_t n, const orc_fhparams* hp) {
 
 /* 2-D tensor [R, C] (row-major). row[R] and col[C] hold the EMAs of the row
  * and column means of g^2 + eps1. */
-void orc_factored_2d(uint16_t* hi, uint16_t* lo, const uint16_t* g, float* row, float* col, int64_t R,
-                     int64_t C, const orc_fhparams* hp, int64_t step) {
-  (void)step;
+void orc_factored_2d(uint16_t* hi, uint16_t* lo, const uint16_t* g, float* row, float* col, uint16_t* mc, float* ms,
+                     int64_t R, int64_t C, const orc_fhparams* hp, int64_t step) {
   if (!g) return;
-  float B2 = (float)hp->beta2, C2 = (float)(1.0 - hp->beta2), EPS1 = (float)hp->eps1;
+  float B2, C2, EPS1 = (float)hp->eps1;
+  f_beta2(hp, step, &B2, &C2);
+  int fm = hp->beta1 != 0.0;
+  float B1 = (float)hp->beta1, C1 = (float)(1.0 - hp->beta1), mbuf[ORC_BLOCK];
   float CWD = (float)(hp->lr * hp->weight_decay);
   int wd = hp->weight_decay != 0.0;
   double* rs = (double*)calloc((size_t)R, sizeof(double));
@@ -464,15 +487,21 @@ void orc_factored_2d(uint16_t* hi, uint16_t* lo, const uint16_t* g, float* row, 
       su += (double)U * (double)U;
     }
   float f = clip_factor(su, R * C, hp);
-  /* 4. apply to the joined master weight and split again */
+  /* 4. apply to the joined master weight and split again; with a first
+   *    moment, re-encode each 256-element block of the flattened tensor */
   for (int64_t i = 0; i < R; ++i)
     for (int64_t j = 0; j < C; ++j) {
       int64_t e = i * C + j;
       float U = (orc_bf16_to_f32(g[e]) * rho[i]) * kap[j];
       float w = f_of(orc_join1(hi[e], lo[e], hp->split_mode));
       float x = U * f;
+      if (fm) x = f_first_moment(x, mc, ms, e, B1, C1, mbuf);
       if (wd) x = fmaf(CWD, w, x);
       orc_split1(u_of(w - x), &hi[e], &lo[e], hp->split_mode);
+      if (fm && (e % ORC_BLOCK == ORC_BLOCK - 1 || e == R * C - 1)) {
+        int64_t b = e / ORC_BLOCK;
+        orc_encode_block(mbuf, (int)(e - b * ORC_BLOCK + 1), ORC_SIGNED, mc + b * ORC_BLOCK, &ms[b]);
+      }
     }
   free(rs);
   free(cs);
@@ -481,11 +510,13 @@ void orc_factored_2d(uint16_t* hi, uint16_t* lo, const uint16_t* g, float* row, 
 }
 
 /* 1-D tensor: unfactored second moment kept in the uint16 codec. */
-void orc_factored_1d(uint16_t* hi, uint16_t* lo, const uint16_t* g, uint16_t* vc, float* vs, int64_t n,
-                     const orc_fhparams* hp, int64_t step) {
-  (void)step;
+void orc_factored_1d(uint16_t* hi, uint16_t* lo, const uint16_t* g, uint16_t* vc, float* vs, uint16_t* mc,
+                     float* ms, int64_t n, const orc_fhparams* hp, int64_t step) {
   if (!g) return;
-  float B2 = (float)hp->beta2, C2 = (float)(1.0 - hp->beta2), EPS1 = (float)hp->eps1;
+  float B2, C2, EPS1 = (float)hp->eps1;
+  f_beta2(hp, step, &B2, &C2);
+  int fm = hp->beta1 != 0.0;
+  float B1 = (float)hp->beta1, C1 = (float)(1.0 - hp->beta1), mbuf[ORC_BLOCK];
   float CWD = (float)(hp->lr * hp->weight_decay);
   int wd = hp->weight_decay != 0.0;
   float* v = (float*)malloc((size_t)n * sizeof(float));
@@ -502,8 +533,13 @@ void orc_factored_1d(uint16_t* hi, uint16_t* lo, const uint16_t* g, uint16_t* vc
     float U = orc_bf16_to_f32(g[e]) * (1.0f / sqrtf(v[e]));
     float w = f_of(orc_join1(hi[e], lo[e], hp->split_mode));
     float x = U * f;
+    if (fm) x = f_first_moment(x, mc, ms, e, B1, C1, mbuf);
     if (wd) x = fmaf(CWD, w, x);
     orc_split1(u_of(w - x), &hi[e], &lo[e], hp->split_mode);
+    if (fm && (e % ORC_BLOCK == ORC_BLOCK - 1 || e == n - 1)) {
+      int64_t b = e / ORC_BLOCK;
+      orc_encode_block(mbuf, (int)(e - b * ORC_BLOCK + 1), ORC_SIGNED, mc + b * ORC_BLOCK, &ms[b]);
+    }
   }
   orc_encode(v, n, ORC_UNSIGNED, vc, vs);
   free(v);

@@ -89,11 +89,12 @@ def test_tensor_without_gradient_is_untouched():
     assert np.array_equal(st.hi, before.hi) and np.array_equal(st.row, before.row)
 
 
-def _dbl_factored_2d(w, g, r, c, hp: FHParams):
+def _dbl_factored_2d(w, g, r, c, hp: FHParams, beta2=None):
     R, C = g.shape
+    b2 = hp.beta2 if beta2 is None else beta2
     q = g * g + hp.eps1
-    r = hp.beta2 * r + (1 - hp.beta2) * q.mean(axis=1)
-    c = hp.beta2 * c + (1 - hp.beta2) * q.mean(axis=0)
+    r = b2 * r + (1 - b2) * q.mean(axis=1)
+    c = b2 * c + (1 - b2) * q.mean(axis=0)
     vhat = np.outer(r, c) / r.mean()                # Adafactor's factored estimate
     U = g / np.sqrt(vhat)
     rms = np.sqrt(np.mean(U * U))
@@ -156,3 +157,83 @@ def test_one_d_vs_double_brute_force():
             assert abs(st.vs[b] / vb.max() - 1) < 1e-6
             k = np.floor(65535 * (vb / vb.max()) ** 0.25 + 0.5)
             assert np.max(np.abs(st.vc[b * 256:(b + 1) * 256].astype(np.int64) - k)) <= 1
+
+
+# ---------------------------------------------------------------------------
+# Adafactor's beta2 schedule and the optional first moment (commit 7983d3d,
+# adafactor_step_param: beta2t = 1 - step^decay_rate; exp_avg of the clipped,
+# lr-scaled update when beta1 is set)
+# ---------------------------------------------------------------------------
+
+def test_schedule_first_update_keeps_exactly_this_steps_means():
+    """At update 1 the schedule gives beta2 = 1 - 1 = 0, so whatever the EMAs
+    held before, they become this step's row and column means of g^2 + eps1
+    (means of the fp32 squares, accumulated exactly and rounded once)."""
+    rng = np.random.default_rng(21)
+    R, C = 40, 56
+    g = _bf16(rng.standard_normal(R * C) * 1e-3)
+    st = _state2d(R, C)
+    st.row[:] = 123.0
+    st.col[:] = 7.0
+    oracle.factored_step(st, g, R, C, FHParams(decay_rate=-0.8), 1)
+    gf = oracle.bf16_to_f32(g).reshape(R, C)
+    q = (gf * gf + np.float32(1e-30)).astype(np.float64)
+    assert np.array_equal(st.row, q.mean(axis=1).astype(np.float32))
+    assert np.array_equal(st.col, q.mean(axis=0).astype(np.float32))
+    st1 = _state1d(300)
+    g1 = _bf16(rng.standard_normal(300) * 1e-3)
+    st1.vs[:] = 5.0
+    st1.vc[:] = 40000
+    oracle.factored_step(st1, g1, 0, 0, FHParams(decay_rate=-0.8), 1)
+    v = oracle.decode(st1.vc, st1.vs, UNSIGNED)
+    g1f = oracle.bf16_to_f32(g1).astype(np.float64)
+    assert np.allclose(v, g1f * g1f + 1e-30, rtol=1e-3, atol=0)
+
+
+def test_schedule_vs_double_brute_force():
+    """Ten steps with beta2_t = 1 - t^-0.8 against the same step in double."""
+    rng = np.random.default_rng(22)
+    R, C = 32, 48
+    hp = FHParams(lr=1e-4, decay_rate=-0.8)
+    st = _state2d(R, C, (rng.standard_normal(R * C) * 0.02).astype(np.float32))
+    for t in range(1, 11):
+        g = _bf16(rng.standard_normal(R * C) * 1e-3)
+        w = oracle.join(st.hi, st.lo).astype(np.float64)
+        gd = oracle.bf16_to_f32(g).astype(np.float64).reshape(R, C)
+        w2, r, c, _ = _dbl_factored_2d(w.reshape(R, C), gd, st.row.astype(np.float64), st.col.astype(np.float64),
+                                       hp, beta2=1.0 - t ** -0.8)
+        oracle.factored_step(st, g, R, C, hp, t)
+        assert np.allclose(st.row, r, rtol=1e-6, atol=0) and np.allclose(st.col, c, rtol=1e-6, atol=0), t
+        wo = oracle.join(st.hi, st.lo).astype(np.float64)
+        w2 = w2.reshape(-1)
+        assert np.all(np.abs(wo - w2) <= 2 * ulp32(w2) + 1e-5 * np.abs(w2 - w)), t
+
+
+@pytest.mark.parametrize("two_d", [True, False])
+def test_first_moment_scales_the_first_step_and_carries_momentum(two_d):
+    """beta1 = 0.9: the first update is (1 - beta1) times the update without a
+    first moment (the EMA starts from zero); a following zero-gradient step
+    (U = 0) still moves the weight by beta1 times the previous step (momentum),
+    up to the signed codec's rounding of the stored moment."""
+    rng = np.random.default_rng(23)
+    R, C = (24, 40) if two_d else (0, 0)
+    n = R * C if two_d else 777
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g = _bf16(rng.standard_normal(n) * 1e-3)
+
+    def fresh():
+        st = _state2d(R, C, w0) if two_d else _state1d(n, w0)
+        st.mc, st.ms, _, _ = oracle.zero_moments(n)
+        return st
+    st_a, st_b = fresh(), fresh()
+    oracle.factored_step(st_a, g, R, C, FHParams(lr=1e-3), 1)
+    oracle.factored_step(st_b, g, R, C, FHParams(lr=1e-3, beta1=0.9), 1)
+    wa = oracle.join(st_a.hi, st_a.lo).astype(np.float64)
+    wb = oracle.join(st_b.hi, st_b.lo).astype(np.float64)
+    base = w0.astype(np.float64)
+    d_a, d_b = wa - base, wb - base
+    assert np.all(np.abs(d_b - 0.1 * d_a) <= 2 * ulp32(wb) + 1e-5 * np.abs(d_a))
+    assert np.any(st_b.mc != 32768) and np.all(st_a.mc == 32768)
+    oracle.factored_step(st_b, np.zeros(n, np.uint16), R, C, FHParams(lr=1e-3, beta1=0.9), 2)
+    wb2 = oracle.join(st_b.hi, st_b.lo).astype(np.float64)
+    assert np.all(np.abs((wb2 - wb) - 0.9 * d_b) <= 2 * ulp32(wb2) + 2e-3 * np.abs(d_b))
