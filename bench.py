@@ -174,11 +174,15 @@ def bench_factored(args):
         else:
             st.v_code = torch.zeros(n, dtype=torch.int16, device=dev)
             st.v_scale = torch.zeros((n + 255) // 256, dtype=torch.float32, device=dev)
+        if args.beta1:
+            st.m_code = torch.full((n,), -32768, dtype=torch.int16, device=dev)
+            st.m_scale = torch.zeros((n + 255) // 256, dtype=torch.float32, device=dev)
         states.append(st)
         grads.append(g)
     recs = ps.make_records(states, grads)
     ws = torch.empty(ps.factored_workspace_size(None, records=recs), dtype=torch.uint8, device=dev)
-    hp = ps.FactoredHParams(lr=3.5e-6, beta2=0.999, eps1=1e-30, clip_threshold=1.0, weight_decay=0.0)
+    hp = ps.FactoredHParams(lr=3.5e-6, beta2=0.999, eps1=1e-30, clip_threshold=1.0, weight_decay=0.0,
+                            decay_rate=args.decay_rate, beta1=args.beta1)
     stream = torch.cuda.current_stream()
     step = 0
     for _ in range(args.warmup):
@@ -196,18 +200,113 @@ def bench_factored(args):
     wall = time.perf_counter() - t0
     step_ms = a.elapsed_time(b) / args.steps
     log(f"[bench] factored: {args.steps} steps, {step_ms:.3f} ms/step (events), {wall * 1e3 / args.steps:.3f} wall")
-    gbs10 = 10 * n_params / (step_ms * 1e-3) / 1e9
-    gbs14 = 14 * n_params / (step_ms * 1e-3) / 1e9
+    n_blocks = sum((s.numel + 255) // 256 for s in shapes)
+    alg = 10 * n_params + ((4 * n_params + 8 * n_blocks) if args.beta1 else 0)
+    gbs10 = alg / (step_ms * 1e-3) / 1e9
+    gbs14 = (alg + 4 * n_params) / (step_ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "factored optimizer-updated params/sec (Adafactor-style step, FLUX double-block shapes)",
         "value": n_params * args.steps / wall, "unit": "params/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl + "_factored", "params": n_params, "tensors": len(shapes), "step_ms": step_ms,
-                   "gbs_10B_per_param": gbs10, "gbs_14B_per_param": gbs14},
+                   "beta1": args.beta1, "decay_rate": args.decay_rate, "algorithmic_bytes": alg,
+                   "gbs_algorithmic": gbs10, "gbs_with_gradient_rereads": gbs14},
         "roofline": {"bound": "hbm", "achieved": gbs10, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs10 / PEAK_HBM_GBS, "traffic": None},
         "cpu_baseline": None}), flush=True)
+
+
+def bench_per_tensor(args):
+    """Per-hook granularity: the pages step each parameter inside its gradient
+    hook, one call per tensor. Same set, slab layout and NAdam step as the
+    headline, but each step is one ps_opt_step_multi call per tensor (records
+    built once, as a hook would keep them). Also times the single launch over
+    all tensors on the same state, and back-to-back single calls on small
+    tensors (host issue time and GPU time per call)."""
+    import torch
+
+    import precision_state_amd as ps
+    import synth
+    dev = "cuda:0"
+    shapes = synth.WORKLOADS[args.workload]()
+    n_params = synth.total_params(shapes)
+    states, grads = build_state(shapes, args.seed, dev, "slab")
+    recs_one = [ps.make_records([st], [g]) for st, g in zip(states, grads)]
+    recs_all = ps.make_records(states, grads)
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6)
+    stream = torch.cuda.current_stream()
+    step = 0
+
+    def per_tensor_step():
+        nonlocal step
+        step += 1
+        for r in recs_one:
+            ps.opt_step_multi(None, None, hp, step, stream=stream, records=r)
+
+    def one_launch():
+        nonlocal step
+        step += 1
+        ps.opt_step_multi(None, None, hp, step, stream=stream, records=recs_all)
+
+    for _ in range(args.warmup):
+        one_launch()
+    per_tensor_step()
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn in (("per_tensor", per_tensor_step), ("one_launch", one_launch)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        issue = 0.0
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(args.steps):
+            t1 = time.perf_counter()
+            fn()
+            issue += time.perf_counter() - t1
+        b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        res[name] = {"wall_ms": wall * 1e3 / args.steps, "gpu_ms": a.elapsed_time(b) / args.steps,
+                     "issue_ms": issue * 1e3 / args.steps}
+        log(f"[bench] {name}: {res[name]}")
+    # back-to-back calls on single small tensors
+    lat = {}
+    for n in (4096, 65536, 3072 * 3072):
+        st, g = build_state([synth.Shape("t", 0, 0, n)], args.seed, dev, "slab")
+        r = ps.make_records(st, g)
+        calls = 400
+        for k in range(20):
+            ps.opt_step_multi(None, None, hp, k + 1, stream=stream, records=r)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record(stream)
+        for k in range(calls):
+            ps.opt_step_multi(None, None, hp, k + 21, stream=stream, records=r)
+        t_issue = time.perf_counter() - t0
+        b.record(stream)
+        torch.cuda.synchronize()
+        lat[n] = {"host_us_per_call": t_issue * 1e6 / calls, "gpu_us_per_call": a.elapsed_time(b) * 1e3 / calls}
+        log(f"[bench] {n} elements, {calls} back-to-back calls: {lat[n]}")
+        del st, g
+    # the binding's own cost per call: an empty list returns after validation
+    empty = ps.make_records([], [])
+    t0 = time.perf_counter()
+    for k in range(2000):
+        ps.opt_step_multi(None, None, hp, 1, stream=stream, records=empty)
+    lat["empty_list"] = {"host_us_per_call": (time.perf_counter() - t0) * 1e6 / 2000}
+    log(f"[bench] empty list (binding + validation only): {lat['empty_list']}")
+    pt = res["per_tensor"]
+    print(json.dumps({
+        "metric": "per-hook optimizer step: params/sec with one call per tensor (FLUX-12B set)",
+        "value": n_params / (pt["wall_ms"] * 1e-3), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": pt["wall_ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload + "_per_tensor", "params": n_params, "calls_per_step": len(shapes),
+                   "per_tensor": pt, "one_launch": res["one_launch"],
+                   "per_tensor_over_one_launch": pt["wall_ms"] / res["one_launch"]["wall_ms"],
+                   "small_tensor_calls": {str(k): v for k, v in lat.items()}},
+        "roofline": None, "cpu_baseline": None}), flush=True)
 
 
 def pcie_ceiling(dev, nbytes=2 << 30):
@@ -326,9 +425,11 @@ def main():
                     help="state in one contiguous allocation per stream (slab) or one per tensor")
     ap.add_argument("--host-blocks", type=int, default=4,
                     help="offload mode: distinct pinned host state sets, reused cyclically by the 57 blocks")
-    ap.add_argument("--mode", default="nadam", choices=["nadam", "factored", "offload"],
+    ap.add_argument("--mode", default="nadam", choices=["nadam", "factored", "offload", "per_tensor"],
                     help="nadam: the fused (N)AdamW step (headline); factored: the Adafactor-style step "
-                         "(no first moment, factored second moment, update clipping) on the same shapes")
+                         "(factored second moment, update clipping; --beta1, --decay-rate) on the double-block "
+                         "shapes; offload: host-resident state over PCIe; per_tensor: one call per tensor, as a "
+                         "gradient hook would step")
     ap.add_argument("--policy", action="store_true",
                     help="nadam mode: fp32 moments for tensors of <= 4096 elements and an fp32 final layer "
                          "(PS_TENSOR_FP32_MOMENTS / PS_TENSOR_FP32_PARAM)")
@@ -338,6 +439,10 @@ def main():
     ap.add_argument("--split", default="trunc", choices=["trunc", "nearest_away", "stochastic"],
                     help="nadam mode: residual split mode; stochastic = stochastic rounding to bf16 with no "
                          "residual (PS_SPLIT_STOCHASTIC, 14 B/param)")
+    ap.add_argument("--beta1", type=float, default=0.0,
+                    help="factored mode: first moment of the clipped update (0 = none)")
+    ap.add_argument("--decay-rate", type=float, default=0.0,
+                    help="factored mode: beta2 of update t is 1 - t^decay_rate (0 = constant 0.999)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="after the timed steps, run 3 plain device copies of GIB GiB (counter calibration "
@@ -362,6 +467,8 @@ def main():
         return bench_factored(args)
     if args.mode == "offload":
         return bench_offload(args)
+    if args.mode == "per_tensor":
+        return bench_per_tensor(args)
     shapes = synth.WORKLOADS[args.workload]()
     n_params = synth.total_params(shapes)
     log(f"[bench] {args.workload}: {len(shapes)} tensors, {n_params} params; generating state on {dev}")

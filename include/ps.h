@@ -146,10 +146,20 @@ typedef struct ps_hparams {
   uint64_t seed;
 } ps_hparams;
 
-/* Factored-second-moment hyperparameters [ADAF; PRODIGY]: no first moment,
- * constant beta2, eps1 added to g^2, update clipped to RMS clip_threshold.
- * Constraints: lr >= 0; 0 <= beta2 < 1; eps1 > 0; clip_threshold > 0;
- * weight_decay >= 0; all finite. */
+/* Factored-second-moment hyperparameters [ADAF; PRODIGY]: eps1 added to g^2,
+ * update clipped to RMS clip_threshold.
+ *   decay_rate  0: constant beta2. < 0: Adafactor's schedule [ADAF]: beta2 of
+ *               update t is 1 - t^decay_rate (beta2 is then ignored); B2 and
+ *               C2 = 1 - beta2_t are each rounded once from double
+ *   beta1       0: no first moment [PRODIGY]. In (0, 1): the clipped,
+ *               lr-scaled update x is replaced by its EMA m = fma(B1, m0, C1*x)
+ *               (B1 = fp32(beta1), C1 = fp32(1 - beta1)) before weight decay
+ *               [ADAF], m kept in m_code / m_scale (signed codec, per-256
+ *               blocks of the flattened tensor); 2-D tensors then need
+ *               cols % 8 == 0 and numel < 2^31 (else PS_ERR_UNSUPPORTED)
+ * Constraints: split_mode in {TRUNC, NEAREST_AWAY}; lr >= 0; 0 <= beta2 < 1;
+ * eps1 > 0; clip_threshold > 0; weight_decay >= 0; decay_rate <= 0;
+ * 0 <= beta1 < 1; all finite. */
 typedef struct ps_factored_hparams {
   int32_t split_mode;
   int32_t reserved; /* must be 0 */
@@ -158,6 +168,8 @@ typedef struct ps_factored_hparams {
   double eps1;
   double clip_threshold;
   double weight_decay;
+  double decay_rate;
+  double beta1;
 } ps_factored_hparams;
 
 /* ps_opt_step_multi - one fused (N)AdamW step over a list of tensors, in ONE
@@ -219,14 +231,17 @@ ps_status ps_decode_moments(const uint16_t* code, const float* scale, float* x, 
  * for this tensor list (partial row/column sums and per-tensor reductions).
  * Host only. */
 ps_status ps_factored_workspace_size(const ps_tensor* tensors, int32_t n_tensors, size_t* bytes);
+/* (The workspace does not depend on the hyperparameters: a first moment lives
+ * in the tensors' m_code / m_scale.) */
 
-/* ps_factored_step - Adafactor-style step without first moment [ADAF;
- * PRODIGY]. For a 2-D tensor [rows, cols] (row-major):
+/* ps_factored_step - Adafactor-style step [ADAF; PRODIGY]. For a 2-D tensor
+ * [rows, cols] (row-major):
  *   q_ij = g_ij*g_ij + EPS1
  *   r_i = fma(B2, r_i, C2*fp32(mean_j q_ij)),  c_j = fma(B2, c_j, C2*fp32(mean_i q_ij))
  *   rbar = fp32(mean_i r_i); rho_i = 1/sqrt(r_i/rbar); kap_j = 1/sqrt(c_j)
  *   U_ij = (g_ij*rho_i)*kap_j; f = fp32(lr / max(1, RMS(U)/clip_threshold))
- *   w' = w - x with x = U*f, then x = fma(CWD, w, x) if weight_decay != 0
+ *   x = U*f; with beta1: m = fma(B1, decode(m), C1*x), x = m, m re-encoded
+ *   w' = w - x after x = fma(CWD, w, x) if weight_decay != 0
  * Means and RMS are accumulated in double. A 1-D tensor keeps v in the
  * uint16 codec: v = fma(B2, decode(v), C2*q); U = g*(1/sqrt(v)); same clip.
  * workspace: device memory of at least ps_factored_workspace_size bytes,

@@ -1,7 +1,9 @@
-// k_factored.hip - Adafactor-style step without first moment: factored
-// second moment (row/column EMAs of mean g^2 + eps1), update clipping by the
-// tensor's RMS, decoupled weight decay, residual split [ADAF,
-// adafactor_step_param; PRODIGY, beta1 = 0 / factored / update clipping].
+// k_factored.hip - Adafactor-style step: factored second moment (row/column
+// EMAs of mean g^2 + eps1, constant beta2 or the 1 - t^decay_rate schedule),
+// update clipping by the tensor's RMS, optional first moment (EMA of the
+// clipped update in the signed codec), decoupled weight decay, residual split
+// [ADAF, adafactor_step_param; PRODIGY, beta1 = 0 / factored / update
+// clipping].
 //
 // 2-D tensors [R, C] are cut into 64 x 256 tiles, one 256-thread workgroup
 // each; thread t handles columns (t % 32) * 8 .. + 8 of rows t / 32 + 8k,
@@ -308,21 +310,31 @@ __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
   const float f = *X.f;
   FlatRun run[2];
   flat_runs(X, item, run);
-  uint4 gv[2], hv[2], lv[2];
+  // first moment: the item's 4 blocks are the 4 DPP rows (16 lanes x 2 runs)
+  const uint32_t n = (uint32_t)X.R * (uint32_t)X.C;
+  const uint32_t blk = item * (uint32_t)kItemBlocks + (threadIdx.x >> 4);
+  const bool blk_ok = blk * (uint32_t)kBlock < n;
+  const float ms_old = (S.fm && blk_ok) ? X.ms[blk] : 0.0f;
+  uint4 gv[2], hv[2], lv[2], mv[2] = {};
   float kap[2][8], rho[2];
   for (int h = 0; h < 2; ++h) {
     if (!run[h].ok) continue;
     gv[h] = *reinterpret_cast<const uint4*>(X.g + run[h].e);
     hv[h] = *reinterpret_cast<const uint4*>(X.hi + run[h].e);
     lv[h] = *reinterpret_cast<const uint4*>(X.lo + run[h].e);
+    if (S.fm) mv[h] = *reinterpret_cast<const uint4*>(X.mc + run[h].e);
     load_kap8(X.kap, run[h].j, kap[h]);
     rho[h] = X.rho[run[h].i];
   }
+  float m[16];
+  float mx = 0.0f;
   for (int h = 0; h < 2; ++h) {
+    for (int j = 0; j < 8; ++j) m[8 * h + j] = 0.0f;
     if (!run[h].ok) continue;
     const uint32_t gw[4] = {gv[h].x, gv[h].y, gv[h].z, gv[h].w};
     const uint32_t hw[4] = {hv[h].x, hv[h].y, hv[h].z, hv[h].w};
     const uint32_t lw[4] = {lv[h].x, lv[h].y, lv[h].z, lv[h].w};
+    const uint32_t mw[4] = {mv[h].x, mv[h].y, mv[h].z, mv[h].w};
     uint32_t oh[4], ol[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -333,6 +345,12 @@ __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
         const float U = (bf16_at(gw, jj) * rho[h]) * kap[h][jj];
         const float w = __uint_as_float(join_pair_elem<SPLIT>(hw[p], lw[p], o));
         float x = U * f;
+        if (S.fm) {
+          const float m0 = dec_signed(o ? code_hi_f(mw[p]) : code_lo_f(mw[p]), ms_old);
+          x = __builtin_fmaf(S.B1, m0, S.C1 * x);
+          m[8 * h + jj] = x;
+          mx = __builtin_fmaxf(mx, __builtin_fabsf(x));
+        }
         if (S.wd) x = __builtin_fmaf(S.CWD, w, x);
         wb[o] = __float_as_uint(w - x);
       }
@@ -341,9 +359,19 @@ __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
     *reinterpret_cast<uint4*>(X.hi + run[h].e) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
     *reinterpret_cast<uint4*>(X.lo + run[h].e) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
   }
+  if (!S.fm) return;   // uniform
+  float sm, inv;
+  block_scale(row16_max(mx), sm, inv);
+  for (int h = 0; h < 2; ++h) {
+    if (!run[h].ok) continue;
+    uint32_t om[4];
+    for (int p = 0; p < 4; ++p)
+      om[p] = enc_signed(m[8 * h + 2 * p], inv) | (enc_signed(m[8 * h + 2 * p + 1], inv) << 16);
+    *reinterpret_cast<uint4*>(X.mc + run[h].e) = make_uint4(om[0], om[1], om[2], om[3]);
+  }
+  if ((threadIdx.x & 15) == 0 && blk_ok) X.ms[blk] = sm;
 }
 
-// ---- 1-D tensors: v update (stored in the workspace) and item sums of U^2 ---
 __global__ __launch_bounds__(64) void k_f1_stats(FPlan P, FScalars S) {
   uint32_t begin;
   const F1D& X = P.t1[find_end(P.item_end, P.n1, blockIdx.x, begin)];
@@ -450,14 +478,17 @@ __global__ __launch_bounds__(64) void k_f1_apply(FPlan P, FScalars S) {
   const int64_t elem0 = (int64_t)(blockIdx.x - begin) * kItemElems;
   const int lane = threadIdx.x, b = lane >> 4, r = lane & 15;
   const int64_t blk = (elem0 >> 8) + b;
+  const bool blk_ok = blk * kBlock < X.n;
   const float f = *X.f;
-  float v[16];
-  float mx = 0.0f;
+  const float ms_old = (S.fm && blk_ok) ? X.ms[blk] : 0.0f;
+  float v[16], m[16];
+  float mx = 0.0f, mxm = 0.0f;
   for (int half = 0; half < 2; ++half) {
     const int64_t e = elem0 + b * kBlock + half * 128 + r * 8;
     for (int j = 0; j < 8; ++j) {
       const int64_t ej = e + j;
       v[half * 8 + j] = 0.0f;
+      m[half * 8 + j] = 0.0f;
       if (ej >= X.n) continue;
       const float vj = X.v[ej];
       v[half * 8 + j] = vj;
@@ -467,6 +498,12 @@ __global__ __launch_bounds__(64) void k_f1_apply(FPlan P, FScalars S) {
       const uint32_t wbits = join_pair_elem<SPLIT>((uint32_t)X.hi[ej], (uint32_t)X.lo[ej], 0);
       const float w = __uint_as_float(wbits);
       float x = U * f;
+      if (S.fm) {
+        const float m0 = dec_signed(code_lo_f((uint32_t)X.mc[ej]), ms_old);
+        x = __builtin_fmaf(S.B1, m0, S.C1 * x);
+        m[half * 8 + j] = x;
+        mxm = __builtin_fmaxf(mxm, __builtin_fabsf(x));
+      }
       if (S.wd) x = __builtin_fmaf(S.CWD, w, x);
       uint32_t h2, l2;
       split_pair<SPLIT>(__float_as_uint(w - x), 0u, h2, l2);
@@ -474,14 +511,21 @@ __global__ __launch_bounds__(64) void k_f1_apply(FPlan P, FScalars S) {
       X.lo[ej] = (uint16_t)l2;
     }
   }
-  float s, inv;
+  float s, inv, sm = 0.0f, invm = 0.0f;
   block_scale(row16_max(mx), s, inv);
+  if (S.fm) block_scale(row16_max(mxm), sm, invm);   // uniform
   for (int half = 0; half < 2; ++half) {
     const int64_t e = elem0 + b * kBlock + half * 128 + r * 8;
     for (int j = 0; j < 8; ++j)
-      if (e + j < X.n) X.vc[e + j] = (uint16_t)enc_unsigned(v[half * 8 + j], inv);
+      if (e + j < X.n) {
+        X.vc[e + j] = (uint16_t)enc_unsigned(v[half * 8 + j], inv);
+        if (S.fm) X.mc[e + j] = (uint16_t)enc_signed(m[half * 8 + j], invm);
+      }
   }
-  if (r == 0 && blk * kBlock < X.n) X.vs[blk] = s;
+  if (r == 0 && blk_ok) {
+    X.vs[blk] = s;
+    if (S.fm) X.ms[blk] = sm;
+  }
 }
 
 template <int SPLIT>

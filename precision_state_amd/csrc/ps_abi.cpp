@@ -246,15 +246,28 @@ ps_status ps_opt_step_multi(const ps_tensor* tensors, int32_t n_tensors, const p
   g_err[0] = 0;
   if (ps_status s = check_hparams(hp)) return s;
   if (step < 1) return fail(PS_ERR_INVALID_ARG, "step must be >= 1 (got %lld)", (long long)step);
-  std::vector<DevTensor> recs;
-  std::vector<uint32_t> ends;
-  std::vector<DevTensorEx> xrecs;
-  std::vector<uint32_t> xends;
+  // Per-thread buffers and the last step's scalars are kept between calls:
+  // a caller that steps tensor by tensor (one call per gradient hook) makes
+  // many calls with the same hyperparameters and step.
+  thread_local std::vector<DevTensor> recs;
+  thread_local std::vector<uint32_t> ends;
+  thread_local std::vector<DevTensorEx> xrecs;
+  thread_local std::vector<uint32_t> xends;
+  recs.clear();
+  ends.clear();
+  xrecs.clear();
+  xends.clear();
   if (ps_status s = build_active(tensors, n_tensors, hp->split_mode != PS_SPLIT_STOCHASTIC, recs, ends, xrecs, xends))
     return s;
   if (recs.empty() && xrecs.empty()) return PS_OK;
-  StepScalars c;
-  step_scalars(*hp, step, &c);
+  thread_local ps_hparams last_hp;
+  thread_local int64_t last_step = 0;
+  thread_local StepScalars c;
+  if (last_step != step || memcmp(&last_hp, hp, sizeof(ps_hparams)) != 0) {
+    step_scalars(*hp, step, &c);
+    last_hp = *hp;
+    last_step = step;
+  }
   hipStream_t s = (hipStream_t)stream;
   if (!xrecs.empty()) {
     const size_t rb = xrecs.size() * sizeof(DevTensorEx), eb = xends.size() * sizeof(uint32_t);

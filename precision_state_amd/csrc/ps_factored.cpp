@@ -6,6 +6,7 @@
 // the new row EMAs per 256-row chunk, rho[R], kap[C], sums of U^2 per tile,
 // the clip factor. Per 1-D tensor: this step's v[n], sums of U^2 per
 // 1024-element item, the clip factor. Every region starts on 256 bytes.
+#include <cmath>
 #include <cstring>
 #include <vector>
 
@@ -29,6 +30,9 @@ ps_status check_fhparams(const ps_factored_hparams* hp) {
     return fail(PS_ERR_INVALID_ARG, "clip_threshold must be finite and > 0");
   if (!is_finite(hp->weight_decay) || hp->weight_decay < 0)
     return fail(PS_ERR_INVALID_ARG, "weight_decay must be finite and >= 0");
+  if (!is_finite(hp->decay_rate) || hp->decay_rate > 0)
+    return fail(PS_ERR_INVALID_ARG, "decay_rate must be finite and <= 0");
+  if (!is_finite(hp->beta1) || hp->beta1 < 0 || hp->beta1 >= 1) return fail(PS_ERR_INVALID_ARG, "beta1 must be in [0, 1)");
   return PS_OK;
 }
 
@@ -46,8 +50,9 @@ struct Layout {
 };
 
 // Validates the list and lays out the workspace starting at `ws` (which may be
-// NULL when only the size is wanted).
-ps_status plan(const ps_tensor* t, int32_t n, char* ws, Layout& L) {
+// NULL when only the size is wanted). fm: a first moment is kept in m_code /
+// m_scale.
+ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, Layout& L) {
   if (n < 0) return fail(PS_ERR_INVALID_ARG, "n_tensors < 0");
   if (n > 0 && !t) return fail(PS_ERR_INVALID_ARG, "tensors is NULL");
   uint64_t tiles = 0, rc = 0, items = 0, tiles_nf = 0, items2 = 0;
@@ -62,6 +67,7 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, Layout& L) {
     if ((s = check_ptr(x.w_hi, "w_hi", i, 16)) || (s = check_ptr(x.w_lo, "w_lo", i, 16)) ||
         (s = check_ptr(x.grad, "grad", i, 16)))
       return s;
+    if (fm && ((s = check_ptr(x.m_code, "m_code", i, 16)) || (s = check_ptr(x.m_scale, "m_scale", i, 4)))) return s;
     if (x.rows != 0 || x.cols != 0) {
       if (x.rows < 1 || x.cols < 1 || x.rows > 0x7FFFFFFF || x.cols > 0x7FFFFFFF || x.rows * x.cols != x.numel)
         return fail(PS_ERR_SHAPE, "tensor %d: rows * cols != numel", i);
@@ -75,6 +81,10 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, Layout& L) {
       d.ncw = (d.C + kFRowColChunk - 1) / kFRowColChunk;
       d.vec = (d.C % 8) == 0;
       d.flat = d.vec && x.numel < (int64_t(1) << 31);
+      if (fm && !d.flat)
+        return fail(PS_ERR_UNSUPPORTED, "tensor %d: a first moment needs cols %% 8 == 0 and numel < 2^31", i);
+      d.mc = fm ? x.m_code : nullptr;
+      d.ms = fm ? x.m_scale : nullptr;
       d.nitems = d.flat ? (int32_t)((x.numel + kItemElems - 1) / kItemElems) : 0;
       d.npart = d.flat ? d.nitems : d.ntr * d.ntc;
       d.rowpart = (double*)take(sizeof(double) * (size_t)d.ntc * d.R);
@@ -101,6 +111,8 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, Layout& L) {
       if ((s = check_ptr(x.v_code, "v_code", i, 16)) || (s = check_ptr(x.v_scale, "v_scale", i, 4))) return s;
       F1D d{};
       d.hi = x.w_hi; d.lo = x.w_lo; d.g = x.grad; d.vc = x.v_code; d.vs = x.v_scale; d.n = x.numel;
+      d.mc = fm ? x.m_code : nullptr;
+      d.ms = fm ? x.m_scale : nullptr;
       d.nitems = (int32_t)((x.numel + kItemElems - 1) / kItemElems);
       d.v = (float*)take(sizeof(float) * (size_t)x.numel);
       d.upart = (double*)take(sizeof(double) * (size_t)d.nitems);
@@ -126,7 +138,7 @@ ps_status ps_factored_workspace_size(const ps_tensor* tensors, int32_t n_tensors
   if (!bytes) return fail(PS_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = 0;
   Layout L;
-  if (ps_status s = plan(tensors, n_tensors, nullptr, L)) return s;
+  if (ps_status s = plan(tensors, n_tensors, nullptr, false, L)) return s;
   *bytes = L.bytes;
   return PS_OK;
 }
@@ -135,15 +147,16 @@ ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps
                            void* workspace, size_t workspace_bytes, ps_stream_t stream) {
   if (ps_status s = check_fhparams(hp)) return s;
   if (step < 1) return fail(PS_ERR_INVALID_ARG, "step must be >= 1 (got %lld)", (long long)step);
+  const bool fm = hp->beta1 != 0.0;
   Layout L;
-  if (ps_status s = plan(tensors, n_tensors, nullptr, L)) return s;
+  if (ps_status s = plan(tensors, n_tensors, nullptr, fm, L)) return s;
   if (L.t2.empty() && L.t1.empty()) return PS_OK;
   if (!workspace) return fail(PS_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.bytes);
   if (!is_aligned(workspace, 256)) return fail(PS_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
   if (workspace_bytes < L.bytes)
     return fail(PS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.bytes);
   Layout W;
-  if (ps_status s = plan(tensors, n_tensors, (char*)workspace, W)) return s;
+  if (ps_status s = plan(tensors, n_tensors, (char*)workspace, fm, W)) return s;
 
   // one device blob: F2D[n2] | F1D[n1] | tile_end | rc_end | tile_nf_end | item2_end [n2] | item_end[n1]
   const size_t b2 = W.t2.size() * sizeof(F2D), b1 = W.t1.size() * sizeof(F1D);
@@ -179,14 +192,17 @@ ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps
   pl.n_tiles_nf = W.tile_nf_end.empty() ? 0 : W.tile_nf_end.back();
   pl.n_items2 = W.item2_end.empty() ? 0 : W.item2_end.back();
   FScalars sc;
-  sc.B2 = (float)hp->beta2;
-  sc.C2 = (float)(1.0 - hp->beta2);
+  const double beta2_t = hp->decay_rate != 0.0 ? 1.0 - std::pow((double)step, hp->decay_rate) : hp->beta2;
+  sc.B2 = (float)beta2_t;
+  sc.C2 = (float)(1.0 - beta2_t);
   sc.EPS1 = (float)hp->eps1;
   sc.CWD = (float)(hp->lr * hp->weight_decay);
+  sc.B1 = (float)hp->beta1;
+  sc.C1 = (float)(1.0 - hp->beta1);
   sc.lr = hp->lr;
   sc.clip = hp->clip_threshold;
   sc.wd = hp->weight_decay != 0.0;
-  sc.pad = 0;
+  sc.fm = fm;
   return launch_factored(pl, sc, hp->split_mode, s);
 }
 

@@ -91,6 +91,8 @@ struct F2D {
   float* kap;        // [C] 1/sqrt(c_j)
   double* upart;     // [ntr * ntc] sums of U^2 per tile
   float* f;          // clip factor lr / max(1, RMS(U)/d)
+  uint16_t* mc;      // first moment codes (signed kind) or NULL
+  float* ms;         // first moment block scales or NULL
   int32_t R, C, ntr, ntc, nrw, ncw;
   int32_t vec;       // C % 8 == 0: 16-byte row segments
   int32_t flat;      // vec and R*C < 2^31: U^2 and apply passes run over 1024-element items
@@ -108,6 +110,8 @@ struct F1D {
   float* v;          // [n] this step's v (workspace)
   double* upart;     // [nitems] sums of U^2 per 1024-element item
   float* f;
+  uint16_t* mc;      // first moment codes (signed kind) or NULL
+  float* ms;         // first moment block scales or NULL
   int64_t n;
   int32_t nitems;
   int32_t pad;
@@ -115,9 +119,10 @@ struct F1D {
 
 struct FScalars {
   float B2, C2, EPS1, CWD;
+  float B1, C1;      // first moment EMA (fm != 0)
   double lr, clip;
   int32_t wd;
-  int32_t pad;
+  int32_t fm;        // first moment kept in mc / ms
 };
 
 struct FPlan {      // device tables of one factored call

@@ -55,6 +55,8 @@ def dev_state(numel, seed=0, tid=0, rows=0, cols=0, factored=False):
         else:
             st.v_code = T.zeros(numel, dtype=T.int16, device=DEV)
             st.v_scale = T.zeros(nb, dtype=T.float32, device=DEV)
+        st.m_code = T.full((numel,), -32768, dtype=T.int16, device=DEV)   # first moment (read only if beta1 > 0)
+        st.m_scale = T.zeros(nb, dtype=T.float32, device=DEV)
     else:
         st.m_code = T.full((numel,), -32768, dtype=T.int16, device=DEV)   # 0x8000: zero code
         st.m_scale = T.zeros(nb, dtype=T.float32, device=DEV)
@@ -73,6 +75,7 @@ def host_state(numel, seed=0, tid=0, rows=0, factored=False, cols=0):
             st.col = np.zeros(cols, np.float32)
         else:
             _, _, st.vc, st.vs = oracle.zero_moments(numel)
+        st.mc, st.ms, _, _ = oracle.zero_moments(numel)
     else:
         st.mc, st.ms, st.vc, st.vs = oracle.zero_moments(numel)
     return st

@@ -134,8 +134,21 @@ def test_factored_workspace_size_and_validation(ps):
     assert L.ps_factored_step(arr, 2, ctypes.byref(hp), 1, 4096 + 16, 1 << 20, None) == 2
     assert L.ps_factored_step(arr, 2, ctypes.byref(hp), 1, 4096, 100, None) == 7
     assert L.ps_factored_step(arr, 2, ctypes.byref(hp), 0, 4096, 1 << 20, None) == 1
-    for k, v in (("eps1", 0.0), ("clip_threshold", -1.0), ("beta2", 1.0), ("lr", float("inf"))):
+    for k, v in (("eps1", 0.0), ("clip_threshold", -1.0), ("beta2", 1.0), ("lr", float("inf")),
+                 ("decay_rate", 0.5), ("beta1", 1.0), ("beta1", -0.1)):
         h = ps.FactoredHParams(**{k: v}).c()
         assert L.ps_factored_step(arr, 2, ctypes.byref(h), 1, 4096, 1 << 20, None) == 1, k
+    # a first moment needs m_code / m_scale and, for 2-D tensors, cols % 8 == 0
+    h = ps.FactoredHParams(beta1=0.9).c()
+    assert L.ps_factored_step((ps.CTensor * 1)(_frec(ps, m_code=0)), 1, ctypes.byref(h), 1, 4096, 1 << 20,
+                              None) == 1
+    assert L.ps_factored_step((ps.CTensor * 1)(_frec(ps, m_code=160, m_scale=82)), 1, ctypes.byref(h), 1, 4096,
+                              1 << 20, None) == 2
+    odd = (ps.CTensor * 1)(_frec(ps, n=33 * 30, rows=33, cols=30, m_code=160, m_scale=176))
+    assert L.ps_factored_step(odd, 1, ctypes.byref(h), 1, 4096, 1 << 20, None) == 4
+    assert "cols % 8" in ps.last_error()
+    # without a first moment m_code is not read (workspace check fails next)
+    h0 = ps.FactoredHParams().c()
+    assert L.ps_factored_step((ps.CTensor * 1)(_frec(ps, m_code=0)), 1, ctypes.byref(h0), 1, None, 0, None) == 7
     empty = (ps.CTensor * 1)(_frec(ps, grad=0))
     assert L.ps_factored_step(empty, 1, ctypes.byref(hp), 1, None, 0, None) == 0

@@ -22,7 +22,8 @@ import precision_state_amd as ps  # noqa: E402
 
 
 def _ofhp(hp):
-    return oracle.FHParams(hp.split_mode, hp.lr, hp.beta2, hp.eps1, hp.clip_threshold, hp.weight_decay)
+    return oracle.FHParams(hp.split_mode, hp.lr, hp.beta2, hp.eps1, hp.clip_threshold, hp.weight_decay,
+                           hp.decay_rate, hp.beta1)
 
 
 def _ulp_dist(a, b):
@@ -33,7 +34,7 @@ def _ulp_dist(a, b):
     return np.abs(key(a.view(np.uint32)) - key(b.view(np.uint32)))
 
 
-def _compare(d, h, rows, what):
+def _compare(d, h, rows, what, first_moment=False):
     dh = to_host(d)
     wd = oracle.join(dh.hi, dh.lo).view(np.uint32)
     wh = oracle.join(h.hi, h.lo).view(np.uint32)
@@ -48,6 +49,11 @@ def _compare(d, h, rows, what):
         rep["v_code_max_diff"] = int(cd.max(initial=0))
         rep["v_scale_max_ulp"] = int(_ulp_dist(dh.vs, h.vs).max(initial=0))
         assert rep["v_code_max_diff"] <= 1, (what, rep)
+    if first_moment:
+        md = np.abs(dh.mc.astype(np.int64) - h.mc.astype(np.int64))
+        rep["m_code_max_diff"] = int(md.max(initial=0))
+        rep["m_scale_max_ulp"] = int(_ulp_dist(dh.ms, h.ms).max(initial=0))
+        assert rep["m_code_max_diff"] <= 1 and rep["m_scale_max_ulp"] <= 1, (what, rep)
     assert rep["w_max_ulp"] <= 4, (what, rep)
     return rep
 
@@ -69,10 +75,11 @@ def _run(shapes, hp, steps, seed, outlier_p, check=None, zero_grad=()):
             s = shapes[i]
             g = np.zeros(s.numel, np.uint16) if i in zero_grad else host_grad(s.numel, seed, i, t, outlier_p)
             oracle.factored_step(hosts[i], g, s.rows, s.cols, _ofhp(hp), t)
+        print(f"  step {t} done", flush=True)
     torch.cuda.synchronize()
     reps = {}
     for i in check:
-        reps[shapes[i].name] = _compare(devs[i], hosts[i], shapes[i].rows, shapes[i].name)
+        reps[shapes[i].name] = _compare(devs[i], hosts[i], shapes[i].rows, shapes[i].name, hp.beta1 != 0.0)
     for k, v in reps.items():
         print(f"  {k}: {v}", flush=True)
     return reps
@@ -117,3 +124,32 @@ def test_zero_gradient_leaves_weights_identical():
     for d, (h, l) in zip(devs, before):
         assert torch.equal(d.w_hi, h) and torch.equal(d.w_lo, l)
     assert bool(torch.isfinite(devs[0].row_ema).all()) and bool(torch.isfinite(devs[0].col_ema).all())
+
+
+def test_factored_schedule_and_first_moment_double_block_6_steps():
+    """Adafactor's beta2 schedule (1 - t^-0.8) and a first moment (beta1 0.9)
+    on the FLUX double-block shapes (all 24 stepped on the GPU in one call per
+    step), 6 steps, wd 0.01; weights, EMAs, v codes and the first-moment codes
+    and scales against the oracle for two 2-D weights (3072 x 3072 and
+    3072 x 12288) and all 14 1-D tensors (the oracle's encode bisects, so the
+    other 2-D weights are left out to keep the test short)."""
+    shapes = synth.WORKLOADS["flux_double_block"]()
+    hp = ps.FactoredHParams(lr=1e-5, eps1=1e-30, clip_threshold=1.0, weight_decay=0.01, decay_rate=-0.8, beta1=0.9)
+    check = [6, 10] + [i for i, s in enumerate(shapes) if not s.is_2d]
+    reps = _run(shapes, hp, 6, 5, 0.001, check=check)
+    assert len(reps) == 16
+
+
+FM_RAGGED = [synth.Shape("e", 129, 8, 129 * 8), synth.Shape("f", 64, 256, 64 * 256), synth.Shape("g", 100, 3000, 300000),
+             synth.Shape("n", 3, 8, 24), synth.Shape("o", 33, 1032, 33 * 1032), synth.Shape("h", 0, 0, 1),
+             synth.Shape("i", 0, 0, 255), synth.Shape("j", 0, 0, 257), synth.Shape("k", 0, 0, 5000),
+             synth.Shape("m", 0, 0, 3000)]
+
+
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY])
+def test_factored_first_moment_ragged(split_mode):
+    """Partial items and blocks (flattened 2-D tensors ending inside a block,
+    1-D tails), a zero gradient in one 2-D and one 1-D tensor (momentum keeps
+    moving them), with the schedule on."""
+    hp = ps.FactoredHParams(split_mode=split_mode, lr=1e-4, weight_decay=0.01, decay_rate=-0.8, beta1=0.8)
+    _run(FM_RAGGED, hp, 5, 9, 0.01, zero_grad=(3, 9))
