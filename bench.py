@@ -65,10 +65,12 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload, moments="codec"):
+def read_traffic(workload, moments="codec", split="trunc"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
-    tag = "" if moments == "codec" else f"_{moments}"
+    tag = {("codec", "trunc"): "", ("f24", "trunc"): "_f24", ("codec", "stochastic"): "_sr"}.get((moments, split))
+    if tag is None:
+        return None
     path = os.path.join(ROOT, "profiles", f"adam_step_{workload}{tag}_counters.txt")
     if not os.path.exists(path):
         return None
@@ -549,7 +551,7 @@ def main():
 
     alg_bytes = sum(step_bytes(s.numel, st.flags, split != ps.SPLIT_STOCHASTIC) for s, st in zip(shapes, states))
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
-    traffic = None if args.policy or args.split != "trunc" else read_traffic(args.workload, args.moments)
+    traffic = None if args.policy else read_traffic(args.workload, args.moments, args.split)
 
     baseline = None
     if not args.no_cpu_baseline:
@@ -580,7 +582,7 @@ def main():
                              else "bf16 weight + u16 residual") + " + bf16 grad + " +
                             ("u16 m/v codes + fp32 per-256 scales" if args.moments == "codec" else
                              "f24 m/v (upper 3 bytes of fp32)"),
-                   "kernel_ms": kernel_ms, "copy_gbs": copy_gbs},
+                   "kernel_ms": kernel_ms, "copy_gbs": copy_gbs, "kernel_source_sha256": kernel_source_hash()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "cpu_baseline": baseline,
