@@ -32,7 +32,8 @@ class _HP(ctypes.Structure):
 class _FHP(ctypes.Structure):
     _fields_ = [("split_mode", ctypes.c_int32), ("reserved", ctypes.c_int32), ("lr", ctypes.c_double),
                 ("beta2", ctypes.c_double), ("eps1", ctypes.c_double), ("clip_threshold", ctypes.c_double),
-                ("weight_decay", ctypes.c_double), ("decay_rate", ctypes.c_double), ("beta1", ctypes.c_double)]
+                ("weight_decay", ctypes.c_double), ("decay_rate", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("seed", ctypes.c_uint64), ("tensor", ctypes.c_int64)]
 
 
 class _Coeffs(ctypes.Structure):
@@ -68,10 +69,12 @@ class FHParams:
     weight_decay: float = 0.0
     decay_rate: float = 0.0   # < 0: beta2 at update t is 1 - t^decay_rate (Adafactor's schedule)
     beta1: float = 0.0        # > 0: first moment of the clipped update, in mc/ms (signed codec)
+    seed: int = 0             # stochastic rounding only
+    tensor: int = 0           # stochastic rounding only: the tensor's index in the step's list
 
     def c(self):
         return _FHP(self.split_mode, 0, self.lr, self.beta2, self.eps1, self.clip_threshold, self.weight_decay,
-                    self.decay_rate, self.beta1)
+                    self.decay_rate, self.beta1, self.seed, self.tensor)
 
 
 _lib = None

@@ -66,6 +66,8 @@ typedef struct {
   double lr, beta2, eps1, clip_threshold, weight_decay;
   double decay_rate; /* 0: constant beta2; < 0: beta2 at update t is 1 - t^decay_rate [ADAF] */
   double beta1;      /* 0: no first moment; > 0: EMA of the clipped update, kept in the signed codec [ADAF] */
+  uint64_t seed;     /* stochastic rounding: the run's seed */
+  int64_t tensor;    /* stochastic rounding: the tensor's index in the step's list */
 } orc_fhparams;
 
 /* Step-dependent fp32 scalars, each computed in double and rounded once. */
@@ -441,6 +443,19 @@ static float f_first_moment(float x, const uint16_t* mc, const float* ms, int64_
   return m;
 }
 
+/* Master weight and split of the factored step; STOCHASTIC as in the (N)AdamW
+ * step (no residual, random bits keyed on seed, update number, tensor). */
+static float f_join(const uint16_t* hi, const uint16_t* lo, int64_t e, const orc_fhparams* hp) {
+  return join_at(hi, lo, e, hp->split_mode);
+}
+
+static void f_split(float w, uint16_t* hi, uint16_t* lo, int64_t e, const orc_fhparams* hp, int64_t step) {
+  if (hp->split_mode == ORC_SPLIT_STOCHASTIC)
+    hi[e] = orc_sr_bf16(w, orc_sr_rand16(hp->seed, step, hp->tensor, e));
+  else
+    orc_split1(u_of(w), &hi[e], &lo[e], hp->split_mode);
+}
+
 /* Update clipping factor: lr / max(1, RMS(U) / d) with RMS over the tensor. */
 static float clip_factor(double sum_sq, int64_t n, const orc_fhparams* hp) {
   double rms = sqrt(sum_sq / (double)n);
@@ -493,11 +508,11 @@ void orc_factored_2d(uint16_t* hi, uint16_t* lo, const uint16_t* g, float* row, 
     for (int64_t j = 0; j < C; ++j) {
       int64_t e = i * C + j;
       float U = (orc_bf16_to_f32(g[e]) * rho[i]) * kap[j];
-      float w = f_of(orc_join1(hi[e], lo[e], hp->split_mode));
+      float w = f_join(hi, lo, e, hp);
       float x = U * f;
       if (fm) x = f_first_moment(x, mc, ms, e, B1, C1, mbuf);
       if (wd) x = fmaf(CWD, w, x);
-      orc_split1(u_of(w - x), &hi[e], &lo[e], hp->split_mode);
+      f_split(w - x, hi, lo, e, hp, step);
       if (fm && (e % ORC_BLOCK == ORC_BLOCK - 1 || e == R * C - 1)) {
         int64_t b = e / ORC_BLOCK;
         orc_encode_block(mbuf, (int)(e - b * ORC_BLOCK + 1), ORC_SIGNED, mc + b * ORC_BLOCK, &ms[b]);
@@ -531,11 +546,11 @@ void orc_factored_1d(uint16_t* hi, uint16_t* lo, const uint16_t* g, uint16_t* vc
   float f = clip_factor(su, n, hp);
   for (int64_t e = 0; e < n; ++e) {
     float U = orc_bf16_to_f32(g[e]) * (1.0f / sqrtf(v[e]));
-    float w = f_of(orc_join1(hi[e], lo[e], hp->split_mode));
+    float w = f_join(hi, lo, e, hp);
     float x = U * f;
     if (fm) x = f_first_moment(x, mc, ms, e, B1, C1, mbuf);
     if (wd) x = fmaf(CWD, w, x);
-    orc_split1(u_of(w - x), &hi[e], &lo[e], hp->split_mode);
+    f_split(w - x, hi, lo, e, hp, step);
     if (fm && (e % ORC_BLOCK == ORC_BLOCK - 1 || e == n - 1)) {
       int64_t b = e / ORC_BLOCK;
       orc_encode_block(mbuf, (int)(e - b * ORC_BLOCK + 1), ORC_SIGNED, mc + b * ORC_BLOCK, &ms[b]);

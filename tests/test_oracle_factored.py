@@ -237,3 +237,32 @@ def test_first_moment_scales_the_first_step_and_carries_momentum(two_d):
     oracle.factored_step(st_b, np.zeros(n, np.uint16), R, C, FHParams(lr=1e-3, beta1=0.9), 2)
     wb2 = oracle.join(st_b.hi, st_b.lo).astype(np.float64)
     assert np.all(np.abs((wb2 - wb) - 0.9 * d_b) <= 2 * ulp32(wb2) + 2e-3 * np.abs(d_b))
+
+
+@pytest.mark.parametrize("two_d", [True, False])
+def test_stochastic_rounding_brackets_the_residual_step(two_d):
+    """Stochastic rounding in the factored step [ADAF's default]: from a bf16
+    weight (residual 0) the result is the fp32 step's weight rounded up in
+    magnitude exactly when its low 16 bits plus the element's random bits
+    carry; the EMAs and v codes equal the residual step's."""
+    rng = np.random.default_rng(24)
+    R, C = (20, 36) if two_d else (0, 0)
+    n = R * C if two_d else 500
+    hi0 = _bf16(rng.standard_normal(n) * 0.02)
+    g = _bf16(rng.standard_normal(n) * 1e-3)
+
+    def fresh():
+        st = _state2d(R, C) if two_d else _state1d(n)
+        st.hi[:] = hi0
+        return st
+    st_t, st_s = fresh(), fresh()
+    oracle.factored_step(st_t, g, R, C, FHParams(lr=1e-3), 1)
+    oracle.factored_step(st_s, g, R, C, FHParams(lr=1e-3, split_mode=oracle.SPLIT_STOCHASTIC, seed=5, tensor=3), 1)
+    assert np.all(st_s.lo == 0)
+    r = oracle.sr_rand16(5, 1, 3, 0, n).astype(np.uint32)
+    carry = st_t.lo.astype(np.uint32) + r >= 65536
+    assert np.array_equal(st_s.hi, (st_t.hi.astype(np.uint32) + carry).astype(np.uint16))
+    if two_d:
+        assert np.array_equal(st_s.row, st_t.row) and np.array_equal(st_s.col, st_t.col)
+    else:
+        assert np.array_equal(st_s.vc, st_t.vc) and np.array_equal(st_s.vs, st_t.vs)
