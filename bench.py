@@ -183,8 +183,10 @@ def bench_factored(args):
         grads.append(g)
     recs = ps.make_records(states, grads)
     ws = torch.empty(ps.factored_workspace_size(None, records=recs), dtype=torch.uint8, device=dev)
+    split = {"trunc": ps.SPLIT_TRUNC, "nearest_away": ps.SPLIT_NEAREST_AWAY,
+             "stochastic": ps.SPLIT_STOCHASTIC}[args.split]
     hp = ps.FactoredHParams(lr=3.5e-6, beta2=0.999, eps1=1e-30, clip_threshold=1.0, weight_decay=0.0,
-                            decay_rate=args.decay_rate, beta1=args.beta1)
+                            decay_rate=args.decay_rate, beta1=args.beta1, split_mode=split, seed=args.seed)
     stream = torch.cuda.current_stream()
     step = 0
     for _ in range(args.warmup):
@@ -203,7 +205,7 @@ def bench_factored(args):
     step_ms = a.elapsed_time(b) / args.steps
     log(f"[bench] factored: {args.steps} steps, {step_ms:.3f} ms/step (events), {wall * 1e3 / args.steps:.3f} wall")
     n_blocks = sum((s.numel + 255) // 256 for s in shapes)
-    alg = 10 * n_params + ((4 * n_params + 8 * n_blocks) if args.beta1 else 0)
+    alg = (10 if split != ps.SPLIT_STOCHASTIC else 6) * n_params + ((4 * n_params + 8 * n_blocks) if args.beta1 else 0)
     gbs10 = alg / (step_ms * 1e-3) / 1e9
     gbs14 = (alg + 4 * n_params) / (step_ms * 1e-3) / 1e9
     print(json.dumps({
@@ -212,7 +214,7 @@ def bench_factored(args):
         "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl + "_factored", "params": n_params, "tensors": len(shapes), "step_ms": step_ms,
-                   "beta1": args.beta1, "decay_rate": args.decay_rate, "algorithmic_bytes": alg,
+                   "beta1": args.beta1, "decay_rate": args.decay_rate, "split": args.split, "algorithmic_bytes": alg,
                    "gbs_algorithmic": gbs10, "gbs_with_gradient_rereads": gbs14},
         "roofline": {"bound": "hbm", "achieved": gbs10, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs10 / PEAK_HBM_GBS, "traffic": None},

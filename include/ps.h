@@ -157,9 +157,11 @@ typedef struct ps_hparams {
  *               [ADAF], m kept in m_code / m_scale (signed codec, per-256
  *               blocks of the flattened tensor); 2-D tensors then need
  *               cols % 8 == 0 and numel < 2^31 (else PS_ERR_UNSUPPORTED)
- * Constraints: split_mode in {TRUNC, NEAREST_AWAY}; lr >= 0; 0 <= beta2 < 1;
- * eps1 > 0; clip_threshold > 0; weight_decay >= 0; decay_rate <= 0;
- * 0 <= beta1 < 1; all finite. */
+ *   split_mode  TRUNC, NEAREST_AWAY, or STOCHASTIC (no residual; the random
+ *               bits exactly as for ps_hparams, from `seed`, the update
+ *               number and the tensor's index in the list)
+ * Constraints: lr >= 0; 0 <= beta2 < 1; eps1 > 0; clip_threshold > 0;
+ * weight_decay >= 0; decay_rate <= 0; 0 <= beta1 < 1; all finite. */
 typedef struct ps_factored_hparams {
   int32_t split_mode;
   int32_t reserved; /* must be 0 */
@@ -170,6 +172,7 @@ typedef struct ps_factored_hparams {
   double weight_decay;
   double decay_rate;
   double beta1;
+  uint64_t seed;
 } ps_factored_hparams;
 
 /* ps_opt_step_multi - one fused (N)AdamW step over a list of tensors, in ONE

@@ -61,7 +61,8 @@ class CHParams(ctypes.Structure):
 class CFHParams(ctypes.Structure):
     _fields_ = [("split_mode", ctypes.c_int32), ("reserved", ctypes.c_int32), ("lr", ctypes.c_double),
                 ("beta2", ctypes.c_double), ("eps1", ctypes.c_double), ("clip_threshold", ctypes.c_double),
-                ("weight_decay", ctypes.c_double), ("decay_rate", ctypes.c_double), ("beta1", ctypes.c_double)]
+                ("weight_decay", ctypes.c_double), ("decay_rate", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("seed", ctypes.c_uint64)]
 
 
 class COffloadGroup(ctypes.Structure):
@@ -150,10 +151,11 @@ class FactoredHParams:
     weight_decay: float = 0.0
     decay_rate: float = 0.0   # < 0: beta2 of update t is 1 - t^decay_rate (Adafactor's schedule)
     beta1: float = 0.0        # > 0: first moment of the clipped update in m_code / m_scale
+    seed: int = 0             # SPLIT_STOCHASTIC: the random stream's seed
 
     def c(self):
         return CFHParams(self.split_mode, 0, self.lr, self.beta2, self.eps1, self.clip_threshold,
-                         self.weight_decay, self.decay_rate, self.beta1)
+                         self.weight_decay, self.decay_rate, self.beta1, self.seed)
 
 
 @dataclass

@@ -74,6 +74,14 @@ __device__ __forceinline__ float bf16_at(const uint32_t* w, int j) {
   return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
 }
 
+// Stochastic rounding: the random 16 bits of element e of the stream s
+// (output e/4, bits 16*(e % 4)), for element runs that do not start on a
+// multiple of 4.
+__device__ __forceinline__ uint32_t sr_bits1(uint64_t s, int64_t e) {
+  const uint64_t w = splitmix64_mix(s + ((uint64_t)(e >> 2) + 1) * kGolden);
+  return (uint32_t)(w >> (16 * (e & 3))) & 0xFFFFu;
+}
+
 // Sum of a double over the 256 threads of the workgroup, fixed tree.
 __device__ __forceinline__ double block_sum(double x, double* red) {
   red[threadIdx.x] = x;
@@ -304,6 +312,7 @@ __global__ __launch_bounds__(64) void k_f_usq_flat(FPlan P) {
 
 template <int SPLIT>
 __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
+  constexpr bool SR = SPLIT == PS_SPLIT_STOCHASTIC;
   uint32_t begin;
   const F2D& X = P.t2[find_end(P.item2_end, P.n2, blockIdx.x, begin)];
   const uint32_t item = blockIdx.x - begin;
@@ -321,7 +330,7 @@ __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
     if (!run[h].ok) continue;
     gv[h] = *reinterpret_cast<const uint4*>(X.g + run[h].e);
     hv[h] = *reinterpret_cast<const uint4*>(X.hi + run[h].e);
-    lv[h] = *reinterpret_cast<const uint4*>(X.lo + run[h].e);
+    lv[h] = SR ? make_uint4(0u, 0u, 0u, 0u) : *reinterpret_cast<const uint4*>(X.lo + run[h].e);
     if (S.fm) mv[h] = *reinterpret_cast<const uint4*>(X.mc + run[h].e);
     load_kap8(X.kap, run[h].j, kap[h]);
     rho[h] = X.rho[run[h].i];
@@ -336,6 +345,7 @@ __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
     const uint32_t lw[4] = {lv[h].x, lv[h].y, lv[h].z, lv[h].w};
     const uint32_t mw[4] = {mv[h].x, mv[h].y, mv[h].z, mv[h].w};
     uint32_t oh[4], ol[4];
+    uint64_t rnd[2] = {0u, 0u};
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       uint32_t wb[2];
@@ -343,7 +353,7 @@ __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
       for (int o = 0; o < 2; ++o) {
         const int jj = 2 * p + o;
         const float U = (bf16_at(gw, jj) * rho[h]) * kap[h][jj];
-        const float w = __uint_as_float(join_pair_elem<SPLIT>(hw[p], lw[p], o));
+        const float w = SR ? bf16_at(hw, jj) : __uint_as_float(join_pair_elem<SPLIT>(hw[p], lw[p], o));
         float x = U * f;
         if (S.fm) {
           const float m0 = dec_signed(o ? code_hi_f(mw[p]) : code_lo_f(mw[p]), ms_old);
@@ -354,10 +364,16 @@ __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
         if (S.wd) x = __builtin_fmaf(S.CWD, w, x);
         wb[o] = __float_as_uint(w - x);
       }
-      split_pair<SPLIT>(wb[0], wb[1], oh[p], ol[p]);
+      if (SR) {
+        if (p == 0) sr_bits8(sr_stream(S.sr_seed, S.sr_step, X.tid), run[h].e, rnd);
+        const uint64_t q = rnd[p >> 1] >> (32 * (p & 1));
+        oh[p] = sr_pair(wb[0], wb[1], (uint32_t)q & 0xFFFFu, (uint32_t)(q >> 16) & 0xFFFFu);
+      } else {
+        split_pair<SPLIT>(wb[0], wb[1], oh[p], ol[p]);
+      }
     }
     *reinterpret_cast<uint4*>(X.hi + run[h].e) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
-    *reinterpret_cast<uint4*>(X.lo + run[h].e) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+    if (!SR) *reinterpret_cast<uint4*>(X.lo + run[h].e) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
   }
   if (!S.fm) return;   // uniform
   float sm, inv;
@@ -432,6 +448,7 @@ __global__ __launch_bounds__(kClipT) void k_f_clip(FPlan P, FScalars S) {
 // ---- apply to 2-D tensors ----------------------------------------------------
 template <int SPLIT>
 __global__ __launch_bounds__(kT) void k_f_apply(FPlan P, FScalars S) {
+  constexpr bool SR = SPLIT == PS_SPLIT_STOCHASTIC;
   uint32_t begin;
   const F2D& X = P.t2[find_end(P.tile_nf_end, P.n2, blockIdx.x, begin)];
   const uint32_t tile = blockIdx.x - begin;
@@ -444,12 +461,14 @@ __global__ __launch_bounds__(kT) void k_f_apply(FPlan P, FScalars S) {
   for (int j = 0; j < 8; ++j) kap[j] = (c + j < X.C) ? X.kap[c + j] : 0.0f;
   for (int k = 0; k < 8; ++k) {
     const int r = tr * kFTileRows + rg + 8 * k;
-    uint32_t gw[4], hw[4], lw[4];
+    uint32_t gw[4], hw[4], lw[4] = {0u, 0u, 0u, 0u};
     const uint32_t valid = load_row8(X.g, X, r, c, gw);
     if (!valid) continue;
     load_row8(X.hi, X, r, c, hw);
-    load_row8(X.lo, X, r, c, lw);
+    if (!SR) load_row8(X.lo, X, r, c, lw);
     const float rho = X.rho[r];
+    const int64_t e0 = (int64_t)r * X.C + c;   // flattened index of column c
+    const uint64_t srs = SR ? sr_stream(S.sr_seed, S.sr_step, X.tid) : 0u;
     uint32_t oh[4], ol[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -458,21 +477,25 @@ __global__ __launch_bounds__(kT) void k_f_apply(FPlan P, FScalars S) {
       for (int o = 0; o < 2; ++o) {
         const int j = 2 * p + o;
         const float U = (bf16_at(gw, j) * rho) * kap[j];
-        const float w = __uint_as_float(join_pair_elem<SPLIT>(hw[p], lw[p], o));
+        const float w = SR ? bf16_at(hw, j) : __uint_as_float(join_pair_elem<SPLIT>(hw[p], lw[p], o));
         float x = U * f;
         if (S.wd) x = __builtin_fmaf(S.CWD, w, x);
         wb[o] = __float_as_uint(w - x);
       }
-      split_pair<SPLIT>(wb[0], wb[1], oh[p], ol[p]);
+      if (SR)
+        oh[p] = sr_pair(wb[0], wb[1], sr_bits1(srs, e0 + 2 * p), sr_bits1(srs, e0 + 2 * p + 1));
+      else
+        split_pair<SPLIT>(wb[0], wb[1], oh[p], ol[p]);
     }
     store_row8(X.hi, X, r, c, valid, oh);
-    store_row8(X.lo, X, r, c, valid, ol);
+    if (!SR) store_row8(X.lo, X, r, c, valid, ol);
   }
 }
 
 // ---- apply to 1-D tensors and re-encode v --------------------------------------
 template <int SPLIT>
 __global__ __launch_bounds__(64) void k_f1_apply(FPlan P, FScalars S) {
+  constexpr bool SR = SPLIT == PS_SPLIT_STOCHASTIC;
   uint32_t begin;
   const F1D& X = P.t1[find_end(P.item_end, P.n1, blockIdx.x, begin)];
   const int64_t elem0 = (int64_t)(blockIdx.x - begin) * kItemElems;
@@ -495,7 +518,7 @@ __global__ __launch_bounds__(64) void k_f1_apply(FPlan P, FScalars S) {
       mx = __builtin_fmaxf(mx, vj);
       const float g = __uint_as_float((uint32_t)X.g[ej] << 16);
       const float U = g * (1.0f / __builtin_sqrtf(vj));
-      const uint32_t wbits = join_pair_elem<SPLIT>((uint32_t)X.hi[ej], (uint32_t)X.lo[ej], 0);
+      const uint32_t wbits = SR ? (uint32_t)X.hi[ej] << 16 : join_pair_elem<SPLIT>((uint32_t)X.hi[ej], (uint32_t)X.lo[ej], 0);
       const float w = __uint_as_float(wbits);
       float x = U * f;
       if (S.fm) {
@@ -505,10 +528,15 @@ __global__ __launch_bounds__(64) void k_f1_apply(FPlan P, FScalars S) {
         mxm = __builtin_fmaxf(mxm, __builtin_fabsf(x));
       }
       if (S.wd) x = __builtin_fmaf(S.CWD, w, x);
-      uint32_t h2, l2;
-      split_pair<SPLIT>(__float_as_uint(w - x), 0u, h2, l2);
-      X.hi[ej] = (uint16_t)h2;
-      X.lo[ej] = (uint16_t)l2;
+      if (SR) {
+        const uint32_t rb = sr_bits1(sr_stream(S.sr_seed, S.sr_step, X.tid), ej);
+        X.hi[ej] = (uint16_t)((__float_as_uint(w - x) + rb) >> 16);
+      } else {
+        uint32_t h2, l2;
+        split_pair<SPLIT>(__float_as_uint(w - x), 0u, h2, l2);
+        X.hi[ej] = (uint16_t)h2;
+        X.lo[ej] = (uint16_t)l2;
+      }
     }
   }
   float s, inv, sm = 0.0f, invm = 0.0f;
@@ -547,6 +575,7 @@ ps_status launch_all(const FPlan& P, const FScalars& S, hipStream_t s) {
 
 ps_status launch_factored(const FPlan& plan, const FScalars& sc, int split_mode, hipStream_t s) {
   if (split_mode == PS_SPLIT_NEAREST_AWAY) return launch_all<PS_SPLIT_NEAREST_AWAY>(plan, sc, s);
+  if (split_mode == PS_SPLIT_STOCHASTIC) return launch_all<PS_SPLIT_STOCHASTIC>(plan, sc, s);
   return launch_all<PS_SPLIT_TRUNC>(plan, sc, s);
 }
 

@@ -20,7 +20,8 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 ps_status check_fhparams(const ps_factored_hparams* hp) {
   if (!hp) return fail(PS_ERR_INVALID_ARG, "factored hparams is NULL");
-  if (hp->split_mode != PS_SPLIT_TRUNC && hp->split_mode != PS_SPLIT_NEAREST_AWAY)
+  if (hp->split_mode != PS_SPLIT_TRUNC && hp->split_mode != PS_SPLIT_NEAREST_AWAY &&
+      hp->split_mode != PS_SPLIT_STOCHASTIC)
     return fail(PS_ERR_INVALID_ARG, "unknown split_mode %d", hp->split_mode);
   if (hp->reserved != 0) return fail(PS_ERR_INVALID_ARG, "reserved must be 0");
   if (!is_finite(hp->lr) || hp->lr < 0) return fail(PS_ERR_INVALID_ARG, "lr must be finite and >= 0");
@@ -52,7 +53,7 @@ struct Layout {
 // Validates the list and lays out the workspace starting at `ws` (which may be
 // NULL when only the size is wanted). fm: a first moment is kept in m_code /
 // m_scale.
-ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, Layout& L) {
+ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, Layout& L) {
   if (n < 0) return fail(PS_ERR_INVALID_ARG, "n_tensors < 0");
   if (n > 0 && !t) return fail(PS_ERR_INVALID_ARG, "tensors is NULL");
   uint64_t tiles = 0, rc = 0, items = 0, tiles_nf = 0, items2 = 0;
@@ -64,7 +65,7 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, Layout& L) {
     if (x.flags || x.reserved) return fail(PS_ERR_UNSUPPORTED, "tensor %d: storage flags are not supported here", i);
     if (x.numel == 0 || x.grad == nullptr) continue;
     ps_status s;
-    if ((s = check_ptr(x.w_hi, "w_hi", i, 16)) || (s = check_ptr(x.w_lo, "w_lo", i, 16)) ||
+    if ((s = check_ptr(x.w_hi, "w_hi", i, 16)) || (residual && (s = check_ptr(x.w_lo, "w_lo", i, 16))) ||
         (s = check_ptr(x.grad, "grad", i, 16)))
       return s;
     if (fm && ((s = check_ptr(x.m_code, "m_code", i, 16)) || (s = check_ptr(x.m_scale, "m_scale", i, 4)))) return s;
@@ -85,6 +86,7 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, Layout& L) {
         return fail(PS_ERR_UNSUPPORTED, "tensor %d: a first moment needs cols %% 8 == 0 and numel < 2^31", i);
       d.mc = fm ? x.m_code : nullptr;
       d.ms = fm ? x.m_scale : nullptr;
+      d.tid = (uint32_t)i;
       d.nitems = d.flat ? (int32_t)((x.numel + kItemElems - 1) / kItemElems) : 0;
       d.npart = d.flat ? d.nitems : d.ntr * d.ntc;
       d.rowpart = (double*)take(sizeof(double) * (size_t)d.ntc * d.R);
@@ -113,6 +115,7 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, Layout& L) {
       d.hi = x.w_hi; d.lo = x.w_lo; d.g = x.grad; d.vc = x.v_code; d.vs = x.v_scale; d.n = x.numel;
       d.mc = fm ? x.m_code : nullptr;
       d.ms = fm ? x.m_scale : nullptr;
+      d.tid = (uint32_t)i;
       d.nitems = (int32_t)((x.numel + kItemElems - 1) / kItemElems);
       d.v = (float*)take(sizeof(float) * (size_t)x.numel);
       d.upart = (double*)take(sizeof(double) * (size_t)d.nitems);
@@ -138,7 +141,7 @@ ps_status ps_factored_workspace_size(const ps_tensor* tensors, int32_t n_tensors
   if (!bytes) return fail(PS_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = 0;
   Layout L;
-  if (ps_status s = plan(tensors, n_tensors, nullptr, false, L)) return s;
+  if (ps_status s = plan(tensors, n_tensors, nullptr, false, false, L)) return s;
   *bytes = L.bytes;
   return PS_OK;
 }
@@ -148,15 +151,16 @@ ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps
   if (ps_status s = check_fhparams(hp)) return s;
   if (step < 1) return fail(PS_ERR_INVALID_ARG, "step must be >= 1 (got %lld)", (long long)step);
   const bool fm = hp->beta1 != 0.0;
+  const bool residual = hp->split_mode != PS_SPLIT_STOCHASTIC;
   Layout L;
-  if (ps_status s = plan(tensors, n_tensors, nullptr, fm, L)) return s;
+  if (ps_status s = plan(tensors, n_tensors, nullptr, fm, residual, L)) return s;
   if (L.t2.empty() && L.t1.empty()) return PS_OK;
   if (!workspace) return fail(PS_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.bytes);
   if (!is_aligned(workspace, 256)) return fail(PS_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
   if (workspace_bytes < L.bytes)
     return fail(PS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.bytes);
   Layout W;
-  if (ps_status s = plan(tensors, n_tensors, (char*)workspace, fm, W)) return s;
+  if (ps_status s = plan(tensors, n_tensors, (char*)workspace, fm, residual, W)) return s;
 
   // one device blob: F2D[n2] | F1D[n1] | tile_end | rc_end | tile_nf_end | item2_end [n2] | item_end[n1]
   const size_t b2 = W.t2.size() * sizeof(F2D), b1 = W.t1.size() * sizeof(F1D);
@@ -203,6 +207,9 @@ ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps
   sc.clip = hp->clip_threshold;
   sc.wd = hp->weight_decay != 0.0;
   sc.fm = fm;
+  sc.sr_seed = residual ? 0 : hp->seed;
+  sc.sr_step = (uint32_t)step;
+  sc.pad = 0;
   return launch_factored(pl, sc, hp->split_mode, s);
 }
 

@@ -98,6 +98,8 @@ struct F2D {
   int32_t flat;      // vec and R*C < 2^31: U^2 and apply passes run over 1024-element items
   int32_t nitems;    // flat: items of 1024 elements
   int32_t npart;     // entries of upart (nitems if flat, else ntr * ntc)
+  uint32_t tid;      // index in the caller's list (stochastic rounding stream key)
+  uint32_t pad;
 };
 
 // 1-D tensor of a factored step (second moment kept in the uint16 codec).
@@ -114,7 +116,7 @@ struct F1D {
   float* ms;         // first moment block scales or NULL
   int64_t n;
   int32_t nitems;
-  int32_t pad;
+  uint32_t tid;      // index in the caller's list (stochastic rounding stream key)
 };
 
 struct FScalars {
@@ -123,6 +125,9 @@ struct FScalars {
   double lr, clip;
   int32_t wd;
   int32_t fm;        // first moment kept in mc / ms
+  uint64_t sr_seed;  // stochastic rounding: the run's seed
+  uint32_t sr_step;  // stochastic rounding: the update number mod 2^32
+  uint32_t pad;
 };
 
 struct FPlan {      // device tables of one factored call

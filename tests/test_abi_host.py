@@ -147,8 +147,15 @@ def test_factored_workspace_size_and_validation(ps):
     odd = (ps.CTensor * 1)(_frec(ps, n=33 * 30, rows=33, cols=30, m_code=160, m_scale=176))
     assert L.ps_factored_step(odd, 1, ctypes.byref(h), 1, 4096, 1 << 20, None) == 4
     assert "cols % 8" in ps.last_error()
+    # stochastic rounding keeps no residual: w_lo may be NULL
+    hs = ps.FactoredHParams(split_mode=ps.SPLIT_STOCHASTIC).c()
+    assert L.ps_factored_step((ps.CTensor * 1)(_frec(ps, w_lo=0, row_ema=0)), 1, ctypes.byref(hs), 1, 4096,
+                              1 << 20, None) == 1
+    assert "row_ema" in ps.last_error()
+    assert L.ps_factored_step((ps.CTensor * 1)(_frec(ps, w_lo=0, row_ema=0)), 1, ctypes.byref(h0 := ps.FactoredHParams().c()),
+                              1, 4096, 1 << 20, None) == 1
+    assert "w_lo" in ps.last_error()
     # without a first moment m_code is not read (workspace check fails next)
-    h0 = ps.FactoredHParams().c()
     assert L.ps_factored_step((ps.CTensor * 1)(_frec(ps, m_code=0)), 1, ctypes.byref(h0), 1, None, 0, None) == 7
     empty = (ps.CTensor * 1)(_frec(ps, grad=0))
     assert L.ps_factored_step(empty, 1, ctypes.byref(hp), 1, None, 0, None) == 0

@@ -21,9 +21,9 @@ if not torch.cuda.is_available():
 import precision_state_amd as ps  # noqa: E402
 
 
-def _ofhp(hp):
+def _ofhp(hp, tensor=0):
     return oracle.FHParams(hp.split_mode, hp.lr, hp.beta2, hp.eps1, hp.clip_threshold, hp.weight_decay,
-                           hp.decay_rate, hp.beta1)
+                           hp.decay_rate, hp.beta1, hp.seed, tensor)
 
 
 def _ulp_dist(a, b):
@@ -74,7 +74,7 @@ def _run(shapes, hp, steps, seed, outlier_p, check=None, zero_grad=()):
         for i in check:
             s = shapes[i]
             g = np.zeros(s.numel, np.uint16) if i in zero_grad else host_grad(s.numel, seed, i, t, outlier_p)
-            oracle.factored_step(hosts[i], g, s.rows, s.cols, _ofhp(hp), t)
+            oracle.factored_step(hosts[i], g, s.rows, s.cols, _ofhp(hp, i), t)
         print(f"  step {t} done", flush=True)
     torch.cuda.synchronize()
     reps = {}
@@ -102,12 +102,14 @@ RAGGED = [synth.Shape("a", 1, 1, 1), synth.Shape("b", 1, 300, 300), synth.Shape(
           synth.Shape("m", 0, 0, 3000)]
 
 
-@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY])
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY, ps.SPLIT_STOCHASTIC])
 @pytest.mark.parametrize("wd", [0.0, 0.01])
 def test_factored_ragged_shapes(split_mode, wd):
     """Partial tiles, C % 8 != 0 rows, 1xC and Rx1 tensors, partial codec
-    blocks, and all-zero gradients in one 2-D and one 1-D tensor."""
-    hp = ps.FactoredHParams(split_mode=split_mode, lr=1e-4, weight_decay=wd)
+    blocks, and all-zero gradients in one 2-D and one 1-D tensor; stochastic
+    rounding draws the same stream as the oracle in the flat, tiled and 1-D
+    kernels."""
+    hp = ps.FactoredHParams(split_mode=split_mode, lr=1e-4, weight_decay=wd, seed=4242)
     _run(RAGGED, hp, 5, 3, 0.01, zero_grad=(11, 12))
 
 
@@ -146,10 +148,10 @@ FM_RAGGED = [synth.Shape("e", 129, 8, 129 * 8), synth.Shape("f", 64, 256, 64 * 2
              synth.Shape("m", 0, 0, 3000)]
 
 
-@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY])
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY, ps.SPLIT_STOCHASTIC])
 def test_factored_first_moment_ragged(split_mode):
     """Partial items and blocks (flattened 2-D tensors ending inside a block,
     1-D tails), a zero gradient in one 2-D and one 1-D tensor (momentum keeps
     moving them), with the schedule on."""
-    hp = ps.FactoredHParams(split_mode=split_mode, lr=1e-4, weight_decay=0.01, decay_rate=-0.8, beta1=0.8)
+    hp = ps.FactoredHParams(split_mode=split_mode, lr=1e-4, weight_decay=0.01, decay_rate=-0.8, beta1=0.8, seed=99)
     _run(FM_RAGGED, hp, 5, 9, 0.01, zero_grad=(3, 9))
