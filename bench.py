@@ -65,6 +65,41 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+VALU_ISSUE_PEAK = 256 * 4 * 2.4e9 / 4   # wave64 VALU instructions/s: 256 CUs x 4 SIMDs, 4 cycles each, 2.4 GHz
+
+
+def read_valu(workload):
+    """VALU wave-instructions and transcendental instructions per launch of the
+    step kernel from the committed counter summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"adam_step_{workload}_valu.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["valu_insts_per_launch"]), float(kv["valu_trans_insts_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def gpu_clocks():
+    """Current clocks from rocm-smi (a child process), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        card = d[sorted(d)[0]]
+        return {k: v for k, v in card.items() if "clock" in k.lower()}
+    except Exception:
+        return None
+
+
 def read_traffic(workload, moments="codec", split="trunc"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
@@ -554,6 +589,15 @@ def main():
     alg_bytes = sum(step_bytes(s.numel, st.flags, split != ps.SPLIT_STOCHASTIC) for s, st in zip(shapes, states))
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
     traffic = None if args.policy else read_traffic(args.workload, args.moments, args.split)
+    valu = None
+    if not args.policy and args.moments == "codec" and args.split == "trunc":
+        vi = read_valu(args.workload)
+        if vi is not None:
+            slots = vi[0] + 3 * vi[1]     # transcendental VALU instructions issue at a quarter of the rate
+            valu = {"wave_instructions_per_launch": vi[0], "transcendental_per_launch": vi[1],
+                    "issue_slots_per_launch": slots, "peak_issue_slots_per_s": VALU_ISSUE_PEAK,
+                    "frac": slots / (kernel_ms * 1e-3) / VALU_ISSUE_PEAK}
+    clocks = gpu_clocks()
 
     baseline = None
     if not args.no_cpu_baseline:
@@ -584,7 +628,10 @@ def main():
                              else "bf16 weight + u16 residual") + " + bf16 grad + " +
                             ("u16 m/v codes + fp32 per-256 scales" if args.moments == "codec" else
                              "f24 m/v (upper 3 bytes of fp32)"),
-                   "kernel_ms": kernel_ms, "copy_gbs": copy_gbs, "kernel_source_sha256": kernel_source_hash()},
+                   "kernel_ms": kernel_ms, "copy_gbs": copy_gbs, "kernel_source_sha256": kernel_source_hash(),
+                   "gbs_18B_per_param": 18 * n_params / (kernel_ms * 1e-3) / 1e9,
+                   "bytes_per_param_algorithmic": alg_bytes / n_params,
+                   "valu_issue": valu, "gpu_clocks_after_timing": clocks},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "cpu_baseline": baseline,

@@ -64,6 +64,7 @@ def test_invalid_arguments_rejected_on_host(ps):
     assert _call(ps, [_rec(ps)], hp=ps.HParams(lr=float("nan"))) == 1
     assert _call(ps, [_rec(ps)], hp=ps.HParams(weight_decay=-1.0)) == 1
     assert _call(ps, [_rec(ps, numel=-1)]) == 3
+    assert _call(ps, [_rec(ps, numel=(1 << 40) + 1)]) == 3
     assert _call(ps, [_rec(ps, w_lo=0)]) == 1
     assert "w_lo" in ps.last_error()
     assert _call(ps, [_rec(ps, m_code=66)]) == 2

@@ -342,3 +342,34 @@ def test_storage_flags_match_oracle(split_mode, large):
             if not fl & (ps.TENSOR_FP32_MOMENTS | ps.TENSOR_F24_MOMENTS):
                 assert np.array_equal(f32(d.m_scale).view(np.uint32), h["ms"].view(np.uint32)), (count, i, "ms")
                 assert np.array_equal(f32(d.v_scale).view(np.uint32), h["vs"].view(np.uint32)), (count, i, "vs")
+
+
+# ---------------------------------------------------------------------------
+# maximum sizes: a tensor beyond 2^31 elements (64-bit element offsets)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_STOCHASTIC])
+def test_tensor_beyond_2_31_elements_sampled(split_mode):
+    """One tensor of 2^31 + 4097 elements (about 21.5 GB of state), 2 NAdamW
+    steps in one launch each; sampled 256-blocks, most of them past element
+    2^31, and the partial last block against the oracle."""
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+    n = (1 << 31) + 4097
+    free, _ = torch.cuda.mem_get_info()
+    if free < 40 * 2**30:
+        pytest.skip(f"needs ~22 GiB of device memory, {free / 2**30:.0f} GiB free")
+    shapes = [synth.Shape("big", 0, 0, n)]
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=1e-4, weight_decay=0.01, split_mode=split_mode, seed=17)
+    dev = [dev_state(n, 3, 0)]
+    for t in (1, 2):
+        g = dev_grad(n, 3, 0, t)
+        ps.opt_step_multi(dev, [g], hp, t)
+        del g
+    torch.cuda.synchronize()
+    nblk = check_sampled_blocks(shapes, dev, hp, 2, 3, per_tensor=64)
+    print(f"  {nblk} sampled blocks bit-exact", flush=True)
+    del dev
+    gc.collect()
+    torch.cuda.empty_cache()
