@@ -109,8 +109,12 @@ __device__ __forceinline__ float code_hi_f(uint32_t c2) { return __uint_as_float
 // Signed decode of one code given as (2^23 + c): sign(k) * D(|k|) * s, k = c - 32768.
 __device__ __forceinline__ float dec_signed(float magic_c, float s) {
   float k = magic_c - (kMagic + 32768.0f);  // exact
-  float t = dmag(k, kK15);                  // (k*K)^2 is sign-free
-  return t * __builtin_copysignf(s, k);
+  // t*|t| squares the magnitude and keeps the sign, so sign(k) * D(|k|) * s
+  // comes out of the same three roundings with no separate sign step.
+  float t = k * kK15;
+  t = t * __builtin_fabsf(t);
+  t = t * __builtin_fabsf(t);
+  return t * s;
 }
 
 __device__ __forceinline__ float dec_unsigned(float magic_c, float s) {
@@ -129,11 +133,11 @@ __device__ __forceinline__ uint32_t code_mag(float x, float y) {
   const float q = (float)Q;
   float z = __builtin_fmaf(y, q, kMagic);  // 2^23 + rint(y*Q)
   float kf = z - kMagic;
-  float dl = __builtin_fmaf(y, q, -kf);    // exact sign of y*Q - k0
-  bool up = dl >= 0.0f;
-  float T = dmag(kf + (up ? 0.5f : -0.5f), K);
+  // y*Q - k0, exact; +0 when equal (never -0), so its sign bit is "below k0"
+  float dl = __builtin_fmaf(y, q, -kf);
+  float T = dmag(kf + __builtin_copysignf(0.5f, dl), K);
   uint32_t k0 = __float_as_uint(z) - 0x4B000000u;
-  return k0 - (up ? 0u : 1u) + (x >= T ? 1u : 0u);
+  return k0 - (__float_as_uint(dl) >> 31) + (x >= T ? 1u : 0u);
 }
 
 __device__ __forceinline__ float fast_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
@@ -157,7 +161,9 @@ __device__ __forceinline__ float sqrt_rn_fast(float v) {
 __device__ __forceinline__ uint32_t enc_signed(float m, float inv) {
   float x = __builtin_fabsf(m) * inv;
   uint32_t k = code_mag<32767>(x, fast_sqrt(fast_sqrt(x)));
-  return m < 0.0f ? 32768u - k : 32768u + k;
+  // 32768 - k for m < 0 (k = 0 for -0), else 32768 + k: negate k by the sign mask
+  const uint32_t neg = (uint32_t)((int32_t)__float_as_uint(m) >> 31);
+  return 32768u + ((k ^ neg) - neg);
 }
 
 // Unsigned code of v >= 0 given inv = 1/scale and y ~ (v*inv)^(1/4).
@@ -193,6 +199,23 @@ __device__ __forceinline__ float row32_max(float x) {
   x = row16_max(x);
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+// The same maxima on the bit patterns of non-negative floats (their unsigned
+// order is the float order): the max folds into one DPP instruction per step
+// and needs no NaN quieting.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t row32_max_u32(uint32_t x) {
+  x = __builtin_elementwise_max(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = __builtin_elementwise_max(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = __builtin_elementwise_max(x, dpp_u32<0x141>(x));  // row_half_mirror
+  x = __builtin_elementwise_max(x, dpp_u32<0x140>(x));  // row_mirror
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return __builtin_elementwise_max((uint32_t)p[0], (uint32_t)p[1]);
 }
 
 // Block scale from the block max: blocks below the smallest normal are

@@ -12,9 +12,10 @@
 // Order of memory traffic within a wave: gradient and moment codes first
 // (they decide the block scales), the weight words only once the scales are
 // known, just before the update needs them. Spreading each wave's traffic
-// this way, with 8 elements per lane (77 VGPRs, 6 waves per SIMD), measured
-// markedly faster than loading every stream up front with 16 elements per
-// lane.
+// this way, with 8 elements per lane, measured markedly faster than loading
+// every stream up front with 16 elements per lane. The block maxima are taken
+// on float bit patterns (one fused DPP max per step); the occupancy hint keeps
+// the NAdam kernels at 70 VGPRs (7 waves per SIMD) without spills.
 //
 // Per element the kernel reads hi, lo, grad, m_code, v_code (10 bytes) and
 // writes hi, lo, m_code, v_code (8 bytes); per block it reads and writes the
@@ -151,7 +152,7 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
   // Decode, EMA, block maxima. Missing tail elements have g = 0 and
   // zero-coded moments, so m = v = 0 and they never raise a maximum.
   float m[8], v[8];
-  float mx_m = 0.0f, mx_v = 0.0f;
+  uint32_t mx_m = 0u, mx_v = 0u;   // maxima of |m| and v as bit patterns (v >= 0, never -0)
   uint32_t tiny = 0xFFFFFFFFu;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -162,8 +163,8 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
     const float v0 = dec_unsigned(odd ? code_hi_f(vw[w]) : code_lo_f(vw[w]), vs_old);
     m[j] = __builtin_fmaf(c.B1, m0, c.C1 * g);
     v[j] = __builtin_fmaf(c.B2, v0, c.C2 * (g * g));
-    mx_m = __builtin_fmaxf(mx_m, __builtin_fabsf(m[j]));
-    mx_v = __builtin_fmaxf(mx_v, v[j]);
+    mx_m = __builtin_elementwise_max(mx_m, __float_as_uint(m[j]) & 0x7FFFFFFFu);
+    mx_v = __builtin_elementwise_max(mx_v, __float_as_uint(v[j]));
     tiny = __builtin_elementwise_min(tiny, __float_as_uint(v[j]) - 1u);
   }
   // 0 < v < 2^-96 anywhere in the wave: the fast square root's residual test
@@ -172,8 +173,8 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
 
   // Block scales (32-lane maximum).
   float sm, inv_m, sv, inv_v;
-  block_scale(row32_max(mx_m), sm, inv_m);
-  block_scale(row32_max(mx_v), sv, inv_v);
+  block_scale(__uint_as_float(row32_max_u32(mx_m)), sm, inv_m);
+  block_scale(__uint_as_float(row32_max_u32(mx_v)), sv, inv_v);
   const float sq_inv_v = fast_sqrt(inv_v);
 
   if (slow_sqrt)
@@ -197,7 +198,7 @@ __device__ __forceinline__ uint32_t item_end(const TBL& t, int i) { return t.ite
 // stride over the items. The tensor of the item is found by a wave-uniform
 // binary search over the prefix ends (scalar loads).
 template <class TBL, int ALGO, bool WD, int SPLIT>
-__global__ __launch_bounds__(64) void k_adam_step(TBL tbl, StepScalars c) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(7))) void k_adam_step(TBL tbl, StepScalars c) {
   const uint32_t item = blockIdx.x;
   int lo = 0, hi = tbl.n - 1;
   while (lo < hi) {
