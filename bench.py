@@ -418,9 +418,10 @@ def bench_offload(args, n_blocks=57):
     log(f"[bench] pinned-copy ceiling: H2D {pcie['h2d']:.1f} GB/s, D2H {pcie['d2h']:.1f} GB/s, "
         f"both at once {pcie['dup_h2d']:.1f} + {pcie['dup_d2h']:.1f} GB/s")
     plan = ps.OffloadPlan(groups)
-    h2d, d2h = plan.bytes()
     n_params = n_blocks * synth.total_params(shapes)
-    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6)
+    sr = args.split == "stochastic"
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, split_mode=ps.SPLIT_STOCHASTIC if sr else ps.SPLIT_TRUNC,
+                    seed=args.seed)
     stream = torch.cuda.current_stream()
     step = 0
     for _ in range(args.warmup):
@@ -433,6 +434,7 @@ def bench_offload(args, n_blocks=57):
         plan.run(hp, step, stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
+    h2d, d2h = plan.bytes()       # of the last run (no residuals under stochastic rounding)
     log(f"[bench] offload: {n_blocks} blocks, {wall * 1e3:.1f} ms/step, PCIe {h2d / wall / 1e9:.1f} GB/s up + "
         f"{d2h / wall / 1e9:.1f} GB/s down")
     print(json.dumps({
@@ -440,10 +442,11 @@ def bench_offload(args, n_blocks=57):
         "value": n_params / wall, "unit": "params/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"flux_double_block_x{n_blocks}_offload", "params": n_params,
+        "config": {"workload": f"flux_double_block_x{n_blocks}_offload", "params": n_params, "split": args.split,
                    "host_state_sets": H, "pcie_h2d_gbs": h2d / wall / 1e9, "pcie_d2h_gbs": d2h / wall / 1e9,
                    "pcie_total_gbs": (h2d + d2h) / wall / 1e9, "h2d_bytes_per_step": h2d,
-                   "hbm_gbs_kernel_18B": 18 * n_params / wall / 1e9, "pinned_copy_ceiling_gbs": pcie},
+                   "hbm_gbs_kernel_18B": (14 if sr else 18) * n_params / wall / 1e9,
+                   "pinned_copy_ceiling_gbs": pcie},
         "roofline": {"bound": "pcie", "achieved": (h2d + d2h) / wall / 1e9, "peak": 128.0, "unit": "GB/s",
                      "frac": (h2d + d2h) / wall / 1e9 / 128.0, "traffic": None},
         "cpu_baseline": None}), flush=True)

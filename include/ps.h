@@ -262,7 +262,13 @@ ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps
  * to a device staging slot on an upload stream, stepped on `stream`, and
  * copied back on a download stream, with two slots so that uploads of k+1
  * and downloads of k-1 overlap the step of k. The results are bit-identical
- * to ps_opt_step_multi on device-resident state. */
+ * to ps_opt_step_multi on device-resident state (for stochastic rounding:
+ * on the concatenation of the groups' tensor lists, whose positions key the
+ * random streams).
+ * Stochastic rounding [NADAM, opening post: the stochastic updates used when
+ * the residual does not fit in host memory]: runs with split_mode STOCHASTIC
+ * move no residuals; w_lo may then be NULL, and a plan with any NULL w_lo
+ * accepts only such runs (PS_ERR_INVALID_ARG otherwise). */
 typedef struct ps_offload_group {
   const ps_tensor* tensors;
   int32_t n_tensors;
@@ -278,7 +284,8 @@ ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_group
  * call returns once all work is queued; host state is final when `stream`
  * completes). */
 ps_status ps_offload_run(ps_offload_plan* plan, const ps_hparams* hp, int64_t step, ps_stream_t stream);
-/* Bytes each run moves host->device and device->host. */
+/* Bytes the most recent run moved host->device and device->host (before
+ * any run: the bytes of a run with residuals). */
 ps_status ps_offload_bytes(const ps_offload_plan* plan, uint64_t* h2d_bytes, uint64_t* d2h_bytes);
 /* Waits for outstanding work and frees everything the plan owns. */
 ps_status ps_offload_plan_destroy(ps_offload_plan* plan);

@@ -1,6 +1,8 @@
 // ps_offload.cpp - host-offload pipeline for the fused (N)AdamW step [NADAM,
 // opening post: the moments (and here the Kahan residuals) stay in host memory
-// and cross PCIe every step; KAHAN: only the 16 residual bits travel].
+// and cross PCIe every step; KAHAN: only the 16 residual bits travel; with
+// stochastic rounding, the pages' setting when host memory is short, no
+// residual exists and only the moments travel].
 //
 // Two device staging slots hold one group's residuals, codes and scales each.
 // Group k uses slot k % 2:
@@ -24,7 +26,8 @@ struct ps_offload_plan {
     size_t bytes;
   };
   struct Group {
-    std::vector<Copy> copies;          // same list for both directions
+    std::vector<Copy> copies;          // codes and scales, same list for both directions
+    std::vector<Copy> lo_copies;       // residuals (skipped under stochastic rounding)
     size_t table_off[2] = {0, 0};      // device table of this group for slot 0 / 1
     int32_t n_active = 0;
     uint32_t total_items = 0;
@@ -36,7 +39,10 @@ struct ps_offload_plan {
   hipStream_t up = nullptr, down = nullptr;
   hipEvent_t in_ev[2] = {nullptr, nullptr}, done_ev[2] = {nullptr, nullptr}, out_ev[2] = {nullptr, nullptr};
   hipEvent_t start_ev = nullptr, end_ev = nullptr;
-  uint64_t bytes_per_dir = 0;
+  uint64_t bytes_per_dir = 0;          // residual modes
+  uint64_t lo_bytes_per_dir = 0;       // of which residuals
+  uint64_t last_bytes_per_dir = 0;     // the most recent run
+  bool has_residual = true;            // every active tensor has w_lo
 };
 
 namespace ps {
@@ -105,6 +111,7 @@ ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_group
   // v scales, tensors in order, 256-byte aligned) and its copy list.
   std::vector<std::vector<DevTensor>> recs(n_groups);
   std::vector<std::vector<uint32_t>> ends(n_groups);
+  uint32_t tid_base = 0;   // stochastic-rounding key: position in the concatenated group lists
   p->groups.resize(n_groups);
   for (int32_t g = 0; g < n_groups; ++g) {
     const ps_offload_group& G = groups[g];
@@ -112,7 +119,7 @@ ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_group
       destroy(p);
       return fail(PS_ERR_INVALID_ARG, "group %d: bad tensor list", g);
     }
-    struct Part { const ps_tensor* t; size_t lo, mc, vc, ms, vs; };
+    struct Part { const ps_tensor* t; size_t lo, mc, vc, ms, vs; uint32_t tid; };
     std::vector<Part> parts;
     size_t off_lo = 0, n16 = 0, nsc = 0;
     for (int32_t i = 0; i < G.n_tensors; ++i) {
@@ -127,14 +134,15 @@ ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_group
       }
       if (x.numel == 0 || !x.grad) continue;
       ps_status st;
+      if (!x.w_lo) p->has_residual = false;   // the plan then runs stochastic rounding only
       if ((st = check_dev(x.w_hi, "w_hi", g, i)) || (st = check_dev(x.grad, "grad", g, i)) ||
-          (st = check_host(x.w_lo, "w_lo", g, i, 16)) || (st = check_host(x.m_code, "m_code", g, i, 16)) ||
+          (x.w_lo && (st = check_host(x.w_lo, "w_lo", g, i, 16))) || (st = check_host(x.m_code, "m_code", g, i, 16)) ||
           (st = check_host(x.v_code, "v_code", g, i, 16)) || (st = check_host(x.m_scale, "m_scale", g, i, 4)) ||
           (st = check_host(x.v_scale, "v_scale", g, i, 4))) {
         destroy(p);
         return st;
       }
-      parts.push_back(Part{&x, 0, 0, 0, 0, 0});
+      parts.push_back(Part{&x, 0, 0, 0, 0, 0, tid_base + (uint32_t)i});
       n16 += up256((size_t)x.numel * 2);
       nsc += up256((size_t)((x.numel + kBlock - 1) / kBlock) * 4);
     }
@@ -160,7 +168,7 @@ ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_group
       ends[g].push_back((uint32_t)items);
       // records are completed with the slot base at upload time (below)
       recs[g].push_back(DevTensor{x.w_hi, (uint16_t*)q.lo, x.grad, (uint16_t*)q.mc, (float*)q.ms, (uint16_t*)q.vc,
-                                  (float*)q.vs, x.numel});
+                                  (float*)q.vs, x.numel, q.tid, 0});
     }
     // copies region by region, tensors in order, so that contiguous host
     // slabs merge into one copy per region
@@ -170,8 +178,13 @@ ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_group
         const size_t b16 = (size_t)x.numel * 2, bsc = (size_t)((x.numel + kBlock - 1) / kBlock) * 4;
         void* const host[5] = {x.w_lo, x.m_code, x.v_code, x.m_scale, x.v_scale};
         const size_t off[5] = {q.lo, q.mc, q.vc, q.ms, q.vs};
-        add_copy(p->groups[g].copies, host[region], off[region], region <= 2 ? b16 : bsc, p->bytes_per_dir);
+        if (region == 0) {
+          if (x.w_lo) add_copy(p->groups[g].lo_copies, host[0], off[0], b16, p->lo_bytes_per_dir);
+        } else {
+          add_copy(p->groups[g].copies, host[region], off[region], region <= 2 ? b16 : bsc, p->bytes_per_dir);
+        }
       }
+    tid_base += (uint32_t)G.n_tensors;
     p->groups[g].n_active = (int32_t)parts.size();
     p->groups[g].total_items = (uint32_t)items;
     const size_t slot = 3 * n16 + 2 * nsc;
@@ -212,6 +225,8 @@ ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_group
       if (n) memcpy(tab.data() + p->groups[g].table_off[s] + up256(n * sizeof(DevTensor)), ends[g].data(),
                     n * sizeof(uint32_t));
     }
+  p->bytes_per_dir += p->lo_bytes_per_dir;
+  p->last_bytes_per_dir = p->bytes_per_dir;
   if (!tab.empty()) st = hip_check(hipMemcpy(p->tables, tab.data(), tab.size(), hipMemcpyHostToDevice), "table upload");
   if (!st) st = hip_check(hipStreamCreateWithFlags(&p->up, hipStreamNonBlocking), "hipStreamCreate");
   if (!st) st = hip_check(hipStreamCreateWithFlags(&p->down, hipStreamNonBlocking), "hipStreamCreate");
@@ -234,8 +249,9 @@ ps_status ps_offload_run(ps_offload_plan* p, const ps_hparams* hp, int64_t step,
   if (!p) return fail(PS_ERR_INVALID_ARG, "plan is NULL");
   if (!hp) return fail(PS_ERR_INVALID_ARG, "hparams is NULL");
   const ps_hparams h = *hp;
-  if (h.split_mode == PS_SPLIT_STOCHASTIC)
-    return fail(PS_ERR_UNSUPPORTED, "the offload pipeline keeps residuals; stochastic rounding is not supported");
+  const bool sr = h.split_mode == PS_SPLIT_STOCHASTIC;
+  if (!sr && !p->has_residual)
+    return fail(PS_ERR_INVALID_ARG, "the plan has tensors without w_lo; only stochastic rounding can run it");
   float scratch_out[10];
   // the resident path's validation of the hyperparameters and the step
   if (ps_status s = ps_step_scalars(&h, step, scratch_out)) return s;
@@ -250,11 +266,12 @@ ps_status ps_offload_run(ps_offload_plan* p, const ps_hparams* hp, int64_t step,
     const auto& grp = p->groups[k];
     const int s = k & 1;
     if (k >= 2) st = hip_check(hipStreamWaitEvent(p->up, p->out_ev[s], 0), "hipStreamWaitEvent");
-    for (const auto& cp : grp.copies) {
-      if (st) break;
-      st = hip_check(hipMemcpyAsync(p->slots[s] + cp.dev_off, cp.host, cp.bytes, hipMemcpyHostToDevice, p->up),
-                     "offload upload");
-    }
+    for (int list = sr ? 1 : 0; list < 2; ++list)
+      for (const auto& cp : list ? grp.copies : grp.lo_copies) {
+        if (st) break;
+        st = hip_check(hipMemcpyAsync(p->slots[s] + cp.dev_off, cp.host, cp.bytes, hipMemcpyHostToDevice, p->up),
+                       "offload upload");
+      }
     if (!st) st = hip_check(hipEventRecord(p->in_ev[s], p->up), "hipEventRecord");
     if (!st) st = hip_check(hipStreamWaitEvent(cs, p->in_ev[s], 0), "hipStreamWaitEvent");
     if (!st && grp.n_active > 0) {
@@ -264,11 +281,12 @@ ps_status ps_offload_run(ps_offload_plan* p, const ps_hparams* hp, int64_t step,
     }
     if (!st) st = hip_check(hipEventRecord(p->done_ev[s], cs), "hipEventRecord");
     if (!st) st = hip_check(hipStreamWaitEvent(p->down, p->done_ev[s], 0), "hipStreamWaitEvent");
-    for (const auto& cp : grp.copies) {
-      if (st) break;
-      st = hip_check(hipMemcpyAsync(cp.host, p->slots[s] + cp.dev_off, cp.bytes, hipMemcpyDeviceToHost, p->down),
-                     "offload download");
-    }
+    for (int list = sr ? 1 : 0; list < 2; ++list)
+      for (const auto& cp : list ? grp.copies : grp.lo_copies) {
+        if (st) break;
+        st = hip_check(hipMemcpyAsync(cp.host, p->slots[s] + cp.dev_off, cp.bytes, hipMemcpyDeviceToHost, p->down),
+                       "offload download");
+      }
     if (!st) st = hip_check(hipEventRecord(p->out_ev[s], p->down), "hipEventRecord");
   }
   // the caller's stream completes only after every download has landed
@@ -276,13 +294,14 @@ ps_status ps_offload_run(ps_offload_plan* p, const ps_hparams* hp, int64_t step,
   if (!st) st = hip_check(hipStreamWaitEvent(cs, p->end_ev, 0), "hipStreamWaitEvent");
   if (!st) st = hip_check(hipEventRecord(p->end_ev, p->up), "hipEventRecord");
   if (!st) st = hip_check(hipStreamWaitEvent(cs, p->end_ev, 0), "hipStreamWaitEvent");
+  if (!st) p->last_bytes_per_dir = sr ? p->bytes_per_dir - p->lo_bytes_per_dir : p->bytes_per_dir;
   return st;
 }
 
 ps_status ps_offload_bytes(const ps_offload_plan* p, uint64_t* h2d, uint64_t* d2h) {
   if (!p || !h2d || !d2h) return fail(PS_ERR_INVALID_ARG, "NULL argument");
-  *h2d = p->bytes_per_dir;
-  *d2h = p->bytes_per_dir;
+  *h2d = p->last_bytes_per_dir;
+  *d2h = p->last_bytes_per_dir;
   return PS_OK;
 }
 

@@ -62,3 +62,43 @@ def test_offload_equals_resident_bitwise():
                 x, y = getattr(a, k).cpu(), getattr(b, k).cpu()
                 assert torch.equal(x, y), (gid, a.numel, k)
     plan.close()
+
+
+def test_offload_stochastic_rounding_moves_no_residual_and_equals_resident():
+    """Stochastic rounding through the pipeline (the pages' setting when the
+    residual does not fit in host memory): some tensors have no residual at
+    all, the run moves only codes and scales, and the bytes equal one resident
+    step over the concatenated group lists (whose positions key the random
+    streams)."""
+    slabs = [ps.StateSlab(sizes, DEV, host_state=True) for sizes in GROUPS]
+    for gid, sl in enumerate(slabs):
+        _fill(sl, gid)
+    torch.cuda.synchronize()
+    resident = [_resident_copy(sl) for sl in slabs]
+    lo_before = [[st.w_lo.clone() for st in sl.states] for sl in slabs]
+    for sl in slabs[1:]:
+        sl.states[0].w_lo = None                       # no residual array for these tensors
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=1e-4, weight_decay=0.01, split_mode=ps.SPLIT_STOCHASTIC, seed=808)
+    plan = ps.OffloadPlan([(sl.states, sl.grads) for sl in slabs])
+    all_res = [st for group in resident for st in group]
+    all_grads = [g for sl in slabs for g in sl.grads]
+    for t in range(1, 4):
+        for gid, sl in enumerate(slabs):
+            for i, g in enumerate(sl.grads):
+                synth.dev_bf16_normal(g, 5, synth.STREAM_GRAD, 100 * gid + i, t, synth.SIGMA_G)
+        plan.run(hp, t)
+        ps.opt_step_multi(all_res, all_grads, hp, t)
+    torch.cuda.synchronize()
+    h2d, d2h = plan.bytes()
+    moved = sum(2 * 2 * n + 8 * ((n + 255) // 256) for sizes in GROUPS for n in sizes)
+    assert h2d == d2h == moved
+    for gid, sl in enumerate(slabs):
+        for i, (a, b) in enumerate(zip(sl.states, resident[gid])):
+            for k in ("w_hi", "m_code", "m_scale", "v_code", "v_scale"):
+                x, y = getattr(a, k).cpu(), getattr(b, k).cpu()
+                assert torch.equal(x, y), (gid, a.numel, k)
+            if a.w_lo is not None:
+                assert torch.equal(a.w_lo.cpu(), lo_before[gid][i].cpu())   # residuals untouched
+    with pytest.raises(ps.PSError):
+        plan.run(ps.HParams(algo=ps.ALGO_NADAM), 4)     # a residual mode needs every w_lo
+    plan.close()
