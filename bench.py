@@ -155,7 +155,7 @@ def build_state(shapes, seed, dev, layout="slab", moments="codec"):
     return states, grads
 
 
-def cpu_baseline(shapes, seed, target_params=40_000_000):
+def cpu_baseline(shapes, seed, target_params=60_000_000):
     """The oracle as it stands, one thread, one NAdam step over the leading
     tensors of the set (about target_params parameters)."""
     import oracle
