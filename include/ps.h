@@ -282,7 +282,9 @@ typedef struct ps_offload_plan ps_offload_plan;
 ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_groups, ps_offload_plan** plan);
 /* Runs one optimizer step over all groups; asynchronous on `stream` (the
  * call returns once all work is queued; host state is final when `stream`
- * completes). */
+ * completes). Successive runs of one plan are ordered among themselves even
+ * when given different streams; one plan must not be run from two host
+ * threads at once. */
 ps_status ps_offload_run(ps_offload_plan* plan, const ps_hparams* hp, int64_t step, ps_stream_t stream);
 /* Bytes the most recent run moved host->device and device->host (before
  * any run: the bytes of a run with residuals). */

@@ -36,9 +36,16 @@
  *  - NAdam: Dozat's Nesterov Adam with the momentum schedule
  *    mu_t = beta1 (1 - 0.5 * 0.96^(t * psi)); decoupled weight decay is added
  *    to the step (w - (u + lr*wd*w)).
- *  - Factored step: eps1 added to g^2 before the means, constant beta2, no
- *    bias correction, V^-1/2 built as (1/sqrt(r_i/mean(r))) * (1/sqrt(c_j)),
- *    RMS over the whole tensor.
+ *  - Factored step: eps1 added to g^2 before the means, no bias correction,
+ *    V^-1/2 built as (1/sqrt(r_i/mean(r))) * (1/sqrt(c_j)), RMS over the
+ *    whole tensor. beta2 is constant unless decay_rate < 0, which gives
+ *    beta2_t = 1 - t^decay_rate [ADAF]; the optional first moment is an EMA
+ *    of the clipped, lr-scaled update, taken before weight decay [ADAF].
+ *  - f24 moments: bits 8..31 of the fp32 word, rounded to nearest even,
+ *    3 little-endian bytes per value, no scale [NADAM, third post].
+ *  - Stochastic rounding: round away from zero with probability
+ *    low16(w)/2^16, the 16 random bits per element drawn from a SplitMix64
+ *    stream keyed on (seed, step, tensor) [KAHAN; NADAM opening post].
  */
 #include <math.h>
 #include <stdint.h>

@@ -43,6 +43,7 @@ struct ps_offload_plan {
   uint64_t lo_bytes_per_dir = 0;       // of which residuals
   uint64_t last_bytes_per_dir = 0;     // the most recent run
   bool has_residual = true;            // every active tensor has w_lo
+  bool out_recorded[2] = {false, false};  // out_ev[s] has been recorded by some run
 };
 
 namespace ps {
@@ -265,7 +266,10 @@ ps_status ps_offload_run(ps_offload_plan* p, const ps_hparams* hp, int64_t step,
   for (int k = 0; k < G && !st; ++k) {
     const auto& grp = p->groups[k];
     const int s = k & 1;
-    if (k >= 2) st = hip_check(hipStreamWaitEvent(p->up, p->out_ev[s], 0), "hipStreamWaitEvent");
+    // the slot is free once its previous download (this run's group k-2, or
+    // an earlier run's last group on it, whatever stream that run was given)
+    // has landed
+    if (p->out_recorded[s]) st = hip_check(hipStreamWaitEvent(p->up, p->out_ev[s], 0), "hipStreamWaitEvent");
     for (int list = sr ? 1 : 0; list < 2; ++list)
       for (const auto& cp : list ? grp.copies : grp.lo_copies) {
         if (st) break;
@@ -288,6 +292,7 @@ ps_status ps_offload_run(ps_offload_plan* p, const ps_hparams* hp, int64_t step,
                        "offload download");
       }
     if (!st) st = hip_check(hipEventRecord(p->out_ev[s], p->down), "hipEventRecord");
+    if (!st) p->out_recorded[s] = true;
   }
   // the caller's stream completes only after every download has landed
   if (!st) st = hip_check(hipEventRecord(p->end_ev, p->down), "hipEventRecord");
