@@ -155,6 +155,32 @@ def build_state(shapes, seed, dev, layout="slab", moments="codec"):
     return states, grads
 
 
+def apply_policy(shapes, states, grads, dev):
+    """The pages' storage policy: tensors of at most 4096 elements keep fp32
+    moments, final-layer tensors keep an fp32 parameter and gradient (no
+    residual). Changes states and grads in place; returns the two counts."""
+    import torch
+
+    import precision_state_amd as ps
+    n_small = n_final = 0
+    for i, (s, st) in enumerate(zip(shapes, states)):
+        if s.name.startswith("final_layer."):
+            w32 = torch.empty(s.numel, dtype=torch.float32, device=dev)
+            ps.join(st.w_hi, st.w_lo, w32)
+            st.w_hi, st.w_lo = w32, torch.empty(0, dtype=torch.int16, device=dev)
+            grads[i] = grads[i].view(torch.bfloat16).float()
+            st.flags |= ps.TENSOR_FP32_PARAM
+            n_final += 1
+        if s.numel <= 4096:
+            st.m_code = torch.zeros(s.numel, dtype=torch.float32, device=dev)
+            st.v_code = torch.zeros(s.numel, dtype=torch.float32, device=dev)
+            st.flags = (st.flags & ~ps.TENSOR_F24_MOMENTS) | ps.TENSOR_FP32_MOMENTS
+            n_small += 1
+    torch.cuda.synchronize()
+    log(f"[bench] policy: {n_small} tensors with fp32 moments, {n_final} fp32 final-layer tensors")
+    return n_small, n_final
+
+
 def cpu_baseline(shapes, seed, target_params=60_000_000):
     """The oracle as it stands, one thread, one NAdam step over the leading
     tensors of the set (about target_params parameters)."""
@@ -239,6 +265,27 @@ def bench_factored(args):
     wall = time.perf_counter() - t0
     step_ms = a.elapsed_time(b) / args.steps
     log(f"[bench] factored: {args.steps} steps, {step_ms:.3f} ms/step (events), {wall * 1e3 / args.steps:.3f} wall")
+    # per-hook granularity: one call per tensor, the workspace shared by all
+    recs_one = [ps.make_records([st], [g]) for st, g in zip(states, grads)]
+    for r in recs_one:
+        step += 1
+        ps.factored_step(None, None, hp, step, workspace=ws, stream=stream, records=r)
+    torch.cuda.synchronize()
+    a1, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    issue = 0.0
+    t0 = time.perf_counter()
+    a1.record(stream)
+    for _ in range(args.steps):
+        step += 1
+        t1 = time.perf_counter()
+        for r in recs_one:
+            ps.factored_step(None, None, hp, step, workspace=ws, stream=stream, records=r)
+        issue += time.perf_counter() - t1
+    b1.record(stream)
+    torch.cuda.synchronize()
+    per_tensor = {"wall_ms": (time.perf_counter() - t0) * 1e3 / args.steps,
+                  "gpu_ms": a1.elapsed_time(b1) / args.steps, "issue_ms": issue * 1e3 / args.steps}
+    log(f"[bench] factored, one call per tensor: {per_tensor}")
     n_blocks = sum((s.numel + 255) // 256 for s in shapes)
     alg = (10 if split != ps.SPLIT_STOCHASTIC else 6) * n_params + ((4 * n_params + 8 * n_blocks) if args.beta1 else 0)
     gbs10 = alg / (step_ms * 1e-3) / 1e9
@@ -250,7 +297,7 @@ def bench_factored(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl + "_factored", "params": n_params, "tensors": len(shapes), "step_ms": step_ms,
                    "beta1": args.beta1, "decay_rate": args.decay_rate, "split": args.split, "algorithmic_bytes": alg,
-                   "gbs_algorithmic": gbs10, "gbs_with_gradient_rereads": gbs14},
+                   "gbs_algorithmic": gbs10, "gbs_with_gradient_rereads": gbs14, "per_tensor_calls": per_tensor},
         "roofline": {"bound": "hbm", "achieved": gbs10, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs10 / PEAK_HBM_GBS, "traffic": None},
         "cpu_baseline": None}), flush=True)
@@ -271,6 +318,9 @@ def bench_per_tensor(args):
     shapes = synth.WORKLOADS[args.workload]()
     n_params = synth.total_params(shapes)
     states, grads = build_state(shapes, args.seed, dev, "slab")
+    n_small = n_final = 0
+    if args.policy:   # flagged tensors go through the device table cache, one table per tensor
+        n_small, n_final = apply_policy(shapes, states, grads, dev)
     recs_one = [ps.make_records([st], [g]) for st, g in zip(states, grads)]
     recs_all = ps.make_records(states, grads)
     hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6)
@@ -342,6 +392,7 @@ def bench_per_tensor(args):
         "warmup": args.warmup, "ms_per_step": pt["wall_ms"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload + "_per_tensor", "params": n_params, "calls_per_step": len(shapes),
+                   "policy": {"fp32_moment_tensors": n_small, "fp32_param_tensors": n_final} if args.policy else None,
                    "per_tensor": pt, "one_launch": res["one_launch"],
                    "per_tensor_over_one_launch": pt["wall_ms"] / res["one_launch"]["wall_ms"],
                    "small_tensor_calls": {str(k): v for k, v in lat.items()}},
@@ -526,21 +577,7 @@ def main():
                     split_mode=split, seed=args.seed)
     n_small = n_final = 0
     if args.policy:
-        for i, (s, st) in enumerate(zip(shapes, states)):
-            if s.name.startswith("final_layer."):
-                w32 = torch.empty(s.numel, dtype=torch.float32, device=dev)
-                ps.join(st.w_hi, st.w_lo, w32)
-                st.w_hi, st.w_lo = w32, torch.empty(0, dtype=torch.int16, device=dev)
-                grads[i] = grads[i].view(torch.bfloat16).float()
-                st.flags |= ps.TENSOR_FP32_PARAM
-                n_final += 1
-            if s.numel <= 4096:
-                st.m_code = torch.zeros(s.numel, dtype=torch.float32, device=dev)
-                st.v_code = torch.zeros(s.numel, dtype=torch.float32, device=dev)
-                st.flags = (st.flags & ~ps.TENSOR_F24_MOMENTS) | ps.TENSOR_FP32_MOMENTS
-                n_small += 1
-        torch.cuda.synchronize()
-        log(f"[bench] policy: {n_small} tensors with fp32 moments, {n_final} fp32 final-layer tensors")
+        n_small, n_final = apply_policy(shapes, states, grads, dev)
     recs = ps.make_records(states, grads)
     stream = torch.cuda.current_stream()
     step = 0

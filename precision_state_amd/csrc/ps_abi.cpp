@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <unordered_map>
 #include <vector>
 
 #include "ps_internal.h"
@@ -122,29 +123,80 @@ ps_status build_active(const ps_tensor* t, int32_t n, bool residual, std::vector
 
 // ---------------------------------------------------------------------------
 // device blob cache: one immutable device copy per distinct host blob (tensor
-// tables, factored-step plans). A training loop passes the same list every
-// step, so after the first call nothing is uploaded.
+// tables, factored-step plans). A training loop passes the same lists every
+// step, also when it steps tensor by tensor from gradient hooks (one blob per
+// tensor, hundreds per model), so after the first step nothing is uploaded.
+// Blobs live in per-device arenas of pinned host staging plus device memory;
+// when an arena limit is reached the device is synchronized and that
+// device's cache is emptied, so no launch can still read a freed blob.
 // ---------------------------------------------------------------------------
 
 struct BlobEntry {
-  int device = -1;
   std::vector<unsigned char> key;
-  void* d_mem = nullptr;
-  void* h_mem = nullptr;  // pinned source of the upload
-  hipEvent_t ready = nullptr;
-  uint64_t last_use = 0;
+  const void* d_mem = nullptr;
+  hipEvent_t ready = nullptr;   // upload done
+  bool done = false;            // the upload is known to have completed
+};
+
+struct Chunk {
+  char* d_mem = nullptr;
+  char* h_mem = nullptr;   // pinned source of the uploads
+  size_t size = 0, used = 0;
+};
+
+struct DeviceCache {
+  std::unordered_multimap<uint64_t, BlobEntry*> by_hash;
+  std::vector<Chunk> chunks;
+  size_t entries = 0, bytes = 0;
 };
 
 std::mutex g_cache_mu;
-std::vector<BlobEntry*> g_cache;
-uint64_t g_clock = 0;
-constexpr size_t kCacheMax = 64;
+std::unordered_map<int, DeviceCache> g_cache;
+constexpr size_t kChunkBytes = size_t(1) << 20;
+constexpr size_t kCacheMaxBytes = size_t(64) << 20;   // per device
+constexpr size_t kCacheMaxEntries = 16384;            // per device
+constexpr size_t kBlobAlign = 256;
 
-void free_entry(BlobEntry* e) {
-  if (e->ready) (void)hipEventDestroy(e->ready);
-  if (e->d_mem) (void)hipFree(e->d_mem);
-  if (e->h_mem) (void)hipHostFree(e->h_mem);
-  delete e;
+uint64_t fnv1a(const void* data, size_t bytes) {
+  const unsigned char* p = (const unsigned char*)data;
+  uint64_t h = 1469598103934665603ull;
+  for (size_t i = 0; i < bytes; ++i) h = (h ^ p[i]) * 1099511628211ull;
+  return h;
+}
+
+void flush(DeviceCache& dc) {
+  for (auto& kv : dc.by_hash) {
+    if (kv.second->ready) (void)hipEventDestroy(kv.second->ready);
+    delete kv.second;
+  }
+  dc.by_hash.clear();
+  for (Chunk& c : dc.chunks) {
+    if (c.d_mem) (void)hipFree(c.d_mem);
+    if (c.h_mem) (void)hipHostFree(c.h_mem);
+  }
+  dc.chunks.clear();
+  dc.entries = dc.bytes = 0;
+}
+
+// Room for `bytes` in the device's arena: the current chunk, else a new one.
+ps_status arena_take(DeviceCache& dc, size_t bytes, char** d, char** h) {
+  const size_t need = (bytes + kBlobAlign - 1) / kBlobAlign * kBlobAlign;
+  if (dc.chunks.empty() || dc.chunks.back().size - dc.chunks.back().used < need) {
+    Chunk c;
+    c.size = need > kChunkBytes ? need : kChunkBytes;
+    if (hipMalloc((void**)&c.d_mem, c.size) != hipSuccess) return fail(PS_ERR_NO_MEMORY, "device table allocation failed");
+    if (hipHostMalloc((void**)&c.h_mem, c.size, hipHostMallocDefault) != hipSuccess) {
+      (void)hipFree(c.d_mem);
+      return fail(PS_ERR_NO_MEMORY, "pinned table staging allocation failed");
+    }
+    dc.chunks.push_back(c);
+    dc.bytes += c.size;
+  }
+  Chunk& c = dc.chunks.back();
+  *d = c.d_mem + c.used;
+  *h = c.h_mem + c.used;
+  c.used += need;
+  return PS_OK;
 }
 
 }  // namespace
@@ -152,44 +204,47 @@ void free_entry(BlobEntry* e) {
 ps_status device_blob(const void* data, size_t bytes, hipStream_t s, const void** dptr) {
   int dev = 0;
   if (ps_status st = hip_check(hipGetDevice(&dev), "hipGetDevice")) return st;
+  const uint64_t h = fnv1a(data, bytes);
   std::lock_guard<std::mutex> lk(g_cache_mu);
-  for (BlobEntry* e : g_cache) {
-    if (e->device == dev && e->key.size() == bytes && !memcmp(e->key.data(), data, bytes)) {
-      e->last_use = ++g_clock;
-      if (ps_status st = hip_check(hipStreamWaitEvent(s, e->ready, 0), "hipStreamWaitEvent")) return st;
-      *dptr = e->d_mem;
-      return PS_OK;
+  DeviceCache& dc = g_cache[dev];
+  auto range = dc.by_hash.equal_range(h);
+  for (auto it = range.first; it != range.second; ++it) {
+    BlobEntry* e = it->second;
+    if (e->key.size() != bytes || memcmp(e->key.data(), data, bytes) != 0) continue;
+    // wait for the upload unless it is known to have completed
+    if (!e->done) {
+      if (hipEventQuery(e->ready) == hipSuccess)
+        e->done = true;
+      else if (ps_status st = hip_check(hipStreamWaitEvent(s, e->ready, 0), "hipStreamWaitEvent"))
+        return st;
     }
+    *dptr = e->d_mem;
+    return PS_OK;
   }
-  if (g_cache.size() >= kCacheMax) {
-    // Evict the least recently used blob; wait for all device work first so
-    // that no launch still reads it.
-    size_t victim = 0;
-    for (size_t i = 1; i < g_cache.size(); ++i)
-      if (g_cache[i]->last_use < g_cache[victim]->last_use) victim = i;
+  if (dc.entries >= kCacheMaxEntries || dc.bytes + bytes > kCacheMaxBytes) {
+    // Every launch that may read a cached blob must end before it is freed.
     if (ps_status st = hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize")) return st;
-    free_entry(g_cache[victim]);
-    g_cache.erase(g_cache.begin() + victim);
+    flush(dc);
   }
+  char *d = nullptr, *hm = nullptr;
+  if (ps_status st = arena_take(dc, bytes, &d, &hm)) return st;
   BlobEntry* e = new BlobEntry;
-  e->device = dev;
   e->key.assign((const unsigned char*)data, (const unsigned char*)data + bytes);
-  if (hipMalloc(&e->d_mem, bytes) != hipSuccess || hipHostMalloc(&e->h_mem, bytes, hipHostMallocDefault) != hipSuccess) {
-    free_entry(e);
-    return fail(PS_ERR_NO_MEMORY, "device table allocation failed");
-  }
-  memcpy(e->h_mem, data, bytes);
+  e->d_mem = d;
+  memcpy(hm, data, bytes);
   ps_status st = hip_check(hipEventCreateWithFlags(&e->ready, hipEventDisableTiming), "hipEventCreate");
-  if (!st) st = hip_check(hipMemcpyAsync(e->d_mem, e->h_mem, bytes, hipMemcpyHostToDevice, s), "table upload");
+  if (!st) st = hip_check(hipMemcpyAsync(d, hm, bytes, hipMemcpyHostToDevice, s), "table upload");
   if (!st) st = hip_check(hipEventRecord(e->ready, s), "hipEventRecord");
   if (st) {
+    // the arena space stays reserved until the next flush
     (void)hipStreamSynchronize(s);
-    free_entry(e);
+    if (e->ready) (void)hipEventDestroy(e->ready);
+    delete e;
     return st;
   }
-  e->last_use = ++g_clock;
-  g_cache.push_back(e);
-  *dptr = e->d_mem;
+  dc.by_hash.emplace(h, e);
+  ++dc.entries;
+  *dptr = d;
   return PS_OK;
 }
 
