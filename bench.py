@@ -265,27 +265,9 @@ def bench_factored(args):
     wall = time.perf_counter() - t0
     step_ms = a.elapsed_time(b) / args.steps
     log(f"[bench] factored: {args.steps} steps, {step_ms:.3f} ms/step (events), {wall * 1e3 / args.steps:.3f} wall")
-    # per-hook granularity: one call per tensor, the workspace shared by all
-    recs_one = [ps.make_records([st], [g]) for st, g in zip(states, grads)]
-    for r in recs_one:
-        step += 1
-        ps.factored_step(None, None, hp, step, workspace=ws, stream=stream, records=r)
-    torch.cuda.synchronize()
-    a1, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    issue = 0.0
-    t0 = time.perf_counter()
-    a1.record(stream)
-    for _ in range(args.steps):
-        step += 1
-        t1 = time.perf_counter()
-        for r in recs_one:
-            ps.factored_step(None, None, hp, step, workspace=ws, stream=stream, records=r)
-        issue += time.perf_counter() - t1
-    b1.record(stream)
-    torch.cuda.synchronize()
-    per_tensor = {"wall_ms": (time.perf_counter() - t0) * 1e3 / args.steps,
-                  "gpu_ms": a1.elapsed_time(b1) / args.steps, "issue_ms": issue * 1e3 / args.steps}
-    log(f"[bench] factored, one call per tensor: {per_tensor}")
+    per_tensor = None
+    if args.per_tensor_calls:
+        per_tensor = time_factored_per_tensor(ps, states, grads, hp, ws, stream, step, args.steps)
     n_blocks = sum((s.numel + 255) // 256 for s in shapes)
     alg = (10 if split != ps.SPLIT_STOCHASTIC else 6) * n_params + ((4 * n_params + 8 * n_blocks) if args.beta1 else 0)
     gbs10 = alg / (step_ms * 1e-3) / 1e9
@@ -301,6 +283,33 @@ def bench_factored(args):
         "roofline": {"bound": "hbm", "achieved": gbs10, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs10 / PEAK_HBM_GBS, "traffic": None},
         "cpu_baseline": None}), flush=True)
+
+
+def time_factored_per_tensor(ps, states, grads, hp, ws, stream, step, steps):
+    """Per-hook granularity of the factored step: one call per tensor, the
+    workspace shared by all calls."""
+    import torch
+    recs_one = [ps.make_records([st], [g]) for st, g in zip(states, grads)]
+    for r in recs_one:
+        step += 1
+        ps.factored_step(None, None, hp, step, workspace=ws, stream=stream, records=r)
+    torch.cuda.synchronize()
+    a1, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    issue = 0.0
+    t0 = time.perf_counter()
+    a1.record(stream)
+    for _ in range(steps):
+        step += 1
+        t1 = time.perf_counter()
+        for r in recs_one:
+            ps.factored_step(None, None, hp, step, workspace=ws, stream=stream, records=r)
+        issue += time.perf_counter() - t1
+    b1.record(stream)
+    torch.cuda.synchronize()
+    res = {"wall_ms": (time.perf_counter() - t0) * 1e3 / steps, "gpu_ms": a1.elapsed_time(b1) / steps,
+           "issue_ms": issue * 1e3 / steps}
+    log(f"[bench] factored, one call per tensor: {res}")
+    return res
 
 
 def bench_per_tensor(args):
@@ -523,6 +532,8 @@ def main():
                          "(factored second moment, update clipping; --beta1, --decay-rate) on the double-block "
                          "shapes; offload: host-resident state over PCIe; per_tensor: one call per tensor, as a "
                          "gradient hook would step")
+    ap.add_argument("--per-tensor-calls", action="store_true",
+                    help="factored mode: also time one call per tensor (the per-hook granularity)")
     ap.add_argument("--policy", action="store_true",
                     help="nadam mode: fp32 moments for tensors of <= 4096 elements and an fp32 final layer "
                          "(PS_TENSOR_FP32_MOMENTS / PS_TENSOR_FP32_PARAM)")

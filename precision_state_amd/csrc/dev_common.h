@@ -96,6 +96,15 @@ constexpr float kK15 = 3.05185094e-05f;  // fp32(1/32767) = 0x38000100
 constexpr float kK16 = 1.52590219e-05f;  // fp32(1/65535) = 0x37800080
 constexpr float kMagic = 8388608.0f;     // 2^23
 
+// Decoder offsets: a code c arrives as the float 2^23 + c, and
+// fma(2^23 + c, K, -(2^23 + bias) * K) is (c - bias) * K rounded once, i.e.
+// exactly the product k * K, because both offsets are fp32 numbers:
+// (2^23 + 2^15) * K15 = 2^8 + 2^0 + 2^-7 + 2^-15 and 2^23 * K16 = 2^7 + 2^-9.
+constexpr float kDecOffS = -(256.0f + 1.0f + 0x1p-7f + 0x1p-15f);
+constexpr float kDecOffU = -(128.0f + 0x1p-9f);
+static_assert((8388608.0 + 32768.0) * (double)kK15 == -(double)kDecOffS, "signed decoder offset is not exact");
+static_assert(8388608.0 * (double)kK16 == -(double)kDecOffU, "unsigned decoder offset is not exact");
+
 __device__ __forceinline__ float dmag(float h, float K) {
   float a = h * K;
   float t = a * a;
@@ -108,18 +117,18 @@ __device__ __forceinline__ float code_hi_f(uint32_t c2) { return __uint_as_float
 
 // Signed decode of one code given as (2^23 + c): sign(k) * D(|k|) * s, k = c - 32768.
 __device__ __forceinline__ float dec_signed(float magic_c, float s) {
-  float k = magic_c - (kMagic + 32768.0f);  // exact
+  float t = __builtin_fmaf(magic_c, kK15, kDecOffS);  // k * K15, one rounding
   // t*|t| squares the magnitude and keeps the sign, so sign(k) * D(|k|) * s
   // comes out of the same three roundings with no separate sign step.
-  float t = k * kK15;
   t = t * __builtin_fabsf(t);
   t = t * __builtin_fabsf(t);
   return t * s;
 }
 
 __device__ __forceinline__ float dec_unsigned(float magic_c, float s) {
-  float k = magic_c - kMagic;
-  return dmag(k, kK16) * s;
+  const float a = __builtin_fmaf(magic_c, kK16, kDecOffU);  // k * K16, one rounding
+  const float t = a * a;
+  return (t * t) * s;
 }
 
 // Code magnitude of x in [0, 1 + 2^-23] given y ~ x^(1/4) (a few ulp): the
@@ -127,8 +136,11 @@ __device__ __forceinline__ float dec_unsigned(float magic_c, float s) {
 // only the boundary on y's side of k0 is tested, with D evaluated exactly as
 // the definition does. Equal to the definition whenever |y*Q - (x^(1/4))*Q|
 // stays well below 1/2 code.
+// The result is biased: 0x4B000000 + k (the bit pattern of 2^23 + k, less
+// or more one), so its low 16 bits are k and bits 16..23 are zero; callers
+// that keep only the low half need no unbiasing.
 template <int Q>
-__device__ __forceinline__ uint32_t code_mag(float x, float y) {
+__device__ __forceinline__ uint32_t code_mag_biased(float x, float y) {
   constexpr float K = (Q == 32767) ? kK15 : kK16;
   const float q = (float)Q;
   float z = __builtin_fmaf(y, q, kMagic);  // 2^23 + rint(y*Q)
@@ -136,9 +148,17 @@ __device__ __forceinline__ uint32_t code_mag(float x, float y) {
   // y*Q - k0, exact; +0 when equal (never -0), so its sign bit is "below k0"
   float dl = __builtin_fmaf(y, q, -kf);
   float T = dmag(kf + __builtin_copysignf(0.5f, dl), K);
-  uint32_t k0 = __float_as_uint(z) - 0x4B000000u;
-  return k0 - (__float_as_uint(dl) >> 31) + (x >= T ? 1u : 0u);
+  return __float_as_uint(z) - (__float_as_uint(dl) >> 31) + (x >= T ? 1u : 0u);
 }
+
+template <int Q>
+__device__ __forceinline__ uint32_t code_mag(float x, float y) {
+  return code_mag_biased<Q>(x, y) - 0x4B000000u;
+}
+
+// Two 16-bit codes (low halves of their words) packed as one word, even
+// element in the low half.
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t even, uint32_t odd) { return perm(odd, even, kSelLoHalves); }
 
 __device__ __forceinline__ float fast_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
 
@@ -157,18 +177,23 @@ __device__ __forceinline__ float sqrt_rn_fast(float v) {
   return s;
 }
 
-// Signed code of m given inv = 1/scale (0 for a flushed block).
-__device__ __forceinline__ uint32_t enc_signed(float m, float inv) {
+// Signed code of m given inv = 1/scale (0 for a flushed block), in the low
+// 16 bits of the result (the upper bits are not zero: pack with pack_lo16).
+__device__ __forceinline__ uint32_t enc_signed_lo16(float m, float inv) {
   float x = __builtin_fabsf(m) * inv;
-  uint32_t k = code_mag<32767>(x, fast_sqrt(fast_sqrt(x)));
-  // 32768 - k for m < 0 (k = 0 for -0), else 32768 + k: negate k by the sign mask
+  uint32_t k = code_mag_biased<32767>(x, fast_sqrt(fast_sqrt(x)));
+  // 32768 - k for m < 0 (k = 0 for -0), else 32768 + k: negate k by the sign
+  // mask; the bias is a multiple of 2^16 and leaves the low half alone
   const uint32_t neg = (uint32_t)((int32_t)__float_as_uint(m) >> 31);
   return 32768u + ((k ^ neg) - neg);
 }
 
-// Unsigned code of v >= 0 given inv = 1/scale and y ~ (v*inv)^(1/4).
-__device__ __forceinline__ uint32_t enc_unsigned_y(float v, float inv, float y) {
-  return code_mag<65535>(v * inv, y);
+__device__ __forceinline__ uint32_t enc_signed(float m, float inv) { return enc_signed_lo16(m, inv) & 0xFFFFu; }
+
+// Unsigned code of v >= 0 given inv = 1/scale and y ~ (v*inv)^(1/4), in the
+// low 16 bits of the result (pack with pack_lo16).
+__device__ __forceinline__ uint32_t enc_unsigned_y_lo16(float v, float inv, float y) {
+  return code_mag_biased<65535>(v * inv, y);
 }
 
 __device__ __forceinline__ uint32_t enc_unsigned(float v, float inv) {

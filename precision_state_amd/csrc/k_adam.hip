@@ -97,8 +97,8 @@ __device__ __forceinline__ void update_store(const DevTensor& T, int64_t e, int6
         u = __builtin_fmaf(c.AG, g, c.AM * m[j]) / d;
       if (WD) u = __builtin_fmaf(c.CWD, wf, u);
       wb[o] = __float_as_uint(wf - u);
-      cm[o] = enc_signed(m[j], inv_m);
-      cv[o] = enc_unsigned_y(v[j], inv_v, fast_sqrt(rv * sq_inv_v));
+      cm[o] = enc_signed_lo16(m[j], inv_m);
+      cv[o] = enc_unsigned_y_lo16(v[j], inv_v, fast_sqrt(rv * sq_inv_v));
     }
     if (SR) {
       const uint64_t q = rnd[w >> 1] >> (32 * (w & 1));
@@ -106,8 +106,8 @@ __device__ __forceinline__ void update_store(const DevTensor& T, int64_t e, int6
     } else {
       split_pair<SPLIT>(wb[0], wb[1], oh[w], ol[w]);
     }
-    omc[w] = cm[0] | (cm[1] << 16);
-    ovc[w] = cv[0] | (cv[1] << 16);
+    omc[w] = pack_lo16(cm[0], cm[1]);
+    ovc[w] = pack_lo16(cv[0], cv[1]);
   }
   if (full) {
     store8(T.hi + e, oh);
@@ -152,7 +152,8 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
   // Decode, EMA, block maxima. Missing tail elements have g = 0 and
   // zero-coded moments, so m = v = 0 and they never raise a maximum.
   float m[8], v[8];
-  uint32_t mx_m = 0u, mx_v = 0u;   // maxima of |m| and v as bit patterns (v >= 0, never -0)
+  float mx_m = 0.0f, mn_m = 0.0f;  // max and min of m: max |m| = max(mx_m, -mn_m)
+  uint32_t mx_v = 0u;              // max of v as a bit pattern (v >= 0, never -0)
   uint32_t tiny = 0xFFFFFFFFu;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -163,7 +164,8 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
     const float v0 = dec_unsigned(odd ? code_hi_f(vw[w]) : code_lo_f(vw[w]), vs_old);
     m[j] = __builtin_fmaf(c.B1, m0, c.C1 * g);
     v[j] = __builtin_fmaf(c.B2, v0, c.C2 * (g * g));
-    mx_m = __builtin_elementwise_max(mx_m, __float_as_uint(m[j]) & 0x7FFFFFFFu);
+    mx_m = __builtin_fmaxf(mx_m, m[j]);
+    mn_m = __builtin_fminf(mn_m, m[j]);
     mx_v = __builtin_elementwise_max(mx_v, __float_as_uint(v[j]));
     tiny = __builtin_elementwise_min(tiny, __float_as_uint(v[j]) - 1u);
   }
@@ -173,7 +175,8 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
 
   // Block scales (32-lane maximum).
   float sm, inv_m, sv, inv_v;
-  block_scale(__uint_as_float(row32_max_u32(mx_m)), sm, inv_m);
+  const float am = __builtin_fmaxf(mx_m, -mn_m);   // +0 or positive
+  block_scale(__uint_as_float(row32_max_u32(__float_as_uint(am))), sm, inv_m);
   block_scale(__uint_as_float(row32_max_u32(mx_v)), sv, inv_v);
   const float sq_inv_v = fast_sqrt(inv_v);
 
