@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+from figures import page_figure
 from oracle import SIGNED, UNSIGNED
 
 Q = {SIGNED: 32767, UNSIGNED: 65535}
@@ -138,7 +139,7 @@ def test_l1_error_at_least_90pct_below_bf16_storage():
         e_u16 = np.abs(oracle.decode(c, s, kind).astype(np.float64) - val).sum()
         bf = torch.from_numpy(val).to(torch.bfloat16).float().numpy()
         e_bf16 = np.abs(bf.astype(np.float64) - val).sum()
-        assert e_u16 <= 0.10 * e_bf16, (kind, e_u16 / e_bf16)
+        assert e_u16 <= page_figure("codec_l1_error_vs_bf16")["max_error_ratio"] * e_bf16, (kind, e_u16 / e_bf16)
 
 
 # ---------------------------------------------------------------------------
@@ -178,4 +179,5 @@ def test_f24_is_about_256x_more_accurate_than_bf16():
         nz = val != 0
         e24 = np.mean(np.abs(f24[nz] / val[nz] - 1))
         e16 = np.mean(np.abs(bf[nz] / val[nz] - 1))
-        assert 200 < e16 / e24 < 320, e16 / e24
+        lo, hi = page_figure("f24_accuracy_vs_bf16")["accepted_range"]
+        assert lo < e16 / e24 < hi, e16 / e24

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+from figures import page_figure
 from oracle import SPLIT_NEAREST_AWAY, SPLIT_TRUNC
 
 
@@ -76,7 +77,15 @@ def test_nearest_away_matches_library_rounding_off_ties():
                   ((tb & 0x7FFFFFFF) + 0x8000) & 0xFFFF0000)
 
 
-@pytest.mark.parametrize("frac,bumps", [(0.25, [4, 8, 12, 16, 20, 24]), (0.2, [6, 11, 16, 21, 26])])
+def _page_period_case():
+    fig = page_figure("kahan_subulp_update_period")
+    f, k = fig["update_fraction_of_ulp"], fig["period_steps"]
+    # at w = 1.0 the fp32 increment is 13107 units of 2^-23 (a fifth of the 65536-unit bf16 step,
+    # rounded down), so k steps fall one unit short of a full step and the moves come at k*j + 1
+    return f, [k + 1 + i * k for i in range(5)]
+
+
+@pytest.mark.parametrize("frac,bumps", [(0.25, [4, 8, 12, 16, 20, 24]), _page_period_case()])
 def test_residual_accumulates_subulp_updates(frac, bumps):
     """PR #2159's closing explanation: an update worth 20% of a bf16 step moves
     the stored bf16 once every five steps (deterministically), where plain

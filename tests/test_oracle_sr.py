@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+from figures import page_figure
 from oracle import HParams
 
 
@@ -21,9 +22,8 @@ def _bf16_bits(x):
 def test_splitmix64_published_outputs():
     """The first three outputs of SplitMix64 from state 0, as the generator's
     reference definition fixes them."""
-    assert oracle.splitmix64_at(0, 0) == 0xE220A8397B1DCDAF
-    assert oracle.splitmix64_at(0, 1) == 0x6E789E6AA1B965F4
-    assert oracle.splitmix64_at(0, 2) == 0x06C45D188009454F
+    for k, want in enumerate(page_figure("splitmix64_state0_outputs")["outputs"]):
+        assert oracle.splitmix64_at(0, k) == int(want, 16), k
 
 
 @pytest.mark.parametrize("bits", [0x3F800001, 0x3F80FFFF, 0x3F808000, 0xBF812345, 0x3F7FFFFF, 0x7F7F8001,
@@ -79,14 +79,17 @@ def test_sr_moves_a_fifth_of_an_ulp_update_once_in_five_steps_on_average():
     n = 1 << 18
     hi = np.full(n, 0x3F80, np.uint32)                     # 1.0
     ulp = 2.0 ** -7
-    x = np.float32(1.0 + 0.2 * ulp)                        # exactly representable in fp32
+    fig = page_figure("kahan_subulp_update_period")
+    p = fig["update_fraction_of_ulp"]
+    assert p == 1.0 / fig["period_steps"]
+    x = np.float32(1.0 + p * ulp)                          # exactly representable in fp32
     r = oracle.sr_rand16(11, 1, 0, 0, n)
     res = ((np.uint32(np.float32(x).view(np.uint32)) + r.astype(np.uint32)) >> 16)
     # the same through the oracle's function on a sample
     for i in range(0, n, 4099):
         assert oracle.sr_bf16(x, r[i]) == res[i]
     frac = float(np.mean(res == hi + 1))
-    assert abs(frac - 0.2) < 4 * np.sqrt(0.2 * 0.8 / n), frac
+    assert abs(frac - p) < 4 * np.sqrt(p * (1 - p) / n), frac
 
 
 def test_sr_step_brackets_the_fp32_step_and_keeps_the_moments():
