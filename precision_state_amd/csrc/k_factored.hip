@@ -107,17 +107,40 @@ __global__ __launch_bounds__(kT) void k_f_stats(FPlan P, FScalars S) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) cacc[j] = 0.0;
   double rs[8];
-  for (int k = 0; k < 8; ++k) {
-    const int r = tr * kFTileRows + rg + 8 * k;
-    uint32_t w[4];
-    const uint32_t valid = load_row8(X.g, X, r, c, w);
-    rs[k] = 0.0;
+  if (X.vec && (tr + 1) * kFTileRows <= X.R && (tc + 1) * kFTileCols <= X.C) {
+    // Interior tile: all eight row segments are requested at once, then
+    // summed in the same order as below.
+    uint32_t w[8][4];
+    const uint16_t* p = X.g + (size_t)(tr * kFTileRows + rg) * (size_t)X.C + (size_t)c;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float g = bf16_at(w, j);
-      const float q = (valid >> j & 1u) ? g * g + S.EPS1 : 0.0f;
-      rs[k] += (double)q;
-      cacc[j] += (double)q;
+    for (int k = 0; k < 8; ++k) {
+      const u32x4 v = *(const GLOBAL u32x4*)(p + (size_t)(8 * k) * (size_t)X.C);
+      w[k][0] = v.x; w[k][1] = v.y; w[k][2] = v.z; w[k][3] = v.w;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      rs[k] = 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float g = bf16_at(w[k], j);
+        const float q = g * g + S.EPS1;
+        rs[k] += (double)q;
+        cacc[j] += (double)q;
+      }
+    }
+  } else {
+    for (int k = 0; k < 8; ++k) {
+      const int r = tr * kFTileRows + rg + 8 * k;
+      uint32_t w[4];
+      const uint32_t valid = load_row8(X.g, X, r, c, w);
+      rs[k] = 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float g = bf16_at(w, j);
+        const float q = (valid >> j & 1u) ? g * g + S.EPS1 : 0.0f;
+        rs[k] += (double)q;
+        cacc[j] += (double)q;
+      }
     }
   }
   // Row sums over the 32 column groups of a half-wave by transpose-reduce:
