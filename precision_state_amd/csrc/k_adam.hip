@@ -26,13 +26,26 @@
 namespace ps {
 namespace {
 
+// Every byte of the state streams through once per step: the 16-byte loads
+// and stores carry the non-temporal hint (3-4% faster per step, but only when
+// both directions use it; loads alone were slower). The f24 arrays' 8-byte
+// accesses stay plain: with the hint they were slower.
+template <class V>
+__device__ __forceinline__ V ld_nt(const V* p) {
+  return __builtin_nontemporal_load((const GLOBAL V*)p);
+}
+template <class V>
+__device__ __forceinline__ void st_nt(V* p, V v) {
+  __builtin_nontemporal_store(v, (GLOBAL V*)p);
+}
+
 __device__ __forceinline__ void load8(const uint16_t* p, uint32_t* dst) {
-  const u32x4 v = *(const GLOBAL u32x4*)p;
+  const u32x4 v = ld_nt((const u32x4*)p);
   dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
 }
 
 __device__ __forceinline__ void store8(uint16_t* p, const uint32_t* src) {
-  *(GLOBAL u32x4*)p = u32x4{src[0], src[1], src[2], src[3]};
+  st_nt((u32x4*)p, u32x4{src[0], src[1], src[2], src[3]});
 }
 
 // Guarded variants for the last work item of a tensor: element e + j exists
@@ -231,7 +244,7 @@ __device__ __forceinline__ void load_f8(const float* p, int64_t e, int64_t n, fl
   const GLOBAL float* q = (const GLOBAL float*)p;
   if (e + 8 <= n) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    const f32x4 a = *(const GLOBAL f32x4*)(q + e), b = *(const GLOBAL f32x4*)(q + e + 4);
+    const f32x4 a = ld_nt((const f32x4*)(p + e)), b = ld_nt((const f32x4*)(p + e + 4));
     d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w; d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
     return;
   }
@@ -242,8 +255,8 @@ __device__ __forceinline__ void store_f8(float* p, int64_t e, int64_t n, const f
   GLOBAL float* q = (GLOBAL float*)p;
   if (e + 8 <= n) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    *(GLOBAL f32x4*)(q + e) = f32x4{s[0], s[1], s[2], s[3]};
-    *(GLOBAL f32x4*)(q + e + 4) = f32x4{s[4], s[5], s[6], s[7]};
+    st_nt((f32x4*)(p + e), f32x4{s[0], s[1], s[2], s[3]});
+    st_nt((f32x4*)(p + e + 4), f32x4{s[4], s[5], s[6], s[7]});
     return;
   }
   for (int j = 0; j < 8; ++j)
