@@ -550,6 +550,69 @@ def bench_offload(args, n_blocks=57):
     plan.close()
 
 
+def bench_elementwise(args):
+    """The standalone kernels: residual split and join (8 B/elem each: fp32 <-> two 16-bit halves) and
+    moment encode and decode (6 B/elem + 4 B per 256-block: fp32 <-> uint16 codes + scales), both modes
+    or kinds, on one array of --elements values (default 2^30: a 4 GiB fp32 array)."""
+    import torch
+
+    import precision_state_amd as ps
+    import synth
+    dev = "cuda:0"
+    n = args.elements
+    nb = (n + 255) // 256
+    hi = torch.empty(n, dtype=torch.int16, device=dev)
+    lo = torch.empty(n, dtype=torch.int16, device=dev)
+    synth.dev_bf16_normal(hi, args.seed, synth.STREAM_HI, 0, 0, synth.SIGMA_W)
+    synth.dev_u16_uniform(lo, args.seed, synth.STREAM_LO, 0, 0)
+    w32 = torch.empty(n, dtype=torch.float32, device=dev)
+    ps.join(hi, lo, w32)
+    m32 = w32 * 1e-3                     # moment-like values of both signs
+    v32 = m32 * m32
+    code = torch.empty(n, dtype=torch.int16, device=dev)
+    scale = torch.empty(nb, dtype=torch.float32, device=dev)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    cases = [
+        ("split_trunc", lambda: ps.split(w32, hi, lo, ps.SPLIT_TRUNC, stream=stream), 8 * n),
+        ("join_trunc", lambda: ps.join(hi, lo, out, ps.SPLIT_TRUNC, stream=stream), 8 * n),
+        ("split_nearest_away", lambda: ps.split(w32, hi, lo, ps.SPLIT_NEAREST_AWAY, stream=stream), 8 * n),
+        ("join_nearest_away", lambda: ps.join(hi, lo, out, ps.SPLIT_NEAREST_AWAY, stream=stream), 8 * n),
+        ("encode_signed", lambda: ps.encode_moments(m32, code, scale, ps.MOMENT_SIGNED, stream=stream), 6 * n + 4 * nb),
+        ("decode_signed", lambda: ps.decode_moments(code, scale, out, ps.MOMENT_SIGNED, stream=stream), 6 * n + 4 * nb),
+        ("encode_unsigned", lambda: ps.encode_moments(v32, code, scale, ps.MOMENT_UNSIGNED, stream=stream), 6 * n + 4 * nb),
+        ("decode_unsigned", lambda: ps.decode_moments(code, scale, out, ps.MOMENT_UNSIGNED, stream=stream), 6 * n + 4 * nb),
+    ]
+    res = {}
+    tot_bytes = tot_ms = 0.0
+    for name, fn, nbytes in cases:
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": ms, "bytes": nbytes, "gbs": gbs, "frac": gbs / PEAK_HBM_GBS}
+        tot_bytes += nbytes
+        tot_ms += ms
+        log(f"[bench] {name}: {ms:.3f} ms, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.3f} of 8 TB/s)")
+    worst = min(res, key=lambda k: res[k]["gbs"])
+    print(json.dumps({
+        "metric": "standalone split/join/encode/decode: algorithmic HBM GB/s over the eight kernels",
+        "value": tot_bytes / (tot_ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": tot_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"elementwise_{n}", "elements": n, "kernels": res},
+        "roofline": {"bound": "hbm", "achieved": res[worst]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": res[worst]["frac"], "traffic": None, "kernel": worst},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -564,11 +627,13 @@ def main():
                     help="state in one contiguous allocation per stream (slab) or one per tensor")
     ap.add_argument("--host-blocks", type=int, default=4,
                     help="offload mode: distinct pinned host state sets, reused cyclically by the 57 blocks")
-    ap.add_argument("--mode", default="nadam", choices=["nadam", "factored", "offload", "per_tensor"],
+    ap.add_argument("--elements", type=int, default=1 << 30,
+                    help="elementwise mode: array length")
+    ap.add_argument("--mode", default="nadam", choices=["nadam", "factored", "offload", "per_tensor", "elementwise"],
                     help="nadam: the fused (N)AdamW step (headline); factored: the Adafactor-style step "
                          "(factored second moment, update clipping; --beta1, --decay-rate) on the double-block "
                          "shapes; offload: host-resident state over PCIe; per_tensor: one call per tensor, as a "
-                         "gradient hook would step")
+                         "gradient hook would step; elementwise: the standalone split/join/encode/decode kernels")
     ap.add_argument("--per-tensor-calls", action="store_true",
                     help="factored mode: also time one call per tensor (the per-hook granularity)")
     ap.add_argument("--policy", action="store_true",
@@ -610,6 +675,8 @@ def main():
         return bench_offload(args)
     if args.mode == "per_tensor":
         return bench_per_tensor(args)
+    if args.mode == "elementwise":
+        return bench_elementwise(args)
     shapes = synth.WORKLOADS[args.workload]()
     n_params = synth.total_params(shapes)
     log(f"[bench] {args.workload}: {len(shapes)} tensors, {n_params} params; generating state on {dev}")

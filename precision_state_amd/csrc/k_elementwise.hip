@@ -2,9 +2,14 @@
 // docstring] and moment encode/decode [NADAM second post] kernels.
 //
 // split/join: one lane handles 8 consecutive elements (one 16-byte access of
-// 16-bit data, two of fp32), grid-stride. encode: the same 16-lanes-per-block
-// mapping as the fused step (each lane 16 elements, DPP row max). decode:
-// 8 elements per lane, one scale per lane (8 divides 256).
+// 16-bit data, two of fp32). encode: each wave takes 4 blocks of 256, 16
+// lanes per block, 16 elements per lane, DPP row max. decode: 8 elements per
+// lane, one scale per lane (8 divides 256). Every launch has one unit of work
+// per lane (the grid covers the array; the loops run once), so workgroups
+// dispatched in index order sweep the arrays front to back: that measured
+// 15-25% faster than a grid of 8 workgroups per CU striding over them.
+// Loads and the 16-bit stores carry the non-temporal hint (each byte is
+// touched once); the fp32 stores stay plain, which measured faster for them.
 #include "dev_common.h"
 #include "ps_internal.h"
 
@@ -13,10 +18,12 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ void ld_f8(const float* p, int64_t e, int64_t n, float* d) {
   if (e + 8 <= n) {
-    float4 a = *reinterpret_cast<const float4*>(p + e);
-    float4 b = *reinterpret_cast<const float4*>(p + e + 4);
+    const f32x4 a = __builtin_nontemporal_load((const GLOBAL f32x4*)(p + e));
+    const f32x4 b = __builtin_nontemporal_load((const GLOBAL f32x4*)(p + e + 4));
     d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
     d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
   } else {
@@ -36,7 +43,7 @@ __device__ __forceinline__ void st_f8(float* p, int64_t e, int64_t n, const floa
 
 __device__ __forceinline__ void ld_h8(const uint16_t* p, int64_t e, int64_t n, uint32_t fill, uint32_t* d) {
   if (e + 8 <= n) {
-    uint4 v = *reinterpret_cast<const uint4*>(p + e);
+    const u32x4 v = __builtin_nontemporal_load((const GLOBAL u32x4*)(p + e));
     d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
   } else {
     for (int j = 0; j < 4; ++j) {
@@ -49,7 +56,7 @@ __device__ __forceinline__ void ld_h8(const uint16_t* p, int64_t e, int64_t n, u
 
 __device__ __forceinline__ void st_h8(uint16_t* p, int64_t e, int64_t n, const uint32_t* s) {
   if (e + 8 <= n) {
-    *reinterpret_cast<uint4*>(p + e) = make_uint4(s[0], s[1], s[2], s[3]);
+    __builtin_nontemporal_store(u32x4{s[0], s[1], s[2], s[3]}, (GLOBAL u32x4*)(p + e));
   } else {
     for (int j = 0; j < 8; ++j)
       if (e + j < n) p[e + j] = (uint16_t)(s[j >> 1] >> (16 * (j & 1)));
@@ -146,10 +153,11 @@ __global__ __launch_bounds__(kThreads) void k_decode(const uint16_t* __restrict_
   }
 }
 
+// Workgroups covering n elements at units_per_block each (at most 2^31 - 1,
+// which covers every n the ABI accepts; the kernels' loops handle any rest).
 uint32_t grid_for(int64_t units_per_block, int64_t n) {
   int64_t g = (n + units_per_block - 1) / units_per_block;
-  int64_t cap = (int64_t)device_cu_count() * 8;
-  if (g > cap) g = cap;
+  if (g > 0x7FFFFFFF) g = 0x7FFFFFFF;
   if (g < 1) g = 1;
   return (uint32_t)g;
 }

@@ -33,18 +33,6 @@ ps_status hip_check(hipError_t e, const char* what) {
   return fail(PS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-int device_cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
-
 // ---------------------------------------------------------------------------
 // validation
 // ---------------------------------------------------------------------------

@@ -157,7 +157,6 @@ bool is_aligned(const void* p, uintptr_t a);
 void step_scalars(const ps_hparams& hp, int64_t step, StepScalars* out);
 
 // ---- device properties (ps_abi.cpp) ----
-int device_cu_count();
 
 // ---- launchers (k_adam.hip, k_elementwise.hip) ----
 ps_status launch_adam_ptr(const TablePtr& tbl, uint32_t total_items, const ps_hparams& hp, const StepScalars& c,
