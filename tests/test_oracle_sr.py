@@ -26,6 +26,21 @@ def test_splitmix64_published_outputs():
         assert oracle.splitmix64_at(0, k) == int(want, 16), k
 
 
+def test_sr_stream_of_key_zero_is_the_published_sequence():
+    """With seed 0, update 0 and tensor 0 the stream starts at state 0
+    (mix(0) = 0), so the random 16-bit values of elements 4k..4k+3, read as
+    one little-endian 64-bit word, are the generator's k-th published output
+    from state 0: this fixes which output word and which 16 bits each element
+    takes."""
+    outs = [int(x, 16) for x in page_figure("splitmix64_state0_outputs")["outputs"]]
+    r = oracle.sr_rand16(0, 0, 0, 0, 4 * len(outs)).astype(np.uint64)
+    for k, want in enumerate(outs):
+        word = sum(int(r[4 * k + j]) << (16 * j) for j in range(4))
+        assert word == want, (k, hex(word))
+    # an offset request reads the same values
+    assert np.array_equal(oracle.sr_rand16(0, 0, 0, 5, 6).astype(np.uint64), r[5:11])
+
+
 @pytest.mark.parametrize("bits", [0x3F800001, 0x3F80FFFF, 0x3F808000, 0xBF812345, 0x3F7FFFFF, 0x7F7F8001,
                                   0x00001234, 0x80017FFF, 0x4B7FC000])
 def test_sr_rounds_away_with_probability_of_the_fractional_distance(bits):
