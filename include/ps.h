@@ -190,10 +190,14 @@ typedef struct ps_factored_hparams {
  *   step's fp32 moments; codes re-encoded with them.
  * Scalars (ps_step_scalars) are computed on the host in double and rounded
  * once. `tensors` is a host array of n_tensors records (n_tensors == 0 is a
- * no-op); it is copied during the call. The library keeps a device copy of
- * each distinct tensor list it has seen (for lists longer than 16 records),
- * so repeated calls with the same list upload nothing. Tensors with storage
- * flags go to a second launch with a generic-format kernel.
+ * no-op); it is copied during the call. Lists of up to 16 records travel in
+ * the kernel arguments; for longer lists, and for the records with storage
+ * flags, the library keeps a device copy of each distinct list it has seen,
+ * so repeated calls with the same list upload nothing. That cache holds up
+ * to 16384 lists or 64 MiB per device; when it is full, the call
+ * synchronizes the device once and empties it. Tensors with storage flags go
+ * to a second launch with a generic-format kernel. Calls from several host
+ * threads, on their own streams and over distinct tensors, are safe.
  * Errors: PS_ERR_INVALID_ARG, PS_ERR_ALIGNMENT, PS_ERR_SHAPE (host checks,
  * before any device work); PS_ERR_HIP; PS_ERR_NO_MEMORY. */
 ps_status ps_opt_step_multi(const ps_tensor* tensors, int32_t n_tensors, const ps_hparams* hp, int64_t step,
@@ -248,7 +252,9 @@ ps_status ps_factored_workspace_size(const ps_tensor* tensors, int32_t n_tensors
  * Means and RMS are accumulated in double. A 1-D tensor keeps v in the
  * uint16 codec: v = fma(B2, decode(v), C2*q); U = g*(1/sqrt(v)); same clip.
  * workspace: device memory of at least ps_factored_workspace_size bytes,
- * 256-byte aligned, owned by the caller; its contents on entry are ignored.
+ * 256-byte aligned, owned by the caller; its contents on entry are ignored;
+ * calls that may run at the same time need distinct workspaces. The step's
+ * device plan goes through the same cache as ps_opt_step_multi's lists.
  * Errors as ps_opt_step_multi, plus PS_ERR_WORKSPACE. */
 ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps_factored_hparams* hp,
                            int64_t step, void* workspace, size_t workspace_bytes, ps_stream_t stream);
