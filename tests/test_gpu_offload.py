@@ -35,13 +35,14 @@ def _resident_copy(slab):
     return out
 
 
-def test_offload_equals_resident_bitwise():
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY])
+def test_offload_equals_resident_bitwise(split_mode):
     slabs = [ps.StateSlab(sizes, DEV, host_state=True) for sizes in GROUPS]
     for gid, sl in enumerate(slabs):
         _fill(sl, gid)
     torch.cuda.synchronize()
     resident = [_resident_copy(sl) for sl in slabs]
-    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=1e-4, weight_decay=0.01)
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=1e-4, weight_decay=0.01, split_mode=split_mode)
     grads = [[None if (gid == 1 and i == 1) else g for i, g in enumerate(sl.grads)] for gid, sl in enumerate(slabs)]
     plan = ps.OffloadPlan([(sl.states, grads[gid]) for gid, sl in enumerate(slabs)])
     h2d, d2h = plan.bytes()
