@@ -25,8 +25,8 @@ constexpr int kT = 256;
 
 // The apply pass touches the weights, residuals and first-moment codes once
 // per step: those accesses carry the non-temporal hint (measured ~9% faster
-// per step). The gradient passes keep plain loads, since the gradient is
-// read three times.
+// per step), and so do the stats pass's interior-tile gradient loads (~1%).
+// The U^2 pass keeps plain loads (the hint there changed nothing).
 __device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
   const u32x4 t = __builtin_nontemporal_load((const GLOBAL u32x4*)p);
   return make_uint4(t.x, t.y, t.z, t.w);
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kT) void k_f_stats(FPlan P, FScalars S) {
     const uint16_t* p = X.g + (size_t)(tr * kFTileRows + rg) * (size_t)X.C + (size_t)c;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const u32x4 v = *(const GLOBAL u32x4*)(p + (size_t)(8 * k) * (size_t)X.C);
+      const u32x4 v = __builtin_nontemporal_load((const GLOBAL u32x4*)(p + (size_t)(8 * k) * (size_t)X.C));
       w[k][0] = v.x; w[k][1] = v.y; w[k][2] = v.z; w[k][3] = v.w;
     }
 #pragma unroll
