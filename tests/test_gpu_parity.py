@@ -155,6 +155,25 @@ def test_single_1024x3072_nadam_10_steps_free_running():
         _assert_exact(dev, host, f"step {t}")
 
 
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_STOCHASTIC])
+def test_single_1024x3072_200_steps_sampled(split_mode):
+    """A long run: 200 NAdamW steps on the [1024, 3072] tensor (lr 1e-4 so
+    that the weights move every few steps; 0.1% gradient outliers x100), then
+    96 sampled 256-blocks, each replayed alone by the oracle over all 200
+    steps from the synthetic start."""
+    n = 1024 * 3072
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=1e-4, weight_decay=0.01, split_mode=split_mode, seed=99)
+    dev = dev_state(n, 4, 0)
+    g = torch.empty(n, dtype=torch.int16, device=DEV)
+    for t in range(1, 201):
+        synth.dev_bf16_normal(g, 4, synth.STREAM_GRAD, 0, t, synth.SIGMA_G, 0.001, 100.0)
+        ps.opt_step_multi([dev], [g], hp, t)
+    torch.cuda.synchronize()
+    shape = synth.Shape("w", 1024, 3072, n)
+    nblk = check_sampled_blocks([shape], [dev], hp, 200, 4, per_tensor=96, outlier_p=0.001)
+    assert nblk == 96
+
+
 @pytest.mark.parametrize("algo", [ps.ALGO_ADAM, ps.ALGO_NADAM])
 @pytest.mark.parametrize("wd", [0.0, 0.01])
 @pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY])
