@@ -645,6 +645,9 @@ def main():
     ap.add_argument("--split", default="trunc", choices=["trunc", "nearest_away", "stochastic"],
                     help="nadam mode: residual split mode; stochastic = stochastic rounding to bf16 with no "
                          "residual (PS_SPLIT_STOCHASTIC, 14 B/param)")
+    ap.add_argument("--weight-decay", type=float, default=0.0,
+                    help="nadam mode: decoupled weight decay (0.01 makes it the NAdamW step of the double-block "
+                         "workload's parity tests)")
     ap.add_argument("--beta1", type=float, default=0.0,
                     help="factored mode: first moment of the clipped update (0 = none)")
     ap.add_argument("--decay-rate", type=float, default=0.0,
@@ -688,7 +691,7 @@ def main():
 
     split = {"trunc": ps.SPLIT_TRUNC, "nearest_away": ps.SPLIT_NEAREST_AWAY,
              "stochastic": ps.SPLIT_STOCHASTIC}[args.split]
-    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=args.weight_decay,
                     split_mode=split, seed=args.seed)
     n_small = n_final = 0
     if args.policy:
@@ -776,7 +779,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "params": n_params, "tensors": len(shapes),
-                   "algo": "nadam", "lr": 3.5e-6, "weight_decay": 0.0, "layout": args.layout,
+                   "algo": "nadam", "lr": 3.5e-6, "weight_decay": args.weight_decay, "layout": args.layout,
                    "policy": {"fp32_moment_tensors": n_small, "fp32_param_tensors": n_final} if args.policy else None,
                    "moments": args.moments, "split": args.split,
                    "state": ("bf16 weight (stochastic rounding, no residual)" if args.split == "stochastic"
