@@ -191,7 +191,7 @@ def host_threads():
     return max(1, min(16, n))
 
 
-def cpu_baseline(shapes, seed, target_params=60_000_000):
+def cpu_baseline(shapes, seed, target_params=60_000_000, weight_decay=0.0):
     """The oracle as it stands, one NAdam step over the leading tensors of the
     set (about target_params parameters): timed on one thread, then on all the
     host threads of this process over block-aligned chunks of the same sample
@@ -216,7 +216,7 @@ def cpu_baseline(shapes, seed, target_params=60_000_000):
                                 synth.host_u16_uniform(n, seed, synth.STREAM_LO, tid, 0), *oracle.zero_moments(n))
         inputs.append((st, synth.host_bf16_normal(n, seed, synth.STREAM_GRAD, tid, 1, synth.SIGMA_G)))
     copies = [(st.copy(), g) for st, g in inputs]
-    hp = oracle.HParams(algo=oracle.ALGO_NADAM, lr=3.5e-6)
+    hp = oracle.HParams(algo=oracle.ALGO_NADAM, lr=3.5e-6, weight_decay=weight_decay)
     t0 = time.perf_counter()
     for st, g in inputs:
         oracle.opt_step(st, g, hp, 1)
@@ -762,7 +762,7 @@ def main():
         del states, grads, recs
         torch.cuda.empty_cache()
         log("[bench] timing the oracle on the host (cpu_baseline)")
-        baseline = cpu_baseline(shapes, args.seed)
+        baseline = cpu_baseline(shapes, args.seed, weight_decay=args.weight_decay)
         log(f"[bench] oracle: {baseline['value']:.3e} params/s ({baseline['sample']})")
 
     out = {
