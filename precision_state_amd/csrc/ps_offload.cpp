@@ -4,19 +4,22 @@
 // stochastic rounding, the pages' setting when host memory is short, no
 // residual exists and only the moments travel].
 //
-// Two device staging slots hold one group's residuals, codes and scales each.
-// Group k uses slot k % 2:
-//   upload stream:   wait(download of k-2 done) -> copies host->slot -> event in[k%2]
-//   compute stream:  wait(in[k%2]) -> fused step of group k -> event done[k%2]
-//   download stream: wait(done[k%2]) -> copies slot->host -> event out[k%2]
+// kSlots (2) device staging slots hold one group's residuals, codes and
+// scales each. Group k uses slot s = k % 2:
+//   upload stream:   wait(download of k-2 done) -> copies host->slot -> event in[s]
+//   compute stream:  wait(in[s]) -> fused step of group k -> event done[s]
+//   download stream: wait(done[s]) -> copies slot->host -> event out[s]
 // so the upload of k+1 and the download of k-1 overlap the step of k, and the
-// two copy directions run concurrently. The step kernel is the resident one,
+// two copy directions run concurrently (a third slot measured no faster: the
+// pipeline already moves data at the link's duplex rate). The step kernel is the resident one,
 // reading the slot through a per-(group, slot) device table, so results are
 // bit-identical to ps_opt_step_multi on device-resident state.
 #include <cstring>
 #include <vector>
 
 #include "ps_internal.h"
+
+constexpr int kSlots = 2;   // device staging slots (group k uses slot k % kSlots)
 
 struct ps_offload_plan {
   int device = -1;
@@ -28,22 +31,22 @@ struct ps_offload_plan {
   struct Group {
     std::vector<Copy> copies;          // codes and scales, same list for both directions
     std::vector<Copy> lo_copies;       // residuals (skipped under stochastic rounding)
-    size_t table_off[2] = {0, 0};      // device table of this group for slot 0 / 1
+    size_t table_off[kSlots] = {};     // device table of this group for each slot
     int32_t n_active = 0;
     uint32_t total_items = 0;
   };
   std::vector<Group> groups;
   size_t slot_bytes = 0;
-  char* slots[2] = {nullptr, nullptr};
+  char* slots[kSlots] = {};
   char* tables = nullptr;
   hipStream_t up = nullptr, down = nullptr;
-  hipEvent_t in_ev[2] = {nullptr, nullptr}, done_ev[2] = {nullptr, nullptr}, out_ev[2] = {nullptr, nullptr};
+  hipEvent_t in_ev[kSlots] = {}, done_ev[kSlots] = {}, out_ev[kSlots] = {};
   hipEvent_t start_ev = nullptr, end_ev = nullptr;
   uint64_t bytes_per_dir = 0;          // residual modes
   uint64_t lo_bytes_per_dir = 0;       // of which residuals
   uint64_t last_bytes_per_dir = 0;     // the most recent run
   bool has_residual = true;            // every active tensor has w_lo
-  bool out_recorded[2] = {false, false};  // out_ev[s] has been recorded by some run
+  bool out_recorded[kSlots] = {};     // out_ev[s] has been recorded by some run
 };
 
 namespace ps {
@@ -55,7 +58,7 @@ size_t up256(size_t x) { return (x + kAlignBytes - 1) / kAlignBytes * kAlignByte
 void destroy(ps_offload_plan* p) {
   if (!p) return;
   if (p->device >= 0) (void)hipDeviceSynchronize();
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < kSlots; ++s) {
     if (p->slots[s]) (void)hipFree(p->slots[s]);
     if (p->in_ev[s]) (void)hipEventDestroy(p->in_ev[s]);
     if (p->done_ev[s]) (void)hipEventDestroy(p->done_ev[s]);
@@ -194,13 +197,13 @@ ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_group
   // device tables: per group and slot, DevTensor[n] then item ends[n]
   std::vector<unsigned char> tab;
   for (int32_t g = 0; g < n_groups; ++g)
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < kSlots; ++s) {
       p->groups[g].table_off[s] = tab.size();
       const size_t n = recs[g].size();
       tab.resize(tab.size() + up256(n * sizeof(DevTensor)) + up256(n * sizeof(uint32_t)));
     }
   ps_status st = PS_OK;
-  for (int s = 0; s < 2 && !st; ++s)
+  for (int s = 0; s < kSlots && !st; ++s)
     if (hipMalloc((void**)&p->slots[s], p->slot_bytes ? p->slot_bytes : 256) != hipSuccess)
       st = fail(PS_ERR_NO_MEMORY, "offload staging slot allocation failed (%zu bytes)", p->slot_bytes);
   if (!st && hipMalloc((void**)&p->tables, tab.empty() ? 256 : tab.size()) != hipSuccess)
@@ -210,7 +213,7 @@ ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_group
     return st;
   }
   for (int32_t g = 0; g < n_groups; ++g)
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < kSlots; ++s) {
       const size_t n = recs[g].size();
       DevTensor* dst = (DevTensor*)(tab.data() + p->groups[g].table_off[s]);
       for (size_t i = 0; i < n; ++i) {
@@ -231,7 +234,7 @@ ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_group
   if (!tab.empty()) st = hip_check(hipMemcpy(p->tables, tab.data(), tab.size(), hipMemcpyHostToDevice), "table upload");
   if (!st) st = hip_check(hipStreamCreateWithFlags(&p->up, hipStreamNonBlocking), "hipStreamCreate");
   if (!st) st = hip_check(hipStreamCreateWithFlags(&p->down, hipStreamNonBlocking), "hipStreamCreate");
-  for (int s = 0; s < 2 && !st; ++s) {
+  for (int s = 0; s < kSlots && !st; ++s) {
     st = hip_check(hipEventCreateWithFlags(&p->in_ev[s], hipEventDisableTiming), "hipEventCreate");
     if (!st) st = hip_check(hipEventCreateWithFlags(&p->done_ev[s], hipEventDisableTiming), "hipEventCreate");
     if (!st) st = hip_check(hipEventCreateWithFlags(&p->out_ev[s], hipEventDisableTiming), "hipEventCreate");
@@ -265,7 +268,7 @@ ps_status ps_offload_run(ps_offload_plan* p, const ps_hparams* hp, int64_t step,
   const int G = (int)p->groups.size();
   for (int k = 0; k < G && !st; ++k) {
     const auto& grp = p->groups[k];
-    const int s = k & 1;
+    const int s = k % kSlots;
     // the slot is free once its previous download (this run's group k-2, or
     // an earlier run's last group on it, whatever stream that run was given)
     // has landed
