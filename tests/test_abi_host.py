@@ -160,3 +160,19 @@ def test_factored_workspace_size_and_validation(ps):
     assert L.ps_factored_step((ps.CTensor * 1)(_frec(ps, m_code=0)), 1, ctypes.byref(h0), 1, None, 0, None) == 7
     empty = (ps.CTensor * 1)(_frec(ps, grad=0))
     assert L.ps_factored_step(empty, 1, ctypes.byref(hp), 1, None, 0, None) == 0
+
+
+def test_build_scripts_load_without_the_built_library():
+    """build() must work in a tree where libps.so does not exist yet: the
+    package refuses to import until it is built, so its build script is loaded
+    by path. Checked in a fresh interpreter that the package stays unimported."""
+    import subprocess
+    import sys
+    code = ("import sys, __graft_entry__ as g\n"
+            "for p in ('precision_state_amd', 'synth', 'oracle'):\n"
+            "    m = g._load_build_module(p)\n"
+            "    assert callable(m.build) and m.LIB.endswith('.so'), p\n"
+            "assert 'precision_state_amd' not in sys.modules\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
