@@ -156,7 +156,7 @@ typedef struct ps_hparams {
  *               (B1 = fp32(beta1), C1 = fp32(1 - beta1)) before weight decay
  *               [ADAF], m kept in m_code / m_scale (signed codec, per-256
  *               blocks of the flattened tensor); 2-D tensors then need
- *               cols % 8 == 0 and numel < 2^31 (else PS_ERR_UNSUPPORTED)
+ *               numel < 2^31 (else PS_ERR_UNSUPPORTED)
  *   split_mode  TRUNC, NEAREST_AWAY, or STOCHASTIC (no residual; the random
  *               bits exactly as for ps_hparams, from `seed`, the update
  *               number and the tensor's index in the list)

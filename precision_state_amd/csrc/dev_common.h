@@ -27,6 +27,25 @@ __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel)
 }
 
 // ---------------------------------------------------------------------------
+// XCD-aware work order. MI355X dispatches consecutive workgroups round-robin
+// over its 8 XCDs, each with its own L2 and address-translation caches, so in
+// index order every XCD touches every page of the range in flight. This
+// bijection on [0, gridDim.x) instead gives each XCD runs of CHUNK
+// consecutive work items (chunk c of XCD x is items (8c + x)·CHUNK ...); the
+// items past the last whole round of 8 chunks keep their own index.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kXcdCount = 8;
+constexpr uint32_t kXcdChunk = 2048;   // (N)AdamW step: 2048 items of 512 elements
+
+template <uint32_t CHUNK = kXcdChunk>
+__device__ __forceinline__ uint32_t xcd_item(uint32_t wg, uint32_t n_wg) {
+  constexpr uint32_t kRound = kXcdCount * CHUNK;
+  if (wg >= n_wg / kRound * kRound) return wg;
+  const uint32_t x = wg % kXcdCount, l = wg / kXcdCount;
+  return (l / CHUNK) * kRound + x * CHUNK + l % CHUNK;
+}
+
+// ---------------------------------------------------------------------------
 // Residual split / join [KAHAN]: fp32 bits = hi << 16 | lo (TRUNC), or the
 // round-to-nearest-away variant whose join subtracts the carry back out.
 // ---------------------------------------------------------------------------

@@ -211,11 +211,14 @@ __device__ __forceinline__ uint32_t item_end(const TBL& t, int i) { return t.ite
 // One work item per 64-lane workgroup. Workgroups are dispatched in index
 // order, so the waves in flight at any moment cover a compact address range;
 // this keeps HBM pages open and measured faster than persistent waves that
-// stride over the items. The tensor of the item is found by a wave-uniform
+// stride over the items. Within that range each XCD takes runs of
+// kXcdChunk consecutive items (xcd_item): 1.7% faster per step than plain
+// index order on the 11.9B set, while runs of 64 items or one contiguous
+// eighth of the list per XCD were 3-5% slower. The tensor of the item is found by a wave-uniform
 // binary search over the prefix ends (scalar loads).
 template <class TBL, int ALGO, bool WD, int SPLIT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(7))) void k_adam_step(TBL tbl, StepScalars c) {
-  const uint32_t item = blockIdx.x;
+  const uint32_t item = xcd_item<>(blockIdx.x, gridDim.x);
   int lo = 0, hi = tbl.n - 1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
@@ -419,7 +422,7 @@ __device__ __forceinline__ void process_item_ex(const DevTensorEx& T, int64_t el
 
 template <int ALGO, bool WD, int SPLIT>
 __global__ __launch_bounds__(64) void k_adam_step_ex(TableExPtr tbl, StepScalars c) {
-  const uint32_t item = blockIdx.x;
+  const uint32_t item = xcd_item<>(blockIdx.x, gridDim.x);
   int lo = 0, hi = tbl.n - 1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;

@@ -17,6 +17,10 @@ namespace ps {
 namespace {
 
 constexpr int kThreads = 256;
+// Each XCD takes runs of 256 consecutive workgroups (512K elements; the
+// encoder's workgroups cover twice as many, so half as many of them): 2-6%
+// faster than plain index order on 2^30 elements, runs of 512 to 2048 slower.
+constexpr uint32_t kEwXcdChunk = 256;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -67,7 +71,7 @@ template <int MODE>
 __global__ __launch_bounds__(kThreads) void k_split(const float* __restrict__ w, uint16_t* __restrict__ hi,
                                                     uint16_t* __restrict__ lo, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * kThreads * 8;
-  for (int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8; e < n; e += stride) {
+  for (int64_t e = ((int64_t)xcd_item<kEwXcdChunk>(blockIdx.x, gridDim.x) * kThreads + threadIdx.x) * 8; e < n; e += stride) {
     float f[8];
     uint32_t h[4], l[4];
     ld_f8(w, e, n, f);
@@ -82,7 +86,7 @@ template <int MODE>
 __global__ __launch_bounds__(kThreads) void k_join(const uint16_t* __restrict__ hi, const uint16_t* __restrict__ lo,
                                                    float* __restrict__ w, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * kThreads * 8;
-  for (int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8; e < n; e += stride) {
+  for (int64_t e = ((int64_t)xcd_item<kEwXcdChunk>(blockIdx.x, gridDim.x) * kThreads + threadIdx.x) * 8; e < n; e += stride) {
     uint32_t h[4], l[4];
     float f[8];
     ld_h8(hi, e, n, 0u, h);
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(const float* __restrict__ x
                                                      float* __restrict__ scale, int64_t n) {
   const int lane = threadIdx.x & 63;
   const int b = lane >> 4, r = lane & 15;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6));
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(xcd_item<kEwXcdChunk / 2>(blockIdx.x, gridDim.x) * (kThreads / 64) + (threadIdx.x >> 6));
   const uint32_t n_waves = gridDim.x * (kThreads / 64);
   const int64_t n_items = (n + kItemElems - 1) / kItemElems;
   for (int64_t item = wave; item < n_items; item += n_waves) {
@@ -134,7 +138,7 @@ template <int KIND>
 __global__ __launch_bounds__(kThreads) void k_decode(const uint16_t* __restrict__ code, const float* __restrict__ scale,
                                                      float* __restrict__ x, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * kThreads * 8;
-  for (int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8; e < n; e += stride) {
+  for (int64_t e = ((int64_t)xcd_item<kEwXcdChunk>(blockIdx.x, gridDim.x) * kThreads + threadIdx.x) * 8; e < n; e += stride) {
     uint32_t c[4];
     float f[8];
     ld_h8(code, e, n, KIND == PS_MOMENT_SIGNED ? 0x80008000u : 0u, c);

@@ -22,6 +22,10 @@ namespace ps {
 namespace {
 
 constexpr int kT = 256;
+// The flat ΣU² and apply passes give each XCD runs of 256 consecutive work
+// items (256K elements): about 2% less time per step than plain index order
+// on the double-block shapes (runs of 128 to 1024 items measured alike).
+constexpr uint32_t kFlatXcdChunk = 256;
 
 // The apply pass touches the weights, residuals and first-moment codes once
 // per step: those accesses carry the non-temporal hint (measured ~9% faster
@@ -317,10 +321,72 @@ __device__ __forceinline__ void load_kap8(const float* __restrict__ kap, uint32_
   k[0] = a.x; k[1] = a.y; k[2] = a.z; k[3] = a.w; k[4] = b.x; k[5] = b.y; k[6] = b.z; k[7] = b.w;
 }
 
+// Flat items of a tensor whose column count is not a multiple of 8 (taken
+// only with a first moment, whose per-256 blocks follow the flattened index):
+// a run of 8 may cross rows and the tensor's last run may be partial, so the
+// row and column of each element are found one by one and the loads and
+// stores of a partial run go element by element. Missing elements read as
+// `fill` and are not written.
+__device__ __forceinline__ uint4 ld_run(const uint16_t* p, uint32_t e, uint32_t n, uint32_t fill, bool nt) {
+  if (e + 8 <= n) return nt ? ld_stream(p + e) : *reinterpret_cast<const uint4*>(p + e);
+  const GLOBAL uint16_t* q = (const GLOBAL uint16_t*)p;
+  uint32_t w[4];
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t a = (e + 2 * j < n) ? q[e + 2 * j] : (fill & 0xFFFFu);
+    const uint32_t b = (e + 2 * j + 1 < n) ? q[e + 2 * j + 1] : (fill >> 16);
+    w[j] = a | (b << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ void st_run(uint16_t* p, uint32_t e, uint32_t n, const uint32_t* w) {
+  if (e + 8 <= n) {
+    st_stream(p + e, make_uint4(w[0], w[1], w[2], w[3]));
+    return;
+  }
+  GLOBAL uint16_t* q = (GLOBAL uint16_t*)p;
+  for (int j = 0; j < 8; ++j)
+    if (e + j < n) q[e + j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+}
+
+// Factor rho_i * kap_j of flattened element e (e < R*C).
+__device__ __forceinline__ void elem_factors(const F2D& X, uint32_t e, float& rho, float& kap) {
+  const uint32_t i = e / (uint32_t)X.C;
+  rho = X.rho[i];
+  kap = X.kap[e - i * (uint32_t)X.C];
+}
+
+// U^2 sum of one item, any column count (same per-lane order as the run path).
+__device__ __forceinline__ void usq_item_any(const F2D& X, uint32_t item) {
+  const uint32_t n = (uint32_t)X.R * (uint32_t)X.C;
+  const uint32_t la = (threadIdx.x >> 4) * (uint32_t)kBlock + (threadIdx.x & 15) * 8u;
+  double acc = 0.0;
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t e = item * (uint32_t)kItemElems + la + 128u * h;
+    if (e >= n) continue;
+    const uint4 gv = ld_run(X.g, e, n, 0u, false);
+    const uint32_t w[4] = {gv.x, gv.y, gv.z, gv.w};
+    for (int jj = 0; jj < 8; ++jj) {
+      if (e + jj >= n) break;
+      float rho, kap;
+      elem_factors(X, e + jj, rho, kap);
+      const float U = (bf16_at(w, jj) * rho) * kap;
+      acc += (double)U * (double)U;
+    }
+  }
+  for (int o = 1; o < 64; o <<= 1) acc += __shfl_xor(acc, o, 64);
+  if (threadIdx.x == 0) X.upart[item] = acc;
+}
+
 __global__ __launch_bounds__(64) void k_f_usq_flat(FPlan P) {
   uint32_t begin;
-  const F2D& X = P.t2[find_end(P.item2_end, P.n2, blockIdx.x, begin)];
-  const uint32_t item = blockIdx.x - begin;
+  const uint32_t wg = xcd_item<kFlatXcdChunk>(blockIdx.x, gridDim.x);
+  const F2D& X = P.t2[find_end(P.item2_end, P.n2, wg, begin)];
+  const uint32_t item = wg - begin;
+  if (!X.vec) {   // uniform per tensor
+    usq_item_any(X, item);
+    return;
+  }
   FlatRun run[2];
   flat_runs(X, item, run);
   uint4 gv[2];
@@ -345,13 +411,88 @@ __global__ __launch_bounds__(64) void k_f_usq_flat(FPlan P) {
   if (threadIdx.x == 0) X.upart[item] = acc;
 }
 
+// Apply of one item, any column count: the arithmetic of the run path below,
+// with each element's own row and column factors.
+template <int SPLIT>
+__device__ __forceinline__ void apply_item_any(const F2D& X, uint32_t item, const FScalars& S, float f) {
+  constexpr bool SR = SPLIT == PS_SPLIT_STOCHASTIC;
+  const uint32_t n = (uint32_t)X.R * (uint32_t)X.C;
+  const uint32_t la = (threadIdx.x >> 4) * (uint32_t)kBlock + (threadIdx.x & 15) * 8u;
+  const uint32_t blk = item * (uint32_t)kItemBlocks + (threadIdx.x >> 4);
+  const bool blk_ok = blk * (uint32_t)kBlock < n;
+  const float ms_old = (S.fm && blk_ok) ? X.ms[blk] : 0.0f;
+  float m[16];
+  float mx = 0.0f;
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t e = item * (uint32_t)kItemElems + la + 128u * h;
+    for (int j = 0; j < 8; ++j) m[8 * h + j] = 0.0f;
+    if (e >= n) continue;
+    const uint4 gv = ld_run(X.g, e, n, 0u, true), hv = ld_run(X.hi, e, n, 0u, true);
+    const uint4 lv = SR ? make_uint4(0u, 0u, 0u, 0u) : ld_run(X.lo, e, n, 0u, true);
+    const uint4 mv = S.fm ? ld_run(X.mc, e, n, 0x80008000u, true) : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+    const uint32_t lw[4] = {lv.x, lv.y, lv.z, lv.w};
+    const uint32_t mw[4] = {mv.x, mv.y, mv.z, mv.w};
+    uint32_t oh[4], ol[4];
+    uint64_t rnd[2] = {0u, 0u};
+    if (SR) sr_bits8(sr_stream(S.sr_seed, S.sr_step, X.tid), e, rnd);
+    for (int p = 0; p < 4; ++p) {
+      uint32_t wb[2];
+      for (int o = 0; o < 2; ++o) {
+        const int jj = 2 * p + o;
+        const float w = SR ? bf16_at(hw, jj) : __uint_as_float(join_pair_elem<SPLIT>(hw[p], lw[p], o));
+        float x = 0.0f;
+        if (e + jj < n) {
+          float rho, kap;
+          elem_factors(X, e + jj, rho, kap);
+          x = ((bf16_at(gw, jj) * rho) * kap) * f;
+          if (S.fm) {
+            const float m0 = dec_signed(o ? code_hi_f(mw[p]) : code_lo_f(mw[p]), ms_old);
+            x = __builtin_fmaf(S.B1, m0, S.C1 * x);
+            m[8 * h + jj] = x;
+            mx = __builtin_fmaxf(mx, __builtin_fabsf(x));
+          }
+          if (S.wd) x = __builtin_fmaf(S.CWD, w, x);
+        }
+        wb[o] = __float_as_uint(w - x);
+      }
+      if (SR) {
+        const uint64_t q = rnd[p >> 1] >> (32 * (p & 1));
+        oh[p] = sr_pair(wb[0], wb[1], (uint32_t)q & 0xFFFFu, (uint32_t)(q >> 16) & 0xFFFFu);
+      } else {
+        split_pair<SPLIT>(wb[0], wb[1], oh[p], ol[p]);
+      }
+    }
+    st_run(X.hi, e, n, oh);
+    if (!SR) st_run(X.lo, e, n, ol);
+  }
+  if (!S.fm) return;   // uniform
+  float sm, inv;
+  block_scale(row16_max(mx), sm, inv);
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t e = item * (uint32_t)kItemElems + la + 128u * h;
+    if (e >= n) continue;
+    uint32_t om[4];
+    for (int p = 0; p < 4; ++p)
+      om[p] = enc_signed(m[8 * h + 2 * p], inv) | (enc_signed(m[8 * h + 2 * p + 1], inv) << 16);
+    st_run(X.mc, e, n, om);
+  }
+  if ((threadIdx.x & 15) == 0 && blk_ok) X.ms[blk] = sm;
+}
+
 template <int SPLIT>
 __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
   constexpr bool SR = SPLIT == PS_SPLIT_STOCHASTIC;
   uint32_t begin;
-  const F2D& X = P.t2[find_end(P.item2_end, P.n2, blockIdx.x, begin)];
-  const uint32_t item = blockIdx.x - begin;
+  const uint32_t wg = xcd_item<kFlatXcdChunk>(blockIdx.x, gridDim.x);
+  const F2D& X = P.t2[find_end(P.item2_end, P.n2, wg, begin)];
+  const uint32_t item = wg - begin;
   const float f = *X.f;
+  if (!X.vec) {   // uniform per tensor
+    apply_item_any<SPLIT>(X, item, S, f);
+    return;
+  }
   FlatRun run[2];
   flat_runs(X, item, run);
   // first moment: the item's 4 blocks are the 4 DPP rows (16 lanes x 2 runs)

@@ -6,6 +6,7 @@
 // the new row EMAs per 256-row chunk, rho[R], kap[C], sums of U^2 per tile,
 // the clip factor. Per 1-D tensor: this step's v[n], sums of U^2 per
 // 1024-element item, the clip factor. Every region starts on 256 bytes.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -81,20 +82,28 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, 
       d.nrw = (d.R + kFRowColChunk - 1) / kFRowColChunk;
       d.ncw = (d.C + kFRowColChunk - 1) / kFRowColChunk;
       d.vec = (d.C % 8) == 0;
-      d.flat = d.vec && x.numel < (int64_t(1) << 31);
+      // Flat items: every tensor below 2^31 elements whose rows are 16-byte
+      // runs, and with a first moment (per-256 blocks of the flattened index)
+      // also the others, whose items then take per-element row/column factors.
+      d.flat = (d.vec || fm) && x.numel < (int64_t(1) << 31);
       if (fm && !d.flat)
-        return fail(PS_ERR_UNSUPPORTED, "tensor %d: a first moment needs cols %% 8 == 0 and numel < 2^31", i);
+        return fail(PS_ERR_UNSUPPORTED, "tensor %d: a first moment needs numel < 2^31", i);
       d.mc = fm ? x.m_code : nullptr;
       d.ms = fm ? x.m_scale : nullptr;
       d.tid = (uint32_t)i;
       d.nitems = d.flat ? (int32_t)((x.numel + kItemElems - 1) / kItemElems) : 0;
       d.npart = d.flat ? d.nitems : d.ntr * d.ntc;
+      // The U^2 partials get room for both forms (items and tiles), so the
+      // workspace layout, and ps_factored_workspace_size, do not depend on
+      // whether a first moment is kept.
+      const int64_t items_any = x.numel < (int64_t(1) << 31) ? (x.numel + kItemElems - 1) / kItemElems : 0;
+      const int64_t upart_n = std::max<int64_t>(items_any, (int64_t)d.ntr * d.ntc);
       d.rowpart = (double*)take(sizeof(double) * (size_t)d.ntc * d.R);
       d.colpart = (double*)take(sizeof(double) * (size_t)d.ntr * d.C);
       d.rpart = (double*)take(sizeof(double) * (size_t)d.nrw);
       d.rho = (float*)take(sizeof(float) * (size_t)d.R);
       d.kap = (float*)take(sizeof(float) * (size_t)d.C);
-      d.upart = (double*)take(sizeof(double) * (size_t)d.npart);
+      d.upart = (double*)take(sizeof(double) * (size_t)upart_n);
       d.f = (float*)take(sizeof(float));
       tiles += (uint64_t)d.ntr * d.ntc;
       rc += (uint64_t)d.nrw + d.ncw;

@@ -95,7 +95,7 @@ struct F2D {
   float* ms;         // first moment block scales or NULL
   int32_t R, C, ntr, ntc, nrw, ncw;
   int32_t vec;       // C % 8 == 0: 16-byte row segments
-  int32_t flat;      // vec and R*C < 2^31: U^2 and apply passes run over 1024-element items
+  int32_t flat;      // R*C < 2^31 and (vec or a first moment): U^2 and apply passes run over 1024-element items
   int32_t nitems;    // flat: items of 1024 elements
   int32_t npart;     // entries of upart (nitems if flat, else ntr * ntc)
   uint32_t tid;      // index in the caller's list (stochastic rounding stream key)

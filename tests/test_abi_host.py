@@ -139,15 +139,15 @@ def test_factored_workspace_size_and_validation(ps):
                  ("decay_rate", 0.5), ("beta1", 1.0), ("beta1", -0.1)):
         h = ps.FactoredHParams(**{k: v}).c()
         assert L.ps_factored_step(arr, 2, ctypes.byref(h), 1, 4096, 1 << 20, None) == 1, k
-    # a first moment needs m_code / m_scale and, for 2-D tensors, cols % 8 == 0
+    # a first moment needs m_code / m_scale and, for 2-D tensors, fewer than 2^31 elements
     h = ps.FactoredHParams(beta1=0.9).c()
     assert L.ps_factored_step((ps.CTensor * 1)(_frec(ps, m_code=0)), 1, ctypes.byref(h), 1, 4096, 1 << 20,
                               None) == 1
     assert L.ps_factored_step((ps.CTensor * 1)(_frec(ps, m_code=160, m_scale=82)), 1, ctypes.byref(h), 1, 4096,
                               1 << 20, None) == 2
-    odd = (ps.CTensor * 1)(_frec(ps, n=33 * 30, rows=33, cols=30, m_code=160, m_scale=176))
-    assert L.ps_factored_step(odd, 1, ctypes.byref(h), 1, 4096, 1 << 20, None) == 4
-    assert "cols % 8" in ps.last_error()
+    big = (ps.CTensor * 1)(_frec(ps, n=1 << 31, rows=1 << 16, cols=1 << 15, m_code=160, m_scale=176))
+    assert L.ps_factored_step(big, 1, ctypes.byref(h), 1, 4096, 1 << 40, None) == 4
+    assert "numel < 2^31" in ps.last_error()
     # stochastic rounding keeps no residual: w_lo may be NULL
     hs = ps.FactoredHParams(split_mode=ps.SPLIT_STOCHASTIC).c()
     assert L.ps_factored_step((ps.CTensor * 1)(_frec(ps, w_lo=0, row_ema=0)), 1, ctypes.byref(hs), 1, 4096,

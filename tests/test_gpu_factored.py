@@ -155,3 +155,19 @@ def test_factored_first_moment_ragged(split_mode):
     moving them), with the schedule on."""
     hp = ps.FactoredHParams(split_mode=split_mode, lr=1e-4, weight_decay=0.01, decay_rate=-0.8, beta1=0.8, seed=99)
     _run(FM_RAGGED, hp, 5, 9, 0.01, zero_grad=(3, 9))
+
+
+FM_ANY_COLS = [synth.Shape("a", 1, 1, 1), synth.Shape("b", 1, 300, 300), synth.Shape("c", 300, 1, 300),
+               synth.Shape("d", 65, 257, 65 * 257), synth.Shape("l", 70, 130, 9100), synth.Shape("p", 5, 3, 15),
+               synth.Shape("q", 401, 499, 401 * 499), synth.Shape("f", 64, 256, 64 * 256),
+               synth.Shape("j", 0, 0, 257)]
+
+
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY, ps.SPLIT_STOCHASTIC])
+def test_factored_first_moment_any_column_count(split_mode):
+    """A first moment on 2-D tensors whose column count is not a multiple of 8
+    (runs of 8 elements that cross one or several rows, tensors ending inside
+    a run, a block and an item; 1 x C, R x 1 and 1 x 1), next to a 16-byte-row
+    tensor and a 1-D tensor in the same call; a zero gradient in one of them."""
+    hp = ps.FactoredHParams(split_mode=split_mode, lr=1e-4, weight_decay=0.01, decay_rate=-0.8, beta1=0.8, seed=7)
+    _run(FM_ANY_COLS, hp, 5, 11, 0.01, zero_grad=(4,))
