@@ -9,13 +9,17 @@
 // contiguous bytes of every 16-bit stream with 16-byte accesses. The block
 // maximum is a butterfly within each row plus one row-pair exchange.
 //
-// Order of memory traffic within a wave: gradient and moment codes first
-// (they decide the block scales), the weight words only once the scales are
-// known, just before the update needs them. Spreading each wave's traffic
-// this way, with 8 elements per lane, measured markedly faster than loading
-// every stream up front with 16 elements per lane. The block maxima are taken
-// on float bit patterns (one fused DPP max per step); the occupancy hint keeps
-// the NAdam kernels at 70 VGPRs (7 waves per SIMD) without spills.
+// Order of memory traffic within a wave: gradient and moment codes into
+// registers (they decide the block scales), and in the same breath the weight
+// words of a full item straight into LDS (global_load_lds_dwordx4, 2 KiB per
+// wave), so all five streams are in flight at once without holding the weight
+// words in VGPRs through the decode, EMA and block-maximum phase; the update
+// reads them from LDS. This measured 1.5% faster per step than loading the
+// weight words into registers after the block scales (which in turn was
+// 3-12% faster than every stream loaded into registers up front with 16
+// elements per lane). The block maxima are taken on float bit patterns (one
+// fused DPP max per step); the occupancy hint keeps the NAdam kernels at 7
+// waves per SIMD without spills.
 //
 // Per element the kernel reads hi, lo, grad, m_code, v_code (10 bytes) and
 // writes hi, lo, m_code, v_code (8 bytes); per block it reads and writes the
@@ -48,6 +52,16 @@ __device__ __forceinline__ void store8(uint16_t* p, const uint32_t* src) {
   st_nt((u32x4*)p, u32x4{src[0], src[1], src[2], src[3]});
 }
 
+// 16 bytes per lane from p straight into LDS: lane i's bytes land at
+// dst + 16 i (dst is wave-uniform). Cache-policy bit 1 (nt) marks the load
+// non-temporal like the register loads; without it the step was 1.5% slower
+// than the register path instead of 1.5% faster.
+constexpr int kLdsDmaNt = 2;
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void load8_to_lds(const uint16_t* p, u32x4* dst) {
+  __builtin_amdgcn_global_load_lds((const GLOBAL void*)p, (lds_void*)dst, 16, 0, kLdsDmaNt);
+}
+
 // Guarded variants for the last work item of a tensor: element e + j exists
 // when e + j < n; missing elements read as `fill` and are not written.
 __device__ __forceinline__ void load8_guard(const uint16_t* p, int64_t e, int64_t n, uint32_t fill, uint32_t* dst) {
@@ -74,17 +88,23 @@ __device__ __forceinline__ void store8_guard(uint16_t* p, int64_t e, int64_t n, 
 }
 
 // Update, residual split and moment encode of one lane's 8 elements, then the
-// stores. The weight words are loaded here, after the block scales are
-// known. SLOW selects the library square root for the whole wave.
+// stores. A full item's weight words are waiting in LDS (wl[0]: hi, wl[1]:
+// lo, one 16-byte entry per lane); a partial item loads them here with
+// per-element guards. SLOW selects the library square root for the wave.
 template <int ALGO, bool WD, int SPLIT, bool SLOW>
 __device__ __forceinline__ void update_store(const DevTensor& T, int64_t e, int64_t n, bool full, const uint32_t* gw,
                                              const float* m, const float* v, const StepScalars& c, float inv_m,
-                                             float inv_v, float sq_inv_v) {
+                                             float inv_v, float sq_inv_v, const u32x4 (*wl)[64]) {
   constexpr bool SR = SPLIT == PS_SPLIT_STOCHASTIC;
   uint32_t hw[4], lw[4] = {0u, 0u, 0u, 0u};
   if (full) {
-    load8(T.hi + e, hw);
-    if (!SR) load8(T.lo + e, lw);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the LDS copies have landed
+    const u32x4 a = wl[0][threadIdx.x];
+    hw[0] = a.x; hw[1] = a.y; hw[2] = a.z; hw[3] = a.w;
+    if (!SR) {
+      const u32x4 b = wl[1][threadIdx.x];
+      lw[0] = b.x; lw[1] = b.y; lw[2] = b.z; lw[3] = b.w;
+    }
   } else {
     load8_guard(T.hi, e, n, 0u, hw);
     if (!SR) load8_guard(T.lo, e, n, 0u, lw);
@@ -146,12 +166,20 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
 
   uint32_t gw[4], mw[4], vw[4];
   float ms_old = 0.0f, vs_old = 0.0f;
+  __shared__ u32x4 wl[2][64];
+  // Both weight pointers are read from the record before the first LDS copy
+  // is issued: read after it, they were fetched with a vector load that
+  // waited for the copy.
+  const uint16_t* const hi_p = T.hi;
+  const uint16_t* const lo_p = T.lo;
   if (full) {
     load8(T.g + e, gw);
     load8(T.mc + e, mw);
     load8(T.vc + e, vw);
     ms_old = ((const GLOBAL float*)T.ms)[blk];
     vs_old = ((const GLOBAL float*)T.vs)[blk];
+    load8_to_lds(hi_p + e, &wl[0][0]);
+    if (SPLIT != PS_SPLIT_STOCHASTIC) load8_to_lds(lo_p + e, &wl[1][0]);
   } else {
     load8_guard(T.g, e, n, 0u, gw);
     load8_guard(T.mc, e, n, 0x80008000u, mw);
@@ -194,9 +222,9 @@ __device__ __forceinline__ void process_item(const DevTensor& T, int64_t elem0, 
   const float sq_inv_v = fast_sqrt(inv_v);
 
   if (slow_sqrt)
-    update_store<ALGO, WD, SPLIT, true>(T, e, n, full, gw, m, v, c, inv_m, inv_v, sq_inv_v);
+    update_store<ALGO, WD, SPLIT, true>(T, e, n, full, gw, m, v, c, inv_m, inv_v, sq_inv_v, wl);
   else
-    update_store<ALGO, WD, SPLIT, false>(T, e, n, full, gw, m, v, c, inv_m, inv_v, sq_inv_v);
+    update_store<ALGO, WD, SPLIT, false>(T, e, n, full, gw, m, v, c, inv_m, inv_v, sq_inv_v, wl);
   if (r == 0 && blk * kBlock < n) {
     ((GLOBAL float*)T.ms)[blk] = sm;
     ((GLOBAL float*)T.vs)[blk] = sv;
