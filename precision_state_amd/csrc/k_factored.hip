@@ -327,7 +327,8 @@ __device__ __forceinline__ void load_kap8(const float* __restrict__ kap, uint32_
 // row and column of each element are found one by one and the loads and
 // stores of a partial run go element by element. Missing elements read as
 // `fill` and are not written.
-__device__ __forceinline__ uint4 ld_run(const uint16_t* p, uint32_t e, uint32_t n, uint32_t fill, bool nt) {
+template <class I>
+__device__ __forceinline__ uint4 ld_run(const uint16_t* p, I e, I n, uint32_t fill, bool nt) {
   if (e + 8 <= n) return nt ? ld_stream(p + e) : *reinterpret_cast<const uint4*>(p + e);
   const GLOBAL uint16_t* q = (const GLOBAL uint16_t*)p;
   uint32_t w[4];
@@ -339,7 +340,8 @@ __device__ __forceinline__ uint4 ld_run(const uint16_t* p, uint32_t e, uint32_t 
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__device__ __forceinline__ void st_run(uint16_t* p, uint32_t e, uint32_t n, const uint32_t* w) {
+template <class I>
+__device__ __forceinline__ void st_run(uint16_t* p, I e, I n, const uint32_t* w) {
   if (e + 8 <= n) {
     st_stream(p + e, make_uint4(w[0], w[1], w[2], w[3]));
     return;
@@ -378,9 +380,18 @@ __device__ __forceinline__ void usq_item_any(const F2D& X, uint32_t item) {
   if (threadIdx.x == 0) X.upart[item] = acc;
 }
 
-__global__ __launch_bounds__(64) void k_f_usq_flat(FPlan P) {
+__device__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w);
+
+// Flat U^2 pass over the 2-D items, then (workgroups n_items2 and up) the 1-D
+// tensors' stats items: one launch where two used to wait on each other's
+// latency (about 7 us per step on the double-block shapes).
+__global__ __launch_bounds__(64) void k_f_usq_flat(FPlan P, FScalars S) {
   uint32_t begin;
   const uint32_t wg = xcd_item<kFlatXcdChunk>(blockIdx.x, gridDim.x);
+  if (wg >= P.n_items2) {   // uniform: an item of a 1-D tensor
+    f1_stats_item(P, S, wg - P.n_items2);
+    return;
+  }
   const F2D& X = P.t2[find_end(P.item2_end, P.n2, wg, begin)];
   const uint32_t item = wg - begin;
   if (!X.vec) {   // uniform per tensor
@@ -481,6 +492,9 @@ __device__ __forceinline__ void apply_item_any(const F2D& X, uint32_t item, cons
   if ((threadIdx.x & 15) == 0 && blk_ok) X.ms[blk] = sm;
 }
 
+// Flat apply over the 2-D items. (The 1-D apply items stay in a launch of
+// their own: riding at the end of this one, they made this kernel's code
+// 25% slower.)
 template <int SPLIT>
 __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
   constexpr bool SR = SPLIT == PS_SPLIT_STOCHASTIC;
@@ -564,10 +578,13 @@ __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
   if ((threadIdx.x & 15) == 0 && blk_ok) X.ms[blk] = sm;
 }
 
-__global__ __launch_bounds__(64) void k_f1_stats(FPlan P, FScalars S) {
+// 1-D tensors, one 1024-element item per 64-lane workgroup (item w of the
+// 1-D list): decode v, its EMA, sum of U^2. These items ride at the end of the
+// flat U^2 launch.
+__device__ __forceinline__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w) {
   uint32_t begin;
-  const F1D& X = P.t1[find_end(P.item_end, P.n1, blockIdx.x, begin)];
-  const int64_t elem0 = (int64_t)(blockIdx.x - begin) * kItemElems;
+  const F1D& X = P.t1[find_end(P.item_end, P.n1, w, begin)];
+  const int64_t elem0 = (int64_t)(w - begin) * kItemElems;
   const int lane = threadIdx.x, b = lane >> 4, r = lane & 15;
   const int64_t blk = (elem0 >> 8) + b;
   const float vs_old = (blk * kBlock < X.n) ? X.vs[blk] : 0.0f;
@@ -586,7 +603,7 @@ __global__ __launch_bounds__(64) void k_f1_stats(FPlan P, FScalars S) {
     }
   }
   for (int o = 1; o < 64; o <<= 1) acc += __shfl_xor(acc, o, 64);
-  if (lane == 0) X.upart[blockIdx.x - begin] = acc;
+  if (lane == 0) X.upart[w - begin] = acc;
 }
 
 // ---- clip factor per tensor: lr / max(1, RMS(U) / clip) ---------------------
@@ -669,62 +686,96 @@ __global__ __launch_bounds__(kT) void k_f_apply(FPlan P, FScalars S) {
 }
 
 // ---- apply to 1-D tensors and re-encode v --------------------------------------
+// Item w of the 1-D list.
 template <int SPLIT>
-__global__ __launch_bounds__(64) void k_f1_apply(FPlan P, FScalars S) {
+__device__ __forceinline__ void f1_apply_item(const FPlan& P, const FScalars& S, uint32_t w) {
   constexpr bool SR = SPLIT == PS_SPLIT_STOCHASTIC;
   uint32_t begin;
-  const F1D& X = P.t1[find_end(P.item_end, P.n1, blockIdx.x, begin)];
-  const int64_t elem0 = (int64_t)(blockIdx.x - begin) * kItemElems;
+  const F1D& X = P.t1[find_end(P.item_end, P.n1, w, begin)];
+  const int64_t n = X.n;
+  const int64_t elem0 = (int64_t)(w - begin) * kItemElems;
   const int lane = threadIdx.x, b = lane >> 4, r = lane & 15;
   const int64_t blk = (elem0 >> 8) + b;
-  const bool blk_ok = blk * kBlock < X.n;
+  const bool blk_ok = blk * kBlock < n;
   const float f = *X.f;
   const float ms_old = (S.fm && blk_ok) ? X.ms[blk] : 0.0f;
+  // Runs of 8 as in the flat 2-D items (16-byte loads and stores, element by
+  // element only in the tensor's last run); this step's v comes from the
+  // stats item through the workspace.
   float v[16], m[16];
   float mx = 0.0f, mxm = 0.0f;
-  for (int half = 0; half < 2; ++half) {
-    const int64_t e = elem0 + b * kBlock + half * 128 + r * 8;
+  for (int h = 0; h < 2; ++h) {
+    const int64_t e = elem0 + b * kBlock + h * 128 + r * 8;
     for (int j = 0; j < 8; ++j) {
-      const int64_t ej = e + j;
-      v[half * 8 + j] = 0.0f;
-      m[half * 8 + j] = 0.0f;
-      if (ej >= X.n) continue;
-      const float vj = X.v[ej];
-      v[half * 8 + j] = vj;
-      mx = __builtin_fmaxf(mx, vj);
-      const float g = __uint_as_float((uint32_t)X.g[ej] << 16);
-      const float U = g * (1.0f / __builtin_sqrtf(vj));
-      const uint32_t wbits = SR ? (uint32_t)X.hi[ej] << 16 : join_pair_elem<SPLIT>((uint32_t)X.hi[ej], (uint32_t)X.lo[ej], 0);
-      const float w = __uint_as_float(wbits);
-      float x = U * f;
-      if (S.fm) {
-        const float m0 = dec_signed(code_lo_f((uint32_t)X.mc[ej]), ms_old);
-        x = __builtin_fmaf(S.B1, m0, S.C1 * x);
-        m[half * 8 + j] = x;
-        mxm = __builtin_fmaxf(mxm, __builtin_fabsf(x));
+      v[8 * h + j] = 0.0f;
+      m[8 * h + j] = 0.0f;
+    }
+    if (e >= n) continue;
+    const uint4 gv = ld_run(X.g, e, n, 0u, true), hv = ld_run(X.hi, e, n, 0u, true);
+    const uint4 lv = SR ? make_uint4(0u, 0u, 0u, 0u) : ld_run(X.lo, e, n, 0u, true);
+    const uint4 mv = S.fm ? ld_run(X.mc, e, n, 0x80008000u, true) : make_uint4(0u, 0u, 0u, 0u);
+    float vv[8];
+    if (e + 8 <= n) {
+      const float4 a = *reinterpret_cast<const float4*>(X.v + e), c = *reinterpret_cast<const float4*>(X.v + e + 4);
+      vv[0] = a.x; vv[1] = a.y; vv[2] = a.z; vv[3] = a.w; vv[4] = c.x; vv[5] = c.y; vv[6] = c.z; vv[7] = c.w;
+    } else {
+      for (int j = 0; j < 8; ++j) vv[j] = (e + j < n) ? X.v[e + j] : 0.0f;
+    }
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+    const uint32_t lw[4] = {lv.x, lv.y, lv.z, lv.w};
+    const uint32_t mw[4] = {mv.x, mv.y, mv.z, mv.w};
+    uint64_t rnd[2] = {0u, 0u};
+    if (SR) sr_bits8(sr_stream(S.sr_seed, S.sr_step, X.tid), e, rnd);
+    uint32_t oh[4], ol[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t wb[2];
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        const int jj = 2 * p + o;
+        const float wv = SR ? bf16_at(hw, jj) : __uint_as_float(join_pair_elem<SPLIT>(hw[p], lw[p], o));
+        float x = 0.0f;
+        if (e + jj < n) {
+          const float vj = vv[jj];
+          v[8 * h + jj] = vj;
+          mx = __builtin_fmaxf(mx, vj);
+          const float U = bf16_at(gw, jj) * (1.0f / __builtin_sqrtf(vj));
+          x = U * f;
+          if (S.fm) {
+            const float m0 = dec_signed(o ? code_hi_f(mw[p]) : code_lo_f(mw[p]), ms_old);
+            x = __builtin_fmaf(S.B1, m0, S.C1 * x);
+            m[8 * h + jj] = x;
+            mxm = __builtin_fmaxf(mxm, __builtin_fabsf(x));
+          }
+          if (S.wd) x = __builtin_fmaf(S.CWD, wv, x);
+        }
+        wb[o] = __float_as_uint(wv - x);
       }
-      if (S.wd) x = __builtin_fmaf(S.CWD, w, x);
       if (SR) {
-        const uint32_t rb = sr_bits1(sr_stream(S.sr_seed, S.sr_step, X.tid), ej);
-        X.hi[ej] = (uint16_t)((__float_as_uint(w - x) + rb) >> 16);
+        const uint64_t q = rnd[p >> 1] >> (32 * (p & 1));
+        oh[p] = sr_pair(wb[0], wb[1], (uint32_t)q & 0xFFFFu, (uint32_t)(q >> 16) & 0xFFFFu);
       } else {
-        uint32_t h2, l2;
-        split_pair<SPLIT>(__float_as_uint(w - x), 0u, h2, l2);
-        X.hi[ej] = (uint16_t)h2;
-        X.lo[ej] = (uint16_t)l2;
+        split_pair<SPLIT>(wb[0], wb[1], oh[p], ol[p]);
       }
     }
+    st_run(X.hi, e, n, oh);
+    if (!SR) st_run(X.lo, e, n, ol);
   }
   float s, inv, sm = 0.0f, invm = 0.0f;
   block_scale(row16_max(mx), s, inv);
   if (S.fm) block_scale(row16_max(mxm), sm, invm);   // uniform
-  for (int half = 0; half < 2; ++half) {
-    const int64_t e = elem0 + b * kBlock + half * 128 + r * 8;
-    for (int j = 0; j < 8; ++j)
-      if (e + j < X.n) {
-        X.vc[e + j] = (uint16_t)enc_unsigned(v[half * 8 + j], inv);
-        if (S.fm) X.mc[e + j] = (uint16_t)enc_signed(m[half * 8 + j], invm);
-      }
+  for (int h = 0; h < 2; ++h) {
+    const int64_t e = elem0 + b * kBlock + h * 128 + r * 8;
+    if (e >= n) continue;
+    uint32_t cv[4], cm[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      cv[p] = enc_unsigned(v[8 * h + 2 * p], inv) | (enc_unsigned(v[8 * h + 2 * p + 1], inv) << 16);
+      cm[p] = S.fm ? enc_signed(m[8 * h + 2 * p], invm) | (enc_signed(m[8 * h + 2 * p + 1], invm) << 16) : 0u;
+    }
+    st_run(X.vc, e, n, cv);
+    if (S.fm) st_run(X.mc, e, n, cm);
   }
   if (r == 0 && blk_ok) {
     X.vs[blk] = s;
@@ -733,13 +784,19 @@ __global__ __launch_bounds__(64) void k_f1_apply(FPlan P, FScalars S) {
 }
 
 template <int SPLIT>
+__global__ __launch_bounds__(64) void k_f1_apply(FPlan P, FScalars S) {
+  f1_apply_item<SPLIT>(P, S, blockIdx.x);
+}
+
+template <int SPLIT>
 ps_status launch_all(const FPlan& P, const FScalars& S, hipStream_t s) {
+  // 2-D flat items and the 1-D stats items share a launch (each below 2^31)
+  const uint32_t n_flat = P.n_items2 + P.n_items;
   if (P.n_tiles) hipLaunchKernelGGL(k_f_stats, dim3(P.n_tiles), dim3(kT), 0, s, P, S);
-  if (P.n_items) hipLaunchKernelGGL(k_f1_stats, dim3(P.n_items), dim3(64), 0, s, P, S);
   if (P.n_rc) hipLaunchKernelGGL(k_f_rowcol, dim3(P.n_rc), dim3(kT), 0, s, P, S);
   if (P.n_rc) hipLaunchKernelGGL(k_f_factors, dim3(P.n_rc), dim3(kT), 0, s, P);
   if (P.n_tiles_nf) hipLaunchKernelGGL(k_f_usq, dim3(P.n_tiles_nf), dim3(kT), 0, s, P);
-  if (P.n_items2) hipLaunchKernelGGL(k_f_usq_flat, dim3(P.n_items2), dim3(64), 0, s, P);
+  if (n_flat) hipLaunchKernelGGL(k_f_usq_flat, dim3(n_flat), dim3(64), 0, s, P, S);
   hipLaunchKernelGGL(k_f_clip, dim3(P.n2 + P.n1), dim3(kClipT), 0, s, P, S);
   if (P.n_tiles_nf) hipLaunchKernelGGL((k_f_apply<SPLIT>), dim3(P.n_tiles_nf), dim3(kT), 0, s, P, S);
   if (P.n_items2) hipLaunchKernelGGL((k_f_apply_flat<SPLIT>), dim3(P.n_items2), dim3(64), 0, s, P, S);
