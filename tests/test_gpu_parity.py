@@ -212,6 +212,25 @@ def test_multi_tensor_ragged_lists(count, split_mode):
         _assert_exact(d, h, f"tensor {i} numel {sizes[i]}")
 
 
+def test_list_past_the_xcd_run_threshold_all_bytes():
+    """Every byte of a list long enough for the XCD-aware work order (about
+    49,000 work items: two whole rounds of 8 runs of 2048 items, then a tail
+    in plain index order), ragged tensors among large ones, 2 NAdamW steps,
+    against the oracle."""
+    sizes = RAGGED + [3072 * 3072, 3072 * 4096, 3000003]
+    items = sum((n + 511) // 512 for n in sizes)
+    assert items > 2 * 8 * 2048
+    hp = ps.HParams(algo=ps.ALGO_NADAM, weight_decay=0.01, lr=1e-4)
+    devs = [dev_state(n, 13, i) for i, n in enumerate(sizes)]
+    hosts = [host_state(n, 13, i) for i, n in enumerate(sizes)]
+    for t in range(1, 3):
+        ps.opt_step_multi(devs, [dev_grad(n, 13, i, t) for i, n in enumerate(sizes)], hp, t)
+        oracle.opt_step_multi(hosts, [host_grad(n, 13, i, t) for i, n in enumerate(sizes)], ohp(hp), t)
+        print(f"  step {t} done", flush=True)
+    for i, (d, h) in enumerate(zip(devs, hosts)):
+        _assert_exact(d, h, f"tensor {i} numel {sizes[i]}")
+
+
 def _clone(st):
     c = ps.TensorState(st.w_hi.clone(), st.w_lo.clone(), st.m_code.clone(), st.m_scale.clone(),
                        st.v_code.clone(), st.v_scale.clone())
