@@ -103,7 +103,7 @@ def test_codec_exhaustive_all_x_in_unit_interval(kind):
 
 
 @pytest.mark.parametrize("kind", [ps.MOMENT_SIGNED, ps.MOMENT_UNSIGNED])
-@pytest.mark.parametrize("n", [0, 1, 255, 256, 257, 1000, 4096, 100003])
+@pytest.mark.parametrize("n", [0, 1, 255, 256, 257, 1000, 4096, 100003, 5000011])
 def test_encode_decode_match_oracle(kind, n):
     rng = np.random.default_rng(1000 + n)
     x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-12, 2, n)).astype(np.float32)
