@@ -246,10 +246,11 @@ __global__ __launch_bounds__(kT) void k_f_factors(FPlan P) {
   }
 }
 
-// ---- pass 4: tile sums of U^2, U = (g * rho_i) * kap_j ----------------------
+// ---- pass 4: tile sums of U^2, U = (g * rho_i) * kap_j (tensors whose rows
+// are not 16-byte runs and that keep no first moment) ---------------------------
 __global__ __launch_bounds__(kT) void k_f_usq(FPlan P) {
   uint32_t begin;
-  const F2D& X = P.t2[find_end(P.tile_nf_end, P.n2, blockIdx.x, begin)];
+  const F2D& X = P.t2[find_end(P.tile_u_end, P.n2, blockIdx.x, begin)];
   const uint32_t tile = blockIdx.x - begin;
   const int tr = (int)(tile / (uint32_t)X.ntc), tc = (int)(tile - (uint32_t)tr * X.ntc);
   const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
@@ -382,44 +383,71 @@ __device__ __forceinline__ void usq_item_any(const F2D& X, uint32_t item) {
 
 __device__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w);
 
-// Flat U^2 pass over the 2-D items, then (workgroups n_items2 and up) the 1-D
-// tensors' stats items: one launch where two used to wait on each other's
-// latency (about 7 us per step on the double-block shapes).
-__global__ __launch_bounds__(64) void k_f_usq_flat(FPlan P, FScalars S) {
+// U^2 sum of one row tile of a tensor whose rows are 16-byte runs: kURows
+// rows x kUCols columns, lane l taking columns c .. c+7 (c = band start +
+// 8 l) of every row of the tile. The lane loads its 8 column factors once and
+// all its rows' gradient runs at once (8 KiB per wave in flight), and each
+// row's factor is one scalar load; per element the flat items instead load a
+// column factor (4 bytes) for every 2-byte gradient. Lane order: row by row,
+// columns in order; then the wave's xor tree. Lanes past the last column and
+// rows past the last row hold g = 0 and add exact zeros.
+__device__ __forceinline__ void usq_row_tile(const FPlan& P, uint32_t w) {
   uint32_t begin;
-  const uint32_t wg = xcd_item<kFlatXcdChunk>(blockIdx.x, gridDim.x);
-  if (wg >= P.n_items2) {   // uniform: an item of a 1-D tensor
-    f1_stats_item(P, S, wg - P.n_items2);
-    return;
+  const F2D& X = P.t2[find_end(P.rt_end, P.n2, w, begin)];
+  const uint32_t t = w - begin;
+  const int tr = (int)(t / (uint32_t)X.nuc), tc = (int)(t - (uint32_t)tr * X.nuc);
+  const int c = tc * kUCols + (int)threadIdx.x * 8;
+  const int r0 = tr * kURows;
+  const bool col_ok = c < X.C;
+  float kap[8];
+  if (col_ok) {
+    load_kap8(X.kap, (uint32_t)c, kap);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kap[j] = 0.0f;
   }
-  const F2D& X = P.t2[find_end(P.item2_end, P.n2, wg, begin)];
-  const uint32_t item = wg - begin;
-  if (!X.vec) {   // uniform per tensor
-    usq_item_any(X, item);
-    return;
-  }
-  FlatRun run[2];
-  flat_runs(X, item, run);
-  uint4 gv[2];
-  float kap[2][8], rho[2];
-  for (int h = 0; h < 2; ++h) {
-    if (!run[h].ok) continue;
-    gv[h] = *reinterpret_cast<const uint4*>(X.g + run[h].e);
-    load_kap8(X.kap, run[h].j, kap[h]);
-    rho[h] = X.rho[run[h].i];
+  uint4 gv[kURows];
+#pragma unroll
+  for (int k = 0; k < kURows; ++k) {
+    const int r = r0 + k;
+    gv[k] = (col_ok && r < X.R) ? ld_stream(X.g + (size_t)r * (size_t)X.C + (size_t)c) : make_uint4(0u, 0u, 0u, 0u);
   }
   double acc = 0.0;
-  for (int h = 0; h < 2; ++h) {
-    if (!run[h].ok) continue;
-    const uint32_t w[4] = {gv[h].x, gv[h].y, gv[h].z, gv[h].w};
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const float U = (bf16_at(w, jj) * rho[h]) * kap[h][jj];
+  for (int k = 0; k < kURows; ++k) {
+    const int r = r0 + k;
+    const float rho = r < X.R ? X.rho[r] : 0.0f;
+    const uint32_t g[4] = {gv[k].x, gv[k].y, gv[k].z, gv[k].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float U = (bf16_at(g, j) * rho) * kap[j];
       acc += (double)U * (double)U;
     }
   }
   for (int o = 1; o < 64; o <<= 1) acc += __shfl_xor(acc, o, 64);
-  if (threadIdx.x == 0) X.upart[item] = acc;
+  if (threadIdx.x == 0) X.upart[t] = acc;
+}
+
+__device__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w);
+
+// The U^2 pass in one launch of 64-lane workgroups: the row tiles of tensors
+// whose rows are 16-byte runs, then the flat items of the other tensors that
+// keep a first moment, then the 1-D tensors' stats items (decode v, EMA,
+// U^2), which thus do not wait on a launch of their own.
+__global__ __launch_bounds__(64) void k_f_usq_flat(FPlan P, FScalars S) {
+  const uint32_t wg = xcd_item<kFlatXcdChunk>(blockIdx.x, gridDim.x);
+  if (wg < P.n_rt) {   // uniform
+    usq_row_tile(P, wg);
+    return;
+  }
+  const uint32_t w2 = wg - P.n_rt;
+  if (w2 >= P.n_items2u) {   // uniform: an item of a 1-D tensor
+    f1_stats_item(P, S, w2 - P.n_items2u);
+    return;
+  }
+  uint32_t begin;
+  const F2D& X = P.t2[find_end(P.item2u_end, P.n2, w2, begin)];
+  usq_item_any(X, w2 - begin);
 }
 
 // Apply of one item, any column count: the arithmetic of the run path below,
@@ -790,13 +818,14 @@ __global__ __launch_bounds__(64) void k_f1_apply(FPlan P, FScalars S) {
 
 template <int SPLIT>
 ps_status launch_all(const FPlan& P, const FScalars& S, hipStream_t s) {
-  // 2-D flat items and the 1-D stats items share a launch (each below 2^31)
-  const uint32_t n_flat = P.n_items2 + P.n_items;
+  // U^2 row tiles, flat items without 16-byte rows and the 1-D stats items
+  // share a launch (their sum is checked on the host to fit 32 bits)
+  const uint32_t n_usq = P.n_rt + P.n_items2u + P.n_items;
   if (P.n_tiles) hipLaunchKernelGGL(k_f_stats, dim3(P.n_tiles), dim3(kT), 0, s, P, S);
   if (P.n_rc) hipLaunchKernelGGL(k_f_rowcol, dim3(P.n_rc), dim3(kT), 0, s, P, S);
   if (P.n_rc) hipLaunchKernelGGL(k_f_factors, dim3(P.n_rc), dim3(kT), 0, s, P);
-  if (P.n_tiles_nf) hipLaunchKernelGGL(k_f_usq, dim3(P.n_tiles_nf), dim3(kT), 0, s, P);
-  if (n_flat) hipLaunchKernelGGL(k_f_usq_flat, dim3(n_flat), dim3(64), 0, s, P, S);
+  if (P.n_tiles_u) hipLaunchKernelGGL(k_f_usq, dim3(P.n_tiles_u), dim3(kT), 0, s, P);
+  if (n_usq) hipLaunchKernelGGL(k_f_usq_flat, dim3(n_usq), dim3(64), 0, s, P, S);
   hipLaunchKernelGGL(k_f_clip, dim3(P.n2 + P.n1), dim3(kClipT), 0, s, P, S);
   if (P.n_tiles_nf) hipLaunchKernelGGL((k_f_apply<SPLIT>), dim3(P.n_tiles_nf), dim3(kT), 0, s, P, S);
   if (P.n_items2) hipLaunchKernelGGL((k_f_apply_flat<SPLIT>), dim3(P.n_items2), dim3(64), 0, s, P, S);

@@ -3,8 +3,9 @@
 //
 // Workspace (caller-owned device memory), per 2-D tensor [R, C]: row sums per
 // tile column [ntc][R] and column sums per tile row [ntr][C] (double), sums of
-// the new row EMAs per 256-row chunk, rho[R], kap[C], sums of U^2 per tile,
-// the clip factor. Per 1-D tensor: this step's v[n], sums of U^2 per
+// the new row EMAs per 256-row chunk, rho[R], kap[C], sums of U^2 (per row
+// tile, flat item or stats tile, whichever form the U^2 pass takes), the clip
+// factor. Per 1-D tensor: this step's v[n], sums of U^2 per
 // 1024-element item, the clip factor. Every region starts on 256 bytes.
 #include <algorithm>
 #include <cmath>
@@ -47,7 +48,7 @@ ps_status check_ptr(const void* p, const char* what, int i, uintptr_t align) {
 struct Layout {
   std::vector<F2D> t2;
   std::vector<F1D> t1;
-  std::vector<uint32_t> tile_end, rc_end, tile_nf_end, item2_end, item_end;
+  std::vector<uint32_t> tile_end, rc_end, tile_nf_end, item2_end, item_end, rt_end, tile_u_end, item2u_end;
   size_t bytes = 0;
 };
 
@@ -57,7 +58,7 @@ struct Layout {
 ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, Layout& L) {
   if (n < 0) return fail(PS_ERR_INVALID_ARG, "n_tensors < 0");
   if (n > 0 && !t) return fail(PS_ERR_INVALID_ARG, "tensors is NULL");
-  uint64_t tiles = 0, rc = 0, items = 0, tiles_nf = 0, items2 = 0;
+  uint64_t tiles = 0, rc = 0, items = 0, tiles_nf = 0, items2 = 0, rt = 0, tiles_u = 0, items2u = 0;
   size_t off = 0;
   auto take = [&](size_t bytes) { char* p = ws ? ws + off : nullptr; off += up(bytes); return p; };
   for (int32_t i = 0; i < n; ++i) {
@@ -92,12 +93,16 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, 
       d.ms = fm ? x.m_scale : nullptr;
       d.tid = (uint32_t)i;
       d.nitems = d.flat ? (int32_t)((x.numel + kItemElems - 1) / kItemElems) : 0;
-      d.npart = d.flat ? d.nitems : d.ntr * d.ntc;
-      // The U^2 partials get room for both forms (items and tiles), so the
-      // workspace layout, and ps_factored_workspace_size, do not depend on
-      // whether a first moment is kept.
+      // U^2 pass: row tiles when rows are 16-byte runs, else the flat items
+      // (first moment) or the stats tiles.
+      d.nuc = d.vec ? (d.C + kUCols - 1) / kUCols : 0;
+      const int32_t nrt = d.vec ? ((d.R + kURows - 1) / kURows) * d.nuc : 0;
+      d.npart = d.vec ? nrt : d.flat ? d.nitems : d.ntr * d.ntc;
+      // The U^2 partials get room for every form a tensor of this shape can
+      // take, so the workspace layout, and ps_factored_workspace_size, do not
+      // depend on whether a first moment is kept.
       const int64_t items_any = x.numel < (int64_t(1) << 31) ? (x.numel + kItemElems - 1) / kItemElems : 0;
-      const int64_t upart_n = std::max<int64_t>(items_any, (int64_t)d.ntr * d.ntc);
+      const int64_t upart_n = d.vec ? (int64_t)nrt : std::max<int64_t>(items_any, (int64_t)d.ntr * d.ntc);
       d.rowpart = (double*)take(sizeof(double) * (size_t)d.ntc * d.R);
       d.colpart = (double*)take(sizeof(double) * (size_t)d.ntr * d.C);
       d.rpart = (double*)take(sizeof(double) * (size_t)d.nrw);
@@ -111,13 +116,23 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, 
         items2 += (uint64_t)d.nitems;
       else
         tiles_nf += (uint64_t)d.ntr * d.ntc;
-      if (tiles > 0x7FFFFFFFull || rc > 0x7FFFFFFFull || items2 > 0x7FFFFFFFull)
+      if (d.vec)
+        rt += (uint64_t)nrt;
+      else if (d.flat)
+        items2u += (uint64_t)d.nitems;
+      else
+        tiles_u += (uint64_t)d.ntr * d.ntc;
+      if (tiles > 0x7FFFFFFFull || rc > 0x7FFFFFFFull || items2 > 0x7FFFFFFFull || rt > 0x7FFFFFFFull ||
+          items2u > 0x7FFFFFFFull)
         return fail(PS_ERR_SHAPE, "tensor list too large");
       L.t2.push_back(d);
       L.tile_end.push_back((uint32_t)tiles);
       L.rc_end.push_back((uint32_t)rc);
       L.tile_nf_end.push_back((uint32_t)tiles_nf);
       L.item2_end.push_back((uint32_t)items2);
+      L.rt_end.push_back((uint32_t)rt);
+      L.tile_u_end.push_back((uint32_t)tiles_u);
+      L.item2u_end.push_back((uint32_t)items2u);
     } else {
       if ((s = check_ptr(x.v_code, "v_code", i, 16)) || (s = check_ptr(x.v_scale, "v_scale", i, 4))) return s;
       F1D d{};
@@ -135,6 +150,9 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, 
       L.item_end.push_back((uint32_t)items);
     }
   }
+  // the U^2 launch takes the row tiles, the flat items that are not row
+  // tiles and the 1-D items in one grid
+  if (rt + items2u + items > 0xFFFFFFFFull) return fail(PS_ERR_SHAPE, "tensor list too large");
   L.bytes = off;
   return PS_OK;
 }
@@ -171,20 +189,18 @@ ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps
   Layout W;
   if (ps_status s = plan(tensors, n_tensors, (char*)workspace, fm, residual, W)) return s;
 
-  // one device blob: F2D[n2] | F1D[n1] | tile_end | rc_end | tile_nf_end | item2_end [n2] | item_end[n1]
+  // one device blob: F2D[n2] | F1D[n1] | the seven [n2] prefix-end lists | item_end[n1]
   const size_t b2 = W.t2.size() * sizeof(F2D), b1 = W.t1.size() * sizeof(F1D);
   const size_t e2 = W.t2.size() * sizeof(uint32_t), e1 = W.t1.size() * sizeof(uint32_t);
-  std::vector<unsigned char> blob(b2 + b1 + 4 * e2 + e1);
+  const std::vector<uint32_t>* lists2[7] = {&W.tile_end, &W.rc_end, &W.tile_nf_end, &W.item2_end,
+                                            &W.rt_end, &W.tile_u_end, &W.item2u_end};
+  std::vector<unsigned char> blob(b2 + b1 + 7 * e2 + e1);
   unsigned char* p = blob.data();
   if (b2) memcpy(p, W.t2.data(), b2);
   if (b1) memcpy(p + b2, W.t1.data(), b1);
-  if (e2) {
-    memcpy(p + b2 + b1, W.tile_end.data(), e2);
-    memcpy(p + b2 + b1 + e2, W.rc_end.data(), e2);
-    memcpy(p + b2 + b1 + 2 * e2, W.tile_nf_end.data(), e2);
-    memcpy(p + b2 + b1 + 3 * e2, W.item2_end.data(), e2);
-  }
-  if (e1) memcpy(p + b2 + b1 + 4 * e2, W.item_end.data(), e1);
+  if (e2)
+    for (int k = 0; k < 7; ++k) memcpy(p + b2 + b1 + k * e2, lists2[k]->data(), e2);
+  if (e1) memcpy(p + b2 + b1 + 7 * e2, W.item_end.data(), e1);
   hipStream_t s = (hipStream_t)stream;
   const void* d = nullptr;
   if (ps_status st = device_blob(blob.data(), blob.size(), s, &d)) return st;
@@ -196,7 +212,10 @@ ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps
   pl.rc_end = (const uint32_t*)(dc + b2 + b1 + e2);
   pl.tile_nf_end = (const uint32_t*)(dc + b2 + b1 + 2 * e2);
   pl.item2_end = (const uint32_t*)(dc + b2 + b1 + 3 * e2);
-  pl.item_end = (const uint32_t*)(dc + b2 + b1 + 4 * e2);
+  pl.rt_end = (const uint32_t*)(dc + b2 + b1 + 4 * e2);
+  pl.tile_u_end = (const uint32_t*)(dc + b2 + b1 + 5 * e2);
+  pl.item2u_end = (const uint32_t*)(dc + b2 + b1 + 6 * e2);
+  pl.item_end = (const uint32_t*)(dc + b2 + b1 + 7 * e2);
   pl.n2 = (int32_t)W.t2.size();
   pl.n1 = (int32_t)W.t1.size();
   pl.n_tiles = W.tile_end.empty() ? 0 : W.tile_end.back();
@@ -204,6 +223,9 @@ ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps
   pl.n_items = W.item_end.empty() ? 0 : W.item_end.back();
   pl.n_tiles_nf = W.tile_nf_end.empty() ? 0 : W.tile_nf_end.back();
   pl.n_items2 = W.item2_end.empty() ? 0 : W.item2_end.back();
+  pl.n_rt = W.rt_end.empty() ? 0 : W.rt_end.back();
+  pl.n_tiles_u = W.tile_u_end.empty() ? 0 : W.tile_u_end.back();
+  pl.n_items2u = W.item2u_end.empty() ? 0 : W.item2u_end.back();
   FScalars sc;
   const double beta2_t = hp->decay_rate != 0.0 ? 1.0 - std::pow((double)step, hp->decay_rate) : hp->beta2;
   sc.B2 = (float)beta2_t;

@@ -76,6 +76,8 @@ struct TableInline {
 constexpr int kFTileRows = 64;     // 2-D tile: 64 rows x 256 columns, one 256-thread workgroup
 constexpr int kFTileCols = 256;
 constexpr int kFRowColChunk = 256; // rows or columns per finalize workgroup
+constexpr int kURows = 8;          // U^2 row tile (C % 8 == 0): 8 rows x 512 columns, one 64-lane wave
+constexpr int kUCols = 512;
 
 // 2-D tensor [R, C] of a factored step; workspace pointers are per tensor.
 struct F2D {
@@ -94,10 +96,11 @@ struct F2D {
   uint16_t* mc;      // first moment codes (signed kind) or NULL
   float* ms;         // first moment block scales or NULL
   int32_t R, C, ntr, ntc, nrw, ncw;
+  int32_t nuc;       // vec: column bands of the U^2 row tiles (kUCols wide)
   int32_t vec;       // C % 8 == 0: 16-byte row segments
   int32_t flat;      // R*C < 2^31 and (vec or a first moment): U^2 and apply passes run over 1024-element items
   int32_t nitems;    // flat: items of 1024 elements
-  int32_t npart;     // entries of upart (nitems if flat, else ntr * ntc)
+  int32_t npart;     // entries of upart: U^2 row tiles if vec, else nitems if flat, else ntr * ntc
   uint32_t tid;      // index in the caller's list (stochastic rounding stream key)
   uint32_t pad;
 };
@@ -136,10 +139,14 @@ struct FPlan {      // device tables of one factored call
   const uint32_t* rc_end;      // [n2] prefix ends over row/column finalize workgroups
   const uint32_t* tile_nf_end; // [n2] prefix ends over tiles of tensors that are not flat
   const uint32_t* item2_end;   // [n2] prefix ends over 1024-element items of flat tensors
+  const uint32_t* rt_end;      // [n2] prefix ends over U^2 row tiles of vec tensors
+  const uint32_t* tile_u_end;  // [n2] prefix ends over U^2 tiles of tensors neither vec nor flat
+  const uint32_t* item2u_end;  // [n2] prefix ends over U^2 items of flat tensors that are not vec
   const F1D* t1;
   const uint32_t* item_end;    // [n1] prefix ends over 1-D items
   int32_t n2, n1;
   uint32_t n_tiles, n_rc, n_items, n_tiles_nf, n_items2;
+  uint32_t n_rt, n_tiles_u, n_items2u;
 };
 
 ps_status launch_factored(const FPlan& plan, const FScalars& sc, int split_mode, hipStream_t s);
