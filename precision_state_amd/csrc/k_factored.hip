@@ -112,77 +112,85 @@ __device__ __forceinline__ double block_sum(double x, double* red) {
 }
 
 // ---- pass 1: tile row and column sums of q = g^2 + eps1 ---------------------
+// One 256 x 256 stats tile per 256-thread workgroup, walked in 4 chunks of 64
+// rows: thread (rg, cg) takes columns c .. c+7 (c = 8 cg) of chunk rows
+// rg + 8 k. Row sums are finished per chunk (a 256-column partial per row);
+// column sums run on across the chunks, so the LDS reduction, its barrier and
+// the column-partial stores come once per 128 KiB of gradient: with one per
+// 64-row tile they took a fifth of the pass.
 __global__ __launch_bounds__(kT) void k_f_stats(FPlan P, FScalars S) {
   uint32_t begin;
   const F2D& X = P.t2[find_end(P.tile_end, P.n2, blockIdx.x, begin)];
   const uint32_t tile = blockIdx.x - begin;
-  const int tr = (int)(tile / (uint32_t)X.ntc), tc = (int)(tile - (uint32_t)tr * X.ntc);
+  const int ts = (int)(tile / (uint32_t)X.ntc), tc = (int)(tile - (uint32_t)ts * X.ntc);
   const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
   const int c = tc * kFTileCols + cg * 8;
   double cacc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) cacc[j] = 0.0;
-  double rs[8];
-  if (X.vec && (tr + 1) * kFTileRows <= X.R && (tc + 1) * kFTileCols <= X.C) {
-    // Interior tile: all eight row segments are requested at once, then
-    // summed in the same order as below.
-    uint32_t w[8][4];
-    const uint16_t* p = X.g + (size_t)(tr * kFTileRows + rg) * (size_t)X.C + (size_t)c;
+  for (int ch = 0; ch < kSTileRows / kFTileRows; ++ch) {
+    const int row0 = ts * kSTileRows + ch * kFTileRows;   // first row of the chunk
+    if (row0 >= X.R) break;   // uniform
+    double rs[8];
+    if (X.vec && row0 + kFTileRows <= X.R && (tc + 1) * kFTileCols <= X.C) {
+      // Interior chunk: all eight row segments are requested at once, then
+      // summed in the same order as below.
+      uint32_t w[8][4];
+      const uint16_t* p = X.g + (size_t)(row0 + rg) * (size_t)X.C + (size_t)c;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const u32x4 v = __builtin_nontemporal_load((const GLOBAL u32x4*)(p + (size_t)(8 * k) * (size_t)X.C));
-      w[k][0] = v.x; w[k][1] = v.y; w[k][2] = v.z; w[k][3] = v.w;
-    }
+      for (int k = 0; k < 8; ++k) {
+        const u32x4 v = __builtin_nontemporal_load((const GLOBAL u32x4*)(p + (size_t)(8 * k) * (size_t)X.C));
+        w[k][0] = v.x; w[k][1] = v.y; w[k][2] = v.z; w[k][3] = v.w;
+      }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      rs[k] = 0.0;
+      for (int k = 0; k < 8; ++k) {
+        rs[k] = 0.0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float g = bf16_at(w[k], j);
-        const float q = g * g + S.EPS1;
-        rs[k] += (double)q;
-        cacc[j] += (double)q;
+        for (int j = 0; j < 8; ++j) {
+          const float g = bf16_at(w[k], j);
+          const float q = g * g + S.EPS1;
+          rs[k] += (double)q;
+          cacc[j] += (double)q;
+        }
+      }
+    } else {
+      for (int k = 0; k < 8; ++k) {
+        const int r = row0 + rg + 8 * k;
+        uint32_t w[4];
+        const uint32_t valid = load_row8(X.g, X, r, c, w);
+        rs[k] = 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float g = bf16_at(w, j);
+          const float q = (valid >> j & 1u) ? g * g + S.EPS1 : 0.0f;
+          rs[k] += (double)q;
+          cacc[j] += (double)q;
+        }
       }
     }
-  } else {
-    for (int k = 0; k < 8; ++k) {
-      const int r = tr * kFTileRows + rg + 8 * k;
-      uint32_t w[4];
-      const uint32_t valid = load_row8(X.g, X, r, c, w);
-      rs[k] = 0.0;
+    // Row sums over the 32 column groups of a half-wave by transpose-reduce:
+    // at each exchange a lane keeps half of its rows and receives its
+    // partner's partial of those rows (9 shuffles instead of 8 x 5). Lane bits
+    // 4, 3, 2 of cg select the row k = 4*b4 + 2*b3 + b2 the lane ends with.
+    const int b4 = (cg >> 4) & 1, b3 = (cg >> 3) & 1, b2 = (cg >> 2) & 1;
+    double a[4], bb[2], x;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float g = bf16_at(w, j);
-        const float q = (valid >> j & 1u) ? g * g + S.EPS1 : 0.0f;
-        rs[k] += (double)q;
-        cacc[j] += (double)q;
-      }
+    for (int q = 0; q < 4; ++q) {
+      const double keep = b4 ? rs[4 + q] : rs[q], send = b4 ? rs[q] : rs[4 + q];
+      a[q] = keep + __shfl_xor(send, 16, 32);
     }
-  }
-  // Row sums over the 32 column groups of a half-wave by transpose-reduce:
-  // at each exchange a lane keeps half of its rows and receives its partner's
-  // partial of those rows (9 shuffles instead of 8 x 5). Lane bits 4, 3, 2 of
-  // cg select the row k = 4*b4 + 2*b3 + b2 the lane ends with.
-  const int b4 = (cg >> 4) & 1, b3 = (cg >> 3) & 1, b2 = (cg >> 2) & 1;
-  double a[4], bb[2], x;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const double keep = b4 ? rs[4 + q] : rs[q], send = b4 ? rs[q] : rs[4 + q];
-    a[q] = keep + __shfl_xor(send, 16, 32);
-  }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const double keep = b3 ? a[2 + q] : a[q], send = b3 ? a[q] : a[2 + q];
-    bb[q] = keep + __shfl_xor(send, 8, 32);
-  }
-  {
-    const double keep = b2 ? bb[1] : bb[0], send = b2 ? bb[0] : bb[1];
-    x = keep + __shfl_xor(send, 4, 32);
-  }
-  x += __shfl_xor(x, 2, 32);
-  x += __shfl_xor(x, 1, 32);
-  {
-    const int r = tr * kFTileRows + rg + 8 * (4 * b4 + 2 * b3 + b2);
+    for (int q = 0; q < 2; ++q) {
+      const double keep = b3 ? a[2 + q] : a[q], send = b3 ? a[q] : a[2 + q];
+      bb[q] = keep + __shfl_xor(send, 8, 32);
+    }
+    {
+      const double keep = b2 ? bb[1] : bb[0], send = b2 ? bb[0] : bb[1];
+      x = keep + __shfl_xor(send, 4, 32);
+    }
+    x += __shfl_xor(x, 2, 32);
+    x += __shfl_xor(x, 1, 32);
+    const int r = row0 + rg + 8 * (4 * b4 + 2 * b3 + b2);
     if ((cg & 3) == 0 && r < X.R) X.rowpart[(size_t)tc * X.R + r] = x;
   }
   __shared__ double lds[8][kFTileCols];
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(kT) void k_f_stats(FPlan P, FScalars S) {
   if (cc < X.C) {
     double s = 0.0;
     for (int q = 0; q < 8; ++q) s += lds[q][threadIdx.x];
-    X.colpart[(size_t)tr * X.C + cc] = s;
+    X.colpart[(size_t)ts * X.C + cc] = s;
   }
 }
 
@@ -222,7 +230,7 @@ __global__ __launch_bounds__(kT) void k_f_rowcol(FPlan P, FScalars S) {
     if (j < X.C) {
       double s = 0.0;
 #pragma unroll 16
-      for (int tr = 0; tr < X.ntr; ++tr) s += X.colpart[(size_t)tr * X.C + j];
+      for (int tr = 0; tr < X.sntr; ++tr) s += X.colpart[(size_t)tr * X.C + j];
       const float mean = (float)(s / (double)X.R);
       X.col[j] = __builtin_fmaf(S.B2, X.col[j], S.C2 * mean);
     }

@@ -2,7 +2,7 @@
 // layout and the device plan [ADAF, adafactor_step_param; PRODIGY].
 //
 // Workspace (caller-owned device memory), per 2-D tensor [R, C]: row sums per
-// tile column [ntc][R] and column sums per tile row [ntr][C] (double), sums of
+// 256-column band [ntc][R] and column sums per 256-row band [sntr][C] (double), sums of
 // the new row EMAs per 256-row chunk, rho[R], kap[C], sums of U^2 (per row
 // tile, flat item or stats tile, whichever form the U^2 pass takes), the clip
 // factor. Per 1-D tensor: this step's v[n], sums of U^2 per
@@ -79,6 +79,7 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, 
       d.hi = x.w_hi; d.lo = x.w_lo; d.g = x.grad; d.row = x.row_ema; d.col = x.col_ema;
       d.R = (int32_t)x.rows; d.C = (int32_t)x.cols;
       d.ntr = (d.R + kFTileRows - 1) / kFTileRows;
+      d.sntr = (d.R + kSTileRows - 1) / kSTileRows;
       d.ntc = (d.C + kFTileCols - 1) / kFTileCols;
       d.nrw = (d.R + kFRowColChunk - 1) / kFRowColChunk;
       d.ncw = (d.C + kFRowColChunk - 1) / kFRowColChunk;
@@ -104,13 +105,13 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, 
       const int64_t items_any = x.numel < (int64_t(1) << 31) ? (x.numel + kItemElems - 1) / kItemElems : 0;
       const int64_t upart_n = d.vec ? (int64_t)nrt : std::max<int64_t>(items_any, (int64_t)d.ntr * d.ntc);
       d.rowpart = (double*)take(sizeof(double) * (size_t)d.ntc * d.R);
-      d.colpart = (double*)take(sizeof(double) * (size_t)d.ntr * d.C);
+      d.colpart = (double*)take(sizeof(double) * (size_t)d.sntr * d.C);
       d.rpart = (double*)take(sizeof(double) * (size_t)d.nrw);
       d.rho = (float*)take(sizeof(float) * (size_t)d.R);
       d.kap = (float*)take(sizeof(float) * (size_t)d.C);
       d.upart = (double*)take(sizeof(double) * (size_t)upart_n);
       d.f = (float*)take(sizeof(float));
-      tiles += (uint64_t)d.ntr * d.ntc;
+      tiles += (uint64_t)d.sntr * d.ntc;
       rc += (uint64_t)d.nrw + d.ncw;
       if (d.flat)
         items2 += (uint64_t)d.nitems;

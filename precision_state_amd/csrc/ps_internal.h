@@ -75,6 +75,7 @@ struct TableInline {
 // ---- factored step (ps_factored.cpp, k_factored.hip) ----
 constexpr int kFTileRows = 64;     // 2-D tile: 64 rows x 256 columns, one 256-thread workgroup
 constexpr int kFTileCols = 256;
+constexpr int kSTileRows = 256;    // stats tile: 256 rows x 256 columns, 4 chunks of kFTileRows rows
 constexpr int kFRowColChunk = 256; // rows or columns per finalize workgroup
 constexpr int kURows = 8;          // U^2 row tile (C % 8 == 0): 8 rows x 512 columns, one 64-lane wave
 constexpr int kUCols = 512;
@@ -87,7 +88,7 @@ struct F2D {
   float* row;        // [R] EMA of row means (caller state)
   float* col;        // [C] EMA of column means (caller state)
   double* rowpart;   // [ntc][R] row sums per tile column
-  double* colpart;   // [ntr][C] column sums per tile row
+  double* colpart;   // [sntr][C] column sums per 256-row stats band
   double* rpart;     // [nrw] sums of the new row EMAs per 256-row chunk
   float* rho;        // [R] 1/sqrt(r_i / mean r)
   float* kap;        // [C] 1/sqrt(c_j)
@@ -97,6 +98,7 @@ struct F2D {
   float* ms;         // first moment block scales or NULL
   int32_t R, C, ntr, ntc, nrw, ncw;
   int32_t nuc;       // vec: column bands of the U^2 row tiles (kUCols wide)
+  int32_t sntr;      // stats tiles along the rows (kSTileRows tall); colpart has sntr rows
   int32_t vec;       // C % 8 == 0: 16-byte row segments
   int32_t flat;      // R*C < 2^31 and (vec or a first moment): U^2 and apply passes run over 1024-element items
   int32_t nitems;    // flat: items of 1024 elements
