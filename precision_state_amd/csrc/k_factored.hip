@@ -22,9 +22,10 @@ namespace ps {
 namespace {
 
 constexpr int kT = 256;
-// The flat ΣU² and apply passes give each XCD runs of 256 consecutive work
-// items (256K elements): about 2% less time per step than plain index order
-// on the double-block shapes (runs of 128 to 1024 items measured alike).
+// The U^2 launch and the flat apply pass give each XCD runs of 256
+// consecutive workgroups: about 2% less time per step than plain index order
+// on the double-block shapes when both ran over 1024-element items (runs of
+// 128 to 1024 items measured alike).
 constexpr uint32_t kFlatXcdChunk = 256;
 
 // The apply pass touches the weights, residuals and first-moment codes once
@@ -284,11 +285,12 @@ __global__ __launch_bounds__(kT) void k_f_usq(FPlan P) {
   if (threadIdx.x == 0) X.upart[tile] = t;
 }
 
-// ---- flat passes over 2-D tensors with C % 8 == 0 ------------------------------
+// ---- flat items of 2-D tensors --------------------------------------------------
 // Same mapping as the fused (N)AdamW step: one 1024-element item per 64-lane
-// workgroup, each lane two runs of 8 consecutive elements; a run never
-// crosses a row because C % 8 == 0. Row and column of a run come from one
-// division per workgroup and a wrap test (C >= 1024) or a division per run.
+// workgroup, each lane two runs of 8 consecutive elements. With C % 8 == 0 a
+// run never crosses a row, and its row and column come from one division per
+// workgroup and a wrap test (C >= 1024) or a division per run; other column
+// counts (only with a first moment) take per-element factors.
 
 __device__ __forceinline__ void run_rc(uint32_t e, uint32_t off, uint32_t i0, uint32_t j0, uint32_t C, uint32_t& i,
                                        uint32_t& j) {
@@ -616,7 +618,7 @@ __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
 
 // 1-D tensors, one 1024-element item per 64-lane workgroup (item w of the
 // 1-D list): decode v, its EMA, sum of U^2. These items ride at the end of the
-// flat U^2 launch.
+// U^2 launch.
 __device__ __forceinline__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w) {
   uint32_t begin;
   const F1D& X = P.t1[find_end(P.item_end, P.n1, w, begin)];
