@@ -89,15 +89,22 @@ def read_valu(workload):
 
 
 def gpu_clocks():
-    """Current clocks from rocm-smi (a child process), or None."""
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        d = json.loads(r.stdout)
-        card = d[sorted(d)[0]]
-        return {k: v for k, v in card.items() if "clock" in k.lower()}
-    except Exception:
-        return None
+    """Current shader and memory clock levels from the amdgpu sysfs files
+    (pp_dpm_sclk / pp_dpm_mclk, the active level marked '*'), or None. Read
+    from files: no helper program is started from this GPU process."""
+    import glob
+    out = {}
+    for kind in ("sclk", "mclk"):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}")):
+            try:
+                with open(path) as f:
+                    cur = [ln.split(":", 1)[1].replace("*", "").strip() for ln in f if ln.rstrip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                out[kind] = cur[0]
+                break
+    return out or None
 
 
 def read_traffic(workload, moments="codec", split="trunc"):

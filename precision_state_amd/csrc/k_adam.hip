@@ -493,6 +493,11 @@ ps_status launch_adam_ptr(const TablePtr& tbl, uint32_t total_items, const ps_hp
   return dispatch(tbl, total_items, hp, c, s);
 }
 
+ps_status launch_adam_one(const TableOne& tbl, uint32_t total_items, const ps_hparams& hp, const StepScalars& c,
+                          hipStream_t s) {
+  return dispatch(tbl, total_items, hp, c, s);
+}
+
 ps_status launch_adam_inline(const TableInline& tbl, uint32_t total_items, const ps_hparams& hp,
                              const StepScalars& c, hipStream_t s) {
   return dispatch(tbl, total_items, hp, c, s);

@@ -324,6 +324,13 @@ ps_status ps_opt_step_multi(const ps_tensor* tensors, int32_t n_tensors, const p
   }
   if (recs.empty()) return PS_OK;
   const uint32_t total = ends.back();
+  if (recs.size() == 1) {   // one call per gradient hook: the smallest argument block
+    TableOne t1;
+    t1.recs[0] = recs[0];
+    t1.item_end[0] = ends[0];
+    t1.n = 1;
+    return launch_adam_one(t1, total, *hp, c, s);
+  }
   if (recs.size() <= (size_t)kInlineMax) {
     TableInline tb;
     memset(&tb, 0, sizeof(tb));

@@ -66,11 +66,17 @@ struct TablePtr {
   int32_t n;
 };
 
-struct TableInline {
-  DevTensor recs[kInlineMax];
-  uint32_t item_end[kInlineMax];
+// Tables that travel in the kernel arguments: up to kInlineMax tensors, and a
+// one-tensor form for per-hook calls (about 72 bytes of arguments instead of
+// about 1.1 KiB).
+template <int N>
+struct TableInlineN {
+  DevTensor recs[N];
+  uint32_t item_end[N];
   int32_t n;
 };
+using TableInline = TableInlineN<kInlineMax>;
+using TableOne = TableInlineN<1>;
 
 // ---- factored step (ps_factored.cpp, k_factored.hip) ----
 constexpr int kFTileRows = 64;     // 2-D tile: 64 rows x 256 columns, one 256-thread workgroup
@@ -169,6 +175,8 @@ void step_scalars(const ps_hparams& hp, int64_t step, StepScalars* out);
 
 // ---- launchers (k_adam.hip, k_elementwise.hip) ----
 ps_status launch_adam_ptr(const TablePtr& tbl, uint32_t total_items, const ps_hparams& hp, const StepScalars& c,
+                          hipStream_t s);
+ps_status launch_adam_one(const TableOne& tbl, uint32_t total_items, const ps_hparams& hp, const StepScalars& c,
                           hipStream_t s);
 ps_status launch_adam_inline(const TableInline& tbl, uint32_t total_items, const ps_hparams& hp,
                              const StepScalars& c, hipStream_t s);
