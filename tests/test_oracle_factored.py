@@ -266,3 +266,124 @@ def test_stochastic_rounding_brackets_the_residual_step(two_d):
         assert np.array_equal(st_s.row, st_t.row) and np.array_equal(st_s.col, st_t.col)
     else:
         assert np.array_equal(st_s.vc, st_t.vc) and np.array_equal(st_s.vs, st_t.vs)
+
+
+# ---------------------------------------------------------------------------
+# The order of adafactor_step_param (commit 7983d3d 'Fused backward pass'):
+# divide U by max(1, RMS(U) / clip_threshold), multiply by lr, replace it by
+# the first-moment EMA when beta1 is set, decay the weight by wd * lr, then
+# subtract. Written here in double from each step's decoded oracle state.
+# ---------------------------------------------------------------------------
+
+def _dbl_adaf_update(U, w, m0, hp: FHParams):
+    """Clip, lr, optional EMA, decoupled decay and the subtraction, in the
+    page's order; returns (new weight, new first moment or None, RMS(U))."""
+    rms = np.sqrt(np.mean(U * U))
+    x = U / max(1.0, rms / hp.clip_threshold) * hp.lr
+    m = None
+    if hp.beta1 != 0.0:
+        m = hp.beta1 * m0 + (1.0 - hp.beta1) * x
+        x = m
+    w = w - hp.weight_decay * hp.lr * w
+    return w - x, m, rms
+
+
+def _dbl_adaf_2d(st, g, R, C, hp: FHParams):
+    gd = oracle.bf16_to_f32(g).astype(np.float64).reshape(R, C)
+    w = oracle.join(st.hi, st.lo).astype(np.float64)
+    q = gd * gd + hp.eps1
+    r = hp.beta2 * st.row.astype(np.float64) + (1 - hp.beta2) * q.mean(axis=1)
+    c = hp.beta2 * st.col.astype(np.float64) + (1 - hp.beta2) * q.mean(axis=0)
+    U = (gd / np.sqrt(np.outer(r, c) / r.mean())).reshape(-1)
+    m0 = oracle.decode(st.mc, st.ms, oracle.SIGNED).astype(np.float64) if hp.beta1 else None
+    w2, m, rms = _dbl_adaf_update(U, w, m0, hp)
+    return w, w2, m, rms
+
+
+def _dbl_adaf_1d(st, g, hp: FHParams):
+    gd = oracle.bf16_to_f32(g).astype(np.float64)
+    w = oracle.join(st.hi, st.lo).astype(np.float64)
+    v0 = oracle.decode(st.vc, st.vs, UNSIGNED).astype(np.float64)
+    v = hp.beta2 * v0 + (1 - hp.beta2) * (gd * gd + hp.eps1)
+    U = gd / np.sqrt(v)
+    m0 = oracle.decode(st.mc, st.ms, oracle.SIGNED).astype(np.float64) if hp.beta1 else None
+    w2, m, rms = _dbl_adaf_update(U, w, m0, hp)
+    return w, w2, m, rms
+
+
+def _assert_codes_near(code, scale, want, what):
+    """Signed codes within 1 of round(32767 (|m| / block max)^(1/4)), scales
+    within 1e-6 of the block max, both from the double brute force."""
+    for b in range(oracle.nblocks(want.size)):
+        mb = want[b * 256:(b + 1) * 256]
+        s = np.max(np.abs(mb))
+        assert abs(scale[b] / s - 1) < 1e-6, (what, b)
+        k = np.floor(32767 * (np.abs(mb) / s) ** 0.25 + 0.5)
+        ref = np.where(mb < 0, 32768 - k, 32768 + k)
+        assert np.max(np.abs(code[b * 256:(b + 1) * 256].astype(np.int64) - ref)) <= 1, (what, b)
+
+
+@pytest.mark.parametrize("two_d", [True, False])
+@pytest.mark.parametrize("wd", [0.01, 0.1])
+def test_first_moment_with_weight_decay_vs_double_brute_force(two_d, wd):
+    """beta1 = 0.9 together with weight decay, 10 lockstep steps against the
+    page's order in double: the EMA holds only the clipped, lr-scaled update
+    and the decay is applied to the weight outside it. Folding the decay into
+    the EMA would scale it by 1 - beta1 on the first step and carry it into
+    the stored moment."""
+    rng = np.random.default_rng(31)
+    R, C = (40, 56) if two_d else (0, 0)
+    n = R * C if two_d else 900
+    hp = FHParams(lr=1e-3, beta1=0.9, weight_decay=wd)
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    st = _state2d(R, C, w0) if two_d else _state1d(n, w0)
+    st.mc, st.ms, _, _ = oracle.zero_moments(n)
+    for t in range(1, 11):
+        g = _bf16(rng.standard_normal(n) * 1e-3)
+        if two_d:
+            w, w2, m, _ = _dbl_adaf_2d(st, g, R, C, hp)
+        else:
+            w, w2, m, _ = _dbl_adaf_1d(st, g, hp)
+        oracle.factored_step(st, g, R, C, hp, t)
+        wo = oracle.join(st.hi, st.lo).astype(np.float64)
+        assert np.all(np.abs(wo - w2) <= 2 * ulp32(w2) + 1e-5 * np.abs(w2 - w)), t
+        _assert_codes_near(st.mc, st.ms, m, t)
+
+
+# (clip threshold, preset of the row/column EMAs or of v, expected clipping):
+# RMS(U) is about 1e-3 / sqrt(preset) for N(0, 1e-3) gradients, so presets of
+# 1.1e-5 and 2.5e-7 give RMS near 0.3 and 2; a zero preset gives about 31.6.
+CLIP_CASES = [(0.5, 1.1e-5, False), (0.5, 2.5e-7, True), (4.0, 2.5e-7, False), (4.0, 0.0, True)]
+
+
+@pytest.mark.parametrize("two_d", [True, False])
+@pytest.mark.parametrize("clip,preset,active", CLIP_CASES)
+def test_clip_threshold_vs_double_brute_force(two_d, clip, preset, active):
+    """Update clipping divides by max(1, RMS(U) / clip_threshold): at
+    thresholds 0.5 and 4.0, with the clip active and inactive, 3 lockstep
+    steps against the double brute force (where the clip is inactive the step
+    is lr * U exactly)."""
+    rng = np.random.default_rng(32)
+    R, C = (48, 40) if two_d else (0, 0)
+    n = R * C if two_d else 1100
+    hp = FHParams(lr=1e-4, clip_threshold=clip, weight_decay=0.01)
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    if two_d:
+        st = _state2d(R, C, w0)
+        st.row[:] = preset
+        st.col[:] = preset
+    else:
+        st = _state1d(n, w0)
+        st.vc[:] = 65535 if preset else 0
+        st.vs[:] = preset
+    for t in range(1, 4):
+        g = _bf16(rng.standard_normal(n) * 1e-3)
+        if two_d:
+            w, w2, _, rms = _dbl_adaf_2d(st, g, R, C, hp)
+        else:
+            w, w2, _, rms = _dbl_adaf_1d(st, g, hp)
+        if t == 1:
+            assert (rms > clip) == active, rms
+        oracle.factored_step(st, g, R, C, hp, t)
+        wo = oracle.join(st.hi, st.lo).astype(np.float64)
+        assert np.all(np.abs(wo - w2) <= 2 * ulp32(w2) + 1e-5 * np.abs(w2 - w)), t
