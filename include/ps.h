@@ -194,8 +194,9 @@ typedef struct ps_factored_hparams {
  * the kernel arguments; for longer lists, and for the records with storage
  * flags, the library keeps a device copy of each distinct list it has seen,
  * so repeated calls with the same list upload nothing. That cache holds up
- * to 16384 lists or 64 MiB per device; when it is full, the call
- * synchronizes the device once and empties it. Tensors with storage flags go
+ * to 16384 lists or 64 MiB per device; when it is full, the call waits
+ * until no other call is between taking a cached list and enqueueing the
+ * launch that reads it, then synchronizes the device once and empties it. Tensors with storage flags go
  * to a second launch with a generic-format kernel. Calls from several host
  * threads, on their own streams and over distinct tensors, are safe.
  * Errors: PS_ERR_INVALID_ARG, PS_ERR_ALIGNMENT, PS_ERR_SHAPE (host checks,

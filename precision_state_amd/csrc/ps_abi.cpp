@@ -5,8 +5,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <mutex>
-#include <unordered_map>
 #include <vector>
 
 #include "ps_internal.h"
@@ -109,143 +107,73 @@ ps_status build_active(const ps_tensor* t, int32_t n, bool residual, std::vector
   return PS_OK;
 }
 
-// ---------------------------------------------------------------------------
-// device blob cache: one immutable device copy per distinct host blob (tensor
-// tables, factored-step plans). A training loop passes the same lists every
-// step, also when it steps tensor by tensor from gradient hooks (one blob per
-// tensor, hundreds per model), so after the first step nothing is uploaded.
-// Blobs live in per-device arenas of pinned host staging plus device memory;
-// when an arena limit is reached the device is synchronized and that
-// device's cache is emptied, so no launch can still read a freed blob.
-// ---------------------------------------------------------------------------
-
-struct BlobEntry {
-  std::vector<unsigned char> key;
-  const void* d_mem = nullptr;
-  hipEvent_t ready = nullptr;   // upload done
-  bool done = false;            // the upload is known to have completed
-};
-
-struct Chunk {
-  char* d_mem = nullptr;
-  char* h_mem = nullptr;   // pinned source of the uploads
-  size_t size = 0, used = 0;
-};
-
-struct DeviceCache {
-  std::unordered_multimap<uint64_t, BlobEntry*> by_hash;
-  std::vector<Chunk> chunks;
-  size_t entries = 0, bytes = 0;
-};
-
-std::mutex g_cache_mu;
-std::unordered_map<int, DeviceCache> g_cache;
-constexpr size_t kChunkBytes = size_t(1) << 20;
-constexpr size_t kCacheMaxBytes = size_t(64) << 20;   // per device
-constexpr size_t kCacheMaxEntries = 16384;            // per device
-constexpr size_t kBlobAlign = 256;
-
-uint64_t fnv1a(const void* data, size_t bytes) {
-  const unsigned char* p = (const unsigned char*)data;
-  uint64_t h = 1469598103934665603ull;
-  for (size_t i = 0; i < bytes; ++i) h = (h ^ p[i]) * 1099511628211ull;
-  return h;
-}
-
-void flush(DeviceCache& dc) {
-  for (auto& kv : dc.by_hash) {
-    if (kv.second->ready) (void)hipEventDestroy(kv.second->ready);
-    delete kv.second;
-  }
-  dc.by_hash.clear();
-  for (Chunk& c : dc.chunks) {
-    if (c.d_mem) (void)hipFree(c.d_mem);
-    if (c.h_mem) (void)hipHostFree(c.h_mem);
-  }
-  dc.chunks.clear();
-  dc.entries = dc.bytes = 0;
-}
-
-// Room for `bytes` in the device's arena: the current chunk, else a new one.
-ps_status arena_take(DeviceCache& dc, size_t bytes, char** d, char** h) {
-  const size_t need = (bytes + kBlobAlign - 1) / kBlobAlign * kBlobAlign;
-  if (dc.chunks.empty() || dc.chunks.back().size - dc.chunks.back().used < need) {
-    Chunk c;
-    c.size = need > kChunkBytes ? need : kChunkBytes;
-    if (hipMalloc((void**)&c.d_mem, c.size) != hipSuccess) return fail(PS_ERR_NO_MEMORY, "device table allocation failed");
-    if (hipHostMalloc((void**)&c.h_mem, c.size, hipHostMallocDefault) != hipSuccess) {
-      (void)hipFree(c.d_mem);
-      return fail(PS_ERR_NO_MEMORY, "pinned table staging allocation failed");
-    }
-    dc.chunks.push_back(c);
-    dc.bytes += c.size;
-  }
-  Chunk& c = dc.chunks.back();
-  *d = c.d_mem + c.used;
-  *h = c.h_mem + c.used;
-  c.used += need;
-  return PS_OK;
-}
-
 }  // namespace
 
-ps_status device_blob(const void* data, size_t bytes, hipStream_t s, const void** dptr) {
+// ---------------------------------------------------------------------------
+// device blob cache (blob_cache.h): HIP backend
+// ---------------------------------------------------------------------------
+
+int HipBlobBackend::alloc_chunk(size_t bytes, char** d, char** h) {
+  if (hipMalloc((void**)d, bytes) != hipSuccess) return fail(PS_ERR_NO_MEMORY, "device table allocation failed");
+  if (hipHostMalloc((void**)h, bytes, hipHostMallocDefault) != hipSuccess) {
+    (void)hipFree(*d);
+    return fail(PS_ERR_NO_MEMORY, "pinned table staging allocation failed");
+  }
+  return PS_OK;
+}
+
+void HipBlobBackend::free_chunk(char* d, char* h) {
+  if (d) (void)hipFree(d);
+  if (h) (void)hipHostFree(h);
+}
+
+int HipBlobBackend::create_event(hipEvent_t* e) {
+  return hip_check(hipEventCreateWithFlags(e, hipEventDisableTiming), "hipEventCreate");
+}
+
+void HipBlobBackend::destroy_event(hipEvent_t e) {
+  if (e) (void)hipEventDestroy(e);
+}
+
+int HipBlobBackend::upload(char* d, const char* h, size_t bytes, hipStream_t s, hipEvent_t e) {
+  if (ps_status st = hip_check(hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, s), "table upload")) return st;
+  return hip_check(hipEventRecord(e, s), "hipEventRecord");
+}
+
+bool HipBlobBackend::event_done(hipEvent_t e) { return hipEventQuery(e) == hipSuccess; }
+
+int HipBlobBackend::stream_wait(hipStream_t s, hipEvent_t e) {
+  return hip_check(hipStreamWaitEvent(s, e, 0), "hipStreamWaitEvent");
+}
+
+int HipBlobBackend::device_sync() { return hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize"); }
+
+void HipBlobBackend::sync_stream(hipStream_t s) { (void)hipStreamSynchronize(s); }
+
+// Up to 16384 blobs or 64 MiB of arena per device, grown 1 MiB at a time.
+// The cache lives until the process ends.
+TableCache& table_cache() {
+  static HipBlobBackend* backend = new HipBlobBackend;
+  static TableCache* cache = new TableCache(*backend, BlobLimits{16384, size_t(64) << 20, size_t(1) << 20});
+  return *cache;
+}
+
+ps_status device_blob(const void* data, size_t bytes, hipStream_t s, const void** dptr, TableLease& lease) {
   int dev = 0;
   if (ps_status st = hip_check(hipGetDevice(&dev), "hipGetDevice")) return st;
-  const uint64_t h = fnv1a(data, bytes);
-  std::lock_guard<std::mutex> lk(g_cache_mu);
-  DeviceCache& dc = g_cache[dev];
-  auto range = dc.by_hash.equal_range(h);
-  for (auto it = range.first; it != range.second; ++it) {
-    BlobEntry* e = it->second;
-    if (e->key.size() != bytes || memcmp(e->key.data(), data, bytes) != 0) continue;
-    // wait for the upload unless it is known to have completed
-    if (!e->done) {
-      if (hipEventQuery(e->ready) == hipSuccess)
-        e->done = true;
-      else if (ps_status st = hip_check(hipStreamWaitEvent(s, e->ready, 0), "hipStreamWaitEvent"))
-        return st;
-    }
-    *dptr = e->d_mem;
-    return PS_OK;
-  }
-  if (dc.entries >= kCacheMaxEntries || dc.bytes + bytes > kCacheMaxBytes) {
-    // Every launch that may read a cached blob must end before it is freed.
-    if (ps_status st = hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize")) return st;
-    flush(dc);
-  }
-  char *d = nullptr, *hm = nullptr;
-  if (ps_status st = arena_take(dc, bytes, &d, &hm)) return st;
-  BlobEntry* e = new BlobEntry;
-  e->key.assign((const unsigned char*)data, (const unsigned char*)data + bytes);
-  e->d_mem = d;
-  memcpy(hm, data, bytes);
-  ps_status st = hip_check(hipEventCreateWithFlags(&e->ready, hipEventDisableTiming), "hipEventCreate");
-  if (!st) st = hip_check(hipMemcpyAsync(d, hm, bytes, hipMemcpyHostToDevice, s), "table upload");
-  if (!st) st = hip_check(hipEventRecord(e->ready, s), "hipEventRecord");
-  if (st) {
-    // the arena space stays reserved until the next flush
-    (void)hipStreamSynchronize(s);
-    if (e->ready) (void)hipEventDestroy(e->ready);
-    delete e;
-    return st;
-  }
-  dc.by_hash.emplace(h, e);
-  ++dc.entries;
-  *dptr = d;
-  return PS_OK;
+  return table_cache().get(dev, data, bytes, s, dptr, lease);
 }
 
 namespace {
 
 ps_status get_table(const std::vector<DevTensor>& recs, const std::vector<uint32_t>& ends, hipStream_t s,
-                    TablePtr* out) {
+                    TablePtr* out, TableLease& lease) {
   const size_t rb = recs.size() * sizeof(DevTensor), eb = ends.size() * sizeof(uint32_t);
   std::vector<unsigned char> blob(rb + eb);
   memcpy(blob.data(), recs.data(), rb);
   memcpy(blob.data() + rb, ends.data(), eb);
   const void* d = nullptr;
-  if (ps_status st = device_blob(blob.data(), blob.size(), s, &d)) return st;
+  if (ps_status st = device_blob(blob.data(), blob.size(), s, &d, lease)) return st;
   *out = TablePtr{(const DevTensor*)d, (const uint32_t*)((const char*)d + rb), (int32_t)recs.size()};
   return PS_OK;
 }
@@ -313,12 +241,13 @@ ps_status ps_opt_step_multi(const ps_tensor* tensors, int32_t n_tensors, const p
   }
   hipStream_t s = (hipStream_t)stream;
   if (!xrecs.empty()) {
+    TableLease lease(table_cache());   // held until the launch that reads the table is enqueued
     const size_t rb = xrecs.size() * sizeof(DevTensorEx), eb = xends.size() * sizeof(uint32_t);
     std::vector<unsigned char> blob(rb + eb);
     memcpy(blob.data(), xrecs.data(), rb);
     memcpy(blob.data() + rb, xends.data(), eb);
     const void* d = nullptr;
-    if (ps_status st = device_blob(blob.data(), blob.size(), s, &d)) return st;
+    if (ps_status st = device_blob(blob.data(), blob.size(), s, &d, lease)) return st;
     TableExPtr tx{(const DevTensorEx*)d, (const uint32_t*)((const char*)d + rb), (int32_t)xrecs.size()};
     if (ps_status st = launch_adam_ex(tx, xends.back(), *hp, c, s)) return st;
   }
@@ -341,8 +270,9 @@ ps_status ps_opt_step_multi(const ps_tensor* tensors, int32_t n_tensors, const p
     tb.n = (int32_t)recs.size();
     return launch_adam_inline(tb, total, *hp, c, s);
   }
+  TableLease lease(table_cache());     // held until the launch is enqueued
   TablePtr tp;
-  if (ps_status st = get_table(recs, ends, s, &tp)) return st;
+  if (ps_status st = get_table(recs, ends, s, &tp, lease)) return st;
   return launch_adam_ptr(tp, total, *hp, c, s);
 }
 

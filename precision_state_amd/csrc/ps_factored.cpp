@@ -204,7 +204,8 @@ ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps
   if (e1) memcpy(p + b2 + b1 + 7 * e2, W.item_end.data(), e1);
   hipStream_t s = (hipStream_t)stream;
   const void* d = nullptr;
-  if (ps_status st = device_blob(blob.data(), blob.size(), s, &d)) return st;
+  TableLease lease(table_cache());   // held until the launches that read the plan are enqueued
+  if (ps_status st = device_blob(blob.data(), blob.size(), s, &d, lease)) return st;
   const char* dc = (const char*)d;
   FPlan pl;
   pl.t2 = (const F2D*)dc;

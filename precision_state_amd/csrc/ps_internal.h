@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/ps.h"
+#include "blob_cache.h"
 
 namespace ps {
 
@@ -163,8 +164,26 @@ ps_status launch_factored(const FPlan& plan, const FScalars& sc, int split_mode,
 ps_status fail(ps_status s, const char* fmt, ...);
 ps_status hip_check(hipError_t e, const char* what);
 
-// Device copy of a host blob, cached by content (ps_abi.cpp).
-ps_status device_blob(const void* data, size_t bytes, hipStream_t s, const void** dptr);
+// Device copies of host blobs, cached by content (blob_cache.h; the HIP
+// backend is in ps_abi.cpp). A caller holds a TableLease from before
+// device_blob until the launches that read the blob are enqueued.
+struct HipBlobBackend {
+  using Stream = hipStream_t;
+  using Event = hipEvent_t;
+  int alloc_chunk(size_t bytes, char** d, char** h);
+  void free_chunk(char* d, char* h);
+  int create_event(hipEvent_t* e);
+  void destroy_event(hipEvent_t e);
+  int upload(char* d, const char* h, size_t bytes, hipStream_t s, hipEvent_t e);
+  bool event_done(hipEvent_t e);
+  int stream_wait(hipStream_t s, hipEvent_t e);
+  int device_sync();
+  void sync_stream(hipStream_t s);
+};
+using TableCache = BlobCache<HipBlobBackend>;
+using TableLease = TableCache::Lease;
+TableCache& table_cache();
+ps_status device_blob(const void* data, size_t bytes, hipStream_t s, const void** dptr, TableLease& lease);
 bool is_finite(double x);
 bool is_aligned(const void* p, uintptr_t a);
 
