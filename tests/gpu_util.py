@@ -202,3 +202,45 @@ def check_sampled_blocks(shapes, devs, hp, steps, seed, per_tensor, outlier_p=0.
                 assert np.array_equal(got[name], want[name]), (shape.name, int(b), name)
         total += len(blocks)
     return total
+
+
+def ofhp(hp, tensor=0):
+    """oracle.FHParams of a precision_state_amd.FactoredHParams (tensor = the
+    tensor's index in the device call's list, for stochastic rounding)."""
+    return oracle.FHParams(hp.split_mode, hp.lr, hp.beta2, hp.eps1, hp.clip_threshold, hp.weight_decay,
+                           hp.decay_rate, hp.beta1, hp.seed, tensor)
+
+
+def ulp_dist(a, b):
+    """Distance in fp32 ulps between bit patterns (monotone integer mapping)."""
+    def key(x):
+        x = x.astype(np.int64)
+        return np.where(x & 0x80000000, 0x80000000 - (x & 0x7FFFFFFF), x + 0x80000000)
+    return np.abs(key(a.view(np.uint32)) - key(b.view(np.uint32)))
+
+
+def compare_factored(d, h, rows, what, first_moment=False):
+    """Factored-step parity of a device state against the oracle's: master
+    weights within 4 fp32 ulp, row/column EMAs within 1 ulp, v and m codes
+    within 1, m scales within 1 ulp; returns the mismatch report."""
+    dh = to_host(d)
+    wd = oracle.join(dh.hi, dh.lo).view(np.uint32)
+    wh = oracle.join(h.hi, h.lo).view(np.uint32)
+    ud = ulp_dist(wd, wh)
+    rep = {"w_exact": int(np.count_nonzero(ud == 0)), "w_n": int(ud.size), "w_max_ulp": int(ud.max(initial=0))}
+    if rows > 0:
+        rd = np.concatenate([ulp_dist(dh.row, h.row), ulp_dist(dh.col, h.col)])
+        rep["rowcol_max_ulp"] = int(rd.max(initial=0))
+        assert rep["rowcol_max_ulp"] <= 1, (what, rep)
+    else:
+        cd = np.abs(dh.vc.astype(np.int64) - h.vc.astype(np.int64))
+        rep["v_code_max_diff"] = int(cd.max(initial=0))
+        rep["v_scale_max_ulp"] = int(ulp_dist(dh.vs, h.vs).max(initial=0))
+        assert rep["v_code_max_diff"] <= 1, (what, rep)
+    if first_moment:
+        md = np.abs(dh.mc.astype(np.int64) - h.mc.astype(np.int64))
+        rep["m_code_max_diff"] = int(md.max(initial=0))
+        rep["m_scale_max_ulp"] = int(ulp_dist(dh.ms, h.ms).max(initial=0))
+        assert rep["m_code_max_diff"] <= 1 and rep["m_scale_max_ulp"] <= 1, (what, rep)
+    assert rep["w_max_ulp"] <= 4, (what, rep)
+    return rep

@@ -1,0 +1,20 @@
+"""Build tests/kernels/libps_probe.so (test-only kernels over the library's
+device helpers) with hipcc for gfx950, with the library's arithmetic flags."""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "libps_probe.so")
+
+
+def build(verbose=False):
+    cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           os.path.join(HERE, "probe_exact.hip"), "-o", LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on probe_exact.hip:\n{r.stderr}")
+    os.replace(LIB + ".tmp", LIB)
+    return LIB

@@ -5,12 +5,15 @@ EMAs within 1 ulp, v codes within 1; the kernels use the oracle's operation
 order everywhere except the order of the double-precision sums (fixed trees
 instead of index order), so exact agreement is expected and mismatch counts
 are reported."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from gpu_util import DEV, dev_grad, dev_state, f32, host_grad, host_state, to_host, u16
+from gpu_util import DEV, compare_factored as _compare, dev_grad, dev_state, host_grad, host_state, ofhp as _ofhp
 
 pytestmark = pytest.mark.gpu
 
@@ -21,48 +24,23 @@ if not torch.cuda.is_available():
 import precision_state_amd as ps  # noqa: E402
 
 
-def _ofhp(hp, tensor=0):
-    return oracle.FHParams(hp.split_mode, hp.lr, hp.beta2, hp.eps1, hp.clip_threshold, hp.weight_decay,
-                           hp.decay_rate, hp.beta1, hp.seed, tensor)
-
-
-def _ulp_dist(a, b):
-    """Distance in fp32 ulps between bit patterns (monotone integer mapping)."""
-    def key(x):
-        x = x.astype(np.int64)
-        return np.where(x & 0x80000000, 0x80000000 - (x & 0x7FFFFFFF), x + 0x80000000)
-    return np.abs(key(a.view(np.uint32)) - key(b.view(np.uint32)))
-
-
-def _compare(d, h, rows, what, first_moment=False):
-    dh = to_host(d)
-    wd = oracle.join(dh.hi, dh.lo).view(np.uint32)
-    wh = oracle.join(h.hi, h.lo).view(np.uint32)
-    ud = _ulp_dist(wd, wh)
-    rep = {"w_exact": int(np.count_nonzero(ud == 0)), "w_n": int(ud.size), "w_max_ulp": int(ud.max(initial=0))}
-    if rows > 0:
-        rd = np.concatenate([_ulp_dist(dh.row, h.row), _ulp_dist(dh.col, h.col)])
-        rep["rowcol_max_ulp"] = int(rd.max(initial=0))
-        assert rep["rowcol_max_ulp"] <= 1, (what, rep)
-    else:
-        cd = np.abs(dh.vc.astype(np.int64) - h.vc.astype(np.int64))
-        rep["v_code_max_diff"] = int(cd.max(initial=0))
-        rep["v_scale_max_ulp"] = int(_ulp_dist(dh.vs, h.vs).max(initial=0))
-        assert rep["v_code_max_diff"] <= 1, (what, rep)
-    if first_moment:
-        md = np.abs(dh.mc.astype(np.int64) - h.mc.astype(np.int64))
-        rep["m_code_max_diff"] = int(md.max(initial=0))
-        rep["m_scale_max_ulp"] = int(_ulp_dist(dh.ms, h.ms).max(initial=0))
-        assert rep["m_code_max_diff"] <= 1 and rep["m_scale_max_ulp"] <= 1, (what, rep)
-    assert rep["w_max_ulp"] <= 4, (what, rep)
-    return rep
+# The oracle steps each checked tensor on its own host thread (ctypes releases
+# the GIL during each call; the tensors' states are independent).
+_POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
 
 
 def _run(shapes, hp, steps, seed, outlier_p, check=None, zero_grad=()):
     devs = [dev_state(s.numel, seed, i, s.rows, s.cols, factored=True) for i, s in enumerate(shapes)]
-    hosts = [host_state(s.numel, seed, i, s.rows, factored=True, cols=s.cols) for i, s in enumerate(shapes)]
-    check = range(len(shapes)) if check is None else check
+    check = list(range(len(shapes)) if check is None else check)
+    hosts = {i: host_state(shapes[i].numel, seed, i, shapes[i].rows, factored=True, cols=shapes[i].cols)
+             for i in check}
     ws = None
+
+    def oracle_step(i, t):
+        s = shapes[i]
+        g = np.zeros(s.numel, np.uint16) if i in zero_grad else host_grad(s.numel, seed, i, t, outlier_p)
+        oracle.factored_step(hosts[i], g, s.rows, s.cols, _ofhp(hp, i), t)
+
     for t in range(1, steps + 1):
         dg = [torch.zeros(s.numel, dtype=torch.int16, device=DEV) if i in zero_grad else
               dev_grad(s.numel, seed, i, t, outlier_p) for i, s in enumerate(shapes)]
@@ -71,10 +49,9 @@ def _run(shapes, hp, steps, seed, outlier_p, check=None, zero_grad=()):
         if ws is None or ws.numel() < need:
             ws = torch.empty(max(need, 256), dtype=torch.uint8, device=DEV)
         ps.factored_step(None, None, hp, t, workspace=ws, records=recs)
-        for i in check:
-            s = shapes[i]
-            g = np.zeros(s.numel, np.uint16) if i in zero_grad else host_grad(s.numel, seed, i, t, outlier_p)
-            oracle.factored_step(hosts[i], g, s.rows, s.cols, _ofhp(hp, i), t)
+        # largest tensors first, so the longest oracle calls start at once
+        for f in [_POOL.submit(oracle_step, i, t) for i in sorted(check, key=lambda i: -shapes[i].numel)]:
+            f.result()
         print(f"  step {t} done", flush=True)
     torch.cuda.synchronize()
     reps = {}
@@ -130,16 +107,26 @@ def test_zero_gradient_leaves_weights_identical():
 
 def test_factored_schedule_and_first_moment_double_block_6_steps():
     """Adafactor's beta2 schedule (1 - t^-0.8) and a first moment (beta1 0.9)
-    on the FLUX double-block shapes (all 24 stepped on the GPU in one call per
-    step), 6 steps, wd 0.01; weights, EMAs, v codes and the first-moment codes
-    and scales against the oracle for two 2-D weights (3072 x 3072 and
-    3072 x 12288) and all 14 1-D tensors (the oracle's encode bisects, so the
-    other 2-D weights are left out to keep the test short)."""
+    on the FLUX double-block shapes (all 24 in one call per step), 6 steps,
+    wd 0.01; weights, EMAs, v codes and the first-moment codes and scales of
+    every tensor against the oracle."""
     shapes = synth.WORKLOADS["flux_double_block"]()
     hp = ps.FactoredHParams(lr=1e-5, eps1=1e-30, clip_threshold=1.0, weight_decay=0.01, decay_rate=-0.8, beta1=0.9)
-    check = [6, 10] + [i for i, s in enumerate(shapes) if not s.is_2d]
-    reps = _run(shapes, hp, 6, 5, 0.001, check=check)
-    assert len(reps) == 16
+    reps = _run(shapes, hp, 6, 5, 0.001)
+    assert len(reps) == 24
+
+
+@pytest.mark.parametrize("clip,decay_rate", [(0.5, 0.0), (4.0, -0.8), (2.5, 0.0)])
+def test_factored_clip_threshold(clip, decay_rate):
+    """Update clipping at thresholds other than 1 (adafactor_step_param divides
+    U by max(1, RMS(U) / clip_threshold)): with zero EMAs and constant beta2
+    the first step's RMS is about 31.6 (clipped at 0.5 and 2.5); with the
+    schedule, beta2 is 0 at update 1 and RMS(U) is near 1, so 4.0 mostly
+    leaves the update unclipped. Ragged shapes (with a first moment at 2.5),
+    4 steps."""
+    hp = ps.FactoredHParams(lr=1e-4, clip_threshold=clip, weight_decay=0.01, decay_rate=decay_rate,
+                            beta1=0.9 if clip == 2.5 else 0.0, seed=3)
+    _run(RAGGED if clip != 2.5 else FM_RAGGED, hp, 4, 13, 0.01)
 
 
 FM_RAGGED = [synth.Shape("e", 129, 8, 129 * 8), synth.Shape("f", 64, 256, 64 * 256), synth.Shape("g", 100, 3000, 300000),

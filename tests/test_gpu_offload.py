@@ -1,11 +1,13 @@
 """The host-offload pipeline (sd-scripts PR #2187 '(N)AdamW / Adan with fused
 backwards pass & CPU offloading', opening post: state offloaded to host memory
-between steps) must give exactly the bytes of the device-resident step."""
+between steps) must give exactly the bytes of the device-resident step, and
+of the oracle's replay of every tensor."""
 import numpy as np
 import pytest
 
+import oracle
 import synth
-from gpu_util import DEV
+from gpu_util import DEV, check_sampled_blocks, f32, ohp, u16
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +105,97 @@ def test_offload_stochastic_rounding_moves_no_residual_and_equals_resident():
     with pytest.raises(ps.PSError):
         plan.run(ps.HParams(algo=ps.ALGO_NADAM), 4)     # a residual mode needs every w_lo
     plan.close()
+
+
+# ---------------------------------------------------------------------------
+# Against the oracle: every tensor of every group regenerated on the host
+# from the same seeded recipe and replayed through the oracle's step.
+# ---------------------------------------------------------------------------
+
+def _oracle_groups(groups, hp, steps, skip=(), seed=5, tid_of=lambda gid, i, pos: 100 * gid + i):
+    """Oracle replay of the offloaded groups. tid_of gives each tensor's
+    synthetic-input key; stochastic rounding is keyed by the tensor's position
+    in the concatenated group lists, as the pipeline keys it."""
+    out, pos = [], 0
+    for gid, sizes in enumerate(groups):
+        grp = []
+        for i, n in enumerate(sizes):
+            tid = tid_of(gid, i, pos + i)
+            st = oracle.TensorState(synth.host_bf16_normal(n, seed, synth.STREAM_HI, tid, 0, synth.SIGMA_W),
+                                    synth.host_u16_uniform(n, seed, synth.STREAM_LO, tid, 0), *oracle.zero_moments(n))
+            if (gid, i) not in skip:
+                for t in range(1, steps + 1):
+                    g = synth.host_bf16_normal(n, seed, synth.STREAM_GRAD, tid, t, synth.SIGMA_G)
+                    oracle.opt_step(st, g, ohp(hp, pos + i), t)
+            grp.append(st)
+        out.append(grp)
+        pos += len(sizes)
+    return out
+
+
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY, ps.SPLIT_STOCHASTIC])
+def test_offload_matches_oracle_every_byte(split_mode):
+    """Three ragged groups (a tensor without a gradient, an empty tensor), 3
+    NAdamW steps through the pipeline; weights, residuals, codes and scales of
+    every tensor equal the oracle's replay."""
+    slabs = [ps.StateSlab(sizes, DEV, host_state=True) for sizes in GROUPS]
+    for gid, sl in enumerate(slabs):
+        _fill(sl, gid)
+    torch.cuda.synchronize()
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=1e-4, weight_decay=0.01, split_mode=split_mode, seed=77)
+    grads = [[None if (gid == 1 and i == 1) else g for i, g in enumerate(sl.grads)] for gid, sl in enumerate(slabs)]
+    plan = ps.OffloadPlan([(sl.states, grads[gid]) for gid, sl in enumerate(slabs)])
+    for t in range(1, 4):
+        for gid, sl in enumerate(slabs):
+            for i, g in enumerate(sl.grads):
+                synth.dev_bf16_normal(g, 5, synth.STREAM_GRAD, 100 * gid + i, t, synth.SIGMA_G)
+        plan.run(hp, t)
+    torch.cuda.synchronize()
+    plan.close()
+    want = _oracle_groups(GROUPS, hp, 3, skip={(1, 1)})
+    for gid, sl in enumerate(slabs):
+        for i, (a, h) in enumerate(zip(sl.states, want[gid])):
+            got = {"hi": u16(a.w_hi), "lo": u16(a.w_lo), "mc": u16(a.m_code), "vc": u16(a.v_code),
+                   "ms": f32(a.m_scale).view(np.uint32), "vs": f32(a.v_scale).view(np.uint32)}
+            exp = {"hi": h.hi, "lo": h.lo, "mc": h.mc, "vc": h.vc, "ms": h.ms.view(np.uint32),
+                   "vs": h.vs.view(np.uint32)}
+            for k in got:
+                assert np.array_equal(got[k], exp[k]), (gid, i, a.numel, k)
+
+
+def test_offload_double_blocks_distinct_host_sets_sampled():
+    """Three groups of unequal size built from FLUX double-block shapes (a
+    whole block, its first 10 tensors, a whole block plus 5 tensors of
+    another), each with its own pinned host state, run for 2 steps so that
+    both staging slots are reused; sampled 256-blocks of every tensor against
+    the oracle (each block evolves from its own inputs only)."""
+    blk = synth.WORKLOADS["flux_double_block"]()
+    group_shapes = [blk, blk[:10], blk + blk[:5]]
+    slabs = [ps.StateSlab([s.numel for s in shapes], DEV, host_state=True) for shapes in group_shapes]
+    pos = 0
+    all_shapes, all_states = [], []
+    for sl, shapes in zip(slabs, group_shapes):
+        for i, st in enumerate(sl.states):
+            tid = pos + i                      # synthetic key = position in the concatenated list
+            h = torch.empty(st.numel, dtype=torch.int16, device=DEV)
+            synth.dev_bf16_normal(st.w_hi, 0, synth.STREAM_HI, tid, 0, synth.SIGMA_W)
+            synth.dev_u16_uniform(h, 0, synth.STREAM_LO, tid, 0)
+            st.w_lo.copy_(h.cpu())
+        pos += len(shapes)
+        all_shapes += shapes
+        all_states += sl.states
+    torch.cuda.synchronize()
+    hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, weight_decay=0.01)
+    plan = ps.OffloadPlan([(sl.states, sl.grads) for sl in slabs])
+    for t in range(1, 3):
+        pos = 0
+        for sl in slabs:
+            for i, g in enumerate(sl.grads):
+                synth.dev_bf16_normal(g, 0, synth.STREAM_GRAD, pos + i, t, synth.SIGMA_G)
+            pos += len(sl.grads)
+        plan.run(hp, t)
+        print(f"  offload step {t} done", flush=True)
+    torch.cuda.synchronize()
+    plan.close()
+    n = check_sampled_blocks(all_shapes, all_states, hp, 2, 0, 6)
+    print(f"  {n} sampled blocks of {len(all_shapes)} tensors exact", flush=True)

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import DEV, dev_grad, dev_state, ohp, u16
+from gpu_util import DEV, compare_factored, dev_grad, dev_state, host_grad, host_state, ofhp, ohp, u16
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,12 @@ def test_per_tensor_factored_calls_equal_one_list_call():
     for i, (x, y) in enumerate(zip(a, b)):
         for fx, fy in zip(_fields(x), _fields(y)):
             assert torch.equal(fx, fy), (i, shapes[i])
+    # and both against the oracle, tensor by tensor
+    for i, (n, r, c) in enumerate(shapes):
+        h = host_state(n, 31, i, r, factored=True, cols=c)
+        for t in range(1, 4):
+            oracle.factored_step(h, host_grad(n, 31, i, t), r, c, ofhp(hp), t)
+        compare_factored(a[i], h, r, (i, shapes[i]), first_moment=True)
 
 
 def _flagged_state(numel, tid, seed=47):
