@@ -260,6 +260,26 @@ ps_status ps_factored_workspace_size(const ps_tensor* tensors, int32_t n_tensors
 ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps_factored_hparams* hp,
                            int64_t step, void* workspace, size_t workspace_bytes, ps_stream_t stream);
 
+/* ps_factored_step_noalloc - for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): ps_factored_step with no workspace argument and no device
+ * allocation. The plan and the workspace go to a scratch array that the
+ * library keeps in each GPU's memory for the life of the process,
+ * PS_NOALLOC_SCRATCH_BYTES per GPU (its address is looked up on the first
+ * call on each device). The plan, rounded up to 256 bytes, plus
+ * ps_factored_workspace_size must fit in it, else the call returns
+ * PS_ERR_WORKSPACE before any device work; one FLUX double block (24 tensors,
+ * 21.8 MiB of workspace) fits. The plan reaches the scratch through kernel
+ * arguments, so the call makes no copy from host memory either. Same kernels
+ * and results as ps_factored_step; the scratch's contents on entry are
+ * ignored. Every call on one GPU uses that GPU's single scratch array: calls
+ * ordered on one stream are safe, calls that may overlap on one GPU (other
+ * streams or host threads without ordering between them) race and must not
+ * be made. Errors as ps_factored_step. */
+#define PS_NOALLOC_SCRATCH_BYTES (32u << 20)
+ps_status ps_factored_step_noalloc(const ps_tensor* tensors, int32_t n_tensors, const ps_factored_hparams* hp,
+                                   int64_t step, ps_stream_t stream);
+
 /* Host-offload pipeline [NADAM, opening post: moments (and here the
  * residuals) live in host memory and cross PCIe every step].
  * A group is one set of tensors stepped together (e.g. one transformer

@@ -33,7 +33,8 @@ STATUS = {0: "PS_OK", 1: "PS_ERR_INVALID_ARG", 2: "PS_ERR_ALIGNMENT", 3: "PS_ERR
           4: "PS_ERR_UNSUPPORTED", 5: "PS_ERR_HIP", 6: "PS_ERR_NO_MEMORY", 7: "PS_ERR_WORKSPACE"}
 
 EXPORTED = ["ps_opt_step_multi", "ps_step_scalars", "ps_split", "ps_join", "ps_encode_moments",
-            "ps_decode_moments", "ps_factored_workspace_size", "ps_factored_step", "ps_offload_plan_create",
+            "ps_decode_moments", "ps_factored_workspace_size", "ps_factored_step", "ps_factored_step_noalloc",
+            "ps_offload_plan_create",
             "ps_offload_run", "ps_offload_bytes", "ps_offload_plan_destroy", "ps_status_string",
             "ps_last_error", "ps_version"]
 
@@ -79,6 +80,7 @@ _sig = {
     "ps_decode_moments": [_vp, _vp, _vp, _i64, _i32, _vp],
     "ps_factored_workspace_size": [ctypes.POINTER(CTensor), _i32, ctypes.POINTER(ctypes.c_size_t)],
     "ps_factored_step": [ctypes.POINTER(CTensor), _i32, ctypes.POINTER(CFHParams), _i64, _vp, ctypes.c_size_t, _vp],
+    "ps_factored_step_noalloc": [ctypes.POINTER(CTensor), _i32, ctypes.POINTER(CFHParams), _i64, _vp],
     "ps_offload_plan_create": [ctypes.POINTER(COffloadGroup), _i32, ctypes.POINTER(ctypes.c_void_p)],
     "ps_offload_run": [_vp, ctypes.POINTER(CHParams), _i64, _vp],
     "ps_offload_bytes": [_vp, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)],
@@ -298,6 +300,17 @@ def factored_step(states, grads=None, hp: FactoredHParams = None, step: int = 1,
     h = (hp or FactoredHParams()).c()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.ps_factored_step(arr, n, ctypes.byref(h), step, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PS_NOALLOC_SCRATCH_BYTES
+
+
+def factored_step_noalloc(states, grads=None, hp: FactoredHParams = None, step: int = 1, stream=None, records=None):
+    """ps_factored_step_noalloc: the factored step with the library's built-in
+    scratch as its workspace (no device allocation)."""
+    arr, n = records if records is not None else make_records(states, grads)
+    h = (hp or FactoredHParams()).c()
+    _check(_lib.ps_factored_step_noalloc(arr, n, ctypes.byref(h), step, _stream(stream)))
 
 
 class OffloadPlan:

@@ -159,6 +159,81 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, 
 }
 
 }  // namespace
+
+ps_status factored_prepare(const ps_tensor* t, int32_t n, const ps_factored_hparams* hp, int64_t step, char* ws,
+                           FactoredCall& c) {
+  if (ps_status s = check_fhparams(hp)) return s;
+  if (step < 1) return fail(PS_ERR_INVALID_ARG, "step must be >= 1 (got %lld)", (long long)step);
+  const bool fm = hp->beta1 != 0.0;
+  const bool residual = hp->split_mode != PS_SPLIT_STOCHASTIC;
+  thread_local Layout W;
+  W.t2.clear(); W.t1.clear(); W.tile_end.clear(); W.rc_end.clear(); W.tile_nf_end.clear(); W.item2_end.clear();
+  W.item_end.clear(); W.rt_end.clear(); W.tile_u_end.clear(); W.item2u_end.clear(); W.bytes = 0;
+  if (ps_status s = plan(t, n, ws, fm, residual, W)) return s;
+  c.empty = W.t2.empty() && W.t1.empty();
+  c.ws_bytes = W.bytes;
+  // the plan image: F2D[n2] | F1D[n1] | the seven [n2] prefix-end lists | item_end[n1]
+  const size_t b2 = W.t2.size() * sizeof(F2D), b1 = W.t1.size() * sizeof(F1D);
+  const size_t e2 = W.t2.size() * sizeof(uint32_t), e1 = W.t1.size() * sizeof(uint32_t);
+  const std::vector<uint32_t>* lists2[7] = {&W.tile_end, &W.rc_end, &W.tile_nf_end, &W.item2_end,
+                                            &W.rt_end, &W.tile_u_end, &W.item2u_end};
+  c.image.resize(b2 + b1 + 7 * e2 + e1);
+  unsigned char* p = c.image.data();
+  if (b2) memcpy(p, W.t2.data(), b2);
+  if (b1) memcpy(p + b2, W.t1.data(), b1);
+  if (e2)
+    for (int k = 0; k < 7; ++k) memcpy(p + b2 + b1 + k * e2, lists2[k]->data(), e2);
+  if (e1) memcpy(p + b2 + b1 + 7 * e2, W.item_end.data(), e1);
+  // table offsets within the image (factored_bind adds the device base)
+  FPlan& pl = c.plan;
+  pl.t2 = (const F2D*)0;
+  pl.t1 = (const F1D*)(b2);
+  pl.tile_end = (const uint32_t*)(b2 + b1);
+  pl.rc_end = (const uint32_t*)(b2 + b1 + e2);
+  pl.tile_nf_end = (const uint32_t*)(b2 + b1 + 2 * e2);
+  pl.item2_end = (const uint32_t*)(b2 + b1 + 3 * e2);
+  pl.rt_end = (const uint32_t*)(b2 + b1 + 4 * e2);
+  pl.tile_u_end = (const uint32_t*)(b2 + b1 + 5 * e2);
+  pl.item2u_end = (const uint32_t*)(b2 + b1 + 6 * e2);
+  pl.item_end = (const uint32_t*)(b2 + b1 + 7 * e2);
+  pl.n2 = (int32_t)W.t2.size();
+  pl.n1 = (int32_t)W.t1.size();
+  pl.n_tiles = W.tile_end.empty() ? 0 : W.tile_end.back();
+  pl.n_rc = W.rc_end.empty() ? 0 : W.rc_end.back();
+  pl.n_items = W.item_end.empty() ? 0 : W.item_end.back();
+  pl.n_tiles_nf = W.tile_nf_end.empty() ? 0 : W.tile_nf_end.back();
+  pl.n_items2 = W.item2_end.empty() ? 0 : W.item2_end.back();
+  pl.n_rt = W.rt_end.empty() ? 0 : W.rt_end.back();
+  pl.n_tiles_u = W.tile_u_end.empty() ? 0 : W.tile_u_end.back();
+  pl.n_items2u = W.item2u_end.empty() ? 0 : W.item2u_end.back();
+  FScalars& sc = c.sc;
+  const double beta2_t = hp->decay_rate != 0.0 ? 1.0 - std::pow((double)step, hp->decay_rate) : hp->beta2;
+  sc.B2 = (float)beta2_t;
+  sc.C2 = (float)(1.0 - beta2_t);
+  sc.EPS1 = (float)hp->eps1;
+  sc.CWD = (float)(hp->lr * hp->weight_decay);
+  sc.B1 = (float)hp->beta1;
+  sc.C1 = (float)(1.0 - hp->beta1);
+  sc.lr = hp->lr;
+  sc.clip = hp->clip_threshold;
+  sc.wd = hp->weight_decay != 0.0;
+  sc.fm = fm;
+  sc.sr_seed = residual ? 0 : hp->seed;
+  sc.sr_step = (uint32_t)step;
+  sc.pad = 0;
+  return PS_OK;
+}
+
+void factored_bind(FactoredCall& c, const void* dev_image) {
+  const uintptr_t base = (uintptr_t)dev_image;
+  FPlan& pl = c.plan;
+  pl.t2 = (const F2D*)(base + (uintptr_t)pl.t2);
+  pl.t1 = (const F1D*)(base + (uintptr_t)pl.t1);
+  const uint32_t** lists[8] = {&pl.tile_end, &pl.rc_end, &pl.tile_nf_end, &pl.item2_end,
+                               &pl.rt_end, &pl.tile_u_end, &pl.item2u_end, &pl.item_end};
+  for (const uint32_t** q : lists) *q = (const uint32_t*)(base + (uintptr_t)*q);
+}
+
 }  // namespace ps
 
 using namespace ps;
@@ -176,74 +251,20 @@ ps_status ps_factored_workspace_size(const ps_tensor* tensors, int32_t n_tensors
 
 ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps_factored_hparams* hp, int64_t step,
                            void* workspace, size_t workspace_bytes, ps_stream_t stream) {
-  if (ps_status s = check_fhparams(hp)) return s;
-  if (step < 1) return fail(PS_ERR_INVALID_ARG, "step must be >= 1 (got %lld)", (long long)step);
-  const bool fm = hp->beta1 != 0.0;
-  const bool residual = hp->split_mode != PS_SPLIT_STOCHASTIC;
-  Layout L;
-  if (ps_status s = plan(tensors, n_tensors, nullptr, fm, residual, L)) return s;
-  if (L.t2.empty() && L.t1.empty()) return PS_OK;
-  if (!workspace) return fail(PS_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.bytes);
+  thread_local FactoredCall c;
+  if (ps_status s = factored_prepare(tensors, n_tensors, hp, step, nullptr, c)) return s;
+  if (c.empty) return PS_OK;
+  if (!workspace) return fail(PS_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", c.ws_bytes);
   if (!is_aligned(workspace, 256)) return fail(PS_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
-  if (workspace_bytes < L.bytes)
-    return fail(PS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.bytes);
-  Layout W;
-  if (ps_status s = plan(tensors, n_tensors, (char*)workspace, fm, residual, W)) return s;
-
-  // one device blob: F2D[n2] | F1D[n1] | the seven [n2] prefix-end lists | item_end[n1]
-  const size_t b2 = W.t2.size() * sizeof(F2D), b1 = W.t1.size() * sizeof(F1D);
-  const size_t e2 = W.t2.size() * sizeof(uint32_t), e1 = W.t1.size() * sizeof(uint32_t);
-  const std::vector<uint32_t>* lists2[7] = {&W.tile_end, &W.rc_end, &W.tile_nf_end, &W.item2_end,
-                                            &W.rt_end, &W.tile_u_end, &W.item2u_end};
-  std::vector<unsigned char> blob(b2 + b1 + 7 * e2 + e1);
-  unsigned char* p = blob.data();
-  if (b2) memcpy(p, W.t2.data(), b2);
-  if (b1) memcpy(p + b2, W.t1.data(), b1);
-  if (e2)
-    for (int k = 0; k < 7; ++k) memcpy(p + b2 + b1 + k * e2, lists2[k]->data(), e2);
-  if (e1) memcpy(p + b2 + b1 + 7 * e2, W.item_end.data(), e1);
+  if (workspace_bytes < c.ws_bytes)
+    return fail(PS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, c.ws_bytes);
+  if (ps_status s = factored_prepare(tensors, n_tensors, hp, step, (char*)workspace, c)) return s;
   hipStream_t s = (hipStream_t)stream;
   const void* d = nullptr;
   TableLease lease(table_cache());   // held until the launches that read the plan are enqueued
-  if (ps_status st = device_blob(blob.data(), blob.size(), s, &d, lease)) return st;
-  const char* dc = (const char*)d;
-  FPlan pl;
-  pl.t2 = (const F2D*)dc;
-  pl.t1 = (const F1D*)(dc + b2);
-  pl.tile_end = (const uint32_t*)(dc + b2 + b1);
-  pl.rc_end = (const uint32_t*)(dc + b2 + b1 + e2);
-  pl.tile_nf_end = (const uint32_t*)(dc + b2 + b1 + 2 * e2);
-  pl.item2_end = (const uint32_t*)(dc + b2 + b1 + 3 * e2);
-  pl.rt_end = (const uint32_t*)(dc + b2 + b1 + 4 * e2);
-  pl.tile_u_end = (const uint32_t*)(dc + b2 + b1 + 5 * e2);
-  pl.item2u_end = (const uint32_t*)(dc + b2 + b1 + 6 * e2);
-  pl.item_end = (const uint32_t*)(dc + b2 + b1 + 7 * e2);
-  pl.n2 = (int32_t)W.t2.size();
-  pl.n1 = (int32_t)W.t1.size();
-  pl.n_tiles = W.tile_end.empty() ? 0 : W.tile_end.back();
-  pl.n_rc = W.rc_end.empty() ? 0 : W.rc_end.back();
-  pl.n_items = W.item_end.empty() ? 0 : W.item_end.back();
-  pl.n_tiles_nf = W.tile_nf_end.empty() ? 0 : W.tile_nf_end.back();
-  pl.n_items2 = W.item2_end.empty() ? 0 : W.item2_end.back();
-  pl.n_rt = W.rt_end.empty() ? 0 : W.rt_end.back();
-  pl.n_tiles_u = W.tile_u_end.empty() ? 0 : W.tile_u_end.back();
-  pl.n_items2u = W.item2u_end.empty() ? 0 : W.item2u_end.back();
-  FScalars sc;
-  const double beta2_t = hp->decay_rate != 0.0 ? 1.0 - std::pow((double)step, hp->decay_rate) : hp->beta2;
-  sc.B2 = (float)beta2_t;
-  sc.C2 = (float)(1.0 - beta2_t);
-  sc.EPS1 = (float)hp->eps1;
-  sc.CWD = (float)(hp->lr * hp->weight_decay);
-  sc.B1 = (float)hp->beta1;
-  sc.C1 = (float)(1.0 - hp->beta1);
-  sc.lr = hp->lr;
-  sc.clip = hp->clip_threshold;
-  sc.wd = hp->weight_decay != 0.0;
-  sc.fm = fm;
-  sc.sr_seed = residual ? 0 : hp->seed;
-  sc.sr_step = (uint32_t)step;
-  sc.pad = 0;
-  return launch_factored(pl, sc, hp->split_mode, s);
+  if (ps_status st = device_blob(c.image.data(), c.image.size(), s, &d, lease)) return st;
+  factored_bind(c, d);
+  return launch_factored(c.plan, c.sc, hp->split_mode, s);
 }
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/ps.h"
 #include "blob_cache.h"
 
@@ -159,6 +161,23 @@ struct FPlan {      // device tables of one factored call
 };
 
 ps_status launch_factored(const FPlan& plan, const FScalars& sc, int split_mode, hipStream_t s);
+
+// One factored call prepared on the host (ps_factored.cpp): the device plan's
+// image (F2D[n2] | F1D[n1] | seven [n2] prefix-end lists | item_end[n1]) with
+// its workspace pointers final, the workspace size and the scalars. The
+// plan's table pointers are offsets into the image until factored_bind.
+struct FactoredCall {
+  std::vector<unsigned char> image;
+  size_t ws_bytes = 0;
+  FPlan plan{};
+  FScalars sc{};
+  bool empty = true;   // no tensor to step
+};
+// Validates the call and lays out the workspace at `ws` (NULL: sizes only).
+ps_status factored_prepare(const ps_tensor* t, int32_t n, const ps_factored_hparams* hp, int64_t step, char* ws,
+                           FactoredCall& c);
+// Points the plan's tables into a device copy of the image.
+void factored_bind(FactoredCall& c, const void* dev_image);
 
 // ---- errors (ps_abi.cpp) ----
 ps_status fail(ps_status s, const char* fmt, ...);

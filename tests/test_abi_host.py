@@ -176,3 +176,20 @@ def test_build_scripts_load_without_the_built_library():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_noalloc_factored_step_rejects_on_host(ps):
+    """The allocation-free factored step validates and sizes the call before
+    any HIP call: a list whose workspace exceeds the built-in scratch, bad
+    hyperparameters and bad shapes are rejected here, with no GPU."""
+    L = ps.lib()
+    big = (ps.CTensor * 1)(ps.CTensor(256, 256, 256, 256, 256, 256, 256, 256, 256, 262144 * 4096, 262144, 4096, 0, 0))
+    h = ps.FactoredHParams().c()
+    assert L.ps_factored_step_noalloc(big, 1, ctypes.byref(h), 1, None) == 7      # PS_ERR_WORKSPACE
+    assert "scratch" in ps.last_error()
+    bad = ps.FactoredHParams(clip_threshold=0.0).c()
+    assert L.ps_factored_step_noalloc(big, 1, ctypes.byref(bad), 1, None) == 1    # PS_ERR_INVALID_ARG
+    assert L.ps_factored_step_noalloc(big, 1, ctypes.byref(h), 0, None) == 1
+    shape = (ps.CTensor * 1)(ps.CTensor(256, 256, 256, 256, 256, 256, 256, 256, 256, 100, 7, 13, 0, 0))
+    assert L.ps_factored_step_noalloc(shape, 1, ctypes.byref(h), 1, None) == 3    # PS_ERR_SHAPE
+    assert L.ps_factored_step_noalloc(shape, 0, ctypes.byref(h), 1, None) == 0    # empty list: no-op
