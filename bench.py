@@ -16,6 +16,11 @@ Reported:
              its stream around each launch; algorithmic bytes per launch =
              18 B/param (read hi, lo, grad, m, v; write hi, lo, m, v) + 16 B
              per 256-block (two scales read and written), against 8 TB/s
+  roofline.practical_peak  a streaming kernel with the step's exact access
+             pattern and no arithmetic (tests/kernels/stream_ceiling.hip) over
+             the same state, timed the same way right after the step: the
+             rate this memory system gives that 5-read/4-write 16-byte mix;
+             frac_of_practical is the step's share of it
   cpu_baseline  the C oracle, single-threaded, on a bounded sample of the
              same workload (the leading tensors of the set, one step)
 """
@@ -65,46 +70,82 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-VALU_ISSUE_PEAK = 256 * 4 * 2.4e9 / 4   # wave64 VALU instructions/s: 256 CUs x 4 SIMDs, 4 cycles each, 2.4 GHz
-
-
-def read_valu(workload):
-    """VALU wave-instructions and transcendental instructions per launch of the
-    step kernel from the committed counter summary, if it was taken on the
-    current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"adam_step_{workload}_valu.txt")
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
-        return None
+def gpu_pci_bus_id():
+    """PCI bus id (domain:bus:device.function) of the current HIP device, from
+    the HIP runtime already loaded in this process, or None."""
+    import ctypes
     try:
-        return float(kv["valu_insts_per_launch"]), float(kv["valu_trans_insts_per_launch"])
-    except (KeyError, ValueError):
+        hip = ctypes.CDLL("libamdhip64.so")
+        dev = ctypes.c_int(0)
+        buf = ctypes.create_string_buffer(64)
+        if hip.hipGetDevice(ctypes.byref(dev)) != 0 or hip.hipDeviceGetPCIBusId(buf, 64, dev) != 0:
+            return None
+        return buf.value.decode().lower()
+    except (OSError, AttributeError):
         return None
 
 
 def gpu_clocks():
-    """Current shader and memory clock levels from the amdgpu sysfs files
-    (pp_dpm_sclk / pp_dpm_mclk, the active level marked '*'), or None. Read
-    from files: no helper program is started from this GPU process."""
-    import glob
-    out = {}
+    """Current shader and memory clock levels of the GPU this process runs on:
+    the amdgpu sysfs files (pp_dpm_sclk / pp_dpm_mclk, active level marked
+    '*') of the PCI device whose bus id HIP reports for the current device.
+    Read from files: no helper program is started from this GPU process."""
+    bdf = gpu_pci_bus_id()
+    if bdf is None:
+        return None
+    out = {"pci_bus_id": bdf}
     for kind in ("sclk", "mclk"):
-        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}")):
-            try:
-                with open(path) as f:
-                    cur = [ln.split(":", 1)[1].replace("*", "").strip() for ln in f if ln.rstrip().endswith("*")]
-            except OSError:
-                continue
-            if cur:
-                out[kind] = cur[0]
-                break
-    return out or None
+        path = f"/sys/bus/pci/devices/{bdf}/pp_dpm_{kind}"
+        try:
+            with open(path) as f:
+                cur = [ln.split(":", 1)[1].replace("*", "").strip() for ln in f if ln.rstrip().endswith("*")]
+        except OSError:
+            continue
+        if cur:
+            out[kind] = cur[0]
+    return out
+
+
+def stream_ceiling(slab, steps, stream):
+    """Practical HBM ceiling of the step's access pattern on this GPU: the
+    no-arithmetic streaming kernels of tests/kernels/stream_ceiling.hip over the
+    same slab arrays as the step, timed with HIP events on the same stream.
+    mode 0 is the step's mix (five 16-byte reads and four 16-byte writes per
+    lane, block scales read and written: 18 B per element + 16 B per block);
+    mode 1 the reads alone (10 B per element + 8 B per block). Overwrites the
+    state, so it runs after the step's timing."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "tests", "kernels", "libps_probe.so")
+    if slab is None or not os.path.exists(path):
+        log(f"[bench] no ceiling measurement ({'no slab' if slab is None else path + ' is not built'})")
+        return None
+    L = ctypes.CDLL(path)
+    L.probe_stream_ceiling.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 8 + [ctypes.c_uint32, ctypes.c_void_p]
+    L.probe_stream_ceiling.restype = ctypes.c_int
+    sl, sc = slab.slab, slab.scales
+    n_items = min(sl["hi"].numel() // 512, sc["ms"].numel() // 2, sc["vs"].numel() // 2)
+    sink = torch.zeros(4, dtype=torch.int32, device=sl["hi"].device)
+    ptrs = [sl[k].data_ptr() for k in ("hi", "lo", "g", "mc", "vc")] + [sc["ms"].data_ptr(), sc["vs"].data_ptr(),
+                                                                      sink.data_ptr()]
+    hs = ctypes.c_void_p(stream.cuda_stream)
+    res = {"elements": n_items * 512}
+    for mode, name, per_item in ((0, "step_mix", 512 * 18 + 32), (1, "reads_only", 512 * 10 + 16)):
+        for _ in range(5):
+            if L.probe_stream_ceiling(mode, *ptrs, n_items, hs) != 0:
+                raise RuntimeError("stream ceiling kernel launch failed")
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            L.probe_stream_ceiling(mode, *ptrs, n_items, hs)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+        res[name] = {"ms": ms, "gbs": n_items * per_item / (ms * 1e-3) / 1e9}
+        log(f"[bench] ceiling {name}: {ms:.3f} ms per launch, {res[name]['gbs']:.0f} GB/s")
+    return res
 
 
 def read_traffic(workload, moments="codec", split="trunc"):
@@ -133,8 +174,9 @@ def build_state(shapes, seed, dev, layout="slab", moments="codec"):
     """Optimizer state for every tensor of the set, filled on the device.
 
     layout "slab": one contiguous allocation per state stream
-    (precision_state_amd.StateSlab); "separate": one allocation per tensor and
-    stream. moments "f24" (slab only): f24 moment arrays instead of codes."""
+    (precision_state_amd.StateSlab, also returned); "separate": one allocation
+    per tensor and stream (slab None). moments "f24" (slab only): f24 moment
+    arrays instead of codes."""
     import torch
 
     import precision_state_amd as ps
@@ -144,6 +186,7 @@ def build_state(shapes, seed, dev, layout="slab", moments="codec"):
                             moments=moments)
         states, grads = slab.states, slab.grads
     else:
+        slab = None
         if moments != "codec":
             raise ValueError("f24 moments need the slab layout")
         states, grads = [], []
@@ -159,7 +202,7 @@ def build_state(shapes, seed, dev, layout="slab", moments="codec"):
         synth.dev_bf16_normal(st.w_hi, seed, synth.STREAM_HI, tid, 0, synth.SIGMA_W)
         synth.dev_u16_uniform(st.w_lo, seed, synth.STREAM_LO, tid, 0)
         synth.dev_bf16_normal(g, seed, synth.STREAM_GRAD, tid, 1, synth.SIGMA_G)
-    return states, grads
+    return states, grads, slab
 
 
 def apply_policy(shapes, states, grads, dev):
@@ -253,6 +296,29 @@ def cpu_baseline(shapes, seed, target_params=60_000_000, weight_decay=0.0):
                       f"single thread {total / dt1:.3e} params/s ({dt1:.1f} s)"}
 
 
+def calibrate_copy(gib, stream, dev):
+    """Three plain device copies of `gib` GiB (the counter calibration of the
+    profiles: a copy's FETCH_SIZE and WRITE_SIZE against the bytes it moves);
+    returns the best copy rate in GB/s (read + write), or None when gib is 0."""
+    if gib <= 0:
+        return None
+    import torch
+    nbytes = int(gib * 2**30) // 16 * 16
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    times = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    copy_gbs = 2 * nbytes / (min(times) * 1e-3) / 1e9
+    log(f"[bench] plain copy of {nbytes} bytes: best {min(times):.3f} ms = {copy_gbs:.0f} GB/s (read + write)")
+    return copy_gbs
+
+
 def bench_factored(args):
     """Adafactor-style step (beta1 = 0, factored v, clip 1.0, beta2 0.999,
     eps1 1e-30, lr 3.5e-6) on the FLUX double-block shapes: 2-D tensors
@@ -312,6 +378,7 @@ def bench_factored(args):
     per_tensor = None
     if args.per_tensor_calls:
         per_tensor = time_factored_per_tensor(ps, states, grads, hp, ws, stream, step, args.steps)
+    copy_gbs = calibrate_copy(args.calibrate_copy, stream, dev)
     n_blocks = sum((s.numel + 255) // 256 for s in shapes)
     alg = (10 if split != ps.SPLIT_STOCHASTIC else 6) * n_params + ((4 * n_params + 8 * n_blocks) if args.beta1 else 0)
     gbs10 = alg / (step_ms * 1e-3) / 1e9
@@ -323,7 +390,8 @@ def bench_factored(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl + "_factored", "params": n_params, "tensors": len(shapes), "step_ms": step_ms,
                    "beta1": args.beta1, "decay_rate": args.decay_rate, "split": args.split, "algorithmic_bytes": alg,
-                   "gbs_algorithmic": gbs10, "gbs_with_gradient_rereads": gbs14, "per_tensor_calls": per_tensor},
+                   "gbs_algorithmic": gbs10, "gbs_with_gradient_rereads": gbs14, "per_tensor_calls": per_tensor,
+                   "copy_gbs": copy_gbs},
         "roofline": {"bound": "hbm", "achieved": gbs10, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs10 / PEAK_HBM_GBS, "traffic": None},
         "cpu_baseline": None}), flush=True)
@@ -370,7 +438,7 @@ def bench_per_tensor(args):
     dev = "cuda:0"
     shapes = synth.WORKLOADS[args.workload]()
     n_params = synth.total_params(shapes)
-    states, grads = build_state(shapes, args.seed, dev, "slab")
+    states, grads, _ = build_state(shapes, args.seed, dev, "slab")
     n_small = n_final = 0
     if args.policy:   # flagged tensors go through the device table cache, one table per tensor
         n_small, n_final = apply_policy(shapes, states, grads, dev)
@@ -414,7 +482,7 @@ def bench_per_tensor(args):
     # back-to-back calls on single small tensors
     lat = {}
     for n in (4096, 65536, 3072 * 3072):
-        st, g = build_state([synth.Shape("t", 0, 0, n)], args.seed, dev, "slab")
+        st, g, _ = build_state([synth.Shape("t", 0, 0, n)], args.seed, dev, "slab")
         r = ps.make_records(st, g)
         calls = 400
         for k in range(20):
@@ -660,6 +728,8 @@ def main():
     ap.add_argument("--decay-rate", type=float, default=0.0,
                     help="factored mode: beta2 of update t is 1 - t^decay_rate (0 = constant 0.999)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="nadam mode: skip the streaming-ceiling kernels timed after the step")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="after the timed steps, run 3 plain device copies of GIB GiB (counter calibration "
                          "and the practical copy bandwidth)")
@@ -691,7 +761,7 @@ def main():
     n_params = synth.total_params(shapes)
     log(f"[bench] {args.workload}: {len(shapes)} tensors, {n_params} params; generating state on {dev}")
     t0 = time.perf_counter()
-    states, grads = build_state(shapes, args.seed, dev, args.layout, args.moments)
+    states, grads, slab = build_state(shapes, args.seed, dev, args.layout, args.moments)
     torch.cuda.synchronize()
     log(f"[bench] state ready in {time.perf_counter() - t0:.1f} s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
@@ -734,35 +804,15 @@ def main():
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, {kernel_ms:.3f} ms/launch (events); "
         f"per launch min {min(per_step):.3f} max {max(per_step):.3f}")
 
-    copy_gbs = None
-    if args.calibrate_copy > 0:
-        nbytes = int(args.calibrate_copy * 2**30) // 16 * 16
-        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        times = []
-        for _ in range(3):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            dst.copy_(src)
-            b.record(stream)
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b))
-        copy_gbs = 2 * nbytes / (min(times) * 1e-3) / 1e9
-        log(f"[bench] plain copy of {nbytes} bytes: best {min(times):.3f} ms = {copy_gbs:.0f} GB/s (read + write)")
-        del src, dst
+    copy_gbs = calibrate_copy(args.calibrate_copy, stream, dev)
 
     alg_bytes = sum(step_bytes(s.numel, st.flags, split != ps.SPLIT_STOCHASTIC) for s, st in zip(shapes, states))
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
     traffic = None if args.policy else read_traffic(args.workload, args.moments, args.split)
-    valu = None
-    if not args.policy and args.moments == "codec" and args.split == "trunc":
-        vi = read_valu(args.workload)
-        if vi is not None:
-            slots = vi[0] + 3 * vi[1]     # transcendental VALU instructions issue at a quarter of the rate
-            valu = {"wave_instructions_per_launch": vi[0], "transcendental_per_launch": vi[1],
-                    "issue_slots_per_launch": slots, "peak_issue_slots_per_s": VALU_ISSUE_PEAK,
-                    "frac": slots / (kernel_ms * 1e-3) / VALU_ISSUE_PEAK}
     clocks = gpu_clocks()
+    ceiling = None
+    if not args.no_ceiling and not args.policy and args.moments == "codec" and args.split != "stochastic":
+        ceiling = stream_ceiling(slab, max(5, min(args.steps, 20)), stream)
 
     baseline = None
     if not args.no_cpu_baseline:
@@ -796,9 +846,11 @@ def main():
                    "kernel_ms": kernel_ms, "copy_gbs": copy_gbs, "kernel_source_sha256": kernel_source_hash(),
                    "gbs_18B_per_param": 18 * n_params / (kernel_ms * 1e-3) / 1e9,
                    "bytes_per_param_algorithmic": alg_bytes / n_params,
-                   "valu_issue": valu, "gpu_clocks_after_timing": clocks},
+                   "gpu_clocks_after_timing": clocks, "stream_ceiling": ceiling},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "practical_peak": ceiling["step_mix"]["gbs"] if ceiling else None,
+                     "frac_of_practical": achieved / ceiling["step_mix"]["gbs"] if ceiling else None},
         "cpu_baseline": baseline,
     }
     print(json.dumps(out), flush=True)
