@@ -27,6 +27,14 @@ constexpr int kT = 256;
 // on the double-block shapes when both ran over 1024-element items (runs of
 // 128 to 1024 items measured alike).
 constexpr uint32_t kFlatXcdChunk = 256;
+// The flat apply pass takes the fused step's lane layout and work order: one
+// 512-element item per 64-lane workgroup, lane t owning elements 8t .. 8t+7
+// (a 256-element block per 32 lanes, so each load or store instruction of a
+// wave covers 1 KiB of one stream), each XCD taking runs of 2048 items. A
+// streaming kernel with this pass's 3-read/2-write mix and no arithmetic ran
+// 6% faster in this layout than with two 8-element runs per lane at offsets
+// la and la + 128 over 1024-element items.
+constexpr uint32_t kApplyXcdChunk = 2048;
 
 // The apply pass touches the weights, residuals and first-moment codes once
 // per step: those accesses carry the non-temporal hint (measured ~9% faster
@@ -286,45 +294,10 @@ __global__ __launch_bounds__(kT) void k_f_usq(FPlan P) {
 }
 
 // ---- flat items of 2-D tensors --------------------------------------------------
-// Same mapping as the fused (N)AdamW step: one 1024-element item per 64-lane
-// workgroup, each lane two runs of 8 consecutive elements. With C % 8 == 0 a
-// run never crosses a row, and its row and column come from one division per
-// workgroup and a wrap test (C >= 1024) or a division per run; other column
-// counts (only with a first moment) take per-element factors.
-
-__device__ __forceinline__ void run_rc(uint32_t e, uint32_t off, uint32_t i0, uint32_t j0, uint32_t C, uint32_t& i,
-                                       uint32_t& j) {
-  if (C >= 1024u) {
-    j = j0 + off;
-    i = i0;
-    if (j >= C) {
-      j -= C;
-      ++i;
-    }
-  } else {
-    i = e / C;
-    j = e - i * C;
-  }
-}
-
-struct FlatRun {
-  uint32_t e, i, j;
-  bool ok;
-};
-
-__device__ __forceinline__ void flat_runs(const F2D& X, uint32_t item, FlatRun* run) {
-  const uint32_t n = (uint32_t)X.R * (uint32_t)X.C;
-  const uint32_t C = (uint32_t)X.C;
-  const uint32_t elem0 = item * (uint32_t)kItemElems;
-  const uint32_t i0 = elem0 / C, j0 = elem0 - i0 * C;
-  const uint32_t la = (threadIdx.x >> 4) * (uint32_t)kBlock + (threadIdx.x & 15) * 8u;
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t off = la + 128u * h;
-    run[h].e = elem0 + off;
-    run[h].ok = run[h].e < n;
-    run_rc(run[h].e, off, i0, j0, C, run[h].i, run[h].j);
-  }
-}
+// The U^2 pass of tensors whose rows are not 16-byte runs takes 1024-element
+// items (each lane two runs of 8); the apply pass takes the fused step's
+// 512-element items (k_f_apply_flat). Column counts that are not a multiple
+// of 8 (only with a first moment) take per-element factors.
 
 __device__ __forceinline__ void load_kap8(const float* __restrict__ kap, uint32_t j, float* k) {
   const float4 a = *reinterpret_cast<const float4*>(kap + j);
@@ -460,22 +433,20 @@ __global__ __launch_bounds__(64) void k_f_usq_flat(FPlan P, FScalars S) {
   usq_item_any(X, w2 - begin);
 }
 
-// Apply of one item, any column count: the arithmetic of the run path below,
-// with each element's own row and column factors.
+// Apply of one 512-element item, any column count: the arithmetic of the run
+// path below, with each element's own row and column factors.
 template <int SPLIT>
 __device__ __forceinline__ void apply_item_any(const F2D& X, uint32_t item, const FScalars& S, float f) {
   constexpr bool SR = SPLIT == PS_SPLIT_STOCHASTIC;
   const uint32_t n = (uint32_t)X.R * (uint32_t)X.C;
-  const uint32_t la = (threadIdx.x >> 4) * (uint32_t)kBlock + (threadIdx.x & 15) * 8u;
-  const uint32_t blk = item * (uint32_t)kItemBlocks + (threadIdx.x >> 4);
+  const uint32_t e = item * (uint32_t)kApplyItemElems + threadIdx.x * 8u;
+  const uint32_t blk = item * 2u + (threadIdx.x >> 5);
   const bool blk_ok = blk * (uint32_t)kBlock < n;
   const float ms_old = (S.fm && blk_ok) ? X.ms[blk] : 0.0f;
-  float m[16];
+  float m[8];
   float mx = 0.0f;
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t e = item * (uint32_t)kItemElems + la + 128u * h;
-    for (int j = 0; j < 8; ++j) m[8 * h + j] = 0.0f;
-    if (e >= n) continue;
+  for (int j = 0; j < 8; ++j) m[j] = 0.0f;
+  if (e < n) {
     const uint4 gv = ld_run(X.g, e, n, 0u, true), hv = ld_run(X.hi, e, n, 0u, true);
     const uint4 lv = SR ? make_uint4(0u, 0u, 0u, 0u) : ld_run(X.lo, e, n, 0u, true);
     const uint4 mv = S.fm ? ld_run(X.mc, e, n, 0x80008000u, true) : make_uint4(0u, 0u, 0u, 0u);
@@ -499,7 +470,7 @@ __device__ __forceinline__ void apply_item_any(const F2D& X, uint32_t item, cons
           if (S.fm) {
             const float m0 = dec_signed(o ? code_hi_f(mw[p]) : code_lo_f(mw[p]), ms_old);
             x = __builtin_fmaf(S.B1, m0, S.C1 * x);
-            m[8 * h + jj] = x;
+            m[jj] = x;
             mx = __builtin_fmaxf(mx, __builtin_fabsf(x));
           }
           if (S.wd) x = __builtin_fmaf(S.CWD, w, x);
@@ -518,26 +489,26 @@ __device__ __forceinline__ void apply_item_any(const F2D& X, uint32_t item, cons
   }
   if (!S.fm) return;   // uniform
   float sm, inv;
-  block_scale(row16_max(mx), sm, inv);
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t e = item * (uint32_t)kItemElems + la + 128u * h;
-    if (e >= n) continue;
+  block_scale(row32_max(mx), sm, inv);
+  if (e < n) {
     uint32_t om[4];
-    for (int p = 0; p < 4; ++p)
-      om[p] = enc_signed(m[8 * h + 2 * p], inv) | (enc_signed(m[8 * h + 2 * p + 1], inv) << 16);
+    for (int p = 0; p < 4; ++p) om[p] = enc_signed(m[2 * p], inv) | (enc_signed(m[2 * p + 1], inv) << 16);
     st_run(X.mc, e, n, om);
   }
-  if ((threadIdx.x & 15) == 0 && blk_ok) X.ms[blk] = sm;
+  if ((threadIdx.x & 31) == 0 && blk_ok) X.ms[blk] = sm;
 }
 
 // Flat apply over the 2-D items. (The 1-D apply items stay in a launch of
 // their own: riding at the end of this one, they made this kernel's code
-// 25% slower.)
+// 25% slower.) Lane t's run is elements 8t .. 8t+7 of the item; with
+// C % 8 == 0 it never crosses a row, and with C >= 512 the item spans at most
+// two rows, so the run's row and column come from one division per workgroup
+// and a wrap test.
 template <int SPLIT>
 __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
   constexpr bool SR = SPLIT == PS_SPLIT_STOCHASTIC;
   uint32_t begin;
-  const uint32_t wg = xcd_item<kFlatXcdChunk>(blockIdx.x, gridDim.x);
+  const uint32_t wg = xcd_item<kApplyXcdChunk>(blockIdx.x, gridDim.x);
   const F2D& X = P.t2[find_end(P.item2_end, P.n2, wg, begin)];
   const uint32_t item = wg - begin;
   const float f = *X.f;
@@ -545,75 +516,81 @@ __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
     apply_item_any<SPLIT>(X, item, S, f);
     return;
   }
-  FlatRun run[2];
-  flat_runs(X, item, run);
-  // first moment: the item's 4 blocks are the 4 DPP rows (16 lanes x 2 runs)
   const uint32_t n = (uint32_t)X.R * (uint32_t)X.C;
-  const uint32_t blk = item * (uint32_t)kItemBlocks + (threadIdx.x >> 4);
+  const uint32_t C = (uint32_t)X.C;
+  const uint32_t elem0 = item * (uint32_t)kApplyItemElems, off = threadIdx.x * 8u;
+  const uint32_t e = elem0 + off;
+  const bool ok = e < n;
+  uint32_t i, j;
+  if (C >= (uint32_t)kApplyItemElems) {
+    i = elem0 / C;
+    j = elem0 - i * C + off;
+    if (j >= C) {
+      j -= C;
+      ++i;
+    }
+  } else {
+    i = e / C;
+    j = e - i * C;
+  }
+  // first moment: the item's 2 blocks are the 2 DPP row pairs (32 lanes each)
+  const uint32_t blk = item * 2u + (threadIdx.x >> 5);
   const bool blk_ok = blk * (uint32_t)kBlock < n;
   const float ms_old = (S.fm && blk_ok) ? X.ms[blk] : 0.0f;
-  uint4 gv[2], hv[2], lv[2], mv[2] = {};
-  float kap[2][8], rho[2];
-  for (int h = 0; h < 2; ++h) {
-    if (!run[h].ok) continue;
-    gv[h] = ld_stream(X.g + run[h].e);
-    hv[h] = ld_stream(X.hi + run[h].e);
-    lv[h] = SR ? make_uint4(0u, 0u, 0u, 0u) : ld_stream(X.lo + run[h].e);
-    if (S.fm) mv[h] = ld_stream(X.mc + run[h].e);
-    load_kap8(X.kap, run[h].j, kap[h]);
-    rho[h] = X.rho[run[h].i];
-  }
-  float m[16];
+  float m[8];
   float mx = 0.0f;
-  for (int h = 0; h < 2; ++h) {
-    for (int j = 0; j < 8; ++j) m[8 * h + j] = 0.0f;
-    if (!run[h].ok) continue;
-    const uint32_t gw[4] = {gv[h].x, gv[h].y, gv[h].z, gv[h].w};
-    const uint32_t hw[4] = {hv[h].x, hv[h].y, hv[h].z, hv[h].w};
-    const uint32_t lw[4] = {lv[h].x, lv[h].y, lv[h].z, lv[h].w};
-    const uint32_t mw[4] = {mv[h].x, mv[h].y, mv[h].z, mv[h].w};
+  for (int jj = 0; jj < 8; ++jj) m[jj] = 0.0f;
+  if (ok) {
+    const uint4 gv = ld_stream(X.g + e), hv = ld_stream(X.hi + e);
+    const uint4 lv = SR ? make_uint4(0u, 0u, 0u, 0u) : ld_stream(X.lo + e);
+    const uint4 mv = S.fm ? ld_stream(X.mc + e) : make_uint4(0u, 0u, 0u, 0u);
+    float kap[8];
+    load_kap8(X.kap, j, kap);
+    const float rho = X.rho[i];
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+    const uint32_t lw[4] = {lv.x, lv.y, lv.z, lv.w};
+    const uint32_t mw[4] = {mv.x, mv.y, mv.z, mv.w};
     uint32_t oh[4], ol[4];
     uint64_t rnd[2] = {0u, 0u};
+    if (SR) sr_bits8(sr_stream(S.sr_seed, S.sr_step, X.tid), e, rnd);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       uint32_t wb[2];
 #pragma unroll
       for (int o = 0; o < 2; ++o) {
         const int jj = 2 * p + o;
-        const float U = (bf16_at(gw, jj) * rho[h]) * kap[h][jj];
+        const float U = (bf16_at(gw, jj) * rho) * kap[jj];
         const float w = SR ? bf16_at(hw, jj) : __uint_as_float(join_pair_elem<SPLIT>(hw[p], lw[p], o));
         float x = U * f;
         if (S.fm) {
           const float m0 = dec_signed(o ? code_hi_f(mw[p]) : code_lo_f(mw[p]), ms_old);
           x = __builtin_fmaf(S.B1, m0, S.C1 * x);
-          m[8 * h + jj] = x;
+          m[jj] = x;
           mx = __builtin_fmaxf(mx, __builtin_fabsf(x));
         }
         if (S.wd) x = __builtin_fmaf(S.CWD, w, x);
         wb[o] = __float_as_uint(w - x);
       }
       if (SR) {
-        if (p == 0) sr_bits8(sr_stream(S.sr_seed, S.sr_step, X.tid), run[h].e, rnd);
         const uint64_t q = rnd[p >> 1] >> (32 * (p & 1));
         oh[p] = sr_pair(wb[0], wb[1], (uint32_t)q & 0xFFFFu, (uint32_t)(q >> 16) & 0xFFFFu);
       } else {
         split_pair<SPLIT>(wb[0], wb[1], oh[p], ol[p]);
       }
     }
-    st_stream(X.hi + run[h].e, make_uint4(oh[0], oh[1], oh[2], oh[3]));
-    if (!SR) st_stream(X.lo + run[h].e, make_uint4(ol[0], ol[1], ol[2], ol[3]));
+    st_stream(X.hi + e, make_uint4(oh[0], oh[1], oh[2], oh[3]));
+    if (!SR) st_stream(X.lo + e, make_uint4(ol[0], ol[1], ol[2], ol[3]));
   }
   if (!S.fm) return;   // uniform
   float sm, inv;
-  block_scale(row16_max(mx), sm, inv);
-  for (int h = 0; h < 2; ++h) {
-    if (!run[h].ok) continue;
+  block_scale(row32_max(mx), sm, inv);
+  if (ok) {
     uint32_t om[4];
-    for (int p = 0; p < 4; ++p)
-      om[p] = enc_signed(m[8 * h + 2 * p], inv) | (enc_signed(m[8 * h + 2 * p + 1], inv) << 16);
-    st_stream(X.mc + run[h].e, make_uint4(om[0], om[1], om[2], om[3]));
+    for (int p = 0; p < 4; ++p) om[p] = enc_signed(m[2 * p], inv) | (enc_signed(m[2 * p + 1], inv) << 16);
+    st_stream(X.mc + e, make_uint4(om[0], om[1], om[2], om[3]));
   }
-  if ((threadIdx.x & 15) == 0 && blk_ok) X.ms[blk] = sm;
+  if ((threadIdx.x & 31) == 0 && blk_ok) X.ms[blk] = sm;
 }
 
 // 1-D tensors, one 1024-element item per 64-lane workgroup (item w of the

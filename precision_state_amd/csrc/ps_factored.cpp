@@ -114,7 +114,7 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, 
       tiles += (uint64_t)d.sntr * d.ntc;
       rc += (uint64_t)d.nrw + d.ncw;
       if (d.flat)
-        items2 += (uint64_t)d.nitems;
+        items2 += (uint64_t)((x.numel + kApplyItemElems - 1) / kApplyItemElems);
       else
         tiles_nf += (uint64_t)d.ntr * d.ntc;
       if (d.vec)

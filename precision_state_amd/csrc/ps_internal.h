@@ -18,6 +18,7 @@ constexpr int kItemElems = kBlock * kItemBlocks;
 constexpr int kStepItemBlocks = 2; // blocks per (N)AdamW step work item: one wave, 32 lanes per block
 constexpr int kStepItemElems = kBlock * kStepItemBlocks;
 constexpr int kInlineMax = 16;     // tensor lists up to this size travel in kernel arguments
+constexpr int kApplyItemElems = 512; // factored apply pass: elements per 64-lane work item (the step's layout)
 
 // Device record of one tensor in a multi-tensor launch (64 bytes).
 struct DevTensor {
