@@ -521,29 +521,54 @@ def bench_per_tensor(args):
 
 
 def pcie_ceiling(dev, nbytes=2 << 30):
-    """Pinned host <-> device copy rates: each direction alone and both at once
-    on two streams (hipMemcpyAsync of 2 GiB)."""
+    """Pinned host <-> device copy rates: both directions at once, then each
+    alone (hipMemcpyAsync of 2 GiB, best of a few). Each direction runs on a
+    stream created with a CU mask, which gets a hardware queue of its own: on
+    a shared queue (HIP's pool of GPU_MAX_HW_QUEUES, 4 by default) the two
+    copies would run one after the other, as the offload pipeline's did before
+    its copy streams got queues of their own."""
+    import ctypes
+
     import torch
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32, ctypes.c_void_p]
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    hip.hipStreamSynchronize.argtypes = [ctypes.c_void_p]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(torch.device(dev)).multi_processor_count
+    words = (cus + 31) // 32
+    mask = (ctypes.c_uint32 * words)(*([0xFFFFFFFF] * words))
+    streams = []
+    for _ in range(2):
+        s = ctypes.c_void_p()
+        if hip.hipExtStreamCreateWithCUMask(ctypes.byref(s), words, mask) != 0:
+            raise RuntimeError("hipExtStreamCreateWithCUMask failed")
+        streams.append(s)
     h = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
     d = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
-    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    H2D, D2H = 1, 2
 
-    def timed(fn):
-        torch.cuda.synchronize()
+    def copy(k, kind):
+        dst, src = (d[k], h[k]) if kind == H2D else (h[k], d[k])
+        if hip.hipMemcpyAsync(dst.data_ptr(), src.data_ptr(), nbytes, kind, streams[k]) != 0:
+            raise RuntimeError("hipMemcpyAsync failed")
+
+    def timed(ops):
         t0 = time.perf_counter()
-        fn()
-        torch.cuda.synchronize()
+        for k, kind in ops:
+            copy(k, kind)
+        for k, _ in ops:
+            hip.hipStreamSynchronize(streams[k])
         return time.perf_counter() - t0
-    for _ in range(2):
-        t_h2d = timed(lambda: d[0].copy_(h[0], non_blocking=True))
-        t_d2h = timed(lambda: h[1].copy_(d[1], non_blocking=True))
-
-    def both():
-        with torch.cuda.stream(s1):
-            d[0].copy_(h[0], non_blocking=True)
-        with torch.cuda.stream(s2):
-            h[1].copy_(d[1], non_blocking=True)
-    t_dup = timed(both)
+    # both directions at once first: once each stream had copied alone, its
+    # later copies in the two directions ran one after the other (28.7 + 28.7
+    # GB/s against 48.7 + 48.7 timed first, same box)
+    t_dup = min(timed([(0, H2D), (1, D2H)]) for _ in range(3))
+    t_h2d = min(timed([(0, H2D)]) for _ in range(2))
+    t_d2h = min(timed([(1, D2H)]) for _ in range(2))
+    for s in streams:
+        hip.hipStreamDestroy(s)
     return {"h2d": nbytes / t_h2d / 1e9, "d2h": nbytes / t_d2h / 1e9, "dup_h2d": nbytes / t_dup / 1e9,
             "dup_d2h": nbytes / t_dup / 1e9}
 
@@ -551,8 +576,8 @@ def pcie_ceiling(dev, nbytes=2 << 30):
 def bench_offload(args, n_blocks=57):
     """Host offload: the FLUX double-block tensor set repeated 57 times; each
     block's bf16 weights and gradients in HBM, its residuals, codes and scales
-    in pinned host memory, moved over PCIe every step by the double-buffered
-    pipeline of ps_offload_run. To bound pinned memory, the 57 blocks cycle
+    in pinned host memory, moved over PCIe every step by ps_offload_run (the
+    step kernel on the host arrays in place, or the staged pipeline). To bound pinned memory, the 57 blocks cycle
     over --host-blocks distinct host state sets (block k uses set k mod H);
     the pipeline's ordering makes this race-free and the bytes moved are the
     same as with 57 distinct sets."""
@@ -561,15 +586,20 @@ def bench_offload(args, n_blocks=57):
     import precision_state_amd as ps
     import synth
     dev = "cuda:0"
+    # The copy ceiling first, before the state's pinned buffers exist: measured
+    # after them, on some boxes the two directions of the probe ran one after
+    # the other while the pipeline's overlapped.
+    pcie = pcie_ceiling(dev)
+    log(f"[bench] pinned-copy ceiling: H2D {pcie['h2d']:.1f} GB/s, D2H {pcie['d2h']:.1f} GB/s, "
+        f"both at once {pcie['dup_h2d']:.1f} + {pcie['dup_d2h']:.1f} GB/s")
     shapes = synth.WORKLOADS["flux_double_block"]()
     numels = [s.numel for s in shapes]
     H = max(1, min(args.host_blocks, n_blocks))
     host_sets = [ps.StateSlab(numels, dev, with_grads=False, host_state=True) for _ in range(H)]
-    for h, hs in enumerate(host_sets):
+    for h, hs in enumerate(host_sets):      # filled on the host: no copies before the timed runs
         for tid, st in enumerate(hs.states):
-            tmp = torch.empty(st.numel, dtype=torch.int16, device=dev)
-            synth.dev_u16_uniform(tmp, args.seed, synth.STREAM_LO, 1000 * h + tid, 0)
-            st.w_lo.copy_(tmp.cpu())
+            st.w_lo.numpy()[:] = synth.host_u16_uniform(st.numel, args.seed, synth.STREAM_LO, 1000 * h + tid,
+                                                        0).view("int16")
     groups = []
     for k in range(n_blocks):
         hs = host_sets[k % H]
@@ -586,10 +616,8 @@ def bench_offload(args, n_blocks=57):
         groups.append((sts, gs))
     # device views must stay 16-byte aligned: all FLUX double-block sizes are multiples of 8
     torch.cuda.synchronize()
-    pcie = pcie_ceiling(dev)
-    log(f"[bench] pinned-copy ceiling: H2D {pcie['h2d']:.1f} GB/s, D2H {pcie['d2h']:.1f} GB/s, "
-        f"both at once {pcie['dup_h2d']:.1f} + {pcie['dup_d2h']:.1f} GB/s")
-    plan = ps.OffloadPlan(groups)
+    mode = {"direct": ps.OFFLOAD_DIRECT, "staged": ps.OFFLOAD_STAGED}[args.offload_mode]
+    plan = ps.OffloadPlan(groups, mode, args.offload_cus)
     n_params = n_blocks * synth.total_params(shapes)
     sr = args.split == "stochastic"
     hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, split_mode=ps.SPLIT_STOCHASTIC if sr else ps.SPLIT_TRUNC,
@@ -607,7 +635,7 @@ def bench_offload(args, n_blocks=57):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
     h2d, d2h = plan.bytes()       # of the last run (no residuals under stochastic rounding)
-    log(f"[bench] offload: {n_blocks} blocks, {wall * 1e3:.1f} ms/step, PCIe {h2d / wall / 1e9:.1f} GB/s up + "
+    log(f"[bench] offload ({args.offload_mode}): {n_blocks} blocks, {wall * 1e3:.1f} ms/step, PCIe {h2d / wall / 1e9:.1f} GB/s up + "
         f"{d2h / wall / 1e9:.1f} GB/s down")
     print(json.dumps({
         "metric": "offloaded optimizer-updated params/sec (host-resident residuals and moments over PCIe)",
@@ -615,10 +643,13 @@ def bench_offload(args, n_blocks=57):
         "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"flux_double_block_x{n_blocks}_offload", "params": n_params, "split": args.split,
+                   "offload_mode": args.offload_mode,
+                   "offload_cus": args.offload_cus if args.offload_mode == "direct" else None,
                    "host_state_sets": H, "pcie_h2d_gbs": h2d / wall / 1e9, "pcie_d2h_gbs": d2h / wall / 1e9,
                    "pcie_total_gbs": (h2d + d2h) / wall / 1e9, "h2d_bytes_per_step": h2d,
                    "hbm_gbs_kernel_18B": (14 if sr else 18) * n_params / wall / 1e9,
-                   "pinned_copy_ceiling_gbs": pcie},
+                   "pinned_copy_ceiling_gbs": pcie,
+                   "frac_of_duplex_ceiling": min(h2d, d2h) / wall / 1e9 / pcie["dup_h2d"]},
         "roofline": {"bound": "pcie", "achieved": (h2d + d2h) / wall / 1e9, "peak": 128.0, "unit": "GB/s",
                      "frac": (h2d + d2h) / wall / 1e9 / 128.0, "traffic": None},
         "cpu_baseline": None}), flush=True)
@@ -709,6 +740,11 @@ def main():
                          "(factored second moment, update clipping; --beta1, --decay-rate) on the double-block "
                          "shapes; offload: host-resident state over PCIe; per_tensor: one call per tensor, as a "
                          "gradient hook would step; elementwise: the standalone split/join/encode/decode kernels")
+    ap.add_argument("--offload-mode", default="direct", choices=["direct", "staged"],
+                    help="offload mode: the step kernel on the host arrays in place over PCIe (direct) or copies "
+                         "through two device staging slots (staged)")
+    ap.add_argument("--offload-cus", type=int, default=8,
+                    help="offload mode direct: compute units the step kernels may use (0 = all)")
     ap.add_argument("--per-tensor-calls", action="store_true",
                     help="factored mode: also time one call per tensor (the per-hook granularity)")
     ap.add_argument("--policy", action="store_true",

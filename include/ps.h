@@ -285,13 +285,20 @@ ps_status ps_factored_step_noalloc(const ps_tensor* tensors, int32_t n_tensors, 
  * A group is one set of tensors stepped together (e.g. one transformer
  * block). For every tensor, w_hi and grad are device pointers; w_lo, m_code,
  * m_scale, v_code and v_scale are PINNED HOST pointers (hipHostMalloc).
- * ps_offload_run steps the groups in order: group k's host state is copied
- * to a device staging slot on an upload stream, stepped on `stream`, and
- * copied back on a download stream, with two slots so that uploads of k+1
- * and downloads of k-1 overlap the step of k. The results are bit-identical
+ * ps_offload_run steps the groups in order. In the STAGED mode group k's
+ * host state is copied to a device staging slot on an upload stream, stepped,
+ * and copied back on a download stream, with two slots so that uploads of
+ * k+1 and downloads of k-1 overlap the step of k; in the DIRECT mode the step
+ * kernel of group k works on the host arrays in place. The results are bit-identical
  * to ps_opt_step_multi on device-resident state (for stochastic rounding:
  * on the concatenation of the groups' tensor lists, whose positions key the
  * random streams).
+ * Streams: STAGED makes an upload and a download stream, each created with a
+ * CU mask (all CUs) so that each gets a hardware queue of its own and the two
+ * directions overlap whatever other streams the process holds, and a
+ * non-blocking stream for the step kernels; DIRECT makes one stream with a
+ * CU mask of n_cus CUs for its kernels. Streams made with a CU mask are
+ * blocking: they order themselves with the null stream of the device.
  * Stochastic rounding [NADAM, opening post: the stochastic updates used when
  * the residual does not fit in host memory]: runs with split_mode STOCHASTIC
  * move no residuals; w_lo may then be NULL, and a plan with any NULL w_lo
@@ -303,10 +310,36 @@ typedef struct ps_offload_group {
 
 typedef struct ps_offload_plan ps_offload_plan;
 
-/* Creates the plan: copies the group descriptions, allocates two device
- * staging slots sized for the largest group, creates two copy streams and the
- * events. Synchronous. */
+/* Plan modes.
+ *   PS_OFFLOAD_DIRECT  the step kernel reads and writes the host-resident
+ *                      arrays in place over PCIe (through the device addresses
+ *                      of the pinned allocations, hipHostGetDevicePointer), one
+ *                      launch per group on a stream of the plan's own that is
+ *                      restricted to n_cus compute units: no staging memory and
+ *                      no copy engines; the rest of the GPU stays free for
+ *                      other work
+ *   PS_OFFLOAD_STAGED  two device staging slots, an upload and a download
+ *                      stream (each with a hardware queue of its own) and the
+ *                      step kernel on a third stream, as described above
+ * Both move the same bytes over PCIe and give the same results. */
+enum { PS_OFFLOAD_DIRECT = 0, PS_OFFLOAD_STAGED = 1 };
+#define PS_OFFLOAD_DEFAULT_CUS 8
+typedef struct ps_offload_options {
+  int32_t mode;      /* PS_OFFLOAD_DIRECT or PS_OFFLOAD_STAGED */
+  int32_t n_cus;     /* DIRECT: compute units the step kernels may use (0: all) */
+  int32_t reserved0; /* must be 0 */
+  int32_t reserved1; /* must be 0 */
+} ps_offload_options;
+
+/* Creates the plan: copies the group descriptions and builds the device
+ * tables, streams and events. DIRECT also checks that every host array has a
+ * device address; STAGED allocates two staging slots sized for the largest
+ * group. Synchronous. options NULL: DIRECT on PS_OFFLOAD_DEFAULT_CUS compute
+ * units. ps_offload_plan_create(g, n, p) is ps_offload_plan_create_ex(g, n,
+ * NULL, p). */
 ps_status ps_offload_plan_create(const ps_offload_group* groups, int32_t n_groups, ps_offload_plan** plan);
+ps_status ps_offload_plan_create_ex(const ps_offload_group* groups, int32_t n_groups,
+                                    const ps_offload_options* options, ps_offload_plan** plan);
 /* Runs one optimizer step over all groups; asynchronous on `stream` (the
  * call returns once all work is queued; host state is final when `stream`
  * completes). Successive runs of one plan are ordered among themselves even

@@ -34,7 +34,7 @@ STATUS = {0: "PS_OK", 1: "PS_ERR_INVALID_ARG", 2: "PS_ERR_ALIGNMENT", 3: "PS_ERR
 
 EXPORTED = ["ps_opt_step_multi", "ps_step_scalars", "ps_split", "ps_join", "ps_encode_moments",
             "ps_decode_moments", "ps_factored_workspace_size", "ps_factored_step", "ps_factored_step_noalloc",
-            "ps_offload_plan_create",
+            "ps_offload_plan_create", "ps_offload_plan_create_ex",
             "ps_offload_run", "ps_offload_bytes", "ps_offload_plan_destroy", "ps_status_string",
             "ps_last_error", "ps_version"]
 
@@ -70,6 +70,15 @@ class COffloadGroup(ctypes.Structure):
     _fields_ = [("tensors", ctypes.POINTER(CTensor)), ("n_tensors", ctypes.c_int32)]
 
 
+class COffloadOptions(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("n_cus", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("reserved1", ctypes.c_int32)]
+
+
+OFFLOAD_DIRECT, OFFLOAD_STAGED = 0, 1
+OFFLOAD_DEFAULT_CUS = 8
+
+
 _vp, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
 _sig = {
     "ps_opt_step_multi": [ctypes.POINTER(CTensor), _i32, ctypes.POINTER(CHParams), _i64, _vp],
@@ -82,6 +91,8 @@ _sig = {
     "ps_factored_step": [ctypes.POINTER(CTensor), _i32, ctypes.POINTER(CFHParams), _i64, _vp, ctypes.c_size_t, _vp],
     "ps_factored_step_noalloc": [ctypes.POINTER(CTensor), _i32, ctypes.POINTER(CFHParams), _i64, _vp],
     "ps_offload_plan_create": [ctypes.POINTER(COffloadGroup), _i32, ctypes.POINTER(ctypes.c_void_p)],
+    "ps_offload_plan_create_ex": [ctypes.POINTER(COffloadGroup), _i32, ctypes.POINTER(COffloadOptions),
+                                  ctypes.POINTER(ctypes.c_void_p)],
     "ps_offload_run": [_vp, ctypes.POINTER(CHParams), _i64, _vp],
     "ps_offload_bytes": [_vp, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)],
     "ps_offload_plan_destroy": [_vp],
@@ -314,10 +325,12 @@ def factored_step_noalloc(states, grads=None, hp: FactoredHParams = None, step: 
 
 
 class OffloadPlan:
-    """Host-offload pipeline (ps_offload_*): groups of tensors whose residual
-    and moment state live in pinned host memory."""
+    """Host-offload plan (ps_offload_*): groups of tensors whose residual and
+    moment state live in pinned host memory. mode OFFLOAD_DIRECT (the step
+    kernel works on the host arrays in place, on n_cus compute units) or
+    OFFLOAD_STAGED (copies through two device staging slots)."""
 
-    def __init__(self, groups):
+    def __init__(self, groups, mode=OFFLOAD_DIRECT, n_cus=OFFLOAD_DEFAULT_CUS):
         # groups: list of (states, grads) with host-pinned lo/codes/scales
         self._recs = [make_records(s, g) for s, g in groups]
         garr = (COffloadGroup * max(1, len(groups)))()
@@ -325,7 +338,8 @@ class OffloadPlan:
             garr[i] = COffloadGroup(ctypes.cast(arr, ctypes.POINTER(CTensor)), n)
         self._garr = garr
         h = ctypes.c_void_p()
-        _check(_lib.ps_offload_plan_create(garr, len(groups), ctypes.byref(h)))
+        opt = COffloadOptions(mode, n_cus, 0, 0)
+        _check(_lib.ps_offload_plan_create_ex(garr, len(groups), ctypes.byref(opt), ctypes.byref(h)))
         self._h = h
 
     def run(self, hp: HParams, step: int, stream=None):

@@ -18,6 +18,7 @@ RECORDS = {
     "ps_factored_hparams": ("CFHParams", ["split_mode", "reserved", "lr", "beta2", "eps1", "clip_threshold",
                                           "weight_decay", "decay_rate", "beta1", "seed"]),
     "ps_offload_group": ("COffloadGroup", ["tensors", "n_tensors"]),
+    "ps_offload_options": ("COffloadOptions", ["mode", "n_cus", "reserved0", "reserved1"]),
 }
 
 

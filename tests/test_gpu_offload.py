@@ -37,8 +37,13 @@ def _resident_copy(slab):
     return out
 
 
+MODES = [(ps.OFFLOAD_DIRECT, ps.OFFLOAD_DEFAULT_CUS), (ps.OFFLOAD_DIRECT, 3), (ps.OFFLOAD_DIRECT, 0),
+         (ps.OFFLOAD_STAGED, 0)]
+
+
+@pytest.mark.parametrize("mode,cus", MODES)
 @pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY])
-def test_offload_equals_resident_bitwise(split_mode):
+def test_offload_equals_resident_bitwise(split_mode, mode, cus):
     slabs = [ps.StateSlab(sizes, DEV, host_state=True) for sizes in GROUPS]
     for gid, sl in enumerate(slabs):
         _fill(sl, gid)
@@ -46,7 +51,7 @@ def test_offload_equals_resident_bitwise(split_mode):
     resident = [_resident_copy(sl) for sl in slabs]
     hp = ps.HParams(algo=ps.ALGO_NADAM, lr=1e-4, weight_decay=0.01, split_mode=split_mode)
     grads = [[None if (gid == 1 and i == 1) else g for i, g in enumerate(sl.grads)] for gid, sl in enumerate(slabs)]
-    plan = ps.OffloadPlan([(sl.states, grads[gid]) for gid, sl in enumerate(slabs)])
+    plan = ps.OffloadPlan([(sl.states, grads[gid]) for gid, sl in enumerate(slabs)], mode, cus)
     h2d, d2h = plan.bytes()
     moved = sum(2 * 3 * n + 8 * ((n + 255) // 256) for gid, sizes in enumerate(GROUPS) for i, n in enumerate(sizes)
                 if not (gid == 1 and i == 1))
@@ -67,7 +72,8 @@ def test_offload_equals_resident_bitwise(split_mode):
     plan.close()
 
 
-def test_offload_stochastic_rounding_moves_no_residual_and_equals_resident():
+@pytest.mark.parametrize("mode", [ps.OFFLOAD_DIRECT, ps.OFFLOAD_STAGED])
+def test_offload_stochastic_rounding_moves_no_residual_and_equals_resident(mode):
     """Stochastic rounding through the pipeline (the pages' setting when the
     residual does not fit in host memory): some tensors have no residual at
     all, the run moves only codes and scales, and the bytes equal one resident
@@ -82,7 +88,7 @@ def test_offload_stochastic_rounding_moves_no_residual_and_equals_resident():
     for sl in slabs[1:]:
         sl.states[0].w_lo = None                       # no residual array for these tensors
     hp = ps.HParams(algo=ps.ALGO_NADAM, lr=1e-4, weight_decay=0.01, split_mode=ps.SPLIT_STOCHASTIC, seed=808)
-    plan = ps.OffloadPlan([(sl.states, sl.grads) for sl in slabs])
+    plan = ps.OffloadPlan([(sl.states, sl.grads) for sl in slabs], mode)
     all_res = [st for group in resident for st in group]
     all_grads = [g for sl in slabs for g in sl.grads]
     for t in range(1, 4):
@@ -133,8 +139,9 @@ def _oracle_groups(groups, hp, steps, skip=(), seed=5, tid_of=lambda gid, i, pos
     return out
 
 
+@pytest.mark.parametrize("mode", [ps.OFFLOAD_DIRECT, ps.OFFLOAD_STAGED])
 @pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY, ps.SPLIT_STOCHASTIC])
-def test_offload_matches_oracle_every_byte(split_mode):
+def test_offload_matches_oracle_every_byte(split_mode, mode):
     """Three ragged groups (a tensor without a gradient, an empty tensor), 3
     NAdamW steps through the pipeline; weights, residuals, codes and scales of
     every tensor equal the oracle's replay."""
@@ -144,7 +151,7 @@ def test_offload_matches_oracle_every_byte(split_mode):
     torch.cuda.synchronize()
     hp = ps.HParams(algo=ps.ALGO_NADAM, lr=1e-4, weight_decay=0.01, split_mode=split_mode, seed=77)
     grads = [[None if (gid == 1 and i == 1) else g for i, g in enumerate(sl.grads)] for gid, sl in enumerate(slabs)]
-    plan = ps.OffloadPlan([(sl.states, grads[gid]) for gid, sl in enumerate(slabs)])
+    plan = ps.OffloadPlan([(sl.states, grads[gid]) for gid, sl in enumerate(slabs)], mode)
     for t in range(1, 4):
         for gid, sl in enumerate(slabs):
             for i, g in enumerate(sl.grads):
@@ -163,12 +170,13 @@ def test_offload_matches_oracle_every_byte(split_mode):
                 assert np.array_equal(got[k], exp[k]), (gid, i, a.numel, k)
 
 
-def test_offload_double_blocks_distinct_host_sets_sampled():
+@pytest.mark.parametrize("mode", [ps.OFFLOAD_DIRECT, ps.OFFLOAD_STAGED])
+def test_offload_double_blocks_distinct_host_sets_sampled(mode):
     """Three groups of unequal size built from FLUX double-block shapes (a
     whole block, its first 10 tensors, a whole block plus 5 tensors of
     another), each with its own pinned host state, run for 2 steps so that
-    both staging slots are reused; sampled 256-blocks of every tensor against
-    the oracle (each block evolves from its own inputs only)."""
+    both staging slots are reused (staged mode); sampled 256-blocks of every
+    tensor against the oracle (each block evolves from its own inputs only)."""
     blk = synth.WORKLOADS["flux_double_block"]()
     group_shapes = [blk, blk[:10], blk + blk[:5]]
     slabs = [ps.StateSlab([s.numel for s in shapes], DEV, host_state=True) for shapes in group_shapes]
@@ -186,7 +194,7 @@ def test_offload_double_blocks_distinct_host_sets_sampled():
         all_states += sl.states
     torch.cuda.synchronize()
     hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, weight_decay=0.01)
-    plan = ps.OffloadPlan([(sl.states, sl.grads) for sl in slabs])
+    plan = ps.OffloadPlan([(sl.states, sl.grads) for sl in slabs], mode)
     for t in range(1, 3):
         pos = 0
         for sl in slabs:
@@ -199,3 +207,20 @@ def test_offload_double_blocks_distinct_host_sets_sampled():
     plan.close()
     n = check_sampled_blocks(all_shapes, all_states, hp, 2, 0, 6)
     print(f"  {n} sampled blocks of {len(all_shapes)} tensors exact", flush=True)
+
+
+def test_offload_plan_rejects_unmapped_host_arrays_and_bad_options():
+    """The direct mode takes each host array's device address at plan
+    creation: pageable (not pinned) host memory is rejected there, and so are
+    unknown modes and negative CU counts."""
+    sl = ps.StateSlab([1000], DEV, host_state=True)
+    st = sl.states[0]
+    pageable = torch.empty(st.numel, dtype=torch.int16)          # not pinned
+    bad = ps.TensorState(st.w_hi, pageable, st.m_code, st.m_scale, st.v_code, st.v_scale)
+    for mode in (ps.OFFLOAD_DIRECT, ps.OFFLOAD_STAGED):
+        with pytest.raises(ps.PSError):
+            ps.OffloadPlan([([bad], sl.grads)], mode)
+    with pytest.raises(ps.PSError):
+        ps.OffloadPlan([(sl.states, sl.grads)], 7)
+    with pytest.raises(ps.PSError):
+        ps.OffloadPlan([(sl.states, sl.grads)], ps.OFFLOAD_DIRECT, -1)
