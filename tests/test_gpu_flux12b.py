@@ -31,7 +31,7 @@ def test_flux_dev_12b_two_steps_sampled(moments):
     import bench
     shapes = synth.WORKLOADS["flux_dev_12b"]()
     seed = 0
-    states, grads = bench.build_state(shapes, seed, "cuda", "slab", moments)
+    states, grads, slab = bench.build_state(shapes, seed, "cuda", "slab", moments)
     hp = ps.HParams(algo=ps.ALGO_NADAM, lr=3.5e-6, weight_decay=0.0)
     recs = ps.make_records(states, grads)
     ps.opt_step_multi(None, None, hp, 1, records=recs)
@@ -43,6 +43,6 @@ def test_flux_dev_12b_two_steps_sampled(moments):
     nblk = check_sampled_blocks(shapes, states, hp, 2, seed, per_tensor=6)
     print(f"  {moments}: {nblk} sampled blocks over {len(shapes)} tensors bit-exact", flush=True)
     assert nblk > 780
-    del states
+    del states, slab
     gc.collect()
     torch.cuda.empty_cache()
