@@ -158,3 +158,24 @@ def test_factored_first_moment_any_column_count(split_mode):
     tensor and a 1-D tensor in the same call; a zero gradient in one of them."""
     hp = ps.FactoredHParams(split_mode=split_mode, lr=1e-4, weight_decay=0.01, decay_rate=-0.8, beta1=0.8, seed=7)
     _run(FM_ANY_COLS, hp, 5, 11, 0.01, zero_grad=(4,))
+
+
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY, ps.SPLIT_STOCHASTIC])
+def test_single_one_d_tensor_calls(split_mode):
+    """Per-hook calls with one 1-D tensor each (biases and norm scales are
+    stepped this way from their gradient hooks): 1 to 70000 elements, partial
+    items and blocks, with a first moment and the schedule, 4 steps, every
+    call against the oracle."""
+    sizes = [1, 255, 256, 1025, 18432, 32768, 32769, 70000]
+    hp = ps.FactoredHParams(split_mode=split_mode, lr=1e-4, weight_decay=0.01, decay_rate=-0.8, beta1=0.9, seed=17)
+    for i, n in enumerate(sizes):
+        shape = synth.Shape(f"v{n}", 0, 0, n)
+        d = dev_state(n, 21, i, 0, 0, factored=True)
+        h = host_state(n, 21, i, 0, factored=True)
+        ws = torch.empty(max(ps.factored_workspace_size([d], [d.w_hi]), 256), dtype=torch.uint8, device=DEV)
+        for t in range(1, 5):
+            g = dev_grad(n, 21, i, t, 0.01)
+            ps.factored_step([d], [g], hp, t, workspace=ws)
+            oracle.factored_step(h, host_grad(n, 21, i, t, 0.01), 0, 0, _ofhp(hp, 0), t)
+        torch.cuda.synchronize()
+        _compare(d, h, 0, shape.name, first_moment=True)
