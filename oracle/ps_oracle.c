@@ -38,7 +38,11 @@
  *    to the step (w - (u + lr*wd*w)).
  *  - Factored step: eps1 added to g^2 before the means, no bias correction,
  *    V^-1/2 built as (1/sqrt(r_i/mean(r))) * (1/sqrt(c_j)), RMS over the
- *    whole tensor. beta2 is constant unless decay_rate < 0, which gives
+ *    whole tensor. The update applies the fp32 U = (g * rho_i) * kap_j; the
+ *    RMS that sets the clip is evaluated in double from the factored estimate
+ *    itself, U_ij^2 = g_ij^2 * mean(r) / (r_i * c_j) (1-D: g^2 / v), so it is
+ *    the RMS of the exact U for the stored EMAs, free of the fp32 rounding of
+ *    rho, kap and U. beta2 is constant unless decay_rate < 0, which gives
  *    beta2_t = 1 - t^decay_rate [ADAF]; the optional first moment is an EMA
  *    of the clipped, lr-scaled update, taken before weight decay [ADAF].
  *  - f24 moments: bits 8..31 of the fp32 word, rounded to nearest even,
@@ -501,12 +505,13 @@ void orc_factored_2d(uint16_t* hi, uint16_t* lo, const uint16_t* g, float* row, 
   float rbar = (float)(rsum / (double)R);
   for (int64_t i = 0; i < R; ++i) rho[i] = 1.0f / sqrtf(row[i] / rbar);
   for (int64_t j = 0; j < C; ++j) kap[j] = 1.0f / sqrtf(col[j]);
-  /* 3. U = g * V^-1/2 and the clip factor from RMS(U) */
-  double su = 0.0;
+  /* 3. the clip factor from RMS(U), U^2 = g^2 / V = g^2 * mean(r) / (r_i c_j)
+   *    evaluated in double */
+  double rmean = rsum / (double)R, su = 0.0;
   for (int64_t i = 0; i < R; ++i)
     for (int64_t j = 0; j < C; ++j) {
-      float U = (orc_bf16_to_f32(g[i * C + j]) * rho[i]) * kap[j];
-      su += (double)U * (double)U;
+      double gd = (double)orc_bf16_to_f32(g[i * C + j]);
+      su += gd * gd * rmean / ((double)row[i] * (double)col[j]);
     }
   float f = clip_factor(su, R * C, hp);
   /* 4. apply to the joined master weight and split again; with a first
@@ -547,8 +552,7 @@ void orc_factored_1d(uint16_t* hi, uint16_t* lo, const uint16_t* g, uint16_t* vc
     float gf = orc_bf16_to_f32(g[e]);
     float q = gf * gf + EPS1;
     v[e] = fmaf(B2, orc_decode1(vc[e], vs[e / ORC_BLOCK], ORC_UNSIGNED), C2 * q);
-    float U = gf * (1.0f / sqrtf(v[e]));
-    su += (double)U * (double)U;
+    su += (double)gf * (double)gf / (double)v[e];   /* U^2 = g^2 / v in double */
   }
   float f = clip_factor(su, n, hp);
   for (int64_t e = 0; e < n; ++e) {
