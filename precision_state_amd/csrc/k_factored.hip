@@ -5,14 +5,19 @@
 // [ADAF, adafactor_step_param; PRODIGY, beta1 = 0 / factored / update
 // clipping].
 //
-// 2-D tensors [R, C] are cut into 64 x 256 tiles, one 256-thread workgroup
-// each; thread t handles columns (t % 32) * 8 .. + 8 of rows t / 32 + 8k,
-// k = 0..7, so each half-wave reads one 512-byte row segment per load.
-// Passes over the gradient: tile row/column sums of q = g^2 + eps1 (double);
+// Passes: statistics (row and column sums of q = g^2 + eps1, in double);
 // row/column finalize (EMAs, chunk sums of the new row EMA); factors
-// rho_i = 1/sqrt(r_i / rbar), kap_j = 1/sqrt(c_j); tile sums of U^2 (double);
-// clip factor per tensor; apply. 1-D tensors keep v in the uint16 codec and
-// use 1024-element items like the fused (N)AdamW step.
+// rho_i = 1/sqrt(r_i / rbar), kap_j = 1/sqrt(c_j); the sum of U^2 over each
+// tensor; clip factor per tensor; apply, with the fp32 U = (g * rho_i) * kap_j.
+// The RMS behind the clip is evaluated in double from the factored estimate,
+// U_ij^2 = g_ij^2 * rbar / (r_i c_j) (1-D: g^2 / v).
+//  - Tensors whose rows are whole multiples of 512 columns (up to 12288) take
+//    the row-strip statistics pass, which also sums g^2 / r_i per column, so
+//    the gradient is read twice per step (statistics, apply).
+//  - Others take 64 x 256 statistics tiles (thread t: columns (t % 32) * 8 ..
+//    + 8 of rows t / 32 + 8k, so each half-wave reads one 512-byte row segment
+//    per load) and a pass of their own for the sum of U^2: three reads.
+// 1-D tensors keep v in the uint16 codec and use 1024-element items.
 //
 // All reductions use fixed trees (no atomics), so results are deterministic.
 #include "dev_common.h"
@@ -47,6 +52,11 @@ __device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
 __device__ __forceinline__ void st_stream(uint16_t* p, uint4 v) {
   __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (GLOBAL u32x4*)p);
 }
+
+// Direct-to-LDS gradient copies of the row-strip pass: lane i's 16 bytes land
+// at dst + 16 i (dst wave-uniform); cache-policy bit 1 marks them non-temporal.
+constexpr int kLdsDmaNt = 2;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // First entry of the wave-uniform prefix-end array greater than x.
 __device__ __forceinline__ int find_end(const uint32_t* __restrict__ end, int n, uint32_t x, uint32_t& begin) {
@@ -214,6 +224,350 @@ __global__ __launch_bounds__(kT) void k_f_stats(FPlan P, FScalars S) {
   }
 }
 
+// ---- pass 1, row strips: row sums, row EMA, column sums of q and of g^2 / r_i
+// Tensors with C % 512 == 0 and C <= kStripMaxC. The sum of U^2 needs no
+// pass of its own: U_ij^2 = g_ij^2 * rbar / (r_i c_j), so
+//   sum_ij U_ij^2 = rbar * sum_j Q_j / c_j,   Q_j = sum_i g_ij^2 / r_i,
+// and r_i, the new row EMA, is known as soon as row i has been read. So a
+// workgroup takes whole rows: a group of rows (the host cuts the strip
+// tensors' rows into groups of equal element counts, one per workgroup),
+// walked in steps of `grows` rows (one row when a row has more 16-byte runs
+// than the workgroup has threads). Thread t owns the runs u0 = t mod Ur (and,
+// for rows of more than kSNT runs, u0 + kSNT) of row t / Ur of a step, so its
+// 8 (or 16) column sums stay in registers for the whole group.
+// The gradient goes straight to LDS (global_load_lds, 16 bytes per lane, each
+// thread later reading back only its own entries) in batches of 48 KiB, three
+// buffers deep: two batches stay in flight while one is summed, and the
+// prefetch costs no registers. One barrier per batch publishes each wave's row
+// partials (a wave lies within one row because Ur % 64 == 0); lane d of every
+// wave then adds the partials of step d's row in wave order and forms that
+// row's EMA from the same double sum the finalize kernel uses. Column sums of
+// q and of g^2 / r_i are in double; the threads of a step that share columns
+// add theirs in row order through LDS at the end of the group.
+
+// Barrier for LDS data only: this wave's LDS accesses complete, gradient
+// loads stay in flight. The empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt left alone
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wave sums of D doubles by transpose-reduce, lane exchanges only (no LDS):
+// lane l ends with the sum over the 64 lanes of v[k], k = l >> (6 - log2 D),
+// in a fixed order. v_permlane32_swap / v_permlane16_swap hand each half (row
+// pair) the other's values, and an exchange of two different values leaves
+// each half the sum of one of them; the last four lane bits are folded by DPP
+// within each row of 16 (every lane of the row ends with the row's sum).
+__device__ __forceinline__ uint32_t lo32(double x) { return (uint32_t)__double_as_longlong(x); }
+__device__ __forceinline__ uint32_t hi32(double x) { return (uint32_t)((uint64_t)__double_as_longlong(x) >> 32); }
+__device__ __forceinline__ double mk64(uint32_t lo, uint32_t hi) {
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// lanes 0..31: a + a of lane + 32; lanes 32..63: b of lane - 32 + b
+__device__ __forceinline__ double swap32_sum(double a, double b) {
+  const auto l = __builtin_amdgcn_permlane32_swap(lo32(a), lo32(b), false, false);
+  const auto h = __builtin_amdgcn_permlane32_swap(hi32(a), hi32(b), false, false);
+  return mk64(l[0], h[0]) + mk64(l[1], h[1]);
+}
+// even rows of 16: a + a of the next row; odd rows: b of the previous row + b
+__device__ __forceinline__ double swap16_sum(double a, double b) {
+  const auto l = __builtin_amdgcn_permlane16_swap(lo32(a), lo32(b), false, false);
+  const auto h = __builtin_amdgcn_permlane16_swap(hi32(a), hi32(b), false, false);
+  return mk64(l[0], h[0]) + mk64(l[1], h[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  return mk64(dpp_u32<CTRL>(lo32(x)), dpp_u32<CTRL>(hi32(x)));
+}
+__device__ __forceinline__ double row16_sum(double x) {
+  x += dpp_f64<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_f64<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_f64<0x141>(x);   // row_half_mirror
+  x += dpp_f64<0x140>(x);   // row_mirror
+  return x;
+}
+template <int D>
+__device__ __forceinline__ double wave_sums(const double* v) {
+  if constexpr (D == 4) {
+    const double a0 = swap32_sum(v[0], v[2]), a1 = swap32_sum(v[1], v[3]);   // index 2 b5 + {0, 1}
+    return row16_sum(swap16_sum(a0, a1));                                     // index 2 b5 + b4
+  } else {
+    static_assert(D == 2, "D is 2 or 4");
+    const double a = swap32_sum(v[0], v[1]);   // index b5
+    return row16_sum(swap16_sum(a, a));
+  }
+}
+
+// Register pinning: an empty asm statement that reads and rewrites x. Placed
+// after each 16-byte run, it keeps the compiler from interleaving the
+// double-precision work of many runs (which needed more registers than three
+// waves per SIMD leave, and the spill reloads then waited on the gradient
+// loads in flight).
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+constexpr int kSWaves = kSNT / 64;
+constexpr int kSBufRuns = 4 * kSNT;    // 16-byte runs per LDS batch buffer (48 KiB)
+constexpr int kSBufBytes = kSBufRuns * 16;
+
+// LDS reads of the batch buffers, in asm: the compiler cannot tell the
+// batch being summed from those still being filled and would wait for every
+// copy in flight before any LDS read of them; after the explicit wait for the
+// batch at hand, the newer ones stay in flight. Each asm statement waits for
+// its own results.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// The N = D * K runs of this thread in a batch buffer, entry (d * K + k) at
+// byte offset (d * K + k) * kSNT * 16 from the thread's first.
+template <int N>
+__device__ __forceinline__ void lds_read_runs(uint32_t a, u32x4 (&x)[N]) {
+  static_assert(N == 4, "a batch holds four runs per thread");
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:12288\n\t"
+      "ds_read_b128 %2, %4 offset:24576\n\t"
+      "ds_read_b128 %3, %4 offset:36864\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])   // early clobber: the address must
+      : "v"(a)                                               // outlive the first read's result
+      : "memory");
+}
+static_assert(kSNT * 16 == 12288, "the offsets in lds_read_runs");
+__device__ __forceinline__ float lds_read4(uint32_t a) {
+  float v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+  return v;
+}
+
+// Three batch buffers; a segment's column sums of the rows after the first of
+// a step pass through the first two at the end (at most kSNT - 64 threads x
+// 16 doubles = 90112 bytes). s_ro holds the old row EMA of each wave's row of
+// each step of a batch, s_wsum the wave row partials by batch parity.
+__shared__ u32x4 s_buf[3][kSBufRuns];
+__shared__ float s_ro[3][4][kSWaves];
+__shared__ double s_wsum[2][4][kSWaves];
+
+__device__ __forceinline__ double* comb_entry(int e) {   // 16 doubles (8 runs) per entry
+  return (double*)&s_buf[0][8 * e];
+}
+static_assert((kSNT - 64) * 8 <= 2 * kSBufRuns, "the column sums fit two buffers");
+
+// What a segment needs of its tensor and the scalars, held in registers: the
+// asm statements' memory clobbers would otherwise make the compiler reload
+// the tensor record (and wait for every load in flight) inside the loop.
+struct StripArgs {
+  const GLOBAL uint16_t* g;
+  const GLOBAL float* row;
+  GLOBAL double* rowpart;
+  GLOBAL double* colpart;
+  GLOBAL double* qpart;
+  int C, row0, row1, slot;
+  float EPS1, B2, C2;
+};
+
+template <int K, int D>
+__device__ __forceinline__ void strip_segment(const StripArgs& A, int& par) {
+  static_assert(D * K * kSNT == kSBufRuns && D * K == 4, "a batch fills one LDS buffer");
+  constexpr int OPS = D * K + D;   // vector memory operations per batch and wave
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int C = A.C, Ur = C >> 3;
+  int grows, rr, u0, nwr, w0;
+  if (K == 1) {
+    grows = kSNT / Ur;
+    rr = __builtin_amdgcn_readfirstlane(t / Ur);   // wave-uniform (Ur % 64 == 0)
+    u0 = t - rr * Ur;
+    nwr = Ur >> 6;
+    w0 = rr * nwr;
+  } else {
+    grows = 1;
+    rr = 0;
+    u0 = t;
+    nwr = kSWaves;
+    w0 = 0;
+  }
+  const bool act = rr < grows;                       // wave-uniform
+  const bool run1 = K == 2 && u0 + kSNT < Ur;        // the second run exists
+  const int row0 = A.row0, row1 = A.row1;
+  const int nsteps = (row1 - row0 + grows - 1) / grows;
+  const int nb = (nsteps + D - 1) / D;
+  double P[K][8], Q[K][8];
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) P[k][j] = Q[k][j] = 0.0;
+
+  auto row_of = [&](int b, int d) { return row0 + (b * D + d) * grows + rr; };
+  // Every wave issues exactly D * K gradient copies and D row-EMA copies per
+  // batch, with addresses clamped into the segment (data of rows past the
+  // segment, of idle threads and of missing second runs are loaded and not
+  // used), so that vmcnt(n * OPS) waits for all but the n newest batches.
+  auto issue = [&](int b) {
+    const int h = b % 3;
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int i = min(row_of(b, d), row1 - 1);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int u = (k == 1 && run1) ? u0 + kSNT : u0;
+        __builtin_amdgcn_global_load_lds((const GLOBAL void*)(A.g + (size_t)i * (size_t)C + (size_t)(8 * u)),
+                                         (lds_void*)&s_buf[h][(d * K + k) * kSNT + wave * 64], 16, 0, kLdsDmaNt);
+      }
+      if (lane == 0)
+        __builtin_amdgcn_global_load_lds((const GLOBAL void*)(A.row + i), (lds_void*)&s_ro[h][d][wave], 4, 0, 0);
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  if (nb > 0) issue(0);
+  if (nb > 1) issue(1);
+  for (int b = 0; b < nb; ++b) {
+    if (b + 2 < nb) issue(b + 2);
+    const int newer = min(nb - 1 - b, 2);   // batches issued after this one
+    if (newer == 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * OPS) : "memory");
+    else if (newer == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int h = b % 3;
+    const uint32_t abuf = lds_addr(&s_buf[h][t]);
+
+    // q = g^2 + eps1 into the column sums and this lane's row partials
+    u32x4 x[4];
+    lds_read_runs(abuf, x);
+    double rp[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      rp[d] = 0.0;
+      if (!(act && row_of(b, d) < row1)) continue;   // wave-uniform
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const uint32_t w[4] = {x[d * K + k].x, x[d * K + k].y, x[d * K + k].z, x[d * K + k].w};
+        double sq = 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float g = bf16_at(w, j);
+          const double q = (double)__builtin_fmaf(g, g, A.EPS1);
+          P[k][j] += q;
+          sq += q;
+        }
+        rp[d] += (k == 0 || run1) ? sq : 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pin(P[k][j]);
+        pin(rp[d]);
+      }
+    }
+    const double ws = wave_sums<D>(rp);
+    if ((lane & (64 / D - 1)) == 0) s_wsum[par][lane / (64 / D)][wave] = ws;
+    lds_barrier();
+
+    // lane d: step d's row sum in wave order, the new row EMA and 1 / r_i
+    double inv_l = 0.0;
+    if (lane < D) {
+      const int i = row_of(b, lane);
+      double sum = 0.0;
+      for (int q = 0; q < nwr; ++q) sum += s_wsum[par][lane][w0 + q];
+      const float mean = (float)(sum / (double)C);
+      const float r = __builtin_fmaf(A.B2, lds_read4(lds_addr(&s_ro[h][lane][wave])), A.C2 * mean);
+      inv_l = 1.0 / (double)r;
+      if (act && i < row1 && wave == w0) A.rowpart[i] = sum;
+    }
+    // then g^2 / r_i into the column sums
+    lds_read_runs(abuf, x);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (!(act && row_of(b, d) < row1)) continue;   // wave-uniform
+      const double inv = mk64(__builtin_amdgcn_readlane(lo32(inv_l), d), __builtin_amdgcn_readlane(hi32(inv_l), d));
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const uint32_t w[4] = {x[d * K + k].x, x[d * K + k].y, x[d * K + k].z, x[d * K + k].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float g = bf16_at(w, j);
+          Q[k][j] = __builtin_fma((double)(g * g), inv, Q[k][j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pin(Q[k][j]);
+      }
+    }
+    par ^= 1;
+  }
+
+  // Threads of a step that share columns (K == 1, grows > 1): rows after the
+  // first deposit their sums, the first row's threads add them in row order.
+  // The first barrier also ends every wave's reads of the batch buffers.
+  if (K == 1 && grows > 1) {   // uniform
+    lds_barrier();
+    if (act && rr > 0) {
+      double* c = comb_entry((rr - 1) * Ur + u0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        c[j] = P[0][j];
+        c[8 + j] = Q[0][j];
+      }
+    }
+    lds_barrier();
+    if (rr == 0) {
+      for (int q = 1; q < grows; ++q) {
+        const double* c = comb_entry((q - 1) * Ur + u0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          P[0][j] += c[j];
+          Q[0][j] += c[8 + j];
+        }
+      }
+    }
+  }
+  // the buffers are free again for the next segment's first batches
+  lds_barrier();
+  if (rr == 0) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (k == 1 && !run1) continue;
+      const size_t o = (size_t)A.slot * (size_t)C + (size_t)(8 * (u0 + k * kSNT));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        A.colpart[o + j] = P[k][j];
+        A.qpart[o + j] = Q[k][j];
+      }
+    }
+  }
+}
+
+// Wave-uniform copies in scalar registers: read once, before the first
+// gradient copies are issued, so no later use waits on the copies in flight.
+template <class T>
+__device__ __forceinline__ GLOBAL T* uni(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (GLOBAL T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__global__ __launch_bounds__(kSNT) void k_f_strip(FPlan P, FScalars S) {
+  const uint32_t g = blockIdx.x;
+  const uint32_t s0 = g ? P.seg_end[g - 1] : 0u, s1 = P.seg_end[g];
+  int par = 0;
+  for (uint32_t s = s0; s < s1; ++s) {
+    const FSeg sg = P.segs[s];
+    const F2D& X = P.t2[sg.t];
+    const StripArgs A{uni(X.g), uni(X.row), uni(X.rowpart), uni(X.colpart), uni(X.qpart), uni(X.C),
+                      uni(sg.row0), uni(sg.row1), uni(sg.slot), S.EPS1, S.B2, S.C2};
+    if ((A.C >> 3) <= kSNT)   // uniform
+      strip_segment<1, 4>(A, par);
+    else
+      strip_segment<2, 2>(A, par);
+  }
+}
+
 // ---- pass 2: row/column EMAs and chunk sums of the new row EMA -------------
 __global__ __launch_bounds__(kT) void k_f_rowcol(FPlan P, FScalars S) {
   uint32_t begin;
@@ -226,7 +580,7 @@ __global__ __launch_bounds__(kT) void k_f_rowcol(FPlan P, FScalars S) {
     if (i < X.R) {
       double s = 0.0;
 #pragma unroll 8
-      for (int tc = 0; tc < X.ntc; ++tc) s += X.rowpart[(size_t)tc * X.R + i];
+      for (int tc = 0; tc < X.nrp; ++tc) s += X.rowpart[(size_t)tc * X.R + i];
       const float mean = (float)(s / (double)X.C);
       const float r = __builtin_fmaf(S.B2, X.row[i], S.C2 * mean);
       X.row[i] = r;
@@ -236,12 +590,24 @@ __global__ __launch_bounds__(kT) void k_f_rowcol(FPlan P, FScalars S) {
     if (threadIdx.x == 0) X.rpart[w] = t;
   } else {
     const int j = (w - X.nrw) * kFRowColChunk + (int)threadIdx.x;
+    double qc = 0.0;
     if (j < X.C) {
       double s = 0.0;
 #pragma unroll 16
       for (int tr = 0; tr < X.sntr; ++tr) s += X.colpart[(size_t)tr * X.C + j];
       const float mean = (float)(s / (double)X.R);
-      X.col[j] = __builtin_fmaf(S.B2, X.col[j], S.C2 * mean);
+      const float c = __builtin_fmaf(S.B2, X.col[j], S.C2 * mean);
+      X.col[j] = c;
+      if (X.strip) {   // uniform
+        double qs = 0.0;
+#pragma unroll 16
+        for (int tr = 0; tr < X.sntr; ++tr) qs += X.qpart[(size_t)tr * X.C + j];
+        qc = qs / (double)c;
+      }
+    }
+    if (X.strip) {   // uniform: this chunk's sum_j Q_j / c_j
+      const double t = block_sum(qc, red);
+      if (threadIdx.x == 0) X.upart[w - X.nrw] = t;
     }
   }
 }
@@ -256,15 +622,22 @@ __global__ __launch_bounds__(kT) void k_f_factors(FPlan P) {
     for (int q = 0; q < X.nrw; ++q) s += X.rpart[q];
     const float rbar = (float)(s / (double)X.R);
     const int i = w * kFRowColChunk + (int)threadIdx.x;
-    if (i < X.R) X.rho[i] = 1.0f / __builtin_sqrtf(X.row[i] / rbar);
+    if (i < X.R) {
+      X.rho[i] = 1.0f / __builtin_sqrtf(X.row[i] / rbar);
+      if (X.rinv) X.rinv[i] = 1.0 / (double)X.row[i];
+    }
   } else {
     const int j = (w - X.nrw) * kFRowColChunk + (int)threadIdx.x;
-    if (j < X.C) X.kap[j] = 1.0f / __builtin_sqrtf(X.col[j]);
+    if (j < X.C) {
+      X.kap[j] = 1.0f / __builtin_sqrtf(X.col[j]);
+      if (X.cinv) X.cinv[j] = 1.0 / (double)X.col[j];
+    }
   }
 }
 
-// ---- pass 4: tile sums of U^2, U = (g * rho_i) * kap_j (tensors whose rows
-// are not 16-byte runs and that keep no first moment) ---------------------------
+// ---- pass 4: sums of U^2 / mean(r) = g^2 / (r_i c_j), in double, for the
+// tensors that do not take the row-strip pass; this per tile (rows that are
+// not 16-byte runs, no first moment) -----------------------------------------
 __global__ __launch_bounds__(kT) void k_f_usq(FPlan P) {
   uint32_t begin;
   const F2D& X = P.t2[find_end(P.tile_u_end, P.n2, blockIdx.x, begin)];
@@ -272,20 +645,20 @@ __global__ __launch_bounds__(kT) void k_f_usq(FPlan P) {
   const int tr = (int)(tile / (uint32_t)X.ntc), tc = (int)(tile - (uint32_t)tr * X.ntc);
   const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
   const int c = tc * kFTileCols + cg * 8;
-  float kap[8];
+  double ci[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) kap[j] = (c + j < X.C) ? X.kap[c + j] : 0.0f;
+  for (int j = 0; j < 8; ++j) ci[j] = (c + j < X.C) ? X.cinv[c + j] : 0.0;
   double acc = 0.0;
   for (int k = 0; k < 8; ++k) {
     const int r = tr * kFTileRows + rg + 8 * k;
     uint32_t w[4];
     const uint32_t valid = load_row8(X.g, X, r, c, w);
     if (!valid) continue;
-    const float rho = X.rho[r];
+    const double ri = X.rinv[r];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float U = (bf16_at(w, j) * rho) * kap[j];
-      acc += (valid >> j & 1u) ? (double)U * (double)U : 0.0;
+      const double g = (double)bf16_at(w, j);
+      acc += (valid >> j & 1u) ? g * g * ri * ci[j] : 0.0;
     }
   }
   __shared__ double red[kT];
@@ -342,7 +715,8 @@ __device__ __forceinline__ void elem_factors(const F2D& X, uint32_t e, float& rh
   kap = X.kap[e - i * (uint32_t)X.C];
 }
 
-// U^2 sum of one item, any column count (same per-lane order as the run path).
+// Sum of g^2 / (r_i c_j) over one item, any column count (same per-lane order
+// as the run path).
 __device__ __forceinline__ void usq_item_any(const F2D& X, uint32_t item) {
   const uint32_t n = (uint32_t)X.R * (uint32_t)X.C;
   const uint32_t la = (threadIdx.x >> 4) * (uint32_t)kBlock + (threadIdx.x & 15) * 8u;
@@ -354,10 +728,9 @@ __device__ __forceinline__ void usq_item_any(const F2D& X, uint32_t item) {
     const uint32_t w[4] = {gv.x, gv.y, gv.z, gv.w};
     for (int jj = 0; jj < 8; ++jj) {
       if (e + jj >= n) break;
-      float rho, kap;
-      elem_factors(X, e + jj, rho, kap);
-      const float U = (bf16_at(w, jj) * rho) * kap;
-      acc += (double)U * (double)U;
+      const uint32_t i = (e + jj) / (uint32_t)X.C;
+      const double g = (double)bf16_at(w, jj);
+      acc += g * g * X.rinv[i] * X.cinv[e + jj - i * (uint32_t)X.C];
     }
   }
   for (int o = 1; o < 64; o <<= 1) acc += __shfl_xor(acc, o, 64);
@@ -366,14 +739,14 @@ __device__ __forceinline__ void usq_item_any(const F2D& X, uint32_t item) {
 
 __device__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w);
 
-// U^2 sum of one row tile of a tensor whose rows are 16-byte runs: kURows
-// rows x kUCols columns, lane l taking columns c .. c+7 (c = band start +
-// 8 l) of every row of the tile. The lane loads its 8 column factors once and
-// all its rows' gradient runs at once (8 KiB per wave in flight), and each
-// row's factor is one scalar load; per element the flat items instead load a
-// column factor (4 bytes) for every 2-byte gradient. Lane order: row by row,
-// columns in order; then the wave's xor tree. Lanes past the last column and
-// rows past the last row hold g = 0 and add exact zeros.
+// Sum of g^2 / (r_i c_j) over one row tile of a tensor whose rows are 16-byte
+// runs (and that does not take the row-strip pass): kURows rows x kUCols
+// columns, lane l taking columns c .. c+7 (c = band start + 8 l) of every row
+// of the tile. The lane loads its 8 column factors once and all its rows'
+// gradient runs at once (8 KiB per wave in flight), and each row's factor is
+// one scalar load. Lane order: row by row, columns in order; then the wave's
+// xor tree. Lanes past the last column and rows past the last row hold g = 0
+// and add exact zeros.
 __device__ __forceinline__ void usq_row_tile(const FPlan& P, uint32_t w) {
   uint32_t begin;
   const F2D& X = P.t2[find_end(P.rt_end, P.n2, w, begin)];
@@ -382,13 +755,9 @@ __device__ __forceinline__ void usq_row_tile(const FPlan& P, uint32_t w) {
   const int c = tc * kUCols + (int)threadIdx.x * 8;
   const int r0 = tr * kURows;
   const bool col_ok = c < X.C;
-  float kap[8];
-  if (col_ok) {
-    load_kap8(X.kap, (uint32_t)c, kap);
-  } else {
+  double ci[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kap[j] = 0.0f;
-  }
+  for (int j = 0; j < 8; ++j) ci[j] = col_ok ? X.cinv[c + j] : 0.0;
   uint4 gv[kURows];
 #pragma unroll
   for (int k = 0; k < kURows; ++k) {
@@ -399,12 +768,12 @@ __device__ __forceinline__ void usq_row_tile(const FPlan& P, uint32_t w) {
 #pragma unroll
   for (int k = 0; k < kURows; ++k) {
     const int r = r0 + k;
-    const float rho = r < X.R ? X.rho[r] : 0.0f;
+    const double ri = r < X.R ? X.rinv[r] : 0.0;
     const uint32_t g[4] = {gv[k].x, gv[k].y, gv[k].z, gv[k].w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float U = (bf16_at(g, j) * rho) * kap[j];
-      acc += (double)U * (double)U;
+      const double gd = (double)bf16_at(g, j);
+      acc += gd * gd * ri * ci[j];
     }
   }
   for (int o = 1; o < 64; o <<= 1) acc += __shfl_xor(acc, o, 64);
@@ -613,8 +982,7 @@ __device__ __forceinline__ void f1_stats_item(const FPlan& P, const FScalars& S,
       const float q = g * g + S.EPS1;
       const float v = __builtin_fmaf(S.B2, v0, S.C2 * q);
       X.v[e + j] = v;
-      const float U = g * (1.0f / __builtin_sqrtf(v));
-      acc += (double)U * (double)U;
+      acc += (double)g * (double)g / (double)v;   // U^2 = g^2 / v in double
     }
   }
   for (int o = 1; o < 64; o <<= 1) acc += __shfl_xor(acc, o, 64);
@@ -629,9 +997,13 @@ __global__ __launch_bounds__(kClipT) void k_f_clip(FPlan P, FScalars S) {
   int np;
   double n;
   float* f;
+  double scale = 1.0;   // 2-D: parts are sums of g^2 / (r_i c_j); times mean(r)
   if ((int)blockIdx.x < P.n2) {
     const F2D& X = P.t2[blockIdx.x];
     parts = X.upart; np = X.npart; n = (double)X.R * (double)X.C; f = X.f;
+    double s = 0.0;
+    for (int q = 0; q < X.nrw; ++q) s += X.rpart[q];
+    scale = s / (double)X.R;
   } else {
     const F1D& X = P.t1[blockIdx.x - P.n2];
     parts = X.upart; np = X.nitems; n = (double)X.n; f = X.f;
@@ -647,7 +1019,7 @@ __global__ __launch_bounds__(kClipT) void k_f_clip(FPlan P, FScalars S) {
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const double rms = sqrt(red[0] / n);
+    const double rms = sqrt(red[0] * scale / n);
     const double r = rms / S.clip;
     *f = (float)(S.lr / (r > 1.0 ? r : 1.0));
   }
@@ -808,6 +1180,7 @@ ps_status launch_all(const FPlan& P, const FScalars& S, hipStream_t s) {
   // U^2 row tiles, flat items without 16-byte rows and the 1-D stats items
   // share a launch (their sum is checked on the host to fit 32 bits)
   const uint32_t n_usq = P.n_rt + P.n_items2u + P.n_items;
+  if (P.n_groups) hipLaunchKernelGGL(k_f_strip, dim3(P.n_groups), dim3(kSNT), 0, s, P, S);
   if (P.n_tiles) hipLaunchKernelGGL(k_f_stats, dim3(P.n_tiles), dim3(kT), 0, s, P, S);
   if (P.n_rc) hipLaunchKernelGGL(k_f_rowcol, dim3(P.n_rc), dim3(kT), 0, s, P, S);
   if (P.n_rc) hipLaunchKernelGGL(k_f_factors, dim3(P.n_rc), dim3(kT), 0, s, P);

@@ -49,8 +49,70 @@ struct Layout {
   std::vector<F2D> t2;
   std::vector<F1D> t1;
   std::vector<uint32_t> tile_end, rc_end, tile_nf_end, item2_end, item_end, rt_end, tile_u_end, item2u_end;
+  std::vector<uint32_t> seg_end;   // [groups] prefix ends over segs
+  std::vector<FSeg> segs;
+  std::vector<int32_t> nseg;       // per caller tensor: strip segments (0 if not in the strip pass)
+  std::vector<std::vector<FSeg>> by_group;
   size_t bytes = 0;
+  void clear() {
+    t2.clear(); t1.clear(); tile_end.clear(); rc_end.clear(); tile_nf_end.clear(); item2_end.clear();
+    item_end.clear(); rt_end.clear(); tile_u_end.clear(); item2u_end.clear(); seg_end.clear(); segs.clear();
+    nseg.clear(); bytes = 0;
+  }
 };
+
+// 2-D tensors whose statistics take the row-strip pass: rows of 16-byte runs
+// that a wave's 64 lanes cover in whole multiples (C % 512 == 0), at most two
+// runs per thread of the workgroup, and flat (fewer than 2^31 elements).
+bool strip_ok(const ps_tensor& x) {
+  return x.grad != nullptr && x.numel > 0 && x.numel < (int64_t(1) << 31) && x.rows >= 1 && x.cols >= 1 &&
+         x.rows <= 0x7FFFFFFF && x.cols <= 0x7FFFFFFF && x.rows * x.cols == x.numel && x.cols % 512 == 0 &&
+         x.cols <= kStripMaxC;
+}
+
+// Splits the rows of the strip tensors, taken in list order as one sequence,
+// into at most kStripGroups groups of nearly equal element counts (a row goes
+// to the group its first element falls in), and each group into segments of
+// one tensor's consecutive rows. Depends on the shapes only.
+void strip_partition(const ps_tensor* t, int32_t n, Layout& L) {
+  L.nseg.assign((size_t)std::max(n, 0), 0);
+  std::vector<int32_t> t2idx((size_t)std::max(n, 0), -1);
+  int32_t k2 = 0;
+  uint64_t total = 0, rows = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const ps_tensor& x = t[i];
+    if (x.numel <= 0 || x.grad == nullptr || (x.rows == 0 && x.cols == 0)) continue;
+    t2idx[i] = k2++;
+    if (strip_ok(x)) {
+      total += (uint64_t)x.numel;
+      rows += (uint64_t)x.rows;
+    }
+  }
+  const uint64_t G = std::min<uint64_t>(kStripGroups, rows);
+  if (G == 0) return;
+  // group g takes the rows whose first element lies in [B(g), B(g + 1))
+  auto B = [&](uint64_t g) { return (uint64_t)(((unsigned __int128)total * g) / G); };
+  auto cdiv = [](uint64_t a, uint64_t b) { return (a + b - 1) / b; };
+  L.by_group.resize(G);
+  for (auto& v : L.by_group) v.clear();
+  uint64_t cum = 0, g = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const ps_tensor& x = t[i];
+    if (t2idx[i] < 0 || !strip_ok(x)) continue;
+    const uint64_t C = (uint64_t)x.cols, R = (uint64_t)x.rows, end = cum + R * C;
+    while (g + 1 < G && B(g + 1) <= cum) ++g;
+    for (uint64_t h = g; h < G && B(h) < end; ++h) {
+      const uint64_t r0 = B(h) > cum ? std::min(R, cdiv(B(h) - cum, C)) : 0;
+      const uint64_t r1 = h + 1 == G ? R : (B(h + 1) > cum ? std::min(R, cdiv(B(h + 1) - cum, C)) : 0);
+      if (r1 > r0) L.by_group[h].push_back(FSeg{(uint32_t)t2idx[i], (int32_t)r0, (int32_t)r1, L.nseg[i]++});
+    }
+    cum = end;
+  }
+  for (uint64_t h = 0; h < G; ++h) {
+    L.segs.insert(L.segs.end(), L.by_group[h].begin(), L.by_group[h].end());
+    L.seg_end.push_back((uint32_t)L.segs.size());
+  }
+}
 
 // Validates the list and lays out the workspace starting at `ws` (which may be
 // NULL when only the size is wanted). fm: a first moment is kept in m_code /
@@ -60,6 +122,7 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, 
   if (n > 0 && !t) return fail(PS_ERR_INVALID_ARG, "tensors is NULL");
   uint64_t tiles = 0, rc = 0, items = 0, tiles_nf = 0, items2 = 0, rt = 0, tiles_u = 0, items2u = 0;
   size_t off = 0;
+  strip_partition(t, n, L);
   auto take = [&](size_t bytes) { char* p = ws ? ws + off : nullptr; off += up(bytes); return p; };
   for (int32_t i = 0; i < n; ++i) {
     const ps_tensor& x = t[i];
@@ -84,6 +147,9 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, 
       d.nrw = (d.R + kFRowColChunk - 1) / kFRowColChunk;
       d.ncw = (d.C + kFRowColChunk - 1) / kFRowColChunk;
       d.vec = (d.C % 8) == 0;
+      d.strip = L.nseg[i] > 0;
+      d.nrp = d.strip ? 1 : d.ntc;
+      if (d.strip) d.sntr = L.nseg[i];
       // Flat items: every tensor below 2^31 elements whose rows are 16-byte
       // runs, and with a first moment (per-256 blocks of the flattened index)
       // also the others, whose items then take per-element row/column factors.
@@ -98,26 +164,32 @@ ps_status plan(const ps_tensor* t, int32_t n, char* ws, bool fm, bool residual, 
       // (first moment) or the stats tiles.
       d.nuc = d.vec ? (d.C + kUCols - 1) / kUCols : 0;
       const int32_t nrt = d.vec ? ((d.R + kURows - 1) / kURows) * d.nuc : 0;
-      d.npart = d.vec ? nrt : d.flat ? d.nitems : d.ntr * d.ntc;
+      d.npart = d.strip ? d.ncw : d.vec ? nrt : d.flat ? d.nitems : d.ntr * d.ntc;
       // The U^2 partials get room for every form a tensor of this shape can
       // take, so the workspace layout, and ps_factored_workspace_size, do not
       // depend on whether a first moment is kept.
       const int64_t items_any = x.numel < (int64_t(1) << 31) ? (x.numel + kItemElems - 1) / kItemElems : 0;
-      const int64_t upart_n = d.vec ? (int64_t)nrt : std::max<int64_t>(items_any, (int64_t)d.ntr * d.ntc);
-      d.rowpart = (double*)take(sizeof(double) * (size_t)d.ntc * d.R);
+      const int64_t upart_n = d.strip ? (int64_t)d.ncw
+                              : d.vec ? (int64_t)nrt : std::max<int64_t>(items_any, (int64_t)d.ntr * d.ntc);
+      d.rowpart = (double*)take(sizeof(double) * (size_t)d.nrp * d.R);
       d.colpart = (double*)take(sizeof(double) * (size_t)d.sntr * d.C);
+      d.qpart = d.strip ? (double*)take(sizeof(double) * (size_t)d.sntr * d.C) : nullptr;
       d.rpart = (double*)take(sizeof(double) * (size_t)d.nrw);
       d.rho = (float*)take(sizeof(float) * (size_t)d.R);
       d.kap = (float*)take(sizeof(float) * (size_t)d.C);
+      d.rinv = d.strip ? nullptr : (double*)take(sizeof(double) * (size_t)d.R);
+      d.cinv = d.strip ? nullptr : (double*)take(sizeof(double) * (size_t)d.C);
       d.upart = (double*)take(sizeof(double) * (size_t)upart_n);
       d.f = (float*)take(sizeof(float));
-      tiles += (uint64_t)d.sntr * d.ntc;
+      if (!d.strip) tiles += (uint64_t)d.sntr * d.ntc;
       rc += (uint64_t)d.nrw + d.ncw;
       if (d.flat)
         items2 += (uint64_t)((x.numel + kApplyItemElems - 1) / kApplyItemElems);
       else
         tiles_nf += (uint64_t)d.ntr * d.ntc;
-      if (d.vec)
+      if (d.strip)
+        ;   // sum of U^2 from the strip pass's column partials
+      else if (d.vec)
         rt += (uint64_t)nrt;
       else if (d.flat)
         items2u += (uint64_t)d.nitems;
@@ -167,23 +239,26 @@ ps_status factored_prepare(const ps_tensor* t, int32_t n, const ps_factored_hpar
   const bool fm = hp->beta1 != 0.0;
   const bool residual = hp->split_mode != PS_SPLIT_STOCHASTIC;
   thread_local Layout W;
-  W.t2.clear(); W.t1.clear(); W.tile_end.clear(); W.rc_end.clear(); W.tile_nf_end.clear(); W.item2_end.clear();
-  W.item_end.clear(); W.rt_end.clear(); W.tile_u_end.clear(); W.item2u_end.clear(); W.bytes = 0;
+  W.clear();
   if (ps_status s = plan(t, n, ws, fm, residual, W)) return s;
   c.empty = W.t2.empty() && W.t1.empty();
   c.ws_bytes = W.bytes;
-  // the plan image: F2D[n2] | F1D[n1] | the seven [n2] prefix-end lists | item_end[n1]
+  // the plan image: F2D[n2] | F1D[n1] | the seven [n2] prefix-end lists |
+  // item_end[n1] | seg_end[groups] | FSeg[segments]
   const size_t b2 = W.t2.size() * sizeof(F2D), b1 = W.t1.size() * sizeof(F1D);
   const size_t e2 = W.t2.size() * sizeof(uint32_t), e1 = W.t1.size() * sizeof(uint32_t);
+  const size_t eg = W.seg_end.size() * sizeof(uint32_t), bs = W.segs.size() * sizeof(FSeg);
   const std::vector<uint32_t>* lists2[7] = {&W.tile_end, &W.rc_end, &W.tile_nf_end, &W.item2_end,
                                             &W.rt_end, &W.tile_u_end, &W.item2u_end};
-  c.image.resize(b2 + b1 + 7 * e2 + e1);
+  c.image.resize(b2 + b1 + 7 * e2 + e1 + eg + bs);
   unsigned char* p = c.image.data();
   if (b2) memcpy(p, W.t2.data(), b2);
   if (b1) memcpy(p + b2, W.t1.data(), b1);
   if (e2)
     for (int k = 0; k < 7; ++k) memcpy(p + b2 + b1 + k * e2, lists2[k]->data(), e2);
   if (e1) memcpy(p + b2 + b1 + 7 * e2, W.item_end.data(), e1);
+  if (eg) memcpy(p + b2 + b1 + 7 * e2 + e1, W.seg_end.data(), eg);
+  if (bs) memcpy(p + b2 + b1 + 7 * e2 + e1 + eg, W.segs.data(), bs);
   // table offsets within the image (factored_bind adds the device base)
   FPlan& pl = c.plan;
   pl.t2 = (const F2D*)0;
@@ -196,6 +271,9 @@ ps_status factored_prepare(const ps_tensor* t, int32_t n, const ps_factored_hpar
   pl.tile_u_end = (const uint32_t*)(b2 + b1 + 5 * e2);
   pl.item2u_end = (const uint32_t*)(b2 + b1 + 6 * e2);
   pl.item_end = (const uint32_t*)(b2 + b1 + 7 * e2);
+  pl.seg_end = (const uint32_t*)(b2 + b1 + 7 * e2 + e1);
+  pl.segs = (const FSeg*)(b2 + b1 + 7 * e2 + e1 + eg);
+  pl.n_groups = (uint32_t)W.seg_end.size();
   pl.n2 = (int32_t)W.t2.size();
   pl.n1 = (int32_t)W.t1.size();
   pl.n_tiles = W.tile_end.empty() ? 0 : W.tile_end.back();
@@ -229,9 +307,10 @@ void factored_bind(FactoredCall& c, const void* dev_image) {
   FPlan& pl = c.plan;
   pl.t2 = (const F2D*)(base + (uintptr_t)pl.t2);
   pl.t1 = (const F1D*)(base + (uintptr_t)pl.t1);
-  const uint32_t** lists[8] = {&pl.tile_end, &pl.rc_end, &pl.tile_nf_end, &pl.item2_end,
-                               &pl.rt_end, &pl.tile_u_end, &pl.item2u_end, &pl.item_end};
+  const uint32_t** lists[9] = {&pl.tile_end, &pl.rc_end, &pl.tile_nf_end, &pl.item2_end, &pl.rt_end,
+                               &pl.tile_u_end, &pl.item2u_end, &pl.item_end, &pl.seg_end};
   for (const uint32_t** q : lists) *q = (const uint32_t*)(base + (uintptr_t)*q);
+  pl.segs = (const FSeg*)(base + (uintptr_t)pl.segs);
 }
 
 }  // namespace ps

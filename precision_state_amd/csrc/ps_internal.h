@@ -89,6 +89,11 @@ constexpr int kSTileRows = 256;    // stats tile: 256 rows x 256 columns, 4 chun
 constexpr int kFRowColChunk = 256; // rows or columns per finalize workgroup
 constexpr int kURows = 8;          // U^2 row tile (C % 8 == 0): 8 rows x 512 columns, one 64-lane wave
 constexpr int kUCols = 512;
+// Row-strip stats pass (tensors with C % 512 == 0 and C <= kStripMaxC): one
+// kSNT-thread workgroup per group of whole rows, at most kStripGroups groups.
+constexpr int kSNT = 768;
+constexpr int kStripGroups = 256;
+constexpr int kStripMaxC = 2 * kSNT * 8;
 
 // 2-D tensor [R, C] of a factored step; workspace pointers are per tensor.
 struct F2D {
@@ -97,12 +102,15 @@ struct F2D {
   const uint16_t* g;
   float* row;        // [R] EMA of row means (caller state)
   float* col;        // [C] EMA of column means (caller state)
-  double* rowpart;   // [ntc][R] row sums per tile column
-  double* colpart;   // [sntr][C] column sums per 256-row stats band
+  double* rowpart;   // [nrp][R] row sums per tile column (strip: [1][R], whole rows)
+  double* colpart;   // [sntr][C] column sums per 256-row stats band (strip: per row segment)
+  double* qpart;     // strip: [sntr][C] column sums of g^2 / r_i per row segment; else NULL
   double* rpart;     // [nrw] sums of the new row EMAs per 256-row chunk
   float* rho;        // [R] 1/sqrt(r_i / mean r)
   float* kap;        // [C] 1/sqrt(c_j)
-  double* upart;     // [ntr * ntc] sums of U^2 per tile
+  double* rinv;      // [R] 1/r_i in double, for the U^2 pass (NULL if strip)
+  double* cinv;      // [C] 1/c_j in double, for the U^2 pass (NULL if strip)
+  double* upart;     // sums of g^2 / (r_i c_j) per column chunk, row tile, item or tile (times mean r: sum of U^2)
   float* f;          // clip factor lr / max(1, RMS(U)/d)
   uint16_t* mc;      // first moment codes (signed kind) or NULL
   float* ms;         // first moment block scales or NULL
@@ -112,9 +120,18 @@ struct F2D {
   int32_t vec;       // C % 8 == 0: 16-byte row segments
   int32_t flat;      // R*C < 2^31 and (vec or a first moment): U^2 and apply passes run over 1024-element items
   int32_t nitems;    // flat: items of 1024 elements
-  int32_t npart;     // entries of upart: U^2 row tiles if vec, else nitems if flat, else ntr * ntc
+  int32_t npart;     // entries of upart: column chunks if strip, U^2 row tiles if vec, else nitems if flat, else ntr * ntc
   uint32_t tid;      // index in the caller's list (stochastic rounding stream key)
-  uint32_t pad;
+  int32_t strip;     // stats in the row-strip pass; sum of U^2 = rbar * sum_j Q_j / c_j (upart: per column chunk)
+  int32_t nrp;       // row partials per row in rowpart (ntc, or 1 for strip)
+  int32_t pad;
+};
+
+// Rows [row0, row1) of 2-D tensor t2[t], one segment of a strip-pass group;
+// its column partials go to row `slot` of the tensor's colpart and qpart.
+struct FSeg {
+  uint32_t t;
+  int32_t row0, row1, slot;
 };
 
 // 1-D tensor of a factored step (second moment kept in the uint16 codec).
@@ -156,15 +173,19 @@ struct FPlan {      // device tables of one factored call
   const uint32_t* item2u_end;  // [n2] prefix ends over U^2 items of flat tensors that are not vec
   const F1D* t1;
   const uint32_t* item_end;    // [n1] prefix ends over 1-D items
+  const uint32_t* seg_end;     // [n_groups] prefix ends over strip segments
+  const FSeg* segs;            // strip segments, group by group
   int32_t n2, n1;
   uint32_t n_tiles, n_rc, n_items, n_tiles_nf, n_items2;
   uint32_t n_rt, n_tiles_u, n_items2u;
+  uint32_t n_groups;           // workgroups of the strip pass
 };
 
 ps_status launch_factored(const FPlan& plan, const FScalars& sc, int split_mode, hipStream_t s);
 
 // One factored call prepared on the host (ps_factored.cpp): the device plan's
-// image (F2D[n2] | F1D[n1] | seven [n2] prefix-end lists | item_end[n1]) with
+// image (F2D[n2] | F1D[n1] | seven [n2] prefix-end lists | item_end[n1] |
+// seg_end[n_groups] | FSeg[]) with
 // its workspace pointers final, the workspace size and the scalars. The
 // plan's table pointers are offsets into the image until factored_bind.
 struct FactoredCall {

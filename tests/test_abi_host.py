@@ -121,9 +121,14 @@ def test_factored_workspace_size_and_validation(ps):
     size = ctypes.c_size_t(0)
     arr = (ps.CTensor * 2)(_frec(ps), _frec(ps, n=300, rows=0, cols=0))
     assert L.ps_factored_workspace_size(arr, 2, ctypes.byref(size)) == 0
-    # 2-D 32x32: rowpart 1x32, colpart 1x32 doubles, rpart 1, rho 32, kap 32 floats, upart 1, f; 1-D 300:
-    # v 300 floats, upart 1, f -- each region rounded up to 256 bytes
-    assert size.value == 256 * (1 + 1 + 1 + 1 + 1 + 1 + 1) + 1280 + 256 + 256
+    # 2-D 32x32: rowpart 1x32, colpart 1x32 doubles, rpart 1, rho 32, kap 32 floats, rinv 32, cinv 32
+    # doubles, upart 1, f; 1-D 300: v 300 floats, upart 1, f -- each region rounded up to 256 bytes
+    assert size.value == 256 * (1 + 1 + 1 + 1 + 1 + 1 + 1 + 1 + 1) + 1280 + 256 + 256
+    # 4x512 takes the row-strip pass: 4 rows, so 4 groups of one row each and 4 segments; rowpart 4,
+    # colpart and qpart 4x512 doubles, rpart 1, rho 4, kap 512 floats, upart 2 column chunks, f
+    strip = (ps.CTensor * 1)(_frec(ps, n=2048, rows=4, cols=512))
+    assert L.ps_factored_workspace_size(strip, 1, ctypes.byref(size)) == 0
+    assert size.value == 256 + 16384 + 16384 + 256 + 256 + 2048 + 256 + 256
     bad = (ps.CTensor * 1)(_frec(ps, rows=33))
     assert L.ps_factored_workspace_size(bad, 1, ctypes.byref(size)) == 3
     bad = (ps.CTensor * 1)(_frec(ps, row_ema=0))
@@ -183,7 +188,7 @@ def test_noalloc_factored_step_rejects_on_host(ps):
     any HIP call: a list whose workspace exceeds the built-in scratch, bad
     hyperparameters and bad shapes are rejected here, with no GPU."""
     L = ps.lib()
-    big = (ps.CTensor * 1)(ps.CTensor(256, 256, 256, 256, 256, 256, 256, 256, 256, 262144 * 4096, 262144, 4096, 0, 0))
+    big = (ps.CTensor * 1)(ps.CTensor(256, 256, 256, 256, 256, 256, 256, 256, 256, 1048576 * 4096, 1048576, 4096, 0, 0))
     h = ps.FactoredHParams().c()
     assert L.ps_factored_step_noalloc(big, 1, ctypes.byref(h), 1, None) == 7      # PS_ERR_WORKSPACE
     assert "scratch" in ps.last_error()

@@ -1,10 +1,12 @@
 """GPU parity of the factored-second-moment step (sd-scripts commit 7983d3d
 'Fused backward pass', adafactor_step_param; konstmish/prodigy PR #25) against
 the oracle. Bar: master weights within 4 fp32 ulp after 10 steps, row/column
-EMAs within 1 ulp, v codes within 1; the kernels use the oracle's operation
-order everywhere except the order of the double-precision sums (fixed trees
-instead of index order), so exact agreement is expected and mismatch counts
-are reported."""
+EMAs within 1 ulp, v codes within 1. The kernels use the oracle's operation
+order except for the order of the double-precision sums (fixed trees instead
+of index order) and, for tensors whose rows are whole multiples of 512
+columns, the sum of U^2, which they form as rbar * sum_j Q_j / c_j with
+Q_j = sum_i g_ij^2 / r_i in double (the same quantity, without the fp32
+rounding of rho_i, kap_j and U); mismatch counts are reported."""
 import os
 from concurrent.futures import ThreadPoolExecutor
 
@@ -179,3 +181,35 @@ def test_single_one_d_tensor_calls(split_mode):
             oracle.factored_step(h, host_grad(n, 21, i, t, 0.01), 0, 0, _ofhp(hp, 0), t)
         torch.cuda.synchronize()
         _compare(d, h, 0, shape.name, first_moment=True)
+
+
+# Row-strip stats pass (C % 512 == 0, C <= 12288): 12, 6, 2 and 1 rows per
+# step, idle waves (C = 4096), a partial second run per thread (C = 8192),
+# two full runs (C = 12288), steps past a segment's last row, a tensor cut
+# across many groups and groups holding several tensors, next to a tensor of
+# the tile path and a 1-D tensor.
+STRIP = [synth.Shape("s512x1", 1, 512, 512), synth.Shape("s512x13", 13, 512, 13 * 512),
+         synth.Shape("s1024x7", 7, 1024, 7 * 1024), synth.Shape("s3072x3", 3, 3072, 3 * 3072),
+         synth.Shape("s3072x257", 257, 3072, 257 * 3072), synth.Shape("s4096x5", 5, 4096, 5 * 4096),
+         synth.Shape("s8192x3", 3, 8192, 3 * 8192), synth.Shape("s12288x33", 33, 12288, 33 * 12288),
+         synth.Shape("s1024x2000", 2000, 1024, 2000 * 1024), synth.Shape("t520x9", 9, 520, 9 * 520),
+         synth.Shape("v3000", 0, 0, 3000)]
+
+
+@pytest.mark.parametrize("split_mode,beta1", [(ps.SPLIT_TRUNC, 0.0), (ps.SPLIT_NEAREST_AWAY, 0.9),
+                                              (ps.SPLIT_STOCHASTIC, 0.9)])
+def test_factored_row_strip_shapes(split_mode, beta1):
+    """Tensors of the row-strip pass in every thread layout it has (more
+    than 256 rows in all, so the rows are cut into 256 groups), 5 steps,
+    wd 0.01, a zero gradient in one of them; every tensor against the oracle."""
+    hp = ps.FactoredHParams(split_mode=split_mode, lr=1e-4, weight_decay=0.01, beta1=beta1, seed=31)
+    _run(STRIP, hp, 5, 17, 0.01, zero_grad=(2,))
+
+
+def test_factored_row_strip_few_rows():
+    """Fewer rows than groups (one group per row), a 12288-column tensor of
+    one row, clip threshold 4 with the schedule."""
+    shapes = [synth.Shape("a", 3, 3072, 3 * 3072), synth.Shape("b", 1, 12288, 12288),
+              synth.Shape("c", 2, 1536, 2 * 1536), synth.Shape("v", 0, 0, 700)]
+    hp = ps.FactoredHParams(lr=1e-4, clip_threshold=4.0, decay_rate=-0.8, seed=5)
+    _run(shapes, hp, 4, 23, 0.01)

@@ -51,11 +51,18 @@ def test_noalloc_equals_workspace_call_twice_second_smaller():
 
 
 def test_noalloc_rejects_a_list_beyond_the_scratch():
+    """The records carry placeholder addresses, so the call must be turned away
+    on the host: the list's workspace alone is checked to exceed the scratch
+    (a host-only size query) before the call is made. A 262144 x 4104 tensor
+    takes the statistics tiles, whose row sums alone need 17 x 262144 doubles
+    (34 MiB)."""
     blk = synth.WORKLOADS["flux_double_block"]()
-    shapes = blk + blk                                   # 43.6 MiB of workspace
+    shapes = blk + [synth.Shape("wide", 262144, 4104, 262144 * 4104)]
     recs = (ps.CTensor * len(shapes))()
     for i, s in enumerate(shapes):
         recs[i] = ps.CTensor(256, 256, 256, 256, 256, 256, 256, 256, 256, s.numel, s.rows, s.cols, 0, 0)
+    need = ps.factored_workspace_size(None, records=(recs, len(shapes)))
+    assert need > ps.NOALLOC_SCRATCH_BYTES, need          # else the call below would reach the GPU
     with pytest.raises(ps.PSError) as e:
         ps.factored_step_noalloc(None, None, ps.FactoredHParams(), 1, records=(recs, len(shapes)))
     assert e.value.status == 7 and "scratch" in str(e.value)
