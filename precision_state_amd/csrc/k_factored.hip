@@ -439,22 +439,30 @@ __device__ __forceinline__ void strip_segment(const StripArgs& A, int& par) {
     const int h = b % 3;
     const uint32_t abuf = lds_addr(&s_buf[h][t]);
 
-    // q = g^2 + eps1 into the column sums and this lane's row partials
+    // g^2 (exact in fp32 for a bf16 g) and q = g^2 + eps1 into the column
+    // sums and this lane's row partials; g^2 stays in registers for the
+    // second half
     u32x4 x[4];
     lds_read_runs(abuf, x);
+    float g2[D][K][8];
     double rp[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       rp[d] = 0.0;
-      if (!(act && row_of(b, d) < row1)) continue;   // wave-uniform
+      const bool ok = act && row_of(b, d) < row1;   // wave-uniform
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const uint32_t w[4] = {x[d * K + k].x, x[d * K + k].y, x[d * K + k].z, x[d * K + k].w};
-        double sq = 0.0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float g = bf16_at(w, j);
-          const double q = (double)__builtin_fmaf(g, g, A.EPS1);
+          g2[d][k][j] = g * g;
+        }
+        if (!ok) continue;
+        double sq = 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const double q = (double)(g2[d][k][j] + A.EPS1);
           P[k][j] += q;
           sq += q;
         }
@@ -468,31 +476,29 @@ __device__ __forceinline__ void strip_segment(const StripArgs& A, int& par) {
     if ((lane & (64 / D - 1)) == 0) s_wsum[par][lane / (64 / D)][wave] = ws;
     lds_barrier();
 
-    // lane d: step d's row sum in wave order, the new row EMA and 1 / r_i
+    // lane d: step d's row sum in wave order, the new row EMA (as the
+    // finalize kernel forms it) and 1 / r_i (reciprocal and two Newton steps)
     double inv_l = 0.0;
     if (lane < D) {
       const int i = row_of(b, lane);
       double sum = 0.0;
       for (int q = 0; q < nwr; ++q) sum += s_wsum[par][lane][w0 + q];
       const float mean = (float)(sum / (double)C);
-      const float r = __builtin_fmaf(A.B2, lds_read4(lds_addr(&s_ro[h][lane][wave])), A.C2 * mean);
-      inv_l = 1.0 / (double)r;
+      const double r = (double)__builtin_fmaf(A.B2, lds_read4(lds_addr(&s_ro[h][lane][wave])), A.C2 * mean);
+      double y = __builtin_amdgcn_rcp(r);
+      y = __builtin_fma(y, __builtin_fma(-r, y, 1.0), y);
+      inv_l = __builtin_fma(y, __builtin_fma(-r, y, 1.0), y);
       if (act && i < row1 && wave == w0) A.rowpart[i] = sum;
     }
     // then g^2 / r_i into the column sums
-    lds_read_runs(abuf, x);
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (!(act && row_of(b, d) < row1)) continue;   // wave-uniform
       const double inv = mk64(__builtin_amdgcn_readlane(lo32(inv_l), d), __builtin_amdgcn_readlane(hi32(inv_l), d));
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const uint32_t w[4] = {x[d * K + k].x, x[d * K + k].y, x[d * K + k].z, x[d * K + k].w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float g = bf16_at(w, j);
-          Q[k][j] = __builtin_fma((double)(g * g), inv, Q[k][j]);
-        }
+        for (int j = 0; j < 8; ++j) Q[k][j] = __builtin_fma((double)g2[d][k][j], inv, Q[k][j]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) pin(Q[k][j]);
       }
