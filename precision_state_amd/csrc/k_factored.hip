@@ -459,14 +459,17 @@ __device__ __forceinline__ void strip_segment(const StripArgs& A, int& par) {
           g2[d][k][j] = g * g;
         }
         if (!ok) continue;
-        double sq = 0.0;
+        double sq;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const double q = (double)(g2[d][k][j] + A.EPS1);
           P[k][j] += q;
-          sq += q;
+          sq = j ? sq + q : q;
         }
-        rp[d] += (k == 0 || run1) ? sq : 0.0;
+        if (k == 0)
+          rp[d] = sq;
+        else
+          rp[d] += run1 ? sq : 0.0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) pin(P[k][j]);
         pin(rp[d]);
@@ -575,7 +578,16 @@ __global__ __launch_bounds__(kSNT) void k_f_strip(FPlan P, FScalars S) {
 }
 
 // ---- pass 2: row/column EMAs and chunk sums of the new row EMA -------------
+__device__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w, int lane);
+
+// Workgroups past the finalize ones (launched only when no U^2 pass runs)
+// take the 1-D tensors' stats items, one per wave.
 __global__ __launch_bounds__(kT) void k_f_rowcol(FPlan P, FScalars S) {
+  if (blockIdx.x >= P.n_rc) {   // uniform
+    const uint32_t w = (blockIdx.x - P.n_rc) * (uint32_t)(kT / 64) + (threadIdx.x >> 6);
+    if (w < P.n_items) f1_stats_item(P, S, w, (int)(threadIdx.x & 63));
+    return;
+  }
   uint32_t begin;
   const F2D& X = P.t2[find_end(P.rc_end, P.n2, blockIdx.x, begin)];
   const int w = (int)(blockIdx.x - begin);
@@ -619,7 +631,18 @@ __global__ __launch_bounds__(kT) void k_f_rowcol(FPlan P, FScalars S) {
 }
 
 // ---- pass 3: factors of V^-1/2 ----------------------------------------------
-__global__ __launch_bounds__(kT) void k_f_factors(FPlan P) {
+template <int NT>
+__device__ void clip_one(const FPlan& P, const FScalars& S, int idx, double* red);
+
+// Workgroups past the factor ones (launched only when no U^2 pass runs, so
+// every sum of U^2 is complete after the finalize launch) take the clip
+// factors, one tensor each.
+__global__ __launch_bounds__(kT) void k_f_factors(FPlan P, FScalars S) {
+  if (blockIdx.x >= P.n_rc) {   // uniform
+    __shared__ double red[kT];
+    clip_one<kT>(P, S, (int)(blockIdx.x - P.n_rc), red);
+    return;
+  }
   uint32_t begin;
   const F2D& X = P.t2[find_end(P.rc_end, P.n2, blockIdx.x, begin)];
   const int w = (int)(blockIdx.x - begin);
@@ -743,7 +766,7 @@ __device__ __forceinline__ void usq_item_any(const F2D& X, uint32_t item) {
   if (threadIdx.x == 0) X.upart[item] = acc;
 }
 
-__device__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w);
+__device__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w, int lane);
 
 // Sum of g^2 / (r_i c_j) over one row tile of a tensor whose rows are 16-byte
 // runs (and that does not take the row-strip pass): kURows rows x kUCols
@@ -786,7 +809,7 @@ __device__ __forceinline__ void usq_row_tile(const FPlan& P, uint32_t w) {
   if (threadIdx.x == 0) X.upart[t] = acc;
 }
 
-__device__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w);
+__device__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w, int lane);
 
 // The U^2 pass in one launch of 64-lane workgroups: the row tiles of tensors
 // whose rows are 16-byte runs, then the flat items of the other tensors that
@@ -800,7 +823,7 @@ __global__ __launch_bounds__(64) void k_f_usq_flat(FPlan P, FScalars S) {
   }
   const uint32_t w2 = wg - P.n_rt;
   if (w2 >= P.n_items2u) {   // uniform: an item of a 1-D tensor
-    f1_stats_item(P, S, w2 - P.n_items2u);
+    f1_stats_item(P, S, w2 - P.n_items2u, (int)threadIdx.x);
     return;
   }
   uint32_t begin;
@@ -968,14 +991,14 @@ __global__ __launch_bounds__(64) void k_f_apply_flat(FPlan P, FScalars S) {
   if ((threadIdx.x & 31) == 0 && blk_ok) X.ms[blk] = sm;
 }
 
-// 1-D tensors, one 1024-element item per 64-lane workgroup (item w of the
-// 1-D list): decode v, its EMA, sum of U^2. These items ride at the end of the
-// U^2 launch.
-__device__ __forceinline__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w) {
+// 1-D tensors, one 1024-element item per 64-lane wave (item w of the 1-D
+// list): decode v, its EMA, sum of U^2. These items ride at the end of the
+// finalize launch, or of the U^2 launch when one runs.
+__device__ __forceinline__ void f1_stats_item(const FPlan& P, const FScalars& S, uint32_t w, int lane) {
   uint32_t begin;
   const F1D& X = P.t1[find_end(P.item_end, P.n1, w, begin)];
   const int64_t elem0 = (int64_t)(w - begin) * kItemElems;
-  const int lane = threadIdx.x, b = lane >> 4, r = lane & 15;
+  const int b = lane >> 4, r = lane & 15;
   const int64_t blk = (elem0 >> 8) + b;
   const float vs_old = (blk * kBlock < X.n) ? X.vs[blk] : 0.0f;
   double acc = 0.0;
@@ -996,31 +1019,30 @@ __device__ __forceinline__ void f1_stats_item(const FPlan& P, const FScalars& S,
 }
 
 // ---- clip factor per tensor: lr / max(1, RMS(U) / clip) ---------------------
-constexpr int kClipT = 1024;
-
-__global__ __launch_bounds__(kClipT) void k_f_clip(FPlan P, FScalars S) {
+// Tensor `idx` of the 2-D list followed by the 1-D list, NT threads.
+template <int NT>
+__device__ __forceinline__ void clip_one(const FPlan& P, const FScalars& S, int idx, double* red) {
   const double* parts;
   int np;
   double n;
   float* f;
   double scale = 1.0;   // 2-D: parts are sums of g^2 / (r_i c_j); times mean(r)
-  if ((int)blockIdx.x < P.n2) {
-    const F2D& X = P.t2[blockIdx.x];
+  if (idx < P.n2) {
+    const F2D& X = P.t2[idx];
     parts = X.upart; np = X.npart; n = (double)X.R * (double)X.C; f = X.f;
     double s = 0.0;
     for (int q = 0; q < X.nrw; ++q) s += X.rpart[q];
     scale = s / (double)X.R;
   } else {
-    const F1D& X = P.t1[blockIdx.x - P.n2];
+    const F1D& X = P.t1[idx - P.n2];
     parts = X.upart; np = X.nitems; n = (double)X.n; f = X.f;
   }
   double s = 0.0;
 #pragma unroll 8
-  for (int q = threadIdx.x; q < np; q += kClipT) s += parts[q];
-  __shared__ double red[kClipT];
+  for (int q = threadIdx.x; q < np; q += NT) s += parts[q];
   red[threadIdx.x] = s;
   __syncthreads();
-  for (int o = kClipT / 2; o > 0; o >>= 1) {
+  for (int o = NT / 2; o > 0; o >>= 1) {
     if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
     __syncthreads();
   }
@@ -1029,6 +1051,13 @@ __global__ __launch_bounds__(kClipT) void k_f_clip(FPlan P, FScalars S) {
     const double r = rms / S.clip;
     *f = (float)(S.lr / (r > 1.0 ? r : 1.0));
   }
+}
+
+constexpr int kClipT = 1024;
+
+__global__ __launch_bounds__(kClipT) void k_f_clip(FPlan P, FScalars S) {
+  __shared__ double red[kClipT];
+  clip_one<kClipT>(P, S, (int)blockIdx.x, red);
 }
 
 // ---- apply to 2-D tensors ----------------------------------------------------
@@ -1185,14 +1214,23 @@ template <int SPLIT>
 ps_status launch_all(const FPlan& P, const FScalars& S, hipStream_t s) {
   // U^2 row tiles, flat items without 16-byte rows and the 1-D stats items
   // share a launch (their sum is checked on the host to fit 32 bits)
-  const uint32_t n_usq = P.n_rt + P.n_items2u + P.n_items;
   if (P.n_groups) hipLaunchKernelGGL(k_f_strip, dim3(P.n_groups), dim3(kSNT), 0, s, P, S);
   if (P.n_tiles) hipLaunchKernelGGL(k_f_stats, dim3(P.n_tiles), dim3(kT), 0, s, P, S);
-  if (P.n_rc) hipLaunchKernelGGL(k_f_rowcol, dim3(P.n_rc), dim3(kT), 0, s, P, S);
-  if (P.n_rc) hipLaunchKernelGGL(k_f_factors, dim3(P.n_rc), dim3(kT), 0, s, P);
-  if (P.n_tiles_u) hipLaunchKernelGGL(k_f_usq, dim3(P.n_tiles_u), dim3(kT), 0, s, P);
-  if (n_usq) hipLaunchKernelGGL(k_f_usq_flat, dim3(n_usq), dim3(64), 0, s, P, S);
-  hipLaunchKernelGGL(k_f_clip, dim3(P.n2 + P.n1), dim3(kClipT), 0, s, P, S);
+  if (P.n_tiles == 0 && P.n_rt == 0 && P.n_items2u == 0 && P.n_tiles_u == 0) {
+    // No U^2 pass (every 2-D tensor took the row-strip pass): the 1-D stats
+    // items ride with the finalize launch and the clip factors with the
+    // factor launch.
+    const uint32_t n1wg = (P.n_items + kT / 64 - 1) / (kT / 64);
+    if (P.n_rc + n1wg) hipLaunchKernelGGL(k_f_rowcol, dim3(P.n_rc + n1wg), dim3(kT), 0, s, P, S);
+    hipLaunchKernelGGL(k_f_factors, dim3(P.n_rc + P.n2 + P.n1), dim3(kT), 0, s, P, S);
+  } else {
+    const uint32_t n_usq = P.n_rt + P.n_items2u + P.n_items;
+    if (P.n_rc) hipLaunchKernelGGL(k_f_rowcol, dim3(P.n_rc), dim3(kT), 0, s, P, S);
+    if (P.n_rc) hipLaunchKernelGGL(k_f_factors, dim3(P.n_rc), dim3(kT), 0, s, P, S);
+    if (P.n_tiles_u) hipLaunchKernelGGL(k_f_usq, dim3(P.n_tiles_u), dim3(kT), 0, s, P);
+    if (n_usq) hipLaunchKernelGGL(k_f_usq_flat, dim3(n_usq), dim3(64), 0, s, P, S);
+    hipLaunchKernelGGL(k_f_clip, dim3(P.n2 + P.n1), dim3(kClipT), 0, s, P, S);
+  }
   if (P.n_tiles_nf) hipLaunchKernelGGL((k_f_apply<SPLIT>), dim3(P.n_tiles_nf), dim3(kT), 0, s, P, S);
   if (P.n_items2) hipLaunchKernelGGL((k_f_apply_flat<SPLIT>), dim3(P.n_items2), dim3(64), 0, s, P, S);
   if (P.n_items) hipLaunchKernelGGL((k_f1_apply<SPLIT>), dim3(P.n_items), dim3(64), 0, s, P, S);
