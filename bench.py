@@ -398,10 +398,13 @@ def bench_factored(args):
 
 
 def time_factored_per_tensor(ps, states, grads, hp, ws, stream, step, steps):
-    """Per-hook granularity of the factored step: one call per tensor, the
-    workspace shared by all calls."""
+    """Per-hook granularity of the factored step: one call per tensor, one
+    workspace (sized for the largest single-tensor call) shared by all calls."""
     import torch
     recs_one = [ps.make_records([st], [g]) for st, g in zip(states, grads)]
+    need = max(ps.factored_workspace_size(None, records=r) for r in recs_one)
+    if need > ws.numel():
+        ws = torch.empty(need, dtype=torch.uint8, device=ws.device)
     for r in recs_one:
         step += 1
         ps.factored_step(None, None, hp, step, workspace=ws, stream=stream, records=r)

@@ -71,9 +71,11 @@ bool strip_ok(const ps_tensor& x) {
 }
 
 // Splits the rows of the strip tensors, taken in list order as one sequence,
-// into at most kStripGroups groups of nearly equal element counts (a row goes
-// to the group its first element falls in), and each group into segments of
-// one tensor's consecutive rows. Depends on the shapes only.
+// into kStripGroups groups of nearly equal element counts (a row goes to the
+// group its first element falls in), and each group into segments of one
+// tensor's consecutive rows; lists with fewer than kStripGroups *
+// kStripMinGroupRows such rows take the statistics tiles instead. Depends on
+// the shapes only.
 void strip_partition(const ps_tensor* t, int32_t n, Layout& L) {
   L.nseg.assign((size_t)std::max(n, 0), 0);
   std::vector<int32_t> t2idx((size_t)std::max(n, 0), -1);
@@ -88,8 +90,8 @@ void strip_partition(const ps_tensor* t, int32_t n, Layout& L) {
       rows += (uint64_t)x.rows;
     }
   }
-  const uint64_t G = std::min<uint64_t>(kStripGroups, rows);
-  if (G == 0) return;
+  if (rows < (uint64_t)kStripGroups * kStripMinGroupRows) return;
+  const uint64_t G = kStripGroups;
   // group g takes the rows whose first element lies in [B(g), B(g + 1))
   auto B = [&](uint64_t g) { return (uint64_t)(((unsigned __int128)total * g) / G); };
   auto cdiv = [](uint64_t a, uint64_t b) { return (a + b - 1) / b; };

@@ -90,9 +90,13 @@ constexpr int kFRowColChunk = 256; // rows or columns per finalize workgroup
 constexpr int kURows = 8;          // U^2 row tile (C % 8 == 0): 8 rows x 512 columns, one 64-lane wave
 constexpr int kUCols = 512;
 // Row-strip stats pass (tensors with C % 512 == 0 and C <= kStripMaxC): one
-// kSNT-thread workgroup per group of whole rows, at most kStripGroups groups.
+// kSNT-thread workgroup per group of whole rows, kStripGroups groups, taken
+// when the list's eligible tensors have at least kStripMinGroupRows rows per
+// group (each group writes and the finalize reads 16 bytes per column, which
+// fewer rows per group would not amortise; smaller lists take the tiles).
 constexpr int kSNT = 768;
 constexpr int kStripGroups = 256;
+constexpr int kStripMinGroupRows = 64;
 constexpr int kStripMaxC = 2 * kSNT * 8;
 
 // 2-D tensor [R, C] of a factored step; workspace pointers are per tensor.

@@ -124,11 +124,18 @@ def test_factored_workspace_size_and_validation(ps):
     # 2-D 32x32: rowpart 1x32, colpart 1x32 doubles, rpart 1, rho 32, kap 32 floats, rinv 32, cinv 32
     # doubles, upart 1, f; 1-D 300: v 300 floats, upart 1, f -- each region rounded up to 256 bytes
     assert size.value == 256 * (1 + 1 + 1 + 1 + 1 + 1 + 1 + 1 + 1) + 1280 + 256 + 256
-    # 4x512 takes the row-strip pass: 4 rows, so 4 groups of one row each and 4 segments; rowpart 4,
-    # colpart and qpart 4x512 doubles, rpart 1, rho 4, kap 512 floats, upart 2 column chunks, f
-    strip = (ps.CTensor * 1)(_frec(ps, n=2048, rows=4, cols=512))
+    # 16384x512 takes the row-strip pass (256 groups of 64 rows, one segment each): rowpart 16384,
+    # colpart and qpart 256x512 doubles, rpart 64, rho 16384, kap 512 floats, upart 2 column chunks, f
+    strip = (ps.CTensor * 1)(_frec(ps, n=16384 * 512, rows=16384, cols=512))
     assert L.ps_factored_workspace_size(strip, 1, ctypes.byref(size)) == 0
-    assert size.value == 256 + 16384 + 16384 + 256 + 256 + 2048 + 256 + 256
+    assert size.value == 131072 + 1048576 + 1048576 + 512 + 65536 + 2048 + 256 + 256
+    # one row fewer takes the tiles: rowpart 2x16383, colpart 64x512, rpart 64 doubles, rho, kap,
+    # rinv 16383, cinv 512 doubles, upart 2048 row tiles (8 rows each), f
+    tiles = (ps.CTensor * 1)(_frec(ps, n=16383 * 512, rows=16383, cols=512))
+    assert L.ps_factored_workspace_size(tiles, 1, ctypes.byref(size)) == 0
+    up = lambda b: (b + 255) // 256 * 256
+    assert size.value == (up(8 * 2 * 16383) + up(8 * 64 * 512) + up(8 * 64) + up(4 * 16383) + up(4 * 512)
+                          + up(8 * 16383) + up(8 * 512) + up(8 * 2048) + 256)
     bad = (ps.CTensor * 1)(_frec(ps, rows=33))
     assert L.ps_factored_workspace_size(bad, 1, ctypes.byref(size)) == 3
     bad = (ps.CTensor * 1)(_frec(ps, row_ema=0))

@@ -183,33 +183,36 @@ def test_single_one_d_tensor_calls(split_mode):
         _compare(d, h, 0, shape.name, first_moment=True)
 
 
-# Row-strip stats pass (C % 512 == 0, C <= 12288): 12, 6, 2 and 1 rows per
-# step, idle waves (C = 4096), a partial second run per thread (C = 8192),
-# two full runs (C = 12288), steps past a segment's last row, a tensor cut
-# across many groups and groups holding several tensors, next to a tensor of
-# the tile path and a 1-D tensor.
+# Row-strip stats pass (C % 512 == 0, C <= 12288; taken when the list's
+# eligible tensors have at least 256 x 64 rows): 12, 6, 2 and 1 rows per
+# step, idle waves (C = 4096), a partial second run per thread (C = 8192), two
+# full runs (C = 12288), single-row segments, steps past a segment's last row,
+# tensors cut across many groups and groups holding several tensors, next to
+# a tensor of the tile path and a 1-D tensor.
 STRIP = [synth.Shape("s512x1", 1, 512, 512), synth.Shape("s512x13", 13, 512, 13 * 512),
          synth.Shape("s1024x7", 7, 1024, 7 * 1024), synth.Shape("s3072x3", 3, 3072, 3 * 3072),
          synth.Shape("s3072x257", 257, 3072, 257 * 3072), synth.Shape("s4096x5", 5, 4096, 5 * 4096),
          synth.Shape("s8192x3", 3, 8192, 3 * 8192), synth.Shape("s12288x33", 33, 12288, 33 * 12288),
-         synth.Shape("s1024x2000", 2000, 1024, 2000 * 1024), synth.Shape("t520x9", 9, 520, 9 * 520),
+         synth.Shape("s1024x2000", 2000, 1024, 2000 * 1024), synth.Shape("s512x16384", 16384, 512, 16384 * 512),
+         synth.Shape("s12288x1", 1, 12288, 12288), synth.Shape("t520x9", 9, 520, 9 * 520),
          synth.Shape("v3000", 0, 0, 3000)]
 
 
 @pytest.mark.parametrize("split_mode,beta1", [(ps.SPLIT_TRUNC, 0.0), (ps.SPLIT_NEAREST_AWAY, 0.9),
                                               (ps.SPLIT_STOCHASTIC, 0.9)])
 def test_factored_row_strip_shapes(split_mode, beta1):
-    """Tensors of the row-strip pass in every thread layout it has (more
-    than 256 rows in all, so the rows are cut into 256 groups), 5 steps,
+    """Tensors of the row-strip pass in every thread layout it has, 4 steps,
     wd 0.01, a zero gradient in one of them; every tensor against the oracle."""
     hp = ps.FactoredHParams(split_mode=split_mode, lr=1e-4, weight_decay=0.01, beta1=beta1, seed=31)
-    _run(STRIP, hp, 5, 17, 0.01, zero_grad=(2,))
+    _run(STRIP, hp, 4, 17, 0.01, zero_grad=(2,))
 
 
-def test_factored_row_strip_few_rows():
-    """Fewer rows than groups (one group per row), a 12288-column tensor of
-    one row, clip threshold 4 with the schedule."""
-    shapes = [synth.Shape("a", 3, 3072, 3 * 3072), synth.Shape("b", 1, 12288, 12288),
-              synth.Shape("c", 2, 1536, 2 * 1536), synth.Shape("v", 0, 0, 700)]
+def test_factored_row_strip_threshold():
+    """The same strip-eligible shapes in a list of 16383 rows (statistics
+    tiles) and of 16384 rows (row-strip pass), clip threshold 4 with the
+    schedule: both against the oracle."""
+    base = [synth.Shape("a", 3, 3072, 3 * 3072), synth.Shape("b", 1, 12288, 12288),
+            synth.Shape("c", 2, 1536, 2 * 1536), synth.Shape("v", 0, 0, 700)]
     hp = ps.FactoredHParams(lr=1e-4, clip_threshold=4.0, decay_rate=-0.8, seed=5)
-    _run(shapes, hp, 4, 23, 0.01)
+    for rows in (16383 - 6, 16384 - 6):
+        _run(base + [synth.Shape("d", rows, 512, rows * 512)], hp, 3, 23, 0.01)
