@@ -106,13 +106,15 @@ def gpu_clocks():
     return out
 
 
-def stream_ceiling(slab, steps, stream):
+def stream_ceiling(slab, steps, stream, stochastic=False):
     """Practical HBM ceiling of the step's access pattern on this GPU: the
     no-arithmetic streaming kernels of tests/kernels/stream_ceiling.hip over the
     same slab arrays as the step, timed with HIP events on the same stream.
     mode 0 is the step's mix (five 16-byte reads and four 16-byte writes per
     lane, block scales read and written: 18 B per element + 16 B per block);
-    mode 1 the reads alone (10 B per element + 8 B per block). Overwrites the
+    mode 1 the reads alone (10 B per element + 8 B per block); with stochastic
+    rounding, mode 2 is the step's mix without the residual stream (14 B per
+    element + 16 B per block) and is reported as step_mix. Overwrites the
     state, so it runs after the step's timing."""
     import ctypes
 
@@ -131,7 +133,9 @@ def stream_ceiling(slab, steps, stream):
                                                                       sink.data_ptr()]
     hs = ctypes.c_void_p(stream.cuda_stream)
     res = {"elements": n_items * 512}
-    for mode, name, per_item in ((0, "step_mix", 512 * 18 + 32), (1, "reads_only", 512 * 10 + 16)):
+    modes = ((2, "step_mix", 512 * 14 + 32),) if stochastic else \
+        ((0, "step_mix", 512 * 18 + 32), (1, "reads_only", 512 * 10 + 16))
+    for mode, name, per_item in modes:
         for _ in range(5):
             if L.probe_stream_ceiling(mode, *ptrs, n_items, hs) != 0:
                 raise RuntimeError("stream ceiling kernel launch failed")
@@ -850,8 +854,8 @@ def main():
     traffic = None if args.policy else read_traffic(args.workload, args.moments, args.split)
     clocks = gpu_clocks()
     ceiling = None
-    if not args.no_ceiling and not args.policy and args.moments == "codec" and args.split != "stochastic":
-        ceiling = stream_ceiling(slab, max(5, min(args.steps, 20)), stream)
+    if not args.no_ceiling and not args.policy and args.moments == "codec":
+        ceiling = stream_ceiling(slab, max(5, min(args.steps, 20)), stream, stochastic=args.split == "stochastic")
 
     baseline = None
     if not args.no_cpu_baseline:

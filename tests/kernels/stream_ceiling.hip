@@ -13,6 +13,9 @@
 //   mode 0: the step's mix, 18 B per element + 16 B per block
 //   mode 1: the five streams and scale reads only (10 B per element + 8 B
 //           per block); a word is stored only if an impossible value appears
+//   mode 2: the stochastic-rounding step's mix (no residual stream: reads of
+//           hi, g, m and v codes, writes of hi, m, v; 14 B per element + 16 B
+//           per block)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,11 +37,12 @@ __global__ __launch_bounds__(64) void k_ceiling(uint16_t* hi, uint16_t* lo, cons
   const uint32_t lane = threadIdx.x, b = lane >> 5, r = lane & 31;
   const size_t e = (size_t)item * 512 + b * 256 + r * 8;
   const size_t blk = (size_t)item * 2 + b;
-  const u32x4 vh = ld(hi + e), vl = ld(lo + e), vg = ld(g + e), vm = ld(mc + e), vv = ld(vc + e);
+  const u32x4 vh = ld(hi + e), vl = MODE == 2 ? u32x4{0u, 0u, 0u, 0u} : ld(lo + e), vg = ld(g + e),
+              vm = ld(mc + e), vv = ld(vc + e);
   const float sm = ((const GLOBAL float*)ms)[blk], sv = ((const GLOBAL float*)vs)[blk];
-  if (MODE == 0) {
+  if (MODE == 0 || MODE == 2) {
     st(hi + e, vh ^ vg);
-    st(lo + e, vl ^ vg);
+    if (MODE == 0) st(lo + e, vl ^ vg);
     st(mc + e, vm ^ vg);
     st(vc + e, vv ^ vg);
     if (r == 0) {
@@ -60,7 +64,11 @@ extern "C" int probe_stream_ceiling(int mode, uint16_t* hi, uint16_t* lo, const 
   if (n_items == 0) return 0;
   if (mode == 0)
     hipLaunchKernelGGL(k_ceiling<0>, dim3(n_items), dim3(64), 0, s, hi, lo, g, mc, vc, ms, vs, sink);
-  else
+  else if (mode == 1)
     hipLaunchKernelGGL(k_ceiling<1>, dim3(n_items), dim3(64), 0, s, hi, lo, g, mc, vc, ms, vs, sink);
+  else if (mode == 2)
+    hipLaunchKernelGGL(k_ceiling<2>, dim3(n_items), dim3(64), 0, s, hi, lo, g, mc, vc, ms, vs, sink);
+  else
+    return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
