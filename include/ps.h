@@ -116,8 +116,9 @@ typedef struct ps_tensor {
 
 /* (N)AdamW hyperparameters [NADAM]. Constraints: algo in {ADAM, NADAM};
  * split_mode in {TRUNC, NEAREST_AWAY, STOCHASTIC}; lr >= 0; 0 <= beta1 < 1;
- * 0 <= beta2 < 1; eps > 0; weight_decay >= 0; momentum_decay >= 0 (NAdam's
- * psi, 0.004 by default); all finite.
+ * 0 <= beta2 < 1; eps > 0 and nonzero once rounded to fp32;
+ * weight_decay >= 0; momentum_decay >= 0 (NAdam's psi, 0.004 by default);
+ * all finite.
  *
  * split_mode STOCHASTIC [KAHAN, PR #2159 body: the stochastic rounding the
  * residual replaces; NADAM opening post]: no residual. w_lo is neither read
@@ -160,8 +161,9 @@ typedef struct ps_hparams {
  *   split_mode  TRUNC, NEAREST_AWAY, or STOCHASTIC (no residual; the random
  *               bits exactly as for ps_hparams, from `seed`, the update
  *               number and the tensor's index in the list)
- * Constraints: lr >= 0; 0 <= beta2 < 1; eps1 > 0; clip_threshold > 0;
- * weight_decay >= 0; decay_rate <= 0; 0 <= beta1 < 1; all finite. */
+ * Constraints: lr >= 0; 0 <= beta2 < 1; eps1 > 0 and nonzero once rounded to fp32;
+ * clip_threshold > 0; weight_decay >= 0; decay_rate <= 0;
+ * 0 <= beta1 < 1; all finite. */
 typedef struct ps_factored_hparams {
   int32_t split_mode;
   int32_t reserved; /* must be 0 */
@@ -247,11 +249,14 @@ ps_status ps_factored_workspace_size(const ps_tensor* tensors, int32_t n_tensors
  *   q_ij = g_ij*g_ij + EPS1
  *   r_i = fma(B2, r_i, C2*fp32(mean_j q_ij)),  c_j = fma(B2, c_j, C2*fp32(mean_i q_ij))
  *   rbar = fp32(mean_i r_i); rho_i = 1/sqrt(r_i/rbar); kap_j = 1/sqrt(c_j)
- *   U_ij = (g_ij*rho_i)*kap_j; f = fp32(lr / max(1, RMS(U)/clip_threshold))
+ *   U_ij = (g_ij*rho_i)*kap_j; f = fp32(lr / max(1, RMS/clip_threshold)),
+ *     RMS = sqrt(mean_ij g_ij^2 * mean_i(r_i) / (r_i c_j)) in double: the RMS
+ *     of the exact U for the new EMAs
  *   x = U*f; with beta1: m = fma(B1, decode(m), C1*x), x = m, m re-encoded
  *   w' = w - x after x = fma(CWD, w, x) if weight_decay != 0
  * Means and RMS are accumulated in double. A 1-D tensor keeps v in the
- * uint16 codec: v = fma(B2, decode(v), C2*q); U = g*(1/sqrt(v)); same clip.
+ * uint16 codec: v = fma(B2, decode(v), C2*q); U = g*(1/sqrt(v)); the clip's
+ * RMS = sqrt(mean g^2 / v) in double.
  * workspace: device memory of at least ps_factored_workspace_size bytes,
  * 256-byte aligned, owned by the caller; its contents on entry are ignored;
  * calls that may run at the same time need distinct workspaces. The step's

@@ -49,7 +49,8 @@ ps_status check_hparams(const ps_hparams* hp) {
   if (!finite(hp->lr) || hp->lr < 0) return fail(PS_ERR_INVALID_ARG, "lr must be finite and >= 0");
   if (!finite(hp->beta1) || hp->beta1 < 0 || hp->beta1 >= 1) return fail(PS_ERR_INVALID_ARG, "beta1 must be in [0, 1)");
   if (!finite(hp->beta2) || hp->beta2 < 0 || hp->beta2 >= 1) return fail(PS_ERR_INVALID_ARG, "beta2 must be in [0, 1)");
-  if (!finite(hp->eps) || !(hp->eps > 0)) return fail(PS_ERR_INVALID_ARG, "eps must be finite and > 0");
+  if (!finite(hp->eps) || !(hp->eps > 0) || !((float)hp->eps > 0.0f))
+    return fail(PS_ERR_INVALID_ARG, "eps must be finite and > 0 once rounded to fp32");
   if (!finite(hp->weight_decay) || hp->weight_decay < 0)
     return fail(PS_ERR_INVALID_ARG, "weight_decay must be finite and >= 0");
   if (!finite(hp->momentum_decay) || hp->momentum_decay < 0)

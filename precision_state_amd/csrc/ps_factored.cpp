@@ -28,7 +28,8 @@ ps_status check_fhparams(const ps_factored_hparams* hp) {
   if (hp->reserved != 0) return fail(PS_ERR_INVALID_ARG, "reserved must be 0");
   if (!is_finite(hp->lr) || hp->lr < 0) return fail(PS_ERR_INVALID_ARG, "lr must be finite and >= 0");
   if (!is_finite(hp->beta2) || hp->beta2 < 0 || hp->beta2 >= 1) return fail(PS_ERR_INVALID_ARG, "beta2 must be in [0, 1)");
-  if (!is_finite(hp->eps1) || !(hp->eps1 > 0)) return fail(PS_ERR_INVALID_ARG, "eps1 must be finite and > 0");
+  if (!is_finite(hp->eps1) || !(hp->eps1 > 0) || !((float)hp->eps1 > 0.0f))
+    return fail(PS_ERR_INVALID_ARG, "eps1 must be finite and > 0 once rounded to fp32");
   if (!is_finite(hp->clip_threshold) || !(hp->clip_threshold > 0))
     return fail(PS_ERR_INVALID_ARG, "clip_threshold must be finite and > 0");
   if (!is_finite(hp->weight_decay) || hp->weight_decay < 0)

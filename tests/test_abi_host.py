@@ -61,6 +61,8 @@ def test_invalid_arguments_rejected_on_host(ps):
     assert _call(ps, [_rec(ps)], hp=ps.HParams(beta1=1.0)) == 1
     assert _call(ps, [_rec(ps)], hp=ps.HParams(beta2=-0.1)) == 1
     assert _call(ps, [_rec(ps)], hp=ps.HParams(eps=0.0)) == 1
+    assert _call(ps, [_rec(ps)], hp=ps.HParams(eps=1e-50)) == 1   # 0 once rounded to fp32
+    assert "fp32" in ps.last_error()
     assert _call(ps, [_rec(ps)], hp=ps.HParams(lr=float("nan"))) == 1
     assert _call(ps, [_rec(ps)], hp=ps.HParams(weight_decay=-1.0)) == 1
     assert _call(ps, [_rec(ps, numel=-1)]) == 3
@@ -199,6 +201,8 @@ def test_noalloc_factored_step_rejects_on_host(ps):
     h = ps.FactoredHParams().c()
     assert L.ps_factored_step_noalloc(big, 1, ctypes.byref(h), 1, None) == 7      # PS_ERR_WORKSPACE
     assert "scratch" in ps.last_error()
+    tiny = ps.FactoredHParams(eps1=1e-50).c()                                     # 0 once rounded to fp32
+    assert L.ps_factored_step_noalloc(big, 1, ctypes.byref(tiny), 1, None) == 1
     bad = ps.FactoredHParams(clip_threshold=0.0).c()
     assert L.ps_factored_step_noalloc(big, 1, ctypes.byref(bad), 1, None) == 1    # PS_ERR_INVALID_ARG
     assert L.ps_factored_step_noalloc(big, 1, ctypes.byref(h), 0, None) == 1
