@@ -38,6 +38,8 @@ METRIC = "optimizer-updated params/sec + achieved HBM GB/s (% of MI355X peak), F
 PEAK_HBM_GBS = 8000.0
 BYTES_PER_BLOCK = 16
 KERNEL_SOURCES = ["precision_state_amd/csrc/k_adam.hip", "precision_state_amd/csrc/dev_common.h"]
+FACTORED_SOURCES = ["precision_state_amd/csrc/k_factored.hip", "precision_state_amd/csrc/dev_common.h",
+                    "precision_state_amd/csrc/ps_internal.h", "precision_state_amd/csrc/ps_factored.cpp"]
 
 
 def step_bytes(numel, flags=0, residual=True):
@@ -62,9 +64,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -152,13 +154,10 @@ def stream_ceiling(slab, steps, stream, stochastic=False):
     return res
 
 
-def read_traffic(workload, moments="codec", split="trunc"):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    tag = {("codec", "trunc"): "", ("f24", "trunc"): "_f24", ("codec", "stochastic"): "_sr"}.get((moments, split))
-    if tag is None:
-        return None
-    path = os.path.join(ROOT, "profiles", f"adam_step_{workload}{tag}_counters.txt")
+def read_counter_summary(name, key, sources=None):
+    """A figure from a committed rocprofv3 counter summary under profiles/, if
+    the summary was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -166,12 +165,20 @@ def read_traffic(workload, moments="codec", split="trunc"):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
+
+
+def read_traffic(workload, moments="codec", split="trunc"):
+    """HBM bytes per launch of the fused step from the committed counter summary."""
+    tag = {("codec", "trunc"): "", ("f24", "trunc"): "_f24", ("codec", "stochastic"): "_sr"}.get((moments, split))
+    if tag is None:
+        return None
+    return read_counter_summary(f"adam_step_{workload}{tag}_counters.txt", "hbm_bytes_per_launch")
 
 
 def build_state(shapes, seed, dev, layout="slab", moments="codec"):
@@ -328,7 +335,9 @@ def bench_factored(args):
     eps1 1e-30, lr 3.5e-6) on the FLUX double-block shapes: 2-D tensors
     factored, 1-D tensors with the uint16 codec. Grads N(0, 1e-3) with 0.1%
     outliers at 100x. Algorithmic bytes: 10 B/param (read hi, lo, grad; write
-    hi, lo); the kernels read the gradient three times (14 B/param)."""
+    hi, lo); the kernels read the gradient twice (12 B/param) for tensors of
+    the row-strip statistics pass and the 1-D tensors, three times for the
+    other 2-D tensors (14 B/param)."""
     import torch
 
     import precision_state_amd as ps
@@ -386,7 +395,16 @@ def bench_factored(args):
     n_blocks = sum((s.numel + 255) // 256 for s in shapes)
     alg = (10 if split != ps.SPLIT_STOCHASTIC else 6) * n_params + ((4 * n_params + 8 * n_blocks) if args.beta1 else 0)
     gbs10 = alg / (step_ms * 1e-3) / 1e9
-    gbs14 = (alg + 4 * n_params) / (step_ms * 1e-3) / 1e9
+    # gradient re-reads of the design: the row-strip pass (2-D tensors with C % 512 == 0, C <= 12288 and
+    # fewer than 2^31 elements, when they have 256 x 64 rows in all) reads it once more, the tiles twice
+    strip = [s for s in shapes if s.is_2d and s.cols % 512 == 0 and s.cols <= 12288 and s.numel < 2 ** 31]
+    strip = strip if sum(s.rows for s in strip) >= 256 * 64 else []
+    rereads = sum(2 * s.numel for s in shapes) + sum(2 * s.numel for s in shapes if s.is_2d and s not in strip)
+    gbs_design = (alg + rereads) / (step_ms * 1e-3) / 1e9
+    traffic = None
+    if not args.beta1 and not args.decay_rate and split == ps.SPLIT_TRUNC and wl == "flux_double_block":
+        traffic = read_counter_summary("factored_step_flux_double_block_counters.txt", "hbm_bytes_per_step",
+                                       FACTORED_SOURCES)
     print(json.dumps({
         "metric": "factored optimizer-updated params/sec (Adafactor-style step, FLUX double-block shapes)",
         "value": n_params * args.steps / wall, "unit": "params/s", "n_gpus": 1, "steps": args.steps,
@@ -394,10 +412,11 @@ def bench_factored(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl + "_factored", "params": n_params, "tensors": len(shapes), "step_ms": step_ms,
                    "beta1": args.beta1, "decay_rate": args.decay_rate, "split": args.split, "algorithmic_bytes": alg,
-                   "gbs_algorithmic": gbs10, "gbs_with_gradient_rereads": gbs14, "per_tensor_calls": per_tensor,
+                   "gbs_algorithmic": gbs10, "gbs_with_gradient_rereads": gbs_design,
+                   "gradient_reread_bytes": rereads, "per_tensor_calls": per_tensor,
                    "copy_gbs": copy_gbs},
         "roofline": {"bound": "hbm", "achieved": gbs10, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": gbs10 / PEAK_HBM_GBS, "traffic": None},
+                     "frac": gbs10 / PEAK_HBM_GBS, "traffic": traffic},
         "cpu_baseline": None}), flush=True)
 
 

@@ -349,12 +349,12 @@ __device__ __forceinline__ float lds_read4(uint32_t a) {
 // a step pass through the first two at the end (at most kSNT - 64 threads x
 // 16 doubles = 90112 bytes). s_ro holds the old row EMA of each wave's row of
 // each step of a batch, s_wsum the wave row partials by batch parity.
-__shared__ u32x4 s_buf[3][kSBufRuns];
+__shared__ u32x4 s_buf[3 * kSBufRuns];   // buffer h at s_buf + h * kSBufRuns
 __shared__ float s_ro[3][4][kSWaves];
 __shared__ double s_wsum[2][4][kSWaves];
 
 __device__ __forceinline__ double* comb_entry(int e) {   // 16 doubles (8 runs) per entry
-  return (double*)&s_buf[0][8 * e];
+  return (double*)&s_buf[8 * e];
 }
 static_assert((kSNT - 64) * 8 <= 2 * kSBufRuns, "the column sums fit two buffers");
 
@@ -417,7 +417,7 @@ __device__ __forceinline__ void strip_segment(const StripArgs& A, int& par) {
       for (int k = 0; k < K; ++k) {
         const int u = (k == 1 && run1) ? u0 + kSNT : u0;
         __builtin_amdgcn_global_load_lds((const GLOBAL void*)(A.g + (size_t)i * (size_t)C + (size_t)(8 * u)),
-                                         (lds_void*)&s_buf[h][(d * K + k) * kSNT + wave * 64], 16, 0, kLdsDmaNt);
+                                         (lds_void*)&s_buf[h * kSBufRuns + (d * K + k) * kSNT + wave * 64], 16, 0, kLdsDmaNt);
       }
       if (lane == 0)
         __builtin_amdgcn_global_load_lds((const GLOBAL void*)(A.row + i), (lds_void*)&s_ro[h][d][wave], 4, 0, 0);
@@ -437,7 +437,7 @@ __device__ __forceinline__ void strip_segment(const StripArgs& A, int& par) {
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const int h = b % 3;
-    const uint32_t abuf = lds_addr(&s_buf[h][t]);
+    const uint32_t abuf = lds_addr(&s_buf[h * kSBufRuns + t]);
 
     // g^2 (exact in fp32 for a bf16 g) and q = g^2 + eps1 into the column
     // sums and this lane's row partials; g^2 stays in registers for the
