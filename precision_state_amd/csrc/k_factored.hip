@@ -683,12 +683,13 @@ __global__ __launch_bounds__(kT) void k_f_usq(FPlan P) {
     uint32_t w[4];
     const uint32_t valid = load_row8(X.g, X, r, c, w);
     if (!valid) continue;
-    const double ri = X.rinv[r];
+    double sr = 0.0;   // sum_j g^2 / c_j over the row segment (g^2 exact in fp32), then times 1 / r_i
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const double g = (double)bf16_at(w, j);
-      acc += (valid >> j & 1u) ? g * g * ri * ci[j] : 0.0;
+      const float g = bf16_at(w, j);
+      sr = (valid >> j & 1u) ? __builtin_fma((double)(g * g), ci[j], sr) : sr;
     }
+    acc = __builtin_fma(sr, X.rinv[r], acc);
   }
   __shared__ double red[kT];
   const double t = block_sum(acc, red);
@@ -793,17 +794,20 @@ __device__ __forceinline__ void usq_row_tile(const FPlan& P, uint32_t w) {
     const int r = r0 + k;
     gv[k] = (col_ok && r < X.R) ? ld_stream(X.g + (size_t)r * (size_t)X.C + (size_t)c) : make_uint4(0u, 0u, 0u, 0u);
   }
+  // per row: sum_j g^2 / c_j (g^2 exact in fp32), then times 1 / r_i
   double acc = 0.0;
 #pragma unroll
   for (int k = 0; k < kURows; ++k) {
     const int r = r0 + k;
     const double ri = r < X.R ? X.rinv[r] : 0.0;
     const uint32_t g[4] = {gv[k].x, gv[k].y, gv[k].z, gv[k].w};
+    double sr = 0.0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const double gd = (double)bf16_at(g, j);
-      acc += gd * gd * ri * ci[j];
+      const float gj = bf16_at(g, j);
+      sr = __builtin_fma((double)(gj * gj), ci[j], sr);
     }
+    acc = __builtin_fma(sr, ri, acc);
   }
   for (int o = 1; o < 64; o <<= 1) acc += __shfl_xor(acc, o, 64);
   if (threadIdx.x == 0) X.upart[t] = acc;
