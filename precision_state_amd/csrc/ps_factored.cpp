@@ -1,12 +1,19 @@
 // ps_factored.cpp - host side of ps_factored_step: validation, workspace
 // layout and the device plan [ADAF, adafactor_step_param; PRODIGY].
 //
-// Workspace (caller-owned device memory), per 2-D tensor [R, C]: row sums per
-// 256-column band [ntc][R] and column sums per 256-row band [sntr][C] (double), sums of
-// the new row EMAs per 256-row chunk, rho[R], kap[C], sums of U^2 (per row
-// tile, flat item or stats tile, whichever form the U^2 pass takes), the clip
-// factor. Per 1-D tensor: this step's v[n], sums of U^2 per
-// 1024-element item, the clip factor. Every region starts on 256 bytes.
+// Workspace (caller-owned device memory), per 2-D tensor [R, C]:
+//  - row-strip tensors: row sums [R] and, per row segment of the strip pass,
+//    column sums of q and of g^2 / r_i [nseg][C] (double); sums of the new row
+//    EMAs per 256-row chunk; rho[R], kap[C]; sums of Q_j / c_j per 256-column
+//    chunk; the clip factor;
+//  - other tensors: row sums per 256-column band [ntc][R] and column sums per
+//    256-row band [sntr][C] (double); sums of the new row EMAs per 256-row
+//    chunk; rho[R], kap[C], 1/r_i [R] and 1/c_j [C] (double); sums of
+//    g^2 / (r_i c_j) (per row tile, flat item or stats tile, whichever form the
+//    U^2 pass takes); the clip factor.
+// Per 1-D tensor: this step's v[n], sums of g^2 / v per 1024-element item, the
+// clip factor. Every region starts on 256 bytes. The plan image also carries
+// the strip pass's groups and segments (strip_partition).
 #include <algorithm>
 #include <cmath>
 #include <cstring>
