@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0
 BYTES_PER_BLOCK = 16
 KERNEL_SOURCES = ["precision_state_amd/csrc/k_adam.hip", "precision_state_amd/csrc/dev_common.h"]
 FACTORED_SOURCES = ["precision_state_amd/csrc/k_factored.hip", "precision_state_amd/csrc/dev_common.h",
-                    "precision_state_amd/csrc/ps_internal.h", "precision_state_amd/csrc/ps_factored.cpp"]
+                    "precision_state_amd/csrc/ps_internal.h"]
 
 
 def step_bytes(numel, flags=0, residual=True):
