@@ -17,7 +17,9 @@ if not torch.cuda.is_available():
 import precision_state_amd as ps  # noqa: E402
 
 SIZES = [5000, 257, 1, 65536, 1024, 3000, 131089, 4096, 100, 255, 256, 70000, 8, 9, 1023, 1025, 20000, 4097]
-SHAPES2D = [(64, 96), (3, 1000), (128, 256), (17, 40)]
+# the last shape puts 16384 rows of 512 columns in each list, so every list
+# runs the row-strip statistics pass as well as the tiles of the others
+SHAPES2D = [(64, 96), (3, 1000), (128, 256), (17, 40), (16384, 512)]
 STEPS = 3
 THREADS = 4
 
