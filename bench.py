@@ -154,6 +154,45 @@ def stream_ceiling(slab, steps, stream, stochastic=False):
     return res
 
 
+def ew_ceiling(n, bufs, steps, stream):
+    """Practical ceilings of the four standalone kernels: probe_ew_ceiling of
+    tests/kernels/stream_ceiling.hip runs each one's grid, lane layout and
+    cache hints with no arithmetic (same bytes per element), timed with HIP
+    events on the same stream. bufs maps split/join/encode/decode to their
+    (in0, in1, out0, out1) tensors; overwrites the outputs, so it runs after
+    the kernels' own timing."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "tests", "kernels", "libps_probe.so")
+    if n % 4096 or not os.path.exists(path):
+        log(f"[bench] no elementwise ceilings ({'n not a multiple of 4096' if n % 4096 else path + ' is not built'})")
+        return None
+    L = ctypes.CDLL(path)
+    if not hasattr(L, "probe_ew_ceiling"):
+        log("[bench] no elementwise ceilings (probe library predates them)")
+        return None
+    L.probe_ew_ceiling.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_void_p]
+    L.probe_ew_ceiling.restype = ctypes.c_int
+    hs = ctypes.c_void_p(stream.cuda_stream)
+    res = {}
+    for kind, name in enumerate(("split", "join", "encode", "decode")):
+        ptrs = [None if t is None else t.data_ptr() for t in bufs[name]]
+        for _ in range(5):
+            if L.probe_ew_ceiling(kind, *ptrs, n, hs) != 0:
+                raise RuntimeError("elementwise ceiling kernel launch failed")
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            L.probe_ew_ceiling(kind, *ptrs, n, hs)
+        b.record(stream)
+        torch.cuda.synchronize()
+        res[name] = {"ms": a.elapsed_time(b) / steps}
+        log(f"[bench] ceiling {name}: {res[name]['ms']:.3f} ms per launch")
+    return res
+
+
 def read_counter_summary(name, key, sources=None):
     """A figure from a committed rocprofv3 counter summary under profiles/, if
     the summary was taken on the current kernel source; else None."""
@@ -733,6 +772,14 @@ def bench_elementwise(args):
         tot_bytes += nbytes
         tot_ms += ms
         log(f"[bench] {name}: {ms:.3f} ms, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.3f} of 8 TB/s)")
+    ceil = ew_ceiling(n, {"split": (w32, None, hi, lo), "join": (hi, lo, out, None),
+                          "encode": (m32, None, code, scale), "decode": (code, scale, out, None)},
+                      args.steps, stream)
+    if ceil:
+        for name, r in res.items():
+            c = ceil[name.split("_")[0]]
+            r["practical_peak_gbs"] = r["bytes"] / (c["ms"] * 1e-3) / 1e9
+            r["frac_of_practical"] = c["ms"] / r["ms"]
     worst = min(res, key=lambda k: res[k]["gbs"])
     print(json.dumps({
         "metric": "standalone split/join/encode/decode: algorithmic HBM GB/s over the eight kernels",
