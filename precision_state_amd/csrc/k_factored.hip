@@ -278,9 +278,12 @@ __device__ __forceinline__ double swap16_sum(double a, double b) {
   const auto h = __builtin_amdgcn_permlane16_swap(hi32(a), hi32(b), false, false);
   return mk64(l[0], h[0]) + mk64(l[1], h[1]);
 }
+// A plain DPP move (no old value: every source lane of these row-local
+// patterns exists, so nothing needs initialising before the move).
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
-  return mk64(dpp_u32<CTRL>(lo32(x)), dpp_u32<CTRL>(hi32(x)));
+  return mk64((uint32_t)__builtin_amdgcn_mov_dpp((int)lo32(x), CTRL, 0xF, 0xF, true),
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)hi32(x), CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ double row16_sum(double x) {
   x += dpp_f64<0xB1>(x);    // quad_perm [1,0,3,2]
@@ -323,27 +326,22 @@ constexpr int kSBufBytes = kSBufRuns * 16;
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-// The N = D * K runs of this thread in a batch buffer, entry (d * K + k) at
-// byte offset (d * K + k) * kSNT * 16 from the thread's first.
-template <int N>
-__device__ __forceinline__ void lds_read_runs(uint32_t a, u32x4 (&x)[N]) {
-  static_assert(N == 4, "a batch holds four runs per thread");
+// The four runs (D * K) of this thread in a batch buffer, entry (d * K + k)
+// at byte offset (d * K + k) * kSNT * 16 from the thread's first at a, and
+// the 4-byte word at b (a row EMA copied in with them).
+__device__ __forceinline__ void lds_read_runs(uint32_t a, uint32_t b, u32x4 (&x)[4], float& w) {
   asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %4 offset:12288\n\t"
-      "ds_read_b128 %2, %4 offset:24576\n\t"
-      "ds_read_b128 %3, %4 offset:36864\n\t"
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %5 offset:12288\n\t"
+      "ds_read_b128 %2, %5 offset:24576\n\t"
+      "ds_read_b128 %3, %5 offset:36864\n\t"
+      "ds_read_b32 %4, %6\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])   // early clobber: the address must
-      : "v"(a)                                               // outlive the first read's result
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(w)   // early clobber: the addresses
+      : "v"(a), "v"(b)                                                  // outlive the first result
       : "memory");
 }
 static_assert(kSNT * 16 == 12288, "the offsets in lds_read_runs");
-__device__ __forceinline__ float lds_read4(uint32_t a) {
-  float v;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
-  return v;
-}
 
 // Three batch buffers; a segment's column sums of the rows after the first of
 // a step pass through the first two at the end (at most kSNT - 64 threads x
@@ -394,6 +392,7 @@ __device__ __forceinline__ void strip_segment(const StripArgs& A, int& par) {
   const bool act = rr < grows;                       // wave-uniform
   const bool run1 = K == 2 && u0 + kSNT < Ur;        // the second run exists
   const int row0 = A.row0, row1 = A.row1;
+  const double Cd = (double)C, rC = 1.0 / Cd;
   const int nsteps = (row1 - row0 + grows - 1) / grows;
   const int nb = (nsteps + D - 1) / D;
   double P[K][8], Q[K][8];
@@ -441,9 +440,11 @@ __device__ __forceinline__ void strip_segment(const StripArgs& A, int& par) {
 
     // g^2 (exact in fp32 for a bf16 g) and q = g^2 + eps1 into the column
     // sums and this lane's row partials; g^2 stays in registers for the
-    // second half
+    // second half. Lane d < D also takes step d's old row EMA (this wave's
+    // own copy, so it is read here, ahead of the barrier).
     u32x4 x[4];
-    lds_read_runs(abuf, x);
+    float ro;
+    lds_read_runs(abuf, lds_addr(&s_ro[h][min(lane, D - 1)][wave]), x, ro);
     float g2[D][K][8];
     double rp[D];
 #pragma unroll
@@ -479,18 +480,35 @@ __device__ __forceinline__ void strip_segment(const StripArgs& A, int& par) {
     if ((lane & (64 / D - 1)) == 0) s_wsum[par][lane / (64 / D)][wave] = ws;
     lds_barrier();
 
-    // lane d: step d's row sum in wave order, the new row EMA (as the
-    // finalize kernel forms it) and 1 / r_i (reciprocal and two Newton steps)
+    // lane d: step d's row sum (the nwr <= 12 wave partials added pairwise
+    // in a fixed order, missing ones as 0), the new row EMA (as the finalize
+    // kernel forms it) and 1 / r_i. Every wave runs this chain right after
+    // the barrier with nothing to overlap it, so it is kept short:
+    //  - sum / C as Markstein's corrected product: with y = RN(1/C), for
+    //    every C = m * 512, m <= 24, y is within 2^-54 of 1/C relatively,
+    //    so q0 = RN(sum * y) is within one ulp of sum / C and
+    //    RN(q0 + (sum - C q0) y) is the correctly rounded quotient, the
+    //    value of an IEEE division; an infinite sum leaves a NaN residual
+    //    and keeps q0 (infinity);
+    //  - 1 / r_i: the reciprocal estimate and one third-order Newton step,
+    //    y (1 + e + e^2) with e = 1 - r y.
     double inv_l = 0.0;
     if (lane < D) {
       const int i = row_of(b, lane);
-      double sum = 0.0;
-      for (int q = 0; q < nwr; ++q) sum += s_wsum[par][lane][w0 + q];
-      const float mean = (float)(sum / (double)C);
-      const double r = (double)__builtin_fmaf(A.B2, lds_read4(lds_addr(&s_ro[h][lane][wave])), A.C2 * mean);
-      double y = __builtin_amdgcn_rcp(r);
-      y = __builtin_fma(y, __builtin_fma(-r, y, 1.0), y);
-      inv_l = __builtin_fma(y, __builtin_fma(-r, y, 1.0), y);
+      double a[kSWaves];
+#pragma unroll
+      for (int q = 0; q < kSWaves; ++q) a[q] = q < nwr ? s_wsum[par][lane][min(w0 + q, kSWaves - 1)] : 0.0;
+      static_assert(kSWaves == 12, "the pairwise order below");
+      const double sum = (((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]))) +
+                         ((a[8] + a[9]) + (a[10] + a[11]));
+      const double q0 = sum * rC;
+      const double res = __builtin_fma(-Cd, q0, sum);
+      const double qc = __builtin_fma(res, rC, q0);
+      const float mean = (float)(res == res ? qc : q0);
+      const double r = (double)__builtin_fmaf(A.B2, ro, A.C2 * mean);
+      const double y = __builtin_amdgcn_rcp(r);
+      const double e = __builtin_fma(-r, y, 1.0);
+      inv_l = __builtin_fma(y, __builtin_fma(e, e, e), y);
       if (act && i < row1 && wave == w0) A.rowpart[i] = sum;
     }
     // then g^2 / r_i into the column sums
