@@ -425,6 +425,7 @@ def bench_factored(args):
     b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clocks = gpu_clocks()
     step_ms = a.elapsed_time(b) / args.steps
     log(f"[bench] factored: {args.steps} steps, {step_ms:.3f} ms/step (events), {wall * 1e3 / args.steps:.3f} wall")
     per_tensor = None
@@ -450,6 +451,7 @@ def bench_factored(args):
         "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl + "_factored", "params": n_params, "tensors": len(shapes), "step_ms": step_ms,
+                   "gpu_clocks_after_timing": clocks,
                    "beta1": args.beta1, "decay_rate": args.decay_rate, "split": args.split, "algorithmic_bytes": alg,
                    "gbs_algorithmic": gbs10, "gbs_with_gradient_rereads": gbs_design,
                    "gradient_reread_bytes": rereads, "per_tensor_calls": per_tensor,
@@ -544,6 +546,7 @@ def bench_per_tensor(args):
         res[name] = {"wall_ms": wall * 1e3 / args.steps, "gpu_ms": a.elapsed_time(b) / args.steps,
                      "issue_ms": issue * 1e3 / args.steps}
         log(f"[bench] {name}: {res[name]}")
+    clocks = gpu_clocks()
     # back-to-back calls on single small tensors
     lat = {}
     for n in (4096, 65536, 3072 * 3072):
@@ -578,6 +581,7 @@ def bench_per_tensor(args):
         "warmup": args.warmup, "ms_per_step": pt["wall_ms"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload + "_per_tensor", "params": n_params, "calls_per_step": len(shapes),
+                   "gpu_clocks_after_timing": clocks,
                    "policy": {"fp32_moment_tensors": n_small, "fp32_param_tensors": n_final} if args.policy else None,
                    "per_tensor": pt, "one_launch": res["one_launch"],
                    "per_tensor_over_one_launch": pt["wall_ms"] / res["one_launch"]["wall_ms"],
@@ -699,6 +703,7 @@ def bench_offload(args, n_blocks=57):
         plan.run(hp, step, stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
+    clocks = gpu_clocks()
     h2d, d2h = plan.bytes()       # of the last run (no residuals under stochastic rounding)
     log(f"[bench] offload ({args.offload_mode}): {n_blocks} blocks, {wall * 1e3:.1f} ms/step, PCIe {h2d / wall / 1e9:.1f} GB/s up + "
         f"{d2h / wall / 1e9:.1f} GB/s down")
@@ -708,7 +713,7 @@ def bench_offload(args, n_blocks=57):
         "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"flux_double_block_x{n_blocks}_offload", "params": n_params, "split": args.split,
-                   "offload_mode": args.offload_mode,
+                   "offload_mode": args.offload_mode, "gpu_clocks_after_timing": clocks,
                    "offload_cus": args.offload_cus if args.offload_mode == "direct" else None,
                    "host_state_sets": H, "pcie_h2d_gbs": h2d / wall / 1e9, "pcie_d2h_gbs": d2h / wall / 1e9,
                    "pcie_total_gbs": (h2d + d2h) / wall / 1e9, "h2d_bytes_per_step": h2d,
@@ -772,6 +777,7 @@ def bench_elementwise(args):
         tot_bytes += nbytes
         tot_ms += ms
         log(f"[bench] {name}: {ms:.3f} ms, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.3f} of 8 TB/s)")
+    clocks = gpu_clocks()
     ceil = ew_ceiling(n, {"split": (w32, None, hi, lo), "join": (hi, lo, out, None),
                           "encode": (m32, None, code, scale), "decode": (code, scale, out, None)},
                       args.steps, stream)
@@ -786,7 +792,7 @@ def bench_elementwise(args):
         "value": tot_bytes / (tot_ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": tot_ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"elementwise_{n}", "elements": n, "kernels": res},
+        "config": {"workload": f"elementwise_{n}", "elements": n, "kernels": res, "gpu_clocks_after_timing": clocks},
         "roofline": {"bound": "hbm", "achieved": res[worst]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": res[worst]["frac"], "traffic": None, "kernel": worst},
         "cpu_baseline": None}), flush=True)
