@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -64,11 +65,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(src):
+    """Source text with comments removed and whitespace collapsed: what the
+    compiler sees of it, so that an edit to a comment does not change it."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash(sources=None):
+    """First 16 hex digits of the SHA-256 of the kernel sources' code text
+    (comments and whitespace removed), in the listed order. A committed
+    counter summary carries the hash of the sources it was taken on."""
     h = hashlib.sha256()
     for p in sources or KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

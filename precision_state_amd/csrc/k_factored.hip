@@ -240,8 +240,9 @@ __global__ __launch_bounds__(kT) void k_f_stats(FPlan P, FScalars S) {
 // buffers deep: two batches stay in flight while one is summed, and the
 // prefetch costs no registers. One barrier per batch publishes each wave's row
 // partials (a wave lies within one row because Ur % 64 == 0); lane d of every
-// wave then adds the partials of step d's row in wave order and forms that
-// row's EMA from the same double sum the finalize kernel uses. Column sums of
+// wave then adds the partials of step d's row in a fixed pairwise order and
+// forms that row's EMA from the same double sum the finalize kernel uses (the
+// sum it stores), with the same correctly rounded mean. Column sums of
 // q and of g^2 / r_i are in double; the threads of a step that share columns
 // add theirs in row order through LDS at the end of the group.
 
