@@ -653,22 +653,44 @@ __global__ __launch_bounds__(kT) void k_f_rowcol(FPlan P, FScalars S) {
 template <int NT>
 __device__ void clip_one(const FPlan& P, const FScalars& S, int idx, double* red);
 
+// Sum of a 2-D tensor's row-chunk sums rpart[0 .. nrw) (mean(r)'s numerator)
+// in an order that does not depend on the block size NT >= kT: thread t < kT
+// adds chunks t, t + kT, ... in turn, then a tree over the kT partials. The
+// factors and the clip factor both take mean(r) from it, so they agree bit
+// for bit, and a tall tensor costs each block nrw / kT loads, not nrw. Every
+// thread of the block must call it; all get the sum.
+template <int NT>
+__device__ __forceinline__ double rpart_sum(const F2D& X, double* red) {
+  static_assert(NT >= kT, "one partial per thread of the first kT");
+  if ((int)threadIdx.x < kT) {
+    double s = 0.0;
+    for (int q = (int)threadIdx.x; q < X.nrw; q += kT) s += X.rpart[q];
+    red[threadIdx.x] = s;
+  }
+  __syncthreads();
+  for (int o = kT / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  const double r = red[0];
+  __syncthreads();
+  return r;
+}
+
 // Workgroups past the factor ones (launched only when no U^2 pass runs, so
 // every sum of U^2 is complete after the finalize launch) take the clip
 // factors, one tensor each.
 __global__ __launch_bounds__(kT) void k_f_factors(FPlan P, FScalars S) {
+  __shared__ double red[kT];
   if (blockIdx.x >= P.n_rc) {   // uniform
-    __shared__ double red[kT];
     clip_one<kT>(P, S, (int)(blockIdx.x - P.n_rc), red);
     return;
   }
   uint32_t begin;
   const F2D& X = P.t2[find_end(P.rc_end, P.n2, blockIdx.x, begin)];
   const int w = (int)(blockIdx.x - begin);
-  if (w < X.nrw) {
-    double s = 0.0;
-    for (int q = 0; q < X.nrw; ++q) s += X.rpart[q];
-    const float rbar = (float)(s / (double)X.R);
+  if (w < X.nrw) {   // uniform
+    const float rbar = (float)(rpart_sum<kT>(X, red) / (double)X.R);
     const int i = w * kFRowColChunk + (int)threadIdx.x;
     if (i < X.R) {
       X.rho[i] = 1.0f / __builtin_sqrtf(X.row[i] / rbar);
@@ -1053,9 +1075,7 @@ __device__ __forceinline__ void clip_one(const FPlan& P, const FScalars& S, int 
   if (idx < P.n2) {
     const F2D& X = P.t2[idx];
     parts = X.upart; np = X.npart; n = (double)X.R * (double)X.C; f = X.f;
-    double s = 0.0;
-    for (int q = 0; q < X.nrw; ++q) s += X.rpart[q];
-    scale = s / (double)X.R;
+    scale = rpart_sum<NT>(X, red) / (double)X.R;
   } else {
     const F1D& X = P.t1[idx - P.n2];
     parts = X.upart; np = X.nitems; n = (double)X.n; f = X.f;

@@ -15,7 +15,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import DEV, compare_factored as _compare, dev_grad, dev_state, host_grad, host_state, ofhp as _ofhp
+from gpu_util import (DEV, compare_factored as _compare, dev_grad, dev_state, host_grad, host_state, ofhp as _ofhp,
+                      ulp_dist)
 
 pytestmark = pytest.mark.gpu
 
@@ -216,3 +217,64 @@ def test_factored_row_strip_threshold():
     hp = ps.FactoredHParams(lr=1e-4, clip_threshold=4.0, decay_rate=-0.8, seed=5)
     for rows in (16383 - 6, 16384 - 6):
         _run(base + [synth.Shape("d", rows, 512, rows * 512)], hp, 3, 23, 0.01)
+
+
+# ---------------------------------------------------------------------------
+# maximum sizes: one 2-D tensor beyond 2^31 elements. It takes neither the
+# row-strip pass nor flat items: statistics tiles, U^2 row tiles and apply
+# tiles, all with 64-bit element offsets, and R / 256 = 8129 row chunks in
+# mean(r).
+# ---------------------------------------------------------------------------
+
+def test_factored_tensor_beyond_2_31_elements():
+    """One [2080903, 1032] tensor (2,147,491,896 elements, about 13 GB of
+    weights, residuals and gradient with 0.1% outliers), one factored step
+    with weight decay, against the oracle on the same bytes (generated on the
+    device, copied to the host): every weight and residual, and the row and
+    column EMAs."""
+    import gc
+    R, C = 2080903, 1032
+    n = R * C
+    assert n > 1 << 31
+    gc.collect()
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    if free < 40 * 2**30:
+        pytest.skip(f"needs ~14 GiB of device memory, {free / 2**30:.0f} GiB free")
+    seed, tid = 29, 0
+    hi = torch.empty(n, dtype=torch.int16, device=DEV)
+    lo = torch.empty(n, dtype=torch.int16, device=DEV)
+    synth.dev_bf16_normal(hi, seed, synth.STREAM_HI, tid, 0, synth.SIGMA_W)
+    synth.dev_u16_uniform(lo, seed, synth.STREAM_LO, tid, 0)
+    g = dev_grad(n, seed, tid, 1, 0.001)
+    st = ps.TensorState(hi, lo, rows=R, cols=C)
+    st.row_ema = torch.zeros(R, dtype=torch.float32, device=DEV)
+    st.col_ema = torch.zeros(C, dtype=torch.float32, device=DEV)
+    host = oracle.TensorState(hi.cpu().numpy().view(np.uint16), lo.cpu().numpy().view(np.uint16))
+    host.row, host.col = np.zeros(R, np.float32), np.zeros(C, np.float32)
+    g_host = g.cpu().numpy().view(np.uint16)
+    print("  inputs on device and host", flush=True)
+
+    hp = ps.FactoredHParams(lr=1e-4, weight_decay=0.01, seed=7)
+    recs = ps.make_records([st], [g])
+    ws = torch.empty(ps.factored_workspace_size(None, records=recs), dtype=torch.uint8, device=DEV)
+    ps.factored_step(None, None, hp, 1, workspace=ws, records=recs)
+    torch.cuda.synchronize()
+    del g, ws
+    print("  device step done", flush=True)
+    oracle.factored_step(host, g_host, R, C, _ofhp(hp, 0), 1)
+    del g_host
+    print("  oracle step done", flush=True)
+
+    rd = np.concatenate([ulp_dist(st.row_ema.cpu().numpy(), host.row), ulp_dist(st.col_ema.cpu().numpy(), host.col)])
+    assert rd.max() <= 1, ("row/col EMA ulp", int(rd.max()))
+    d_hi = st.w_hi.cpu().numpy().view(np.uint16)
+    d_lo = st.w_lo.cpu().numpy().view(np.uint16)
+    bad = np.flatnonzero((d_hi != host.hi) | (d_lo != host.lo))
+    worst = 0
+    if bad.size:
+        wd = oracle.join(d_hi[bad], d_lo[bad]).view(np.uint32)
+        wh = oracle.join(host.hi[bad], host.lo[bad]).view(np.uint32)
+        worst = int(ulp_dist(wd, wh).max())
+    print(f"  {n - bad.size} of {n} weights bit-identical, max {worst} ulp; EMAs max {int(rd.max())} ulp", flush=True)
+    assert worst <= 4
