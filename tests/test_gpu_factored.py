@@ -184,6 +184,19 @@ def test_single_one_d_tensor_calls(split_mode):
         _compare(d, h, 0, shape.name, first_moment=True)
 
 
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_STOCHASTIC])
+def test_one_d_only_lists(split_mode):
+    """Lists of 1-D tensors only (no 2-D tensor, so no statistics or strip
+    pass: the stats items ride the finalize launch and the clip factors the
+    factor launch): ragged sizes from 1 to 32768 elements, then the same list
+    with a tensor of 34 items added; a zero gradient, first moment and
+    schedule, 4 steps, every tensor against the oracle."""
+    small = [synth.Shape(f"v{n}", 0, 0, n) for n in (1, 128, 255, 1024, 1025, 3072, 9216, 32768)]
+    hp = ps.FactoredHParams(split_mode=split_mode, lr=1e-4, weight_decay=0.01, decay_rate=-0.8, beta1=0.9, seed=41)
+    _run(small, hp, 4, 37, 0.01, zero_grad=(2,))
+    _run(small + [synth.Shape("v33793", 0, 0, 33793)], hp, 4, 37, 0.01, zero_grad=(2,))
+
+
 # Row-strip stats pass (C % 512 == 0, C <= 12288; taken when the list's
 # eligible tensors have at least 256 x 64 rows): 12, 6, 2 and 1 rows per
 # step, idle waves (C = 4096), a partial second run per thread (C = 8192), two
