@@ -21,8 +21,11 @@ Reported:
              the same state, timed the same way right after the step: the
              rate this memory system gives that 5-read/4-write 16-byte mix;
              frac_of_practical is the step's share of it
-  cpu_baseline  the C oracle, single-threaded, on a bounded sample of the
-             same workload (the leading tensors of the set, one step)
+  cpu_baseline  the C oracle as it stands on a bounded sample of the same
+             workload, on one thread and on the host threads (the leading
+             tensors of the set for the NAdam step, here and in the
+             per-tensor and offload modes; the whole double block for the
+             factored step; 2^24 elements for the standalone kernels)
 """
 import argparse
 import hashlib
@@ -358,6 +361,106 @@ def cpu_baseline(shapes, seed, target_params=60_000_000, weight_decay=0.0):
                       f"single thread {total / dt1:.3e} params/s ({dt1:.1f} s)"}
 
 
+def cpu_baseline_factored(shapes, seed, hp):
+    """The oracle's factored step as it stands, one step over every tensor of
+    the set: timed on one thread, then on this process's host threads with one
+    tensor per task (each tensor's step is independent; ctypes releases the
+    GIL during each call). The oracle itself is unchanged."""
+    import concurrent.futures
+    import dataclasses
+
+    import numpy as np
+
+    import oracle
+    import synth
+    ohp = oracle.FHParams(hp.split_mode, hp.lr, hp.beta2, hp.eps1, hp.clip_threshold, hp.weight_decay,
+                          hp.decay_rate, hp.beta1, hp.seed, 0)
+    inputs = []
+    for tid, s in enumerate(shapes):
+        n = s.numel
+        st = oracle.TensorState(synth.host_bf16_normal(n, seed, synth.STREAM_HI, tid, 0, synth.SIGMA_W),
+                                synth.host_u16_uniform(n, seed, synth.STREAM_LO, tid, 0))
+        if s.is_2d:
+            st.row, st.col = np.zeros(s.rows, np.float32), np.zeros(s.cols, np.float32)
+        else:
+            _, _, st.vc, st.vs = oracle.zero_moments(n)
+        if hp.beta1:
+            st.mc, st.ms, _, _ = oracle.zero_moments(n)
+        g = synth.host_bf16_normal(n, seed, synth.STREAM_GRAD, tid, 1, synth.SIGMA_G, 0.001, 100.0)
+        inputs.append((tid, s, st, g))
+    copies = [(tid, s, st.copy(), g) for tid, s, st, g in inputs]
+
+    def one(item):
+        tid, s, st, g = item
+        oracle.factored_step(st, g, s.rows, s.cols, dataclasses.replace(ohp, tensor=tid), 1)
+
+    t0 = time.perf_counter()
+    for item in inputs:
+        one(item)
+    dt1 = time.perf_counter() - t0
+    threads = min(host_threads(), len(copies))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as pool:
+        t0 = time.perf_counter()
+        list(pool.map(one, sorted(copies, key=lambda it: -it[1].numel)))   # largest first
+        dtn = time.perf_counter() - t0
+    for (_, _, x, _), (_, _, y, _) in zip(inputs, copies):   # the threaded run must give the same bytes
+        if not (np.array_equal(x.hi, y.hi) and np.array_equal(x.lo, y.lo)):
+            raise RuntimeError("threaded oracle run differs from the single-thread run")
+    total = sum(s.numel for s in shapes)
+    return {"value": total / dtn, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "sample": f"all {len(shapes)} tensors of the set ({total} params), one factored step, {threads} threads "
+                      f"with one tensor per task, {dtn:.2f} s; single thread {total / dt1:.3e} params/s ({dt1:.1f} s)"}
+
+
+def cpu_baseline_elementwise(seed, n=1 << 24):
+    """The oracle's split and join (both modes) and moment encode and decode
+    (both kinds) as they stand, on n elements of the same values as the GPU
+    run: timed on one thread, then on this process's host threads over
+    block-aligned chunks. Value: algorithmic GB/s over the eight calls, as the
+    GPU line counts them."""
+    import concurrent.futures
+
+    import numpy as np
+
+    import oracle
+    import synth
+    hi = synth.host_bf16_normal(n, seed, synth.STREAM_HI, 0, 0, synth.SIGMA_W)
+    lo = synth.host_u16_uniform(n, seed, synth.STREAM_LO, 0, 0)
+    w = oracle.join(hi, lo)
+    m = w * np.float32(1e-3)
+    v = m * m
+    cs, ss = oracle.encode(m, oracle.SIGNED)
+    cu, su = oracle.encode(v, oracle.UNSIGNED)
+    nb = (n + 255) // 256
+
+    def blk(a, b):
+        return slice(a // 256, (b + 255) // 256)
+    ops = [(lambda a, b: oracle.split(w[a:b], oracle.SPLIT_TRUNC), 8 * n),
+           (lambda a, b: oracle.join(hi[a:b], lo[a:b], oracle.SPLIT_TRUNC), 8 * n),
+           (lambda a, b: oracle.split(w[a:b], oracle.SPLIT_NEAREST_AWAY), 8 * n),
+           (lambda a, b: oracle.join(hi[a:b], lo[a:b], oracle.SPLIT_NEAREST_AWAY), 8 * n),
+           (lambda a, b: oracle.encode(m[a:b], oracle.SIGNED), 6 * n + 4 * nb),
+           (lambda a, b: oracle.decode(cs[a:b], ss[blk(a, b)], oracle.SIGNED), 6 * n + 4 * nb),
+           (lambda a, b: oracle.encode(v[a:b], oracle.UNSIGNED), 6 * n + 4 * nb),
+           (lambda a, b: oracle.decode(cu[a:b], su[blk(a, b)], oracle.UNSIGNED), 6 * n + 4 * nb)]
+    total = sum(nbytes for _, nbytes in ops)
+    t0 = time.perf_counter()
+    for fn, _ in ops:
+        fn(0, n)
+    dt1 = time.perf_counter() - t0
+    chunk = 1 << 20
+    threads = host_threads()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as pool:
+        t0 = time.perf_counter()
+        for fn, _ in ops:
+            list(pool.map(lambda a: fn(a, min(n, a + chunk)), range(0, n, chunk)))
+        dtn = time.perf_counter() - t0
+    return {"value": total / dtn / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} elements, the eight calls, {threads} threads over {(n + chunk - 1) // chunk} "
+                      f"block-aligned chunks each, {dtn:.2f} s; single thread {total / dt1 / 1e9:.3f} GB/s "
+                      f"({dt1:.1f} s)"}
+
+
 def calibrate_copy(gib, stream, dev):
     """Three plain device copies of `gib` GiB (the counter calibration of the
     profiles: a copy's FETCH_SIZE and WRITE_SIZE against the bytes it moves);
@@ -453,6 +556,11 @@ def bench_factored(args):
     strip = strip if sum(s.rows for s in strip) >= 256 * 64 else []
     rereads = sum(2 * s.numel for s in shapes) + sum(2 * s.numel for s in shapes if s.is_2d and s not in strip)
     gbs_design = (alg + rereads) / (step_ms * 1e-3) / 1e9
+    baseline = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host (cpu_baseline)")
+        baseline = cpu_baseline_factored(shapes, args.seed, hp)
+        log(f"[bench] cpu_baseline: {baseline}")
     traffic = None
     if not args.beta1 and not args.decay_rate and split == ps.SPLIT_TRUNC and wl == "flux_double_block":
         traffic = read_counter_summary("factored_step_flux_double_block_counters.txt", "hbm_bytes_per_step",
@@ -470,7 +578,7 @@ def bench_factored(args):
                    "copy_gbs": copy_gbs},
         "roofline": {"bound": "hbm", "achieved": gbs10, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs10 / PEAK_HBM_GBS, "traffic": traffic},
-        "cpu_baseline": None}), flush=True)
+        "cpu_baseline": baseline}), flush=True)
 
 
 def time_factored_per_tensor(ps, states, grads, hp, ws, stream, step, steps):
@@ -587,6 +695,13 @@ def bench_per_tensor(args):
     lat["empty_list"] = {"host_us_per_call": (time.perf_counter() - t0) * 1e6 / 2000}
     log(f"[bench] empty list (binding + validation only): {lat['empty_list']}")
     pt = res["per_tensor"]
+    # the same bytes as the single launch: the roofline of the per-tensor calls' GPU time
+    alg = sum(step_bytes(sh.numel, st.flags) for sh, st in zip(shapes, states))
+    gbs = alg / (pt["gpu_ms"] * 1e-3) / 1e9
+    baseline = None
+    if not args.no_cpu_baseline:   # the same NAdam step as the headline's, so the same oracle sample
+        log("[bench] timing the oracle on the host (cpu_baseline)")
+        baseline = cpu_baseline(shapes, args.seed)
     print(json.dumps({
         "metric": "per-hook optimizer step: params/sec with one call per tensor (FLUX-12B set)",
         "value": n_params / (pt["wall_ms"] * 1e-3), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
@@ -597,8 +712,10 @@ def bench_per_tensor(args):
                    "policy": {"fp32_moment_tensors": n_small, "fp32_param_tensors": n_final} if args.policy else None,
                    "per_tensor": pt, "one_launch": res["one_launch"],
                    "per_tensor_over_one_launch": pt["wall_ms"] / res["one_launch"]["wall_ms"],
-                   "small_tensor_calls": {str(k): v for k, v in lat.items()}},
-        "roofline": None, "cpu_baseline": None}), flush=True)
+                   "small_tensor_calls": {str(k): v for k, v in lat.items()}, "algorithmic_bytes": alg},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+        "cpu_baseline": baseline}), flush=True)
 
 
 def pcie_ceiling(dev, nbytes=2 << 30):
@@ -719,6 +836,10 @@ def bench_offload(args, n_blocks=57):
     h2d, d2h = plan.bytes()       # of the last run (no residuals under stochastic rounding)
     log(f"[bench] offload ({args.offload_mode}): {n_blocks} blocks, {wall * 1e3:.1f} ms/step, PCIe {h2d / wall / 1e9:.1f} GB/s up + "
         f"{d2h / wall / 1e9:.1f} GB/s down")
+    baseline = None
+    if not args.no_cpu_baseline:   # the offloaded step is the resident NAdam step: the same oracle on one block
+        log("[bench] timing the oracle on the host (cpu_baseline)")
+        baseline = cpu_baseline(shapes, args.seed)
     print(json.dumps({
         "metric": "offloaded optimizer-updated params/sec (host-resident residuals and moments over PCIe)",
         "value": n_params / wall, "unit": "params/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -734,7 +855,7 @@ def bench_offload(args, n_blocks=57):
                    "frac_of_duplex_ceiling": min(h2d, d2h) / wall / 1e9 / pcie["dup_h2d"]},
         "roofline": {"bound": "pcie", "achieved": (h2d + d2h) / wall / 1e9, "peak": 128.0, "unit": "GB/s",
                      "frac": (h2d + d2h) / wall / 1e9 / 128.0, "traffic": None},
-        "cpu_baseline": None}), flush=True)
+        "cpu_baseline": baseline}), flush=True)
     plan.close()
 
 
@@ -799,6 +920,11 @@ def bench_elementwise(args):
             r["practical_peak_gbs"] = r["bytes"] / (c["ms"] * 1e-3) / 1e9
             r["frac_of_practical"] = c["ms"] / r["ms"]
     worst = min(res, key=lambda k: res[k]["gbs"])
+    baseline = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host (cpu_baseline)")
+        baseline = cpu_baseline_elementwise(args.seed)
+        log(f"[bench] cpu_baseline: {baseline}")
     print(json.dumps({
         "metric": "standalone split/join/encode/decode: algorithmic HBM GB/s over the eight kernels",
         "value": tot_bytes / (tot_ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -807,7 +933,7 @@ def bench_elementwise(args):
         "config": {"workload": f"elementwise_{n}", "elements": n, "kernels": res, "gpu_clocks_after_timing": clocks},
         "roofline": {"bound": "hbm", "achieved": res[worst]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": res[worst]["frac"], "traffic": None, "kernel": worst},
-        "cpu_baseline": None}), flush=True)
+        "cpu_baseline": baseline}), flush=True)
 
 
 def main():
