@@ -291,3 +291,34 @@ def test_factored_tensor_beyond_2_31_elements():
         worst = int(ulp_dist(wd, wh).max())
     print(f"  {n - bad.size} of {n} weights bit-identical, max {worst} ulp; EMAs max {int(rd.max())} ulp", flush=True)
     assert worst <= 4
+
+
+def test_factored_steps_are_deterministic():
+    """The same three steps run twice from the same state (the double-block
+    shapes, whose 2-D tensors take the row-strip pass, plus a tile-path
+    tensor and ragged 1-D tensors; first moment, schedule, stochastic
+    rounding): every output byte is equal, with a fresh workspace the first
+    time and the first run's workspace, still holding its values, the second.
+    All reductions are fixed trees, so no run-to-run variation is allowed."""
+    shapes = synth.WORKLOADS["flux_double_block"]() + [synth.Shape("t", 300, 1000, 300000),
+                                                       synth.Shape("v", 0, 0, 4097)]
+    hp = ps.FactoredHParams(split_mode=ps.SPLIT_STOCHASTIC, lr=1e-4, weight_decay=0.01, decay_rate=-0.8,
+                            beta1=0.9, seed=11)
+    grads = {t: [dev_grad(s.numel, 43, i, t, 0.001) for i, s in enumerate(shapes)] for t in (1, 2, 3)}
+    ws = None
+    outs = []
+    for run in range(2):
+        devs = [dev_state(s.numel, 43, i, s.rows, s.cols, factored=True) for i, s in enumerate(shapes)]
+        for t in (1, 2, 3):
+            recs = ps.make_records(devs, grads[t])
+            if ws is None:
+                ws = torch.zeros(ps.factored_workspace_size(None, records=recs), dtype=torch.uint8, device=DEV)
+            ps.factored_step(None, None, hp, t, workspace=ws, records=recs)
+        torch.cuda.synchronize()
+        outs.append([[a.clone() for a in (d.w_hi, d.w_lo, d.m_code, d.m_scale,
+                                         d.row_ema if d.row_ema is not None else d.v_code,
+                                         d.col_ema if d.col_ema is not None else d.v_scale)] for d in devs])
+        del devs
+    for i, (a, b) in enumerate(zip(*outs)):
+        for k, (x, y) in enumerate(zip(a, b)):
+            assert torch.equal(x, y), (shapes[i].name, k)
