@@ -221,6 +221,17 @@ def test_factored_row_strip_shapes(split_mode, beta1):
     _run(STRIP, hp, 4, 17, 0.01, zero_grad=(2,))
 
 
+@pytest.mark.parametrize("eps1", [1e-40, 1e-3])
+def test_factored_eps1_extremes(eps1):
+    """eps1 at a subnormal fp32 value (rows of zero gradient then carry
+    subnormal q, row EMAs near 1e-43 and 1/r_i near 1e43 through the row-strip
+    pass, the tiles and the 1-D path) and at 1e-3 (eps1 dominates q): the
+    strip shapes, zero gradients in two tensors, 3 steps, every tensor against
+    the oracle."""
+    hp = ps.FactoredHParams(lr=1e-4, eps1=eps1, weight_decay=0.01, seed=3)
+    _run(STRIP, hp, 3, 19, 0.01, zero_grad=(2, 5))
+
+
 def test_factored_row_strip_threshold():
     """The same strip-eligible shapes in a list of 16383 rows (statistics
     tiles) and of 16384 rows (row-strip pass), clip threshold 4 with the
