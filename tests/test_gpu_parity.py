@@ -188,6 +188,41 @@ def test_step_variants(algo, wd, split_mode):
     _assert_exact(dev, host, f"algo {algo} wd {wd} split {split_mode}")
 
 
+# Gradient magnitudes far from the default: subnormal v (below 2^-96, where a
+# wave takes the library square root, and block maxima flushed to 0), large
+# finite g (g^2 near 1e33), exact zeros, and one tensor at the default scale.
+EXTREME_SIGMAS = [1e-20, 1e-3, 1e16, 0.0]
+EXTREME_HPARAMS = [dict(algo=ps.ALGO_NADAM, beta1=0.0, beta2=0.5, eps=1e-30, lr=1.0, weight_decay=0.1,
+                        momentum_decay=0.0),
+                   dict(algo=ps.ALGO_NADAM, beta1=0.99, beta2=0.9999, eps=1.0, lr=1e-6, weight_decay=0.0,
+                        momentum_decay=0.1),
+                   dict(algo=ps.ALGO_ADAM, beta1=0.5, beta2=0.0, eps=1e-12, lr=0.1, weight_decay=0.5)]
+
+
+@pytest.mark.parametrize("split_mode", [ps.SPLIT_TRUNC, ps.SPLIT_NEAREST_AWAY, ps.SPLIT_STOCHASTIC])
+@pytest.mark.parametrize("which", range(len(EXTREME_HPARAMS)))
+def test_step_extreme_magnitudes_and_hparams(which, split_mode):
+    """Extreme hyperparameters (beta1 0 or 0.99, beta2 0 to 0.9999, eps from
+    1e-30 to 1, lr up to 1, heavy weight decay, the NAdam momentum decay) on a
+    list whose tensors' gradients are N(0, sigma) with sigma 1e-20, 1e-3, 1e16
+    and 0; ragged sizes, 4 steps, every byte against the oracle."""
+    hp = ps.HParams(split_mode=split_mode, seed=5 + which, **EXTREME_HPARAMS[which])
+    sizes = [5000, 70001, 3000, 1025]
+    devs = [dev_state(n, 8, i) for i, n in enumerate(sizes)]
+    hosts = [host_state(n, 8, i) for i, n in enumerate(sizes)]
+    for t in range(1, 5):
+        grads = []
+        for i, (n, sigma) in enumerate(zip(sizes, EXTREME_SIGMAS)):
+            g = torch.empty(n, dtype=torch.int16, device=DEV)
+            synth.dev_bf16_normal(g, 8, synth.STREAM_GRAD, i, t, sigma)
+            grads.append(g)
+            oracle.opt_step(hosts[i], synth.host_bf16_normal(n, 8, synth.STREAM_GRAD, i, t, sigma), ohp(hp, i), t)
+        ps.opt_step_multi(devs, grads, hp, t)
+    torch.cuda.synchronize()
+    for i, sigma in enumerate(EXTREME_SIGMAS):
+        _assert_exact(devs[i], hosts[i], f"hparams {which} split {split_mode} sigma {sigma}")
+
+
 RAGGED = [0, 1, 7, 8, 64, 128, 255, 256, 257, 1000, 1023, 1024, 1025, 3000, 4096, 65539, 131089]
 
 
