@@ -352,9 +352,26 @@ def test_storage_flags_match_oracle(split_mode, large):
     elements on the pages), f24 moments and fp32 parameters (the final
     layer), ragged sizes, both the kernel-argument and the device-table
     paths, 3 NAdamW steps; bit-exact against the oracle."""
+    hp = ps.HParams(algo=ps.ALGO_NADAM, weight_decay=0.01, lr=1e-4, split_mode=split_mode, seed=77)
+    _storage_flags_run(hp, large, (synth.SIGMA_G,))
+
+
+@pytest.mark.parametrize("split_mode,large,which", [(ps.SPLIT_TRUNC, ps.TENSOR_F24_MOMENTS, 0),
+                                                    (ps.SPLIT_STOCHASTIC, ps.TENSOR_F24_MOMENTS, 2),
+                                                    (ps.SPLIT_NEAREST_AWAY, 0, 1)])
+def test_storage_flags_extreme_scales(split_mode, large, which):
+    """The same mixed-format list with the extreme hyperparameters and the
+    gradient scales 1e-20, 1e-3, 1e16 and 0 taken in turn by its tensors:
+    subnormal and near-1e33 moments through fp32, f24 and the codec, and
+    through fp32 parameters; bit-exact against the oracle."""
+    hp = ps.HParams(split_mode=split_mode, seed=21 + which, **EXTREME_HPARAMS[which])
+    _storage_flags_run(hp, large, EXTREME_SIGMAS)
+
+
+def _storage_flags_run(hp, large, sigmas):
+    split_mode = hp.split_mode
     sizes = [64, 128, 3072, 4096, 1000, 300001, 257, 18432, 3000, 5, 6144 * 8, 2048, 100, 4096, 77, 65536, 999]
     flag_of = _flag_mix(sizes, large)
-    hp = ps.HParams(algo=ps.ALGO_NADAM, weight_decay=0.01, lr=1e-4, split_mode=split_mode, seed=77)
     for count in (len(sizes), 9):
         devs, hosts = [], []
         for i, (n, fl) in enumerate(zip(sizes[:count], flag_of[:count])):
@@ -387,7 +404,7 @@ def test_storage_flags_match_oracle(split_mode, large):
         for t in range(1, 4):
             grads_d, grads_h = [], []
             for i, (n, fl) in enumerate(zip(sizes[:count], flag_of[:count])):
-                g16 = synth.host_bf16_normal(n, 13, synth.STREAM_GRAD, i, t, synth.SIGMA_G)
+                g16 = synth.host_bf16_normal(n, 13, synth.STREAM_GRAD, i, t, sigmas[i % len(sigmas)])
                 if fl & ps.TENSOR_FP32_PARAM:
                     g32 = oracle.bf16_to_f32(g16).copy()
                     grads_h.append(g32)
