@@ -81,15 +81,15 @@ def host_state(numel, seed=0, tid=0, rows=0, factored=False, cols=0):
     return st
 
 
-def dev_grad(numel, seed, tid, step, outlier_p=0.0):
+def dev_grad(numel, seed, tid, step, outlier_p=0.0, sigma=SIGMA_G):
     T = torch()
     g = T.empty(numel, dtype=T.int16, device=DEV)
-    synth.dev_bf16_normal(g, seed, STREAM_GRAD, tid, step, SIGMA_G, outlier_p, 100.0)
+    synth.dev_bf16_normal(g, seed, STREAM_GRAD, tid, step, sigma, outlier_p, 100.0)
     return g
 
 
-def host_grad(numel, seed, tid, step, outlier_p=0.0):
-    return synth.host_bf16_normal(numel, seed, STREAM_GRAD, tid, step, SIGMA_G, outlier_p, 100.0)
+def host_grad(numel, seed, tid, step, outlier_p=0.0, sigma=SIGMA_G):
+    return synth.host_bf16_normal(numel, seed, STREAM_GRAD, tid, step, sigma, outlier_p, 100.0)
 
 
 def to_host(st):

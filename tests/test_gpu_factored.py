@@ -32,7 +32,7 @@ import precision_state_amd as ps  # noqa: E402
 _POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
 
 
-def _run(shapes, hp, steps, seed, outlier_p, check=None, zero_grad=()):
+def _run(shapes, hp, steps, seed, outlier_p, check=None, zero_grad=(), sigmas=(synth.SIGMA_G,)):
     devs = [dev_state(s.numel, seed, i, s.rows, s.cols, factored=True) for i, s in enumerate(shapes)]
     check = list(range(len(shapes)) if check is None else check)
     hosts = {i: host_state(shapes[i].numel, seed, i, shapes[i].rows, factored=True, cols=shapes[i].cols)
@@ -41,12 +41,13 @@ def _run(shapes, hp, steps, seed, outlier_p, check=None, zero_grad=()):
 
     def oracle_step(i, t):
         s = shapes[i]
-        g = np.zeros(s.numel, np.uint16) if i in zero_grad else host_grad(s.numel, seed, i, t, outlier_p)
+        g = (np.zeros(s.numel, np.uint16) if i in zero_grad else
+             host_grad(s.numel, seed, i, t, outlier_p, sigmas[i % len(sigmas)]))
         oracle.factored_step(hosts[i], g, s.rows, s.cols, _ofhp(hp, i), t)
 
     for t in range(1, steps + 1):
         dg = [torch.zeros(s.numel, dtype=torch.int16, device=DEV) if i in zero_grad else
-              dev_grad(s.numel, seed, i, t, outlier_p) for i, s in enumerate(shapes)]
+              dev_grad(s.numel, seed, i, t, outlier_p, sigmas[i % len(sigmas)]) for i, s in enumerate(shapes)]
         recs = ps.make_records(devs, dg)
         need = ps.factored_workspace_size(None, records=recs)
         if ws is None or ws.numel() < need:
@@ -230,6 +231,17 @@ def test_factored_eps1_extremes(eps1):
     the oracle."""
     hp = ps.FactoredHParams(lr=1e-4, eps1=eps1, weight_decay=0.01, seed=3)
     _run(STRIP, hp, 3, 19, 0.01, zero_grad=(2, 5))
+
+
+@pytest.mark.parametrize("split_mode,beta1", [(ps.SPLIT_TRUNC, 0.0), (ps.SPLIT_STOCHASTIC, 0.9)])
+def test_factored_extreme_gradient_scales(split_mode, beta1):
+    """Gradients N(0, sigma) with sigma 1e-20 (g^2 subnormal in fp32, so q is
+    eps1 plus a subnormal), 1e16 (g^2 near 1e33, row sums near 1e37) and 1e-3
+    taken in turn by the strip shapes' tensors, lr 0.1, clip 0.5, the
+    schedule: 3 steps, every tensor against the oracle."""
+    hp = ps.FactoredHParams(split_mode=split_mode, lr=0.1, clip_threshold=0.5, weight_decay=0.01,
+                            decay_rate=-0.8, beta1=beta1, seed=9)
+    _run(STRIP, hp, 3, 27, 0.0, sigmas=(1e-20, 1e16, 1e-3))
 
 
 def test_factored_row_strip_threshold():
