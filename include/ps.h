@@ -131,10 +131,13 @@ typedef struct ps_tensor {
  * 0x9E3779B97F4A7C15): for the tensor at index i of the list and update
  * `step`, the stream starts at s = mix(seed ^ mix((step mod 2^32) << 32 | i));
  * element e takes bits 16*(e % 4) .. 16*(e % 4) + 15 of mix(s + (e/4 + 1) * G).
- * The same (seed, step, list position) always gives the same bits.
- * Supported by ps_opt_step_multi only; ps_split, ps_join and the offload
- * pipeline return PS_ERR_UNSUPPORTED for it. `seed` is not read in the other
- * modes. */
+ * The same (seed, step, list position) always gives the same bits, so a
+ * caller that steps one tensor per call (position 0 every time, as from a
+ * gradient hook) should give each tensor a seed of its own, or all of them
+ * draw the same stream. Supported by ps_opt_step_multi, the factored step
+ * (ps_factored_hparams.seed) and the offload pipeline (which then moves no
+ * residual); ps_split and ps_join return PS_ERR_UNSUPPORTED for it. `seed`
+ * is not read in the other modes. */
 typedef struct ps_hparams {
   int32_t algo;
   int32_t split_mode;
