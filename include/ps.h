@@ -277,7 +277,7 @@ ps_status ps_factored_step(const ps_tensor* tensors, int32_t n_tensors, const ps
  * call on each device). The plan, rounded up to 256 bytes, plus
  * ps_factored_workspace_size must fit in it, else the call returns
  * PS_ERR_WORKSPACE before any device work; one FLUX double block (24 tensors,
- * 21.8 MiB of workspace) fits. The plan reaches the scratch through kernel
+ * 22.0 MiB of workspace) fits. The plan reaches the scratch through kernel
  * arguments, so the call makes no copy from host memory either. Same kernels
  * and results as ps_factored_step; the scratch's contents on entry are
  * ignored. Every call on one GPU uses that GPU's single scratch array: calls
