@@ -21,6 +21,17 @@ LIB_PATH = os.path.join(_HERE, "libps.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
 
+# libps.so needs libamdhip64.so.7. PyTorch ships a HIP runtime of its own:
+# with torch loaded first the library binds to that one, and the process has a
+# single HIP runtime whose device pointers and streams both sides share.
+# Loaded first, the library would map the system runtime and torch its own
+# afterwards: two runtimes on one GPU, each unable to use the other's memory
+# and streams. So torch is imported before the library whenever it exists.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 ALGO_ADAM, ALGO_NADAM = 0, 1

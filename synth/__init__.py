@@ -20,6 +20,10 @@ def lib():
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build()")
+        try:   # torch's HIP runtime first, so that the library binds to it (one runtime per process)
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(_LIB_PATH)
         L.syn_host_fill_bf16_normal.argtypes = [_vp, _i64, _i64, _u64, _u64, _u64, _u64, _f64, _f64, _f64]
         L.syn_host_fill_bf16_normal.restype = None

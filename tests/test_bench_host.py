@@ -2,13 +2,13 @@
 byte counts behind its roofline figures, and the kernel-source hash that
 decides whether a committed counter summary still describes the kernels."""
 import bench
-import precision_state_amd as ps
 
 
 def test_step_bytes_per_format():
     """Read hi, lo, grad, m, v and write hi, lo, m, v: 18 B per element, plus
     two scales read and written (16 B) per 256-block, a partial block counted
     whole; the storage formats change only their own streams."""
+    import precision_state_amd as ps   # here, not at collection: only when the test runs
     assert bench.step_bytes(256) == 18 * 256 + 16
     assert bench.step_bytes(257) == 18 * 257 + 2 * 16
     assert bench.step_bytes(256, 0, residual=False) == 14 * 256 + 16          # stochastic rounding
